@@ -1,0 +1,8 @@
+"""Plain fp64 CPU oracle for the ButterflyMoE expert-layer forward.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it. The HIP library never
+calls into it, and it shares no code, table or constant generator with the
+HIP path.
+"""
+from .bmoe_oracle import *  # noqa: F401,F403
