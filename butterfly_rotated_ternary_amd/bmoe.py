@@ -1,0 +1,164 @@
+"""Thin ctypes binding of libbmoe.so (declared in include/bmoe.h).
+
+Argument marshalling only: every step of the forward runs in the library's
+HIP kernels. torch supplies device memory and the current stream. There is
+no CPU fallback: if the library is missing, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbmoe.so")
+_lib = None
+
+BMOE_F32 = 0
+BMOE_BF16 = 1
+
+STATUS = {
+    0: "BMOE_OK", 1: "BMOE_E_NULL", 2: "BMOE_E_SHAPE", 3: "BMOE_E_DTYPE",
+    4: "BMOE_E_TERNARY", 5: "BMOE_E_EXPERT", 6: "BMOE_E_WORKSPACE", 7: "BMOE_E_HIP",
+    8: "BMOE_E_ALIGN",
+}
+
+
+class BmoeError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(code, code)} ({lib().bmoe_status_str(code).decode()})")
+        self.code = code
+
+
+def lib():
+    """Load libbmoe.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m butterfly_rotated_ternary_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        c_int, c_sz, vp, c_f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+        L.bmoe_packed_words.argtypes = [c_int]
+        L.bmoe_packed_words.restype = c_sz
+        L.bmoe_param_count.argtypes = [c_int, c_int]
+        L.bmoe_param_count.restype = c_sz
+        L.bmoe_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
+        L.bmoe_workspace_bytes.restype = c_sz
+        L.bmoe_pack_workspace_bytes.argtypes = []
+        L.bmoe_pack_workspace_bytes.restype = c_sz
+        L.bmoe_pack_ternary.argtypes = [vp, c_int, vp, vp, c_sz, vp]
+        L.bmoe_pack_ternary.restype = c_int
+        L.bmoe_forward.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp, c_f,
+                                   vp, vp, c_sz, vp, vp]
+        L.bmoe_forward.restype = c_int
+        L.bmoe_sync_status.argtypes = [vp, vp]
+        L.bmoe_sync_status.restype = c_int
+        L.bmoe_status_str.argtypes = [c_int]
+        L.bmoe_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise BmoeError(code, what)
+
+
+# ---- the C entry points, same names -------------------------------------
+
+def bmoe_packed_words(d: int) -> int:
+    return lib().bmoe_packed_words(d)
+
+
+def bmoe_param_count(d: int, n_experts: int) -> int:
+    return lib().bmoe_param_count(d, n_experts)
+
+
+def bmoe_workspace_bytes(dt: int, T: int, d: int, n_experts: int, k: int) -> int:
+    return lib().bmoe_workspace_bytes(dt, T, d, n_experts, k)
+
+
+def bmoe_pack_workspace_bytes() -> int:
+    return lib().bmoe_pack_workspace_bytes()
+
+
+def bmoe_pack_ternary(w: torch.Tensor, d: int, packed: torch.Tensor, ws: torch.Tensor,
+                      stream=None) -> int:
+    return lib().bmoe_pack_ternary(_ptr(w), d, _ptr(packed), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream))
+
+
+def bmoe_forward(dt: int, T: int, d: int, n_experts: int, k: int, x, ids, gates, theta, phi,
+                 w_packed, alpha: float, y, ws, route_out=None, stream=None) -> int:
+    return lib().bmoe_forward(dt, T, d, n_experts, k, _ptr(x), _ptr(ids), _ptr(gates), _ptr(theta),
+                              _ptr(phi), _ptr(w_packed), float(alpha), _ptr(y), _ptr(ws),
+                              ws.numel() * ws.element_size(), _ptr(route_out), _stream(stream))
+
+
+def bmoe_sync_status(ws: torch.Tensor, stream=None) -> int:
+    return lib().bmoe_sync_status(_ptr(ws), _stream(stream))
+
+
+def bmoe_status_str(code: int) -> str:
+    return lib().bmoe_status_str(code).decode()
+
+
+# ---- conveniences over the entry points (allocation + error checks) -------
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BMOE_BF16
+    if t.dtype == torch.float32:
+        return BMOE_F32
+    raise TypeError(f"x must be float32 or bfloat16, got {t.dtype}")
+
+
+def pack_ternary(w: torch.Tensor) -> torch.Tensor:
+    """int8 [d][d] device tensor -> packed uint32 words (as int32 storage)."""
+    d = w.shape[0]
+    n = bmoe_packed_words(d)
+    if n == 0:
+        raise BmoeError(2, "bmoe_pack_ternary")
+    packed = torch.empty(n, dtype=torch.int32, device=w.device)
+    ws = torch.empty(bmoe_pack_workspace_bytes(), dtype=torch.uint8, device=w.device)
+    _check(bmoe_pack_ternary(w.contiguous(), d, packed, ws), "bmoe_pack_ternary")
+    _check(bmoe_sync_status(ws), "bmoe_pack_ternary")
+    return packed
+
+
+class Workspace:
+    """Caller-owned workspace sized for one shape (reused across calls)."""
+
+    def __init__(self, dt: int, T: int, d: int, n_experts: int, k: int, device="cuda"):
+        n = bmoe_workspace_bytes(dt, T, d, n_experts, k)
+        if n == 0:
+            raise BmoeError(2, "bmoe_workspace_bytes")
+        self.buf = torch.empty(n, dtype=torch.uint8, device=device)
+        self.key = (dt, T, d, n_experts, k)
+
+
+def forward(x: torch.Tensor, ids: torch.Tensor, gates: torch.Tensor, theta: torch.Tensor,
+            phi: torch.Tensor, w_packed: torch.Tensor, alpha: float, *, y=None, ws=None,
+            route_out=None, stream=None) -> torch.Tensor:
+    T, d = x.shape
+    k = ids.shape[1]
+    N = theta.shape[0]
+    dt = dtype_code(x)
+    if y is None:
+        y = torch.empty_like(x)
+    if ws is None:
+        ws = Workspace(dt, T, d, N, k, device=x.device)
+    _check(bmoe_forward(dt, T, d, N, k, x, ids, gates, theta, phi, w_packed, alpha, y, ws.buf,
+                        route_out, stream), "bmoe_forward")
+    return y

@@ -1,0 +1,44 @@
+// Internal launchers of the ButterflyMoE kernels (host side, not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bmoe.h"
+
+namespace bmoe {
+
+struct RouteTables {
+  int32_t* offsets;  // [N+1]
+  int32_t* perm;     // [M] sorted slot -> routed index
+  int32_t* inv;      // [M] routed index -> sorted slot
+  int32_t* slot_e;   // [M] sorted slot -> expert
+};
+
+// Routing (histogram, scan, stable scatter) and the per-call cos/sin tables
+// of both rotation sides, in one launch.
+hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, const float* phi,
+                       int d, RouteTables rt, float2* cs_in, float2* cs_out, int32_t* status,
+                       hipStream_t s);
+
+// Z[q] = B(theta_e)^T x[t]   (t = perm[q] / k, e = slot_e[q]).
+hipError_t launch_bfly_in(bmoe_dtype dt, int M, int d, int k, const void* x,
+                          const RouteTables& rt, const float2* cs_in, void* z, hipStream_t s);
+
+// H = alpha * Z W_base^T over all M sorted rows.
+hipError_t launch_gemm(bmoe_dtype dt, int M, int d, const void* z, const uint32_t* w_packed,
+                       float alpha, float* h, hipStream_t s);
+
+// U[r] = g_r * B(phi_e) H[q] for r = perm[q], written in routed order.
+hipError_t launch_bfly_out(int M, int d, const float* h, const float* gates,
+                           const RouteTables& rt, const float2* cs_out, float* u,
+                           hipStream_t s);
+
+// y[t] = sum_j U[t*k + j], ascending j.
+hipError_t launch_combine(bmoe_dtype dt, int T, int d, int k, const float* u, void* y,
+                          hipStream_t s);
+
+hipError_t launch_pack(const int8_t* w, int d, uint32_t* packed, int32_t* status,
+                       hipStream_t s);
+
+}  // namespace bmoe

@@ -1,0 +1,203 @@
+// Per-call preparation, one launch:
+//  * routing: per-expert histogram, exclusive scan and a stable scatter of
+//    routed rows r = t*k + j grouped by expert (ascending r inside a group);
+//  * the cos/sin tables of both rotation sides, computed once per call so no
+//    row ever evaluates a trigonometric function.
+// Rows are grouped so that consecutive rows share one expert's rotation
+// coefficients (ButterflyMoE gist.science summary, §2.3: every routed token is
+// rotated by its own expert's butterflies around the shared substrate).
+#include "common.h"
+#include "kernels.h"
+
+namespace bmoe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+struct PrepParams {
+  const int32_t* ids;
+  int M, N, nbits;
+  int chunk, n_route_blocks;
+  RouteTables rt;
+  int32_t* status;
+  const float* theta;
+  const float* phi;
+  float2* cs_in;
+  float2* cs_out;
+  long long n_ang;  // angles per side: N * L * d/2
+};
+
+__device__ __forceinline__ int clamp_expert(int e, int N, bool& bad) {
+  if ((unsigned)e >= (unsigned)N) {
+    bad = true;
+    return e < 0 ? 0 : N - 1;
+  }
+  return e;
+}
+
+// Exclusive prefix sum of one int per thread over the 256-thread block.
+__device__ int block_exclusive_scan(int v, int* scratch) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int u = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += u;
+  }
+  if (lane == kWave - 1) scratch[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += scratch[w];
+  __syncthreads();
+  return before + incl - v;
+}
+
+__global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
+  if ((int)blockIdx.x >= p.n_route_blocks) {
+    // ---- cos/sin tables -------------------------------------------------
+    const long long total = 2 * p.n_ang;
+    const long long stride = (long long)(gridDim.x - p.n_route_blocks) * kThreads;
+    for (long long i = (long long)(blockIdx.x - p.n_route_blocks) * kThreads + threadIdx.x;
+         i < total; i += stride) {
+      const bool out_side = i >= p.n_ang;
+      const long long j = out_side ? i - p.n_ang : i;
+      const float a = out_side ? p.phi[j] : p.theta[j];
+      float s, c;
+      sincosf(a, &s, &c);
+      (out_side ? p.cs_out : p.cs_in)[j] = make_float2(c, s);
+    }
+    return;
+  }
+
+  // ---- routing ----------------------------------------------------------
+  extern __shared__ int sh[];
+  const int N = p.N, M = p.M;
+  int* cnt = sh;            // [N] counts, then offsets
+  int* before = sh + N;     // [N] counts of rows before this chunk, then bases
+  int* wcur = sh + 2 * N;   // [kWaves][N] per-wave counts, then cursors
+  __shared__ int scratch[kWaves];
+
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int r0 = blockIdx.x * p.chunk;
+  const int r1 = min(M, r0 + p.chunk);
+
+  for (int i = tid; i < (2 + kWaves) * N; i += kThreads) sh[i] = 0;
+  __syncthreads();
+
+  bool bad = false;
+  for (int r = tid; r < M; r += kThreads) {
+    const int e = clamp_expert(p.ids[r], N, bad);
+    atomicAdd(&cnt[e], 1);
+    if (r < r0) atomicAdd(&before[e], 1);
+  }
+  __syncthreads();
+
+  // Exclusive scan of the counts: each thread owns a contiguous segment.
+  const int per = (N + kThreads - 1) / kThreads;
+  const int lo = min(N, tid * per), hi = min(N, lo + per);
+  int seg = 0;
+  for (int e = lo; e < hi; ++e) seg += cnt[e];
+  int run = block_exclusive_scan(seg, scratch);
+  for (int e = lo; e < hi; ++e) {
+    const int c = cnt[e];
+    cnt[e] = run;
+    run += c;
+  }
+  const bool any_bad = __syncthreads_or(bad);
+  if (blockIdx.x == 0) {
+    for (int e = tid; e < N; e += kThreads) p.rt.offsets[e] = cnt[e];
+    if (tid == 0) {
+      p.rt.offsets[N] = M;
+      *p.status = any_bad ? BMOE_E_EXPERT : BMOE_OK;
+    }
+  }
+  for (int e = tid; e < N; e += kThreads) before[e] += cnt[e];
+
+  // Each wave owns a contiguous quarter of the chunk.
+  const int len = r1 - r0;
+  const int quarter = (len + kWaves - 1) / kWaves;
+  const int wb = min(r1, r0 + wave * quarter), we = min(r1, wb + quarter);
+  int* mycur = wcur + wave * N;
+  for (int r = wb + lane; r < we; r += kWave) {
+    bool dummy = false;
+    atomicAdd(&mycur[clamp_expert(p.ids[r], N, dummy)], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < N; e += kThreads) {
+    int c0 = before[e];
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = wcur[w * N + e];
+      wcur[w * N + e] = c0;
+      c0 += c;
+    }
+  }
+  __syncthreads();
+
+  // Stable ranks inside each 64-row step: lanes holding the same expert are
+  // found with one ballot per key bit; their order is the lane order.
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int base = wb; base < we; base += kWave) {
+    const int r = base + lane;
+    const bool valid = r < we;
+    bool dummy = false;
+    const int e = valid ? clamp_expert(p.ids[r], N, dummy) : 0;
+    uint64_t mask = __ballot(valid);
+    for (int b = 0; b < p.nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      mask &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(mask & lt);
+    const int grp = __popcll(mask);
+    int cur = 0;
+    if (valid) cur = mycur[e];
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      const int q = cur + rank;
+      p.rt.perm[q] = r;
+      p.rt.inv[r] = q;
+      p.rt.slot_e[q] = e;
+      if (rank == grp - 1) mycur[e] = cur + grp;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, const float* phi,
+                       int d, RouteTables rt, float2* cs_in, float2* cs_out, int32_t* status,
+                       hipStream_t s) {
+  int L = 0;
+  while ((1 << L) < d) ++L;
+  PrepParams p;
+  p.ids = ids;
+  p.M = M;
+  p.N = N;
+  p.nbits = 0;
+  while ((1 << p.nbits) < N) ++p.nbits;
+  p.chunk = M <= 8192 ? 1024 : 2048;
+  p.n_route_blocks = (M + p.chunk - 1) / p.chunk;
+  if (p.n_route_blocks < 1) p.n_route_blocks = 1;
+  p.rt = rt;
+  p.status = status;
+  p.theta = theta;
+  p.phi = phi;
+  p.cs_in = cs_in;
+  p.cs_out = cs_out;
+  p.n_ang = (long long)N * L * (d / 2);
+  long long trig_blocks = (2 * p.n_ang + kThreads * 8 - 1) / (kThreads * 8);
+  if (trig_blocks > 65536) trig_blocks = 65536;
+  const size_t shmem = sizeof(int) * (size_t)(2 + kWaves) * N;
+  if (shmem > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(prep_kernel, dim3(p.n_route_blocks + (int)trig_blocks), dim3(kThreads),
+                     shmem, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace bmoe

@@ -1,0 +1,137 @@
+/*
+ * bmoe.h — C ABI of libbmoe.so: the ButterflyMoE expert-layer forward on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method (ButterflyMoE: Sub-Linear Ternary Experts via Structured Butterfly
+ * Orbits, gist.science technical summary):
+ *   §2.1  expert i is W_i = B(phi_i) * W_base * B(theta_i)^T, with one ternary
+ *         W_base in {-1,0,+1} shared by all experts and butterfly-structured
+ *         rotations B(.) holding O(d log d) angles per expert;
+ *   §2.3  inference never forms W_i: the input is rotated by B(theta_i)^T,
+ *         multiplied by W_base, then rotated by B(phi_i).
+ * The layer output of token t with top-k experts e_tj and gates g_tj is
+ *   y_t = sum_j g_tj * alpha * B(phi_{e_tj}) W_base B(theta_{e_tj})^T x_t.
+ *
+ * Readings the pages leave open (fixed here):
+ *   - B(a) = S_{L-1}(a_{L-1}) ... S_0(a_0), L = log2 d. Stage s rotates every
+ *     pair (i, i + 2^s) with bit s of i clear; pair index p counts those i in
+ *     ascending order. A rotation maps (x_i, x_j) to
+ *     (c x_i - s x_j, s x_i + c x_j), c = cos a, s = sin a.
+ *   - angles are fp32 [N][L][d/2] (expert, stage, pair), theta on the input
+ *     side and phi on the output side;
+ *   - one fp32 scale alpha multiplies W_base;
+ *   - gates are used as given (no renormalisation).
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers owned by the caller, 16-byte
+ *     aligned. The library allocates nothing on the call path and keeps no
+ *     state between calls besides the loaded code object.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *     asynchronously; a call returns before the GPU finishes.
+ *   - A non-BMOE_OK return comes from host-side validation, before anything
+ *     is enqueued; outputs are then untouched. Errors the GPU detects (an
+ *     expert id outside [0, N), a W_base entry outside {-1,0,+1}) are written
+ *     to a status word in the workspace and read back by bmoe_sync_status().
+ *   - Calls are re-entrant for distinct workspaces; two calls sharing one
+ *     workspace must be ordered on one stream.
+ */
+#ifndef BMOE_H
+#define BMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BMOE_OK = 0,
+  BMOE_E_NULL = 1,       /* a required pointer is NULL */
+  BMOE_E_SHAPE = 2,      /* d not a power of two in [16, 8192], N < 1 or N > 4096,
+                            k < 1 or k > N, T < 0, or T*k beyond 2^31 - 1 */
+  BMOE_E_DTYPE = 3,      /* unknown bmoe_dtype */
+  BMOE_E_TERNARY = 4,    /* device: a W_base entry outside {-1, 0, +1} */
+  BMOE_E_EXPERT = 5,     /* device: an expert id outside [0, N) */
+  BMOE_E_WORKSPACE = 6,  /* workspace NULL or smaller than required */
+  BMOE_E_HIP = 7,        /* a HIP runtime call failed */
+  BMOE_E_ALIGN = 8       /* a pointer is not 16-byte aligned */
+} bmoe_status;
+
+typedef enum {
+  BMOE_F32 = 0,   /* x and y fp32; all arithmetic fp32 (substrate product exact
+                     to fp32 via a three-way bf16 split of the activations) */
+  BMOE_BF16 = 1   /* x and y bf16; rotations in fp32, substrate product on bf16
+                     MFMA with fp32 accumulation */
+} bmoe_dtype;
+
+/* Number of uint32 words of the packed substrate: d * ceil(d/16). */
+size_t bmoe_packed_words(int d);
+
+/* Stored parameters of one layer, d*d + 2 * N * log2(d) * (d/2)
+ * (the memory model O(d^2 + N d log d) of §2.2 made exact by the stage layout
+ * above). Returns 0 for an invalid d or N. */
+size_t bmoe_param_count(int d, int n_experts);
+
+/* Workspace bytes bmoe_forward needs for this shape (0 if the shape is
+ * invalid). The workspace holds the routing tables, the per-call rotation
+ * coefficient tables and the intermediate activations. */
+size_t bmoe_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts, int k);
+
+/* Workspace bytes bmoe_pack_ternary needs (a status word). */
+size_t bmoe_pack_workspace_bytes(void);
+
+/*
+ * Pack the shared ternary substrate (§2.1: entries in {-1,0,+1}) into 2 bits
+ * per entry.
+ *   w        int8 [d][d], row o = output, column c = input.
+ *   packed   uint32 [d][ceil(d/16)] (output). Row o, word g holds columns
+ *            c = 16g .. 16g+15: column v = c - 16g with v = 2j keeps its
+ *            nonzero flag at bit j and its sign at bit 8+j; v = 2j+1 at bits
+ *            16+j and 24+j. +1 = (nz 1, sign 0), -1 = (1, 1), 0 = (0, 0).
+ *   ws       at least bmoe_pack_workspace_bytes(); receives the status word.
+ * Invalid entries are packed as 0 and reported as BMOE_E_TERNARY by
+ * bmoe_sync_status(ws, stream).
+ */
+bmoe_status bmoe_pack_ternary(const int8_t* w, int d, uint32_t* packed, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/*
+ * Forward of one ButterflyMoE expert layer for T tokens (§2.3 order).
+ *   dt        BMOE_F32 or BMOE_BF16: element type of x and y.
+ *   x         [T][d] tokens.
+ *   ids       int32 [T][k] expert ids in [0, N). Routed index r = t*k + j.
+ *   gates     fp32 [T][k] gate weights g_tj.
+ *   theta     fp32 [N][log2 d][d/2] input-side angles.
+ *   phi       fp32 [N][log2 d][d/2] output-side angles.
+ *   w_packed  uint32 [d][ceil(d/16)] from bmoe_pack_ternary.
+ *   alpha     scale of W_base.
+ *   y         [T][d] output (must not alias x).
+ *   ws        workspace of at least bmoe_workspace_bytes(dt, T, d, N, k).
+ *   route_out optional (may be NULL): int32 [N+1 + 2*T*k] receiving
+ *             offsets[N+1] (exclusive prefix of per-expert row counts),
+ *             perm[T*k] (sorted slot -> routed index; experts ascending,
+ *             ascending r within an expert) and inv[T*k] (routed index ->
+ *             sorted slot). These are the tables the forward itself uses.
+ * T = 0 is a no-op. Bad expert ids are clamped for addressing (so every
+ * access stays in bounds) and reported by bmoe_sync_status(); y is then
+ * unspecified.
+ */
+bmoe_status bmoe_forward(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
+                         const int32_t* ids, const float* gates, const float* theta,
+                         const float* phi, const uint32_t* w_packed, float alpha, void* y,
+                         void* ws, size_t ws_bytes, int32_t* route_out, void* stream);
+
+/* Wait for `stream`, then return the device-side status of the last forward
+ * or pack that used `ws` (BMOE_OK, BMOE_E_EXPERT or BMOE_E_TERNARY), or
+ * BMOE_E_HIP if the wait itself failed. */
+bmoe_status bmoe_sync_status(const void* ws, void* stream);
+
+/* Static description of a status code. */
+const char* bmoe_status_str(bmoe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BMOE_H */

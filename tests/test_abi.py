@@ -1,0 +1,84 @@
+"""The C-ABI library loads and exports every entry point include/bmoe.h
+declares; the host-only size queries behave as documented (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from butterfly_rotated_ternary_amd import bmoe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bmoe.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bmoe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["bmoe_forward", "bmoe_pack_ternary", "bmoe_workspace_bytes", "bmoe_sync_status",
+              "bmoe_packed_words", "bmoe_param_count", "bmoe_status_str",
+              "bmoe_pack_workspace_bytes"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(bmoe._LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    # and the binding wraps each under the same name
+    for n in declared_functions():
+        assert callable(getattr(bmoe, n)), n
+
+
+def test_param_count_matches_fixture(golden_dir):
+    for line in open(os.path.join(golden_dir, "param_counts.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        d, N, cnt = map(int, line.split())
+        assert bmoe.bmoe_param_count(d, N) == cnt
+
+
+def test_packed_words():
+    assert bmoe.bmoe_packed_words(16) == 16
+    assert bmoe.bmoe_packed_words(512) == 512 * 32
+    assert bmoe.bmoe_packed_words(4096) == 4096 * 256
+    for bad in (0, 8, 24, 16384, -16):
+        assert bmoe.bmoe_packed_words(bad) == 0
+
+
+def test_workspace_bytes_validates_shape():
+    ok = bmoe.bmoe_workspace_bytes(bmoe.BMOE_BF16, 4096, 512, 64, 2)
+    # at least the activations: Z bf16 + H fp32 + U fp32 over M = T*k rows
+    assert ok >= 8192 * 512 * (2 + 4 + 4)
+    assert bmoe.bmoe_workspace_bytes(bmoe.BMOE_BF16, 0, 512, 64, 2) > 0
+    for args in [(bmoe.BMOE_BF16, 16, 500, 64, 2),   # d not a power of two
+                 (bmoe.BMOE_BF16, 16, 512, 64, 65),  # k > N
+                 (bmoe.BMOE_BF16, 16, 512, 0, 1),    # N < 1
+                 (bmoe.BMOE_BF16, -1, 512, 64, 2),   # T < 0
+                 (bmoe.BMOE_BF16, 16, 512, 5000, 2),  # N too large
+                 (7, 16, 512, 64, 2)]:               # bad dtype
+        assert bmoe.bmoe_workspace_bytes(*args) == 0
+
+
+def test_status_strings():
+    for code in range(9):
+        assert bmoe.bmoe_status_str(code)
+
+
+def test_host_validation_needs_no_gpu():
+    # These return before any HIP call: shape, dtype and null checks.
+    lib = bmoe.lib()
+    assert lib.bmoe_forward(9, 4, 512, 8, 2, None, None, None, None, None, None, 1.0, None, None,
+                            0, None, None) == 3
+    assert lib.bmoe_forward(1, 4, 500, 8, 2, None, None, None, None, None, None, 1.0, None, None,
+                            0, None, None) == 2
+    assert lib.bmoe_forward(1, 4, 512, 8, 2, None, None, None, None, None, None, 1.0, None, None,
+                            0, None, None) == 1
+    assert lib.bmoe_forward(1, 0, 512, 8, 2, None, None, None, None, None, None, 1.0, None, None,
+                            0, None, None) == 0     # T = 0 is a no-op
+    assert lib.bmoe_pack_ternary(None, 16, None, None, 0, None) == 1
