@@ -53,6 +53,12 @@ def lib():
         L.bmoe_forward.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp, c_f,
                                    vp, vp, c_sz, vp, vp]
         L.bmoe_forward.restype = c_int
+        L.bmoe_forward_timed.argtypes = L.bmoe_forward.argtypes + [vp]
+        L.bmoe_forward_timed.restype = c_int
+        L.bmoe_forward_kernel_count.argtypes = [c_int, c_int, c_int, c_int, c_int]
+        L.bmoe_forward_kernel_count.restype = c_int
+        L.bmoe_forward_kernel_name.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int]
+        L.bmoe_forward_kernel_name.restype = ctypes.c_char_p
         L.bmoe_sync_status.argtypes = [vp, vp]
         L.bmoe_sync_status.restype = c_int
         L.bmoe_status_str.argtypes = [c_int]
@@ -104,6 +110,27 @@ def bmoe_forward(dt: int, T: int, d: int, n_experts: int, k: int, x, ids, gates,
     return lib().bmoe_forward(dt, T, d, n_experts, k, _ptr(x), _ptr(ids), _ptr(gates), _ptr(theta),
                               _ptr(phi), _ptr(w_packed), float(alpha), _ptr(y), _ptr(ws),
                               ws.numel() * ws.element_size(), _ptr(route_out), _stream(stream))
+
+
+def bmoe_forward_timed(dt: int, T: int, d: int, n_experts: int, k: int, x, ids, gates, theta, phi,
+                       w_packed, alpha: float, y, ws, route_out=None, stream=None,
+                       events=None) -> int:
+    """``events``: sequence of raw hipEvent_t handles (ints), kernel count + 1."""
+    ev = None
+    if events is not None:
+        ev = (ctypes.c_void_p * len(events))(*events)
+    return lib().bmoe_forward_timed(dt, T, d, n_experts, k, _ptr(x), _ptr(ids), _ptr(gates),
+                                    _ptr(theta), _ptr(phi), _ptr(w_packed), float(alpha), _ptr(y),
+                                    _ptr(ws), ws.numel() * ws.element_size(), _ptr(route_out),
+                                    _stream(stream), ev)
+
+
+def bmoe_forward_kernel_count(dt: int, T: int, d: int, n_experts: int, k: int) -> int:
+    return lib().bmoe_forward_kernel_count(dt, T, d, n_experts, k)
+
+
+def bmoe_forward_kernel_name(dt: int, T: int, d: int, n_experts: int, k: int, i: int) -> str:
+    return lib().bmoe_forward_kernel_name(dt, T, d, n_experts, k, i).decode()
 
 
 def bmoe_sync_status(ws: torch.Tensor, stream=None) -> int:

@@ -88,10 +88,11 @@ bmoe_status bmoe_pack_ternary(const int8_t* w, int d, uint32_t* packed, void* ws
   return BMOE_OK;
 }
 
-bmoe_status bmoe_forward(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
-                         const int32_t* ids, const float* gates, const float* theta,
-                         const float* phi, const uint32_t* w_packed, float alpha, void* y,
-                         void* ws, size_t ws_bytes, int32_t* route_out, void* stream) {
+bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
+                               const int32_t* ids, const float* gates, const float* theta,
+                               const float* phi, const uint32_t* w_packed, float alpha, void* y,
+                               void* ws, size_t ws_bytes, int32_t* route_out, void* stream,
+                               void* const* events) {
   if (dt != BMOE_F32 && dt != BMOE_BF16) return BMOE_E_DTYPE;
   if (!shape_ok(dt, T, d, n_experts, k)) return BMOE_E_SHAPE;
   if (T == 0) return BMOE_OK;
@@ -124,13 +125,44 @@ bmoe_status bmoe_forward(bmoe_dtype dt, int T, int d, int n_experts, int k, cons
   float* u = reinterpret_cast<float*>(base + l.u);
   hipStream_t s = static_cast<hipStream_t>(stream);
 
+  int ki = 0;
+  auto mark = [&]() -> bool {
+    if (!events) return true;
+    return hipEventRecord(static_cast<hipEvent_t>(events[ki++]), s) == hipSuccess;
+  };
+  if (!mark()) return BMOE_E_HIP;
   if (launch_prep(ids, M, n_experts, theta, phi, d, rt, cs_in, cs_out, status, s) != hipSuccess)
     return BMOE_E_HIP;
+  if (!mark()) return BMOE_E_HIP;
   if (launch_bfly_in(dt, M, d, k, x, rt, cs_in, z, s) != hipSuccess) return BMOE_E_HIP;
+  if (!mark()) return BMOE_E_HIP;
   if (launch_gemm(dt, M, d, z, w_packed, alpha, h, s) != hipSuccess) return BMOE_E_HIP;
+  if (!mark()) return BMOE_E_HIP;
   if (launch_bfly_out(M, d, h, gates, rt, cs_out, u, s) != hipSuccess) return BMOE_E_HIP;
+  if (!mark()) return BMOE_E_HIP;
   if (launch_combine(dt, T, d, k, u, y, s) != hipSuccess) return BMOE_E_HIP;
+  if (!mark()) return BMOE_E_HIP;
   return BMOE_OK;
+}
+
+bmoe_status bmoe_forward(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
+                         const int32_t* ids, const float* gates, const float* theta,
+                         const float* phi, const uint32_t* w_packed, float alpha, void* y,
+                         void* ws, size_t ws_bytes, int32_t* route_out, void* stream) {
+  return bmoe_forward_timed(dt, T, d, n_experts, k, x, ids, gates, theta, phi, w_packed, alpha, y,
+                            ws, ws_bytes, route_out, stream, nullptr);
+}
+
+int bmoe_forward_kernel_count(bmoe_dtype dt, int T, int d, int n_experts, int k) {
+  if (!shape_ok(dt, T, d, n_experts, k) || T == 0) return 0;
+  return 5;
+}
+
+const char* bmoe_forward_kernel_name(bmoe_dtype dt, int T, int d, int n_experts, int k, int i) {
+  static const char* names_bf16[] = {"prep_kernel", "bfly_in_kernel", "gemm_kernel",
+                                     "bfly_out_kernel", "combine_kernel"};
+  if (i < 0 || i >= bmoe_forward_kernel_count(dt, T, d, n_experts, k)) return "";
+  return names_bf16[i];
 }
 
 bmoe_status bmoe_sync_status(const void* ws, void* stream) {

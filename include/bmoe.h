@@ -122,6 +122,24 @@ bmoe_status bmoe_forward(bmoe_dtype dt, int T, int d, int n_experts, int k, cons
                          const float* phi, const uint32_t* w_packed, float alpha, void* y,
                          void* ws, size_t ws_bytes, int32_t* route_out, void* stream);
 
+/* Number of kernels bmoe_forward enqueues for this shape (0 if invalid), and
+ * the name of kernel i (as it appears in a kernel trace). */
+int bmoe_forward_kernel_count(bmoe_dtype dt, int T, int d, int n_experts, int k);
+const char* bmoe_forward_kernel_name(bmoe_dtype dt, int T, int d, int n_experts, int k, int i);
+
+/*
+ * bmoe_forward, additionally recording events[i] on `stream` right before
+ * kernel i is enqueued and events[count] after the last one, where count =
+ * bmoe_forward_kernel_count(...). `events` holds count + 1 hipEvent_t created
+ * by the caller (NULL behaves as bmoe_forward). For measuring per-kernel
+ * durations with hipEventElapsedTime; results are identical to bmoe_forward.
+ */
+bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
+                               const int32_t* ids, const float* gates, const float* theta,
+                               const float* phi, const uint32_t* w_packed, float alpha, void* y,
+                               void* ws, size_t ws_bytes, int32_t* route_out, void* stream,
+                               void* const* events);
+
 /* Wait for `stream`, then return the device-side status of the last forward
  * or pack that used `ws` (BMOE_OK, BMOE_E_EXPERT or BMOE_E_TERNARY), or
  * BMOE_E_HIP if the wait itself failed. */
