@@ -47,8 +47,8 @@ FwdLayout fwd_layout(bmoe_dtype dt, int T, int d, int N, int k) {
   l.cs_in = off;   off = align_up(off + sizeof(float2) * N * L * (d / 2));
   l.cs_out = off;  off = align_up(off + sizeof(float2) * N * L * (d / 2));
   l.z = off;       off = align_up(off + zel * M * d);
-  l.h = off;       off = align_up(off + sizeof(float) * M * d);
-  l.u = off;       off = align_up(off + sizeof(float) * M * d);
+  l.h = off;       off = align_up(off + zel * M * d);
+  l.u = off;       off = align_up(off + zel * M * d);
   l.total = off;
   return l;
 }
@@ -121,8 +121,8 @@ bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k
   float2* cs_in = reinterpret_cast<float2*>(base + l.cs_in);
   float2* cs_out = reinterpret_cast<float2*>(base + l.cs_out);
   void* z = base + l.z;
-  float* h = reinterpret_cast<float*>(base + l.h);
-  float* u = reinterpret_cast<float*>(base + l.u);
+  void* h = base + l.h;
+  void* u = base + l.u;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   int ki = 0;
@@ -138,7 +138,7 @@ bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k
   if (!mark()) return BMOE_E_HIP;
   if (launch_gemm(dt, M, d, z, w_packed, alpha, h, s) != hipSuccess) return BMOE_E_HIP;
   if (!mark()) return BMOE_E_HIP;
-  if (launch_bfly_out(M, d, h, gates, rt, cs_out, u, s) != hipSuccess) return BMOE_E_HIP;
+  if (launch_bfly_out(dt, M, d, h, gates, rt, cs_out, u, s) != hipSuccess) return BMOE_E_HIP;
   if (!mark()) return BMOE_E_HIP;
   if (launch_combine(dt, T, d, k, u, y, s) != hipSuccess) return BMOE_E_HIP;
   if (!mark()) return BMOE_E_HIP;

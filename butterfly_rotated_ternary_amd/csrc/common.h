@@ -30,12 +30,12 @@ __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v 
 // Packed substrate word -> 8 dwords, each two bf16 values of {-1, 0, +1}.
 // Word layout: column v = 2j has its nonzero flag at bit j and sign at bit
 // 8+j; v = 2j+1 at bits 16+j and 24+j. Dword j = (value 2j, value 2j+1):
-// the two nonzero flags are moved to bits 0 and 16 and scaled by 0x3F80
-// (the bf16 pattern of 1.0), the two signs are moved to bits 15 and 31.
+// shifting left by 7-j puts the two nonzero flags at bits 7 and 23 and the
+// two signs at bits 15 and 31; flag * 0x7F spreads a flag into 0x3F80 (the
+// bf16 pattern of 1.0, shifted by 0 or 16) and the signs are added on top.
 __device__ __forceinline__ uint32_t unpack_pair(uint32_t w, int j) {
-  uint32_t n = (w >> j) & 0x00010001u;
-  uint32_t s = (w << (7 - j)) & 0x80008000u;
-  return n * 0x3F80u | s;
+  const uint32_t t = w << (7 - j);
+  return __umul24(t & 0x00800080u, 0x7Fu) + (t & 0x80008000u);
 }
 
 // Index of the j-th element of a block of 2^g elements whose varying index

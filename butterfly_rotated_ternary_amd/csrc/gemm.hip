@@ -1,21 +1,26 @@
 // Shared-substrate product H = alpha * Z W_base^T over every routed row at
 // once (ButterflyMoE gist.science summary, §2.3 step 2: one ternary W_base
-// serves all experts, so the contraction is a single dense GEMM).
+// serves all experts, so the contraction is a single dense GEMM over all
+// routed rows, whatever their expert).
 //
-// bf16 MFMA (v_mfma_f32_16x16x32_bf16) with fp32 accumulation. The packed
-// 2-bit substrate is expanded to exact bf16 {-1,0,+1} while staging it in
-// LDS, so the products are exact. For fp32 activations each Z value is split
-// into three bf16 terms (hi + mid + lo represent it to within 2^-24 relative),
+// bf16 MFMA (v_mfma_f32_32x32x16_bf16) with fp32 accumulation. The packed
+// 2-bit substrate is expanded to exact bf16 {-1,0,+1} while it is staged in
+// LDS, so every product is exact. For fp32 activations each Z value is split
+// into three bf16 terms (hi + mid + lo represent it to within 2^-24 relative)
 // and the three partial products accumulate in fp32.
+//
+// Tiling: BM x BN output tile per workgroup, K in steps of 64, LDS double
+// buffered (global loads for step k+1 are in flight while step k runs on the
+// matrix cores; one barrier per step). Tiles are ordered so that the
+// workgroups one XCD runs at a time share their rows of Z in that XCD's L2.
 #include "common.h"
 #include "kernels.h"
 
 namespace bmoe {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int BM = 64, BN = 64, BK = 32;
-constexpr int LDA = BK + 8;  // bf16 per LDS row (pad breaks bank aliasing)
+constexpr int BK = 64;
+constexpr int LDK = BK + 8;  // bf16 per LDS row; the pad spreads rows over banks
 
 __device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
   hi = f32_to_bf16_bits(x);
@@ -25,106 +30,425 @@ __device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uin
   lo = f32_to_bf16_bits(r2);
 }
 
-template <bool F32A>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const void* zv, const uint32_t* wp,
-                                                        float* H, int M, int d, float alpha) {
-  constexpr int SPL = F32A ? 3 : 1;
-  __shared__ __attribute__((aligned(16))) uint16_t As[SPL][BM * LDA];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDA];
+template <int BM_, int BN_, int WM_, int WN_, bool F32A_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr bool F32A = F32A_;
+  static constexpr int SPL = F32A ? 3 : 1;
+  static constexpr int THREADS = 64 * WM * WN;
+  static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
+  static constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 MFMA blocks per wave
+  // A tile: BM rows x BK. bf16 A: 16-byte chunks (8 values); fp32 A: 16-byte
+  // chunks of 4 values.
+  static constexpr int A_VALS = F32A ? 4 : 8;
+  static constexpr int A_CHUNKS = BM * BK / A_VALS;
+  static constexpr int A_PER_THREAD = A_CHUNKS / THREADS;
+  // B tile: BN rows x BK = BN * BK/16 packed words.
+  static constexpr int B_WORDS = BN * (BK / 16);
+  static constexpr int B_PER_THREAD = (B_WORDS + THREADS - 1) / THREADS;
+  static constexpr int A_LDS = SPL * BM * LDK;  // bf16 elements per buffer
+  static constexpr int B_LDS = BN * LDK;
+  static constexpr size_t LDS_BYTES = 2 * (A_LDS + B_LDS) * sizeof(uint16_t);
+  static_assert(A_CHUNKS % THREADS == 0, "A tile must split evenly");
+};
 
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
-  const int G = d / 16;
+template <class C>
+struct Stage {
+  uint4 a[C::A_PER_THREAD];
+  uint32_t b[C::B_PER_THREAD];
+};
 
-  f32x4 acc[2][2];
+template <class C>
+__device__ __forceinline__ void load_stage(Stage<C>& st, const void* zv, const uint32_t* wp, int M,
+                                           int d, int m0, int n0, int k0) {
+  const int tid = threadIdx.x;
+  constexpr int CPR = BK / C::A_VALS;  // chunks per row
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int k0 = 0; k0 < d; k0 += BK) {
-    if constexpr (!F32A) {
-      const uint16_t* Z = static_cast<const uint16_t*>(zv);
-      const int row = tid >> 2, kc = (tid & 3) * 8;
-      const int gr = m0 + row;
-      uint4 v = {0u, 0u, 0u, 0u};
-      if (gr < M && k0 + kc < d) v = *reinterpret_cast<const uint4*>(Z + (size_t)gr * d + k0 + kc);
-      *reinterpret_cast<uint4*>(&As[0][row * LDA + kc]) = v;
-    } else {
-      const float* Z = static_cast<const float*>(zv);
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int idx = tid + it * kThreads;
-        const int row = idx >> 3, kc = (idx & 7) * 4;
-        const int gr = m0 + row;
-        float4 v = {0.f, 0.f, 0.f, 0.f};
-        if (gr < M && k0 + kc < d) v = *reinterpret_cast<const float4*>(Z + (size_t)gr * d + k0 + kc);
-        uint32_t h[4], m[4], l[4];
-        split3(v.x, h[0], m[0], l[0]);
-        split3(v.y, h[1], m[1], l[1]);
-        split3(v.z, h[2], m[2], l[2]);
-        split3(v.w, h[3], m[3], l[3]);
-        *reinterpret_cast<uint2*>(&As[0][row * LDA + kc]) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-        *reinterpret_cast<uint2*>(&As[1][row * LDA + kc]) = make_uint2(m[0] | (m[1] << 16), m[2] | (m[3] << 16));
-        *reinterpret_cast<uint2*>(&As[2][row * LDA + kc]) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
-      }
+  for (int i = 0; i < C::A_PER_THREAD; ++i) {
+    const int c = tid + i * C::THREADS;
+    const int row = c / CPR, kc = (c % CPR) * C::A_VALS;
+    const int gr = m0 + row;
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (gr < M && k0 + kc < d) {
+      if constexpr (C::F32A)
+        v = *reinterpret_cast<const uint4*>(static_cast<const float*>(zv) + (size_t)gr * d + k0 + kc);
+      else
+        v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(zv) + (size_t)gr * d + k0 + kc);
     }
-    if (tid < BN * (BK / 16)) {
-      const int o = tid >> 1, wi = tid & 1;
-      const int go = n0 + o, c0 = k0 + wi * 16;
-      uint32_t w = 0;
-      if (go < d && c0 < d) w = wp[(size_t)go * G + c0 / 16];
+    st.a[i] = v;
+  }
+  const int G = d / 16;
+#pragma unroll
+  for (int i = 0; i < C::B_PER_THREAD; ++i) {
+    const int wi = tid + i * C::THREADS;
+    const int o = wi / (BK / 16), g = wi % (BK / 16);
+    const int go = n0 + o, c0 = k0 + g * 16;
+    uint32_t w = 0;
+    if (wi < C::B_WORDS && go < d && c0 < d) w = wp[(size_t)go * G + c0 / 16];
+    st.b[i] = w;
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void store_stage(const Stage<C>& st, uint16_t* As, uint16_t* Bs) {
+  const int tid = threadIdx.x;
+  constexpr int CPR = BK / C::A_VALS;
+#pragma unroll
+  for (int i = 0; i < C::A_PER_THREAD; ++i) {
+    const int c = tid + i * C::THREADS;
+    const int row = c / CPR, kc = (c % CPR) * C::A_VALS;
+    if constexpr (C::F32A) {
+      uint32_t h[4], m[4], l[4];
+      split3(__uint_as_float(st.a[i].x), h[0], m[0], l[0]);
+      split3(__uint_as_float(st.a[i].y), h[1], m[1], l[1]);
+      split3(__uint_as_float(st.a[i].z), h[2], m[2], l[2]);
+      split3(__uint_as_float(st.a[i].w), h[3], m[3], l[3]);
+      *reinterpret_cast<uint2*>(&As[(0 * C::BM + row) * LDK + kc]) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      *reinterpret_cast<uint2*>(&As[(1 * C::BM + row) * LDK + kc]) = make_uint2(m[0] | (m[1] << 16), m[2] | (m[3] << 16));
+      *reinterpret_cast<uint2*>(&As[(2 * C::BM + row) * LDK + kc]) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+    } else {
+      *reinterpret_cast<uint4*>(&As[row * LDK + kc]) = st.a[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < C::B_PER_THREAD; ++i) {
+    const int wi = tid + i * C::THREADS;
+    if (wi < C::B_WORDS) {
+      const int o = wi / (BK / 16), g = wi % (BK / 16);
+      const uint32_t w = st.b[i];
       uint4 lo4, hi4;
       lo4.x = unpack_pair(w, 0); lo4.y = unpack_pair(w, 1);
       lo4.z = unpack_pair(w, 2); lo4.w = unpack_pair(w, 3);
       hi4.x = unpack_pair(w, 4); hi4.y = unpack_pair(w, 5);
       hi4.z = unpack_pair(w, 6); hi4.w = unpack_pair(w, 7);
-      *reinterpret_cast<uint4*>(&Bs[o * LDA + wi * 16]) = lo4;
-      *reinterpret_cast<uint4*>(&Bs[o * LDA + wi * 16 + 8]) = hi4;
+      *reinterpret_cast<uint4*>(&Bs[o * LDK + g * 16]) = lo4;
+      *reinterpret_cast<uint4*>(&Bs[o * LDK + g * 16 + 8]) = hi4;
     }
-    __syncthreads();
+  }
+}
 
-    bf16x8 b[2];
+template <class C, typename OutT>
+__global__ __launch_bounds__(C::THREADS) void gemm_kernel(const void* zv, const uint32_t* wp,
+                                                          OutT* H, int M, int d, float alpha,
+                                                          int tiles_m, int tiles_n) {
+  extern __shared__ uint4 lds_raw[];
+  uint16_t* const lds = reinterpret_cast<uint16_t*>(lds_raw);
+  constexpr int BUF = C::A_LDS + C::B_LDS;  // bf16 elements per buffer
+
+  // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a
+  // contiguous range of tiles (row-block major) so concurrently resident
+  // tiles on one XCD share their rows of Z.
+  const int ntiles = tiles_m * tiles_n;
+  const int b = blockIdx.x;
+  int tile = b;
+  if (ntiles % 8 == 0) tile = (b % 8) * (ntiles / 8) + b / 8;
+  const int m0 = (tile / tiles_n) * C::BM, n0 = (tile % tiles_n) * C::BN;
+
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+
+  f32x16 acc[C::FM][C::FN];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      b[j] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * 32 + j * 16 + (lane & 15)) * LDA + 8 * (lane >> 4)]);
+  for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int sp = 0; sp < SPL; ++sp) {
+    for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            &As[SPL - 1 - sp][(wm * 32 + i * 16 + (lane & 15)) * LDA + 8 * (lane >> 4)]);
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  Stage<C> st;
+  load_stage<C>(st, zv, wp, M, d, m0, n0, 0);
+  store_stage<C>(st, lds, lds + C::A_LDS);
+  __syncthreads();
+
+  const int nk = (d + BK - 1) / BK;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_stage<C>(st, zv, wp, M, d, m0, n0, (kt + 1) * BK);
+    const uint16_t* A = lds + cur * BUF;
+    const uint16_t* B = lds + cur * BUF + C::A_LDS;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[i][j], 0, 0, 0);
+    for (int kk = 0; kk < BK; kk += 16) {
+      bf16x8 bf[C::FN];
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+        bf[j] = *reinterpret_cast<const bf16x8*>(
+            &B[(wn * C::TN + j * 32 + (lane & 31)) * LDK + kk + 8 * (lane >> 5)]);
+#pragma unroll
+      for (int sp = 0; sp < C::SPL; ++sp) {
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+          const bf16x8 af = *reinterpret_cast<const bf16x8*>(
+              &A[((C::SPL - 1 - sp) * C::BM + wm * C::TM + i * 32 + (lane & 31)) * LDK + kk +
+                 8 * (lane >> 5)]);
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[j], acc[i][j], 0, 0, 0);
+        }
       }
     }
+    if (kt + 1 < nk) store_stage<C>(st, lds + (cur ^ 1) * BUF, lds + (cur ^ 1) * BUF + C::A_LDS);
     __syncthreads();
   }
 
+  // 32x32 block layout: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4,
+  // column l%32.
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < C::FN; ++j) {
+      const int col = n0 + wn * C::TN + j * 32 + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = m0 + wm * 32 + i * 16 + 4 * (lane >> 4) + r;
-        const int col = n0 + wn * 32 + j * 16 + (lane & 15);
-        if (row < M && col < d) H[(size_t)row * d + col] = alpha * acc[i][j][r];
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * C::TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row < M && col < d) {
+          const float v = alpha * acc[i][j][r];
+          if constexpr (sizeof(OutT) == 2)
+            H[(size_t)row * d + col] = (OutT)f32_to_bf16_bits(v);
+          else
+            H[(size_t)row * d + col] = v;
+        }
       }
+    }
+}
+
+template <class C, typename OutT>
+hipError_t launch_cfg(const void* z, const uint32_t* wp, OutT* h, int M, int d, float alpha,
+                      hipStream_t s) {
+  const int tm = (M + C::BM - 1) / C::BM, tn = (d + C::BN - 1) / C::BN;
+  auto kern = gemm_kernel<C, OutT>;
+  if (C::LDS_BYTES > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3(tm * tn), dim3(C::THREADS), C::LDS_BYTES, s, z, wp, h, M, d, alpha,
+                     tm, tn);
+  return hipGetLastError();
+}
+
+
+// ---------------------------------------------------------------------------
+// Pipelined bf16 kernel for d % 128 == 0 and d % BN == 0.
+//
+// Z tiles go straight from global memory into LDS (global_load_lds_dwordx4:
+// lane l of a wave lands in 16-byte slot l of a 1 KiB LDS block), so they
+// occupy no registers. LDS rows are 128 bytes (64 bf16 of K) with their eight
+// 16-byte chunks XOR-swizzled by (row >> 1) & 7, which keeps the 16-lane
+// phases of the fragment reads on distinct banks. Packed substrate words come
+// through registers two steps ahead and are expanded to bf16 in LDS in four
+// slices between the MFMA groups of the current step. Z rows past M are
+// clamped (computed, then dropped at the store), so nothing is predicated.
+constexpr int kRowBytes = 128;  // one LDS row: BK = 64 bf16
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * kRowBytes + 16 * (chunk ^ ((row >> 1) & 7));
+}
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct DCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int WAVES = WM * WN, THREADS = 64 * WAVES;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  static constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
+  static constexpr int A_LOADS = A_BYTES / 1024 / WAVES;  // 1 KiB wave loads per wave
+  static constexpr int B_PER = BN * (BK / 16) / THREADS;  // packed words per thread
+  static_assert(A_LOADS >= 1 && B_PER >= 1, "tile too small for the thread count");
+};
+
+// vmcnt(n) with expcnt / lgkmcnt left unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
+template <class C>
+__device__ __forceinline__ void d_load_a(char* abuf, const uint16_t* Z, int M, int d, int m0,
+                                         int k0) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int j = 0; j < C::A_LOADS; ++j) {
+    const int blk = wave * C::A_LOADS + j;    // 1 KiB block = 8 rows
+    const int row = blk * 8 + lane / 8;
+    const int chunk = (lane % 8) ^ ((row >> 1) & 7);  // slot lane%8 holds this chunk
+    const int grow = min(m0 + row, M - 1);
+    const uint16_t* g = Z + (size_t)grow * d + k0 + chunk * 8;
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)g,
+        (__attribute__((address_space(3))) void*)(abuf + blk * 1024), 16, 0, 0);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void d_load_b(uint32_t (&rb)[C::B_PER], const uint32_t* wp, int d,
+                                         int n0, int k0) {
+  const int G = d / 16;
+#pragma unroll
+  for (int i = 0; i < C::B_PER; ++i) {
+    const int wi = threadIdx.x + i * C::THREADS;
+    rb[i] = wp[(size_t)(n0 + wi / (BK / 16)) * G + k0 / 16 + wi % (BK / 16)];
+  }
+}
+
+// Expand slice `part` (of 4) of the packed words into bf16 LDS rows.
+template <class C>
+__device__ __forceinline__ void d_write_b(const uint32_t (&rb)[C::B_PER], char* bbuf, int part) {
+#pragma unroll
+  for (int i = 0; i < C::B_PER; ++i) {
+    if ((i * 4) / C::B_PER != part) continue;
+    const int wi = threadIdx.x + i * C::THREADS;
+    const int o = wi / (BK / 16), g = wi % (BK / 16);
+    const uint32_t w = rb[i];
+    *reinterpret_cast<uint4*>(bbuf + swz(o, 2 * g)) =
+        make_uint4(unpack_pair(w, 0), unpack_pair(w, 1), unpack_pair(w, 2), unpack_pair(w, 3));
+    *reinterpret_cast<uint4*>(bbuf + swz(o, 2 * g + 1)) =
+        make_uint4(unpack_pair(w, 4), unpack_pair(w, 5), unpack_pair(w, 6), unpack_pair(w, 7));
+  }
+}
+
+template <class C>
+struct DFrags {
+  bf16x8 a[C::FM];
+  bf16x8 b[C::FN];
+};
+
+template <class C>
+__device__ __forceinline__ void d_read(DFrags<C>& f, const char* abuf, const char* bbuf, int wm,
+                                       int wn, int lane, int kk) {
+  const int chunk = kk / 8 + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+    f.a[i] = *reinterpret_cast<const bf16x8*>(abuf + swz(wm * C::TM + i * 32 + (lane & 31), chunk));
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j)
+    f.b[j] = *reinterpret_cast<const bf16x8*>(bbuf + swz(wn * C::TN + j * 32 + (lane & 31), chunk));
+}
+
+template <class C>
+__device__ __forceinline__ void d_mfma(f32x16 (&acc)[C::FM][C::FN], const DFrags<C>& f) {
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// One K-step on (acur, bcur). LOAD: start step kt+1's Z tile into anxt and
+// step kt+2's packed words into rl. WRITE: expand rn (step kt+1's words) into
+// bnxt. Ends with every Z load of this step landed and a barrier.
+template <class C, bool LOAD, bool WRITE>
+__device__ __forceinline__ void d_step(f32x16 (&acc)[C::FM][C::FN], const char* acur,
+                                       const char* bcur, char* anxt, char* bnxt,
+                                       uint32_t (&rn)[C::B_PER], uint32_t (&rl)[C::B_PER],
+                                       const uint16_t* Z, const uint32_t* wp, int M, int d,
+                                       int m0, int n0, int kt, int wm, int wn, int lane) {
+  if constexpr (LOAD) {
+    d_load_a<C>(anxt, Z, M, d, m0, (kt + 1) * BK);
+    d_load_b<C>(rl, wp, d, n0, (kt + 2) * BK);
+  }
+  DFrags<C> f0, f1;
+  d_read<C>(f0, acur, bcur, wm, wn, lane, 0);
+  d_read<C>(f1, acur, bcur, wm, wn, lane, 16);
+  d_mfma<C>(acc, f0);
+  if constexpr (WRITE) d_write_b<C>(rn, bnxt, 0);
+  d_read<C>(f0, acur, bcur, wm, wn, lane, 32);
+  d_mfma<C>(acc, f1);
+  if constexpr (WRITE) d_write_b<C>(rn, bnxt, 1);
+  d_read<C>(f1, acur, bcur, wm, wn, lane, 48);
+  d_mfma<C>(acc, f0);
+  if constexpr (WRITE) d_write_b<C>(rn, bnxt, 2);
+  d_mfma<C>(acc, f1);
+  if constexpr (WRITE) d_write_b<C>(rn, bnxt, 3);
+  if constexpr (LOAD) wait_vmcnt<C::B_PER>();  // Z tile of kt+1 has landed
+  __syncthreads();
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void gemm_dl_kernel(const uint16_t* Z,
+                                                             const uint32_t* wp, uint16_t* H,
+                                                             int M, int d, float alpha,
+                                                             int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char a0[C::A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char a1[C::A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char b0[C::B_BYTES];
+  __shared__ __attribute__((aligned(1024))) char b1[C::B_BYTES];
+
+  const int ntiles = tiles_m * tiles_n;
+  const int bid = blockIdx.x;
+  int tile = bid;
+  if (ntiles % 8 == 0) tile = (bid % 8) * (ntiles / 8) + bid / 8;
+  const int m0 = (tile / tiles_n) * C::BM, n0 = (tile % tiles_n) * C::BN;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = d / BK;  // even
+  uint32_t r0[C::B_PER], r1[C::B_PER];
+  d_load_a<C>(a0, Z, M, d, m0, 0);
+  d_load_b<C>(r0, wp, d, n0, 0);
+  d_load_b<C>(r1, wp, d, n0, BK);
+#pragma unroll
+  for (int part = 0; part < 4; ++part) d_write_b<C>(r0, b0, part);
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  int kt = 0;
+  for (; kt + 2 < nk; kt += 2) {
+    d_step<C, true, true>(acc, a0, b0, a1, b1, r1, r0, Z, wp, M, d, m0, n0, kt, wm, wn, lane);
+    d_step<C, true, true>(acc, a1, b1, a0, b0, r0, r1, Z, wp, M, d, m0, n0, kt + 1, wm, wn, lane);
+  }
+  // kt = nk - 2: its Z tile for nk-1 still has to be fetched.
+  d_load_a<C>(a1, Z, M, d, m0, (kt + 1) * BK);
+  d_step<C, false, true>(acc, a0, b0, a1, b1, r1, r0, Z, wp, M, d, m0, n0, kt, wm, wn, lane);
+  // (the barrier inside d_step<.., false, ..> needs the Z loads landed first)
+  d_step<C, false, false>(acc, a1, b1, a0, b0, r0, r1, Z, wp, M, d, m0, n0, kt + 1, wm, wn, lane);
+
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int col = n0 + wn * C::TN + j * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * C::TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row < M) H[(size_t)row * d + col] = (uint16_t)f32_to_bf16_bits(alpha * acc[i][j][r]);
+      }
+    }
+}
+
+template <class C>
+hipError_t launch_dl(const uint16_t* z, const uint32_t* wp, uint16_t* h, int M, int d,
+                     float alpha, hipStream_t s) {
+  const int tm = (M + C::BM - 1) / C::BM, tn = d / C::BN;
+  hipLaunchKernelGGL(gemm_dl_kernel<C>, dim3(tm * tn), dim3(C::THREADS), 0, s, z, wp, h, M, d,
+                     alpha, tm, tn);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm(bmoe_dtype dt, int M, int d, const void* z, const uint32_t* w_packed,
-                       float alpha, float* h, hipStream_t s) {
-  dim3 grid((M + BM - 1) / BM, (d + BN - 1) / BN);
-  if (dt == BMOE_BF16)
-    hipLaunchKernelGGL(gemm_kernel<false>, grid, dim3(kThreads), 0, s, z, w_packed, h, M, d, alpha);
-  else
-    hipLaunchKernelGGL(gemm_kernel<true>, grid, dim3(kThreads), 0, s, z, w_packed, h, M, d, alpha);
-  return hipGetLastError();
+                       float alpha, void* h, hipStream_t s) {
+  if (dt == BMOE_F32)
+    return launch_cfg<Cfg<64, 64, 2, 2, true>, float>(z, w_packed, static_cast<float*>(h), M, d,
+                                                      alpha, s);
+  uint16_t* hb = static_cast<uint16_t*>(h);
+  const uint16_t* zb = static_cast<const uint16_t*>(z);
+  // Large problems: 256x256 tiles (4 waves of 128x128). Smaller ones: 128x128
+  // tiles so that the grid still covers the 256 CUs.
+  const long long big_tiles = (long long)((M + 255) / 256) * (d / 256);
+  if (d >= 256 && big_tiles >= 512)
+    return launch_dl<DCfg<256, 256, 2, 4>>(zb, w_packed, hb, M, d, alpha, s);
+  if (d >= 128) return launch_dl<DCfg<128, 128, 2, 2>>(zb, w_packed, hb, M, d, alpha, s);
+  return launch_cfg<Cfg<64, 64, 2, 2, false>, uint16_t>(z, w_packed, hb, M, d, alpha, s);
 }
 
 }  // namespace bmoe

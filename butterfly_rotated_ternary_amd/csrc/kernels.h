@@ -25,17 +25,18 @@ hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, con
 hipError_t launch_bfly_in(bmoe_dtype dt, int M, int d, int k, const void* x,
                           const RouteTables& rt, const float2* cs_in, void* z, hipStream_t s);
 
-// H = alpha * Z W_base^T over all M sorted rows.
+// H = alpha * Z W_base^T over all M sorted rows (H bf16 on the bf16 path,
+// fp32 on the fp32 path; Z likewise).
 hipError_t launch_gemm(bmoe_dtype dt, int M, int d, const void* z, const uint32_t* w_packed,
-                       float alpha, float* h, hipStream_t s);
+                       float alpha, void* h, hipStream_t s);
 
 // U[r] = g_r * B(phi_e) H[q] for r = perm[q], written in routed order.
-hipError_t launch_bfly_out(int M, int d, const float* h, const float* gates,
-                           const RouteTables& rt, const float2* cs_out, float* u,
+hipError_t launch_bfly_out(bmoe_dtype dt, int M, int d, const void* h, const float* gates,
+                           const RouteTables& rt, const float2* cs_out, void* u,
                            hipStream_t s);
 
 // y[t] = sum_j U[t*k + j], ascending j.
-hipError_t launch_combine(bmoe_dtype dt, int T, int d, int k, const float* u, void* y,
+hipError_t launch_combine(bmoe_dtype dt, int T, int d, int k, const void* u, void* y,
                           hipStream_t s);
 
 hipError_t launch_pack(const int8_t* w, int d, uint32_t* packed, int32_t* status,

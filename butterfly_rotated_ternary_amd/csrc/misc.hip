@@ -9,25 +9,39 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// y[t] = sum_j U[t*k + j] for ascending j. U rows already carry their gate.
-template <typename YT>
-__global__ __launch_bounds__(kThreads) void combine_kernel(const float* U, YT* y, int T, int d,
+// y[t] = sum_j U[t*k + j] for ascending j, in fp32. U rows already carry
+// their gate. Each thread handles 8 consecutive values of one token.
+template <typename UT, typename YT>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const UT* U, YT* y, int T, int d,
                                                            int k) {
-  const int d4 = d / 4;
-  const size_t n = (size_t)T * d4;
+  const int d8 = d / 8;
+  const size_t n = (size_t)T * d8;
   for (size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x; idx < n;
        idx += (size_t)gridDim.x * kThreads) {
-    const size_t t = idx / d4, c = idx % d4;
-    const float4* row = reinterpret_cast<const float4*>(U + t * k * d) + c;
-    float4 acc = row[0];
-    for (int j = 1; j < k; ++j) {
-      const float4 v = row[(size_t)j * d4];
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    const size_t t = idx / d8, c = (idx % d8) * 8;
+    float acc[8];
+    for (int j = 0; j < k; ++j) {
+      const UT* row = U + (t * k + j) * d + c;
+      float v[8];
+      if constexpr (sizeof(UT) == 2) {
+        const uint4 w = *reinterpret_cast<const uint4*>(row);
+        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+        v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+      } else {
+        const float4 a = *reinterpret_cast<const float4*>(row);
+        const float4 b = *reinterpret_cast<const float4*>(row + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[m] = j == 0 ? v[m] : acc[m] + v[m];
     }
+    YT* out = y + t * d + c;
     if constexpr (sizeof(YT) == 2) {
-      reinterpret_cast<uint2*>(y)[idx] = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+      *reinterpret_cast<uint4*>(out) = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                                  pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
     } else {
-      reinterpret_cast<float4*>(y)[idx] = acc;
+      *reinterpret_cast<float4*>(out) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      *reinterpret_cast<float4*>(out + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
     }
   }
 }
@@ -74,15 +88,15 @@ int grid_for(size_t n) {
 
 }  // namespace
 
-hipError_t launch_combine(bmoe_dtype dt, int T, int d, int k, const float* u, void* y,
+hipError_t launch_combine(bmoe_dtype dt, int T, int d, int k, const void* u, void* y,
                           hipStream_t s) {
-  const int g = grid_for((size_t)T * (d / 4));
+  const int g = grid_for((size_t)T * (d / 8));
   if (dt == BMOE_BF16)
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(g), dim3(kThreads), 0, s, u,
-                       static_cast<uint16_t*>(y), T, d, k);
+    hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t>), dim3(g), dim3(kThreads), 0, s,
+                       static_cast<const uint16_t*>(u), static_cast<uint16_t*>(y), T, d, k);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(g), dim3(kThreads), 0, s, u,
-                       static_cast<float*>(y), T, d, k);
+    hipLaunchKernelGGL((combine_kernel<float, float>), dim3(g), dim3(kThreads), 0, s,
+                       static_cast<const float*>(u), static_cast<float*>(y), T, d, k);
   return hipGetLastError();
 }
 

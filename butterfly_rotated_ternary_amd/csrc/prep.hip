@@ -73,9 +73,10 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
   // ---- routing ----------------------------------------------------------
   extern __shared__ int sh[];
   const int N = p.N, M = p.M;
-  int* cnt = sh;            // [N] counts, then offsets
-  int* before = sh + N;     // [N] counts of rows before this chunk, then bases
-  int* wcur = sh + 2 * N;   // [kWaves][N] per-wave counts, then cursors
+  int* cnt = sh;                 // [N] counts, then offsets
+  int* before = sh + N;          // [N] counts of rows before this chunk, then bases
+  int* wcur = sh + 2 * N;        // [kWaves][N] per-wave counts, then cursors
+  int* cid = sh + (2 + kWaves) * N;  // [chunk] this chunk's expert ids (clamped)
   __shared__ int scratch[kWaves];
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -85,11 +86,32 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
   for (int i = tid; i < (2 + kWaves) * N; i += kThreads) sh[i] = 0;
   __syncthreads();
 
+  // Histogram of every id (all blocks need the global offsets), 4 ids per
+  // load, several loads in flight per thread.
   bool bad = false;
-  for (int r = tid; r < M; r += kThreads) {
+  const int M4 = M / 4;
+  const int4* ids4 = reinterpret_cast<const int4*>(p.ids);
+#pragma unroll 4
+  for (int i = tid; i < M4; i += kThreads) {
+    const int4 v = ids4[i];
+    const int r = 4 * i;
+    const int e0 = clamp_expert(v.x, N, bad), e1 = clamp_expert(v.y, N, bad);
+    const int e2 = clamp_expert(v.z, N, bad), e3 = clamp_expert(v.w, N, bad);
+    atomicAdd(&cnt[e0], 1); atomicAdd(&cnt[e1], 1);
+    atomicAdd(&cnt[e2], 1); atomicAdd(&cnt[e3], 1);
+    if (r < r0) {  // chunks start at multiples of 4
+      atomicAdd(&before[e0], 1); atomicAdd(&before[e1], 1);
+      atomicAdd(&before[e2], 1); atomicAdd(&before[e3], 1);
+    }
+  }
+  for (int r = 4 * M4 + tid; r < M; r += kThreads) {
     const int e = clamp_expert(p.ids[r], N, bad);
     atomicAdd(&cnt[e], 1);
     if (r < r0) atomicAdd(&before[e], 1);
+  }
+  for (int r = r0 + tid; r < r1; r += kThreads) {
+    bool dummy = false;
+    cid[r - r0] = clamp_expert(p.ids[r], N, dummy);
   }
   __syncthreads();
 
@@ -117,12 +139,9 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
   // Each wave owns a contiguous quarter of the chunk.
   const int len = r1 - r0;
   const int quarter = (len + kWaves - 1) / kWaves;
-  const int wb = min(r1, r0 + wave * quarter), we = min(r1, wb + quarter);
+  const int wb = min(len, wave * quarter), we = min(len, wb + quarter);
   int* mycur = wcur + wave * N;
-  for (int r = wb + lane; r < we; r += kWave) {
-    bool dummy = false;
-    atomicAdd(&mycur[clamp_expert(p.ids[r], N, dummy)], 1);
-  }
+  for (int r = wb + lane; r < we; r += kWave) atomicAdd(&mycur[cid[r]], 1);
   __syncthreads();
   for (int e = tid; e < N; e += kThreads) {
     int c0 = before[e];
@@ -138,10 +157,9 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
   // found with one ballot per key bit; their order is the lane order.
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   for (int base = wb; base < we; base += kWave) {
-    const int r = base + lane;
-    const bool valid = r < we;
-    bool dummy = false;
-    const int e = valid ? clamp_expert(p.ids[r], N, dummy) : 0;
+    const int rl = base + lane;
+    const bool valid = rl < we;
+    const int e = valid ? cid[rl] : 0;
     uint64_t mask = __ballot(valid);
     for (int b = 0; b < p.nbits; ++b) {
       const bool bit = (e >> b) & 1;
@@ -155,6 +173,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
     __builtin_amdgcn_wave_barrier();
     if (valid) {
       const int q = cur + rank;
+      const int r = r0 + rl;
       p.rt.perm[q] = r;
       p.rt.inv[r] = q;
       p.rt.slot_e[q] = e;
@@ -189,7 +208,7 @@ hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, con
   p.n_ang = (long long)N * L * (d / 2);
   long long trig_blocks = (2 * p.n_ang + kThreads * 8 - 1) / (kThreads * 8);
   if (trig_blocks > 65536) trig_blocks = 65536;
-  const size_t shmem = sizeof(int) * (size_t)(2 + kWaves) * N;
+  const size_t shmem = sizeof(int) * ((size_t)(2 + kWaves) * N + p.chunk);
   if (shmem > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
