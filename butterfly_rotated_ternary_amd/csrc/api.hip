@@ -23,7 +23,7 @@ int log2i(int d) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct FwdLayout {
-  size_t status, offsets, perm, inv, slot_e, cs_in, cs_out, z, h, u, total;
+  size_t status, offsets, perm, inv, slot_e, cs_in, cs_out, z, h, u, w16, total;
 };
 
 bool shape_ok(bmoe_dtype dt, int T, int d, int N, int k) {
@@ -49,6 +49,8 @@ FwdLayout fwd_layout(bmoe_dtype dt, int T, int d, int N, int k) {
   l.z = off;       off = align_up(off + zel * M * d);
   l.h = off;       off = align_up(off + zel * M * d);
   l.u = off;       off = align_up(off + zel * M * d);
+  l.w16 = off;
+  if (fused_supported(dt, d)) off = align_up(off + sizeof(uint16_t) * (size_t)d * d);
   l.total = off;
   return l;
 }
@@ -130,10 +132,21 @@ bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k
     if (!events) return true;
     return hipEventRecord(static_cast<hipEvent_t>(events[ki++]), s) == hipSuccess;
   };
+  const bool fused = fused_supported(dt, d);
+  uint16_t* w16 = fused ? reinterpret_cast<uint16_t*>(base + l.w16) : nullptr;
   if (!mark()) return BMOE_E_HIP;
-  if (launch_prep(ids, M, n_experts, theta, phi, d, rt, cs_in, cs_out, status, s) != hipSuccess)
+  if (launch_prep(ids, M, n_experts, theta, phi, d, rt, cs_in, cs_out, status, w_packed, w16, s) !=
+      hipSuccess)
     return BMOE_E_HIP;
   if (!mark()) return BMOE_E_HIP;
+  if (fused) {
+    if (launch_fused(M, d, k, x, gates, rt, cs_in, cs_out, w16, alpha, u, s) != hipSuccess)
+      return BMOE_E_HIP;
+    if (!mark()) return BMOE_E_HIP;
+    if (launch_combine(dt, T, d, k, u, y, s) != hipSuccess) return BMOE_E_HIP;
+    if (!mark()) return BMOE_E_HIP;
+    return BMOE_OK;
+  }
   if (launch_bfly_in(dt, M, d, k, x, rt, cs_in, z, s) != hipSuccess) return BMOE_E_HIP;
   if (!mark()) return BMOE_E_HIP;
   if (launch_gemm(dt, M, d, z, w_packed, alpha, h, s) != hipSuccess) return BMOE_E_HIP;
@@ -155,14 +168,15 @@ bmoe_status bmoe_forward(bmoe_dtype dt, int T, int d, int n_experts, int k, cons
 
 int bmoe_forward_kernel_count(bmoe_dtype dt, int T, int d, int n_experts, int k) {
   if (!shape_ok(dt, T, d, n_experts, k) || T == 0) return 0;
-  return 5;
+  return fused_supported(dt, d) ? 3 : 5;
 }
 
 const char* bmoe_forward_kernel_name(bmoe_dtype dt, int T, int d, int n_experts, int k, int i) {
-  static const char* names_bf16[] = {"prep_kernel", "bfly_in_kernel", "gemm_kernel",
-                                     "bfly_out_kernel", "combine_kernel"};
+  static const char* fused_names[] = {"prep_kernel", "fused_kernel", "combine_kernel"};
+  static const char* split_names[] = {"prep_kernel", "bfly_in_kernel", "gemm_kernel",
+                                      "bfly_out_kernel", "combine_kernel"};
   if (i < 0 || i >= bmoe_forward_kernel_count(dt, T, d, n_experts, k)) return "";
-  return names_bf16[i];
+  return fused_supported(dt, d) ? fused_names[i] : split_names[i];
 }
 
 bmoe_status bmoe_sync_status(const void* ws, void* stream) {

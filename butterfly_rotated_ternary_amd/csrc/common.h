@@ -38,6 +38,15 @@ __device__ __forceinline__ uint32_t unpack_pair(uint32_t w, int j) {
   return __umul24(t & 0x00800080u, 0x7Fu) + (t & 0x80008000u);
 }
 
+// Workgroup barrier ordering LDS traffic only: waits for this wave's LDS
+// operations, then s_barrier. Unlike __syncthreads it does not wait for
+// global->LDS loads still in flight; code that needs their data waits for
+// them explicitly (vmcnt) first. The memory clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Index of the j-th element of a block of 2^g elements whose varying index
 // bits start at bit s_lo; `b` enumerates blocks (all other index bits).
 __device__ __forceinline__ int block_base(int b, int s_lo, int g) {

@@ -361,7 +361,8 @@ __device__ __forceinline__ void d_step(f32x16 (&acc)[C::FM][C::FN], const char* 
   d_mfma<C>(acc, f1);
   if constexpr (WRITE) d_write_b<C>(rn, bnxt, 3);
   if constexpr (LOAD) wait_vmcnt<C::B_PER>();  // Z tile of kt+1 has landed
-  __syncthreads();
+  else wait_vmcnt<0>();
+  lds_barrier();
 }
 
 template <class C>

@@ -15,11 +15,21 @@ struct RouteTables {
   int32_t* slot_e;   // [M] sorted slot -> expert
 };
 
-// Routing (histogram, scan, stable scatter) and the per-call cos/sin tables
-// of both rotation sides, in one launch.
+// Routing (histogram, scan, stable scatter), the per-call cos/sin tables of
+// both rotation sides and (if w16 is not NULL) the bf16 expansion of the
+// packed substrate, in one launch.
 hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, const float* phi,
                        int d, RouteTables rt, float2* cs_in, float2* cs_out, int32_t* status,
-                       hipStream_t s);
+                       const uint32_t* w_packed, uint16_t* w16, hipStream_t s);
+
+// Whether the fused d <= 512 path handles this shape.
+bool fused_supported(bmoe_dtype dt, int d);
+
+// Fused per-tile forward for d <= 512 (bf16): U[r] = g_r * B(phi_e) *
+// alpha * W_base * B(theta_e)^T x[t] for every routed row, in routed order.
+hipError_t launch_fused(int M, int d, int k, const void* x, const float* gates,
+                        const RouteTables& rt, const float2* cs_in, const float2* cs_out,
+                        const uint16_t* w16, float alpha, void* u, hipStream_t s);
 
 // Z[q] = B(theta_e)^T x[t]   (t = perm[q] / k, e = slot_e[q]).
 hipError_t launch_bfly_in(bmoe_dtype dt, int M, int d, int k, const void* x,

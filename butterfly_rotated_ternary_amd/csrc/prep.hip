@@ -1,4 +1,5 @@
 // Per-call preparation, one launch:
+//  * (fused path) the packed substrate expanded to bf16 rows once per call;
 //  * routing: per-expert histogram, exclusive scan and a stable scatter of
 //    routed rows r = t*k + j grouped by expert (ascending r inside a group);
 //  * the cos/sin tables of both rotation sides, computed once per call so no
@@ -26,6 +27,10 @@ struct PrepParams {
   float2* cs_in;
   float2* cs_out;
   long long n_ang;  // angles per side: N * L * d/2
+  // Optional expansion of the packed substrate to bf16 [d][d] (NULL: none).
+  const uint32_t* w_packed;
+  uint16_t* w16;
+  int d, n_trig_blocks;
 };
 
 __device__ __forceinline__ int clamp_expert(int e, int N, bool& bad) {
@@ -54,10 +59,24 @@ __device__ int block_exclusive_scan(int v, int* scratch) {
 }
 
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
+  if ((int)blockIdx.x >= p.n_route_blocks + p.n_trig_blocks) {
+    // ---- packed substrate -> bf16 rows ----------------------------------
+    const int G = p.d / 16;
+    const size_t nwords = (size_t)p.d * G;
+    const int b = blockIdx.x - p.n_route_blocks - p.n_trig_blocks;
+    const int nb = gridDim.x - p.n_route_blocks - p.n_trig_blocks;
+    for (size_t i = (size_t)b * kThreads + threadIdx.x; i < nwords; i += (size_t)nb * kThreads) {
+      const uint32_t w = p.w_packed[i];
+      uint4* dst = reinterpret_cast<uint4*>(p.w16 + i * 16);
+      dst[0] = make_uint4(unpack_pair(w, 0), unpack_pair(w, 1), unpack_pair(w, 2), unpack_pair(w, 3));
+      dst[1] = make_uint4(unpack_pair(w, 4), unpack_pair(w, 5), unpack_pair(w, 6), unpack_pair(w, 7));
+    }
+    return;
+  }
   if ((int)blockIdx.x >= p.n_route_blocks) {
     // ---- cos/sin tables -------------------------------------------------
     const long long total = 2 * p.n_ang;
-    const long long stride = (long long)(gridDim.x - p.n_route_blocks) * kThreads;
+    const long long stride = (long long)p.n_trig_blocks * kThreads;
     for (long long i = (long long)(blockIdx.x - p.n_route_blocks) * kThreads + threadIdx.x;
          i < total; i += stride) {
       const bool out_side = i >= p.n_ang;
@@ -187,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
 
 hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, const float* phi,
                        int d, RouteTables rt, float2* cs_in, float2* cs_out, int32_t* status,
-                       hipStream_t s) {
+                       const uint32_t* w_packed, uint16_t* w16, hipStream_t s) {
   int L = 0;
   while ((1 << L) < d) ++L;
   PrepParams p;
@@ -208,13 +227,22 @@ hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, con
   p.n_ang = (long long)N * L * (d / 2);
   long long trig_blocks = (2 * p.n_ang + kThreads * 8 - 1) / (kThreads * 8);
   if (trig_blocks > 65536) trig_blocks = 65536;
+  p.n_trig_blocks = (int)trig_blocks;
+  p.w_packed = w_packed;
+  p.w16 = w16;
+  p.d = d;
+  int w_blocks = 0;
+  if (w16) {
+    const long long words = (long long)d * (d / 16);
+    w_blocks = (int)((words + kThreads * 4 - 1) / (kThreads * 4));
+  }
   const size_t shmem = sizeof(int) * ((size_t)(2 + kWaves) * N + p.chunk);
   if (shmem > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(prep_kernel, dim3(p.n_route_blocks + (int)trig_blocks), dim3(kThreads),
+  hipLaunchKernelGGL(prep_kernel, dim3(p.n_route_blocks + p.n_trig_blocks + w_blocks), dim3(kThreads),
                      shmem, s, p);
   return hipGetLastError();
 }
