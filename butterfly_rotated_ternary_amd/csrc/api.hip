@@ -140,7 +140,7 @@ bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k
     return BMOE_E_HIP;
   if (!mark()) return BMOE_E_HIP;
   if (fused) {
-    if (launch_fused(M, d, k, x, gates, rt, cs_in, cs_out, w16, alpha, u, s) != hipSuccess)
+    if (launch_fused(M, d, k, x, gates, rt, cs_in, cs_out, w16, w_packed, alpha, u, s) != hipSuccess)
       return BMOE_E_HIP;
     if (!mark()) return BMOE_E_HIP;
     if (launch_combine(dt, T, d, k, u, y, s) != hipSuccess) return BMOE_E_HIP;

@@ -13,8 +13,9 @@
 // LDS (160 KiB at d = 512): four ring stages and the A tile, each its own
 // array so the compiler can tell the stage being read from the stages the
 // DMA is filling. The fp32 rows live inside ring stages 1..3 (14 rows per
-// stage; they are used only before and after the GEMM), so ring stage 0 is
-// filled while butterfly-in runs.
+// stage; they are used only before and after the GEMM). The first K-steps of
+// the GEMM take the substrate from packed words in registers, which leaves
+// time for the ring to fill after the rows are dead.
 #include "common.h"
 #include "kernels.h"
 
@@ -31,8 +32,14 @@ template <int D>
 struct FCfg {
   static constexpr int L = D == 128 ? 7 : D == 256 ? 8 : 9;
   static constexpr int PD = D + D / 8;              // padded fp32 row (floats)
-  static constexpr int KS = 32;                     // K per ring stage
+  static constexpr int KS = 32;                     // K per GEMM step
   static constexpr int NSTEP = D / KS;
+  // The first NP steps take B from the packed 2-bit words (registers, VALU
+  // expansion); the remaining NR steps from the bf16 substrate via the ring.
+  // Splitting K balances VALU against L2 bandwidth: with every CU streaming
+  // the substrate at once, bf16 alone is L2-bound, packed alone VALU-bound.
+  static constexpr int NP = NSTEP * 3 / 4;
+  static constexpr int NR = NSTEP - NP;  // <= 4: every ring stage is prefetched
   static constexpr int STAGE_BYTES = D * KS * 2;    // D rows of 64 bytes
   static constexpr int NSTAGE = 4;
   static constexpr int ZT_BYTES = kBM * D * 2;
@@ -46,7 +53,7 @@ struct FCfg {
   static constexpr int LPW = STAGE_BYTES / 1024 / kWavesF;  // 1 KiB wave loads per wave per stage
   static_assert(FN >= 1 && LPW >= 1, "d too small for this tiling");
   static_assert(3 * RPS >= kBM && 2 * RPS < kBM, "rows must end in ring stage 3");
-  static_assert(NSTEP >= 4, "ring needs at least four K-steps");
+  static_assert(NR >= 1 && NR <= NSTAGE, "ring steps must fit the four stages");
   static_assert(META_OFF + 2 * kBM * 4 <= STAGE_BYTES, "metadata must fit in stage 3");
 };
 
@@ -223,6 +230,7 @@ struct BflyCoef {
 
 template <int D>
 __device__ __forceinline__ void ring_load(char* stage, const uint16_t* w16, int step) {
+  // step: global K-step index (K offset step * KS)
   using C = FCfg<D>;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
 #pragma unroll
@@ -237,6 +245,18 @@ __device__ __forceinline__ void ring_load(char* stage, const uint16_t* w16, int 
   }
 }
 
+// Eight bf16 {-1,0,+1} of one packed word: values 8h .. 8h+7 (h = 0, 1).
+__device__ __forceinline__ bf16x8 unpack_frag(uint32_t w, int h) {
+  const int s0 = 7 - 4 * h;
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t t = w << (s0 - i);
+    r[i] = __umul24(t & 0x00800080u, 0x7Fu) + (t & 0x80008000u);
+  }
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
@@ -248,7 +268,8 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(int M, int k, const uin
                                                          const int32_t* slot_e,
                                                          const float2* cs_in,
                                                          const float2* cs_out,
-                                                         const uint16_t* w16, float alpha,
+                                                         const uint16_t* w16,
+                                                         const uint32_t* wp, float alpha,
                                                          uint16_t* u) {
   using C = FCfg<D>;
   __shared__ __attribute__((aligned(1024))) char st0[C::STAGE_BYTES];
@@ -273,15 +294,16 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(int M, int k, const uin
   const int q_meta = q0 + min(lane & 31, nr - 1);
   const int my_e = slot_e[q_meta];
   const int my_r = perm[q_meta];
+  const int my_t = my_r / k;
   if (tid < kBM) {
     sh_e[tid] = my_e;
     sh_r[tid] = my_r;
   }
-  __syncthreads();
 
   // Gather x rows (8 bf16 per 16-byte chunk) into registers, fetch the
-  // butterfly-in coefficients, and only then start ring stage 0 (global loads
-  // complete in issue order, so later loads would wait behind the DMA).
+  // butterfly-in coefficients and the packed substrate words of the first NP
+  // K-steps. Token indices come from the lanes holding them (no LDS round
+  // trip). Tail rows past nr repeat the last row: computed, never stored.
   constexpr int CPR = D / 8;
   constexpr int XPT = kBM * CPR / kThreads;
   uint4 xv[XPT];
@@ -289,12 +311,20 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(int M, int k, const uin
   for (int it = 0; it < XPT; ++it) {
     const int c = tid + it * kThreads;
     const int i = c / CPR, ch = c % CPR;
-    xv[it] = make_uint4(0u, 0u, 0u, 0u);
-    if (i < nr) xv[it] = *reinterpret_cast<const uint4*>(x + (size_t)(sh_r[i] / k) * D + ch * 8);
+    const int t = __shfl(my_t, i, 64);
+    xv[it] = *reinterpret_cast<const uint4*>(x + (size_t)t * D + ch * 8);
   }
   BflyCoef<D, true> cin;
-  cin.prefetch(cs_in, sh_e);
-  ring_load<D>(st0, w16, 0);  // stage 0 does not overlap the rows
+  cin.prefetch_from_lanes(cs_in, my_e);
+  // lane l needs W rows o = wave*WN + 32j + (l & 31), two words per K-step.
+  uint2 pw[C::NP][C::FN];
+#pragma unroll
+  for (int ks = 0; ks < C::NP; ++ks)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int o = wave * C::WN + j * 32 + (lane & 31);
+      pw[ks][j] = *reinterpret_cast<const uint2*>(wp + (size_t)o * (D / 16) + 2 * ks);
+    }
 #pragma unroll
   for (int it = 0; it < XPT; ++it) {
     const int c = tid + it * kThreads;
@@ -304,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(int M, int k, const uin
     dst[0] = bf16_lo(v.x); dst[1] = bf16_hi(v.x); dst[2] = bf16_lo(v.y); dst[3] = bf16_hi(v.y);
     dst[4] = bf16_lo(v.z); dst[5] = bf16_hi(v.z); dst[6] = bf16_lo(v.w); dst[7] = bf16_hi(v.w);
   }
-  lds_barrier();
+  __syncthreads();
 
   cin.apply(rows, cs_in, sh_e);
 
@@ -319,8 +349,15 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(int M, int k, const uin
                    pack_bf16x2(s[6], s[7]));
   }
   lds_barrier();  // rows are dead from here until the GEMM ends
-  ring_load<D>(st1, w16, 1);
-  ring_load<D>(st2, w16, 2);
+  // Butterfly-out coefficients (for the expert of each thread's first row)
+  // and then every ring stage are requested now; the packed K-steps run while
+  // they land. Loads complete in issue order, so the coefficients go first.
+  BflyCoef<D, false> cout;
+  cout.prefetch_from_lanes(cs_out, my_e);
+  ring_load<D>(st0, w16, C::NP);
+  if (C::NR > 1) ring_load<D>(st1, w16, C::NP + 1);
+  if (C::NR > 2) ring_load<D>(st2, w16, C::NP + 2);
+  if (C::NR > 3) ring_load<D>(st3, w16, C::NP + 3);
 
   // ---- substrate GEMM: wave w computes rows 0..31 x columns [w*WN, (w+1)*WN)
   f32x16 acc[C::FN];
@@ -329,20 +366,36 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(int M, int k, const uin
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
 
+  const int ra = lane & 31;
+  // K-steps from the packed words.
 #pragma unroll
-  for (int ks = 0; ks < C::NSTEP; ++ks) {
-    // Loads issued after step ks: steps ks+1, ks+2 (while they exist).
-    const int after = (ks + 2 < C::NSTEP) ? 2 : (ks + 1 < C::NSTEP ? 1 : 0);
-    if (after == 2) wait_vm<2 * C::LPW>();
-    else if (after == 1) wait_vm<C::LPW>();
-    else wait_vm<0>();
-    lds_barrier();  // step ks visible to all waves; step ks-1's stage is free
-    if (ks + 3 < C::NSTEP) ring_load<D>(stage((ks + 3) % 4), w16, ks + 3);
-    const char* st = stage(ks % 4);
+  for (int ks = 0; ks < C::NP; ++ks) {
 #pragma unroll
     for (int kk = 0; kk < C::KS; kk += 16) {
       const int ca = (ks * C::KS + kk) / 8 + (lane >> 5);
-      const int ra = lane & 31;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(zt + ra * (2 * D) + 16 * (ca ^ (ra & 15)));
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        const bf16x8 b = unpack_frag(kk == 0 ? pw[ks][j].x : pw[ks][j].y, lane >> 5);
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+      }
+    }
+  }
+  // K-steps from the bf16 ring.
+#pragma unroll
+  for (int rs = 0; rs < C::NR; ++rs) {
+    // Stages requested after stage rs: rs+1 .. NR-1.
+    const int after = C::NR - 1 - rs;
+    if (after == 3) wait_vm<3 * C::LPW>();
+    else if (after == 2) wait_vm<2 * C::LPW>();
+    else if (after == 1) wait_vm<C::LPW>();
+    else wait_vm<0>();
+    lds_barrier();  // every wave's part of stage rs has landed
+    const char* st = stage(rs);
+    const int ks = C::NP + rs;
+#pragma unroll
+    for (int kk = 0; kk < C::KS; kk += 16) {
+      const int ca = (ks * C::KS + kk) / 8 + (lane >> 5);
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(zt + ra * (2 * D) + 16 * (ca ^ (ra & 15)));
       const int cb = kk / 8 + (lane >> 5);
 #pragma unroll
@@ -353,10 +406,6 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(int M, int k, const uin
       }
     }
   }
-  // Butterfly-out coefficients for the expert of each thread's first row,
-  // fetched while the GEMM results go to LDS.
-  BflyCoef<D, false> cout;
-  cout.prefetch_from_lanes(cs_out, my_e);
   __syncthreads();  // every wave is done with the ring: rows may be rewritten
   if (tid < kBM) {
     sh_e[tid] = my_e;
@@ -396,11 +445,11 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(int M, int k, const uin
 
 template <int D>
 hipError_t launch_d(int M, int k, const void* x, const float* gates, const RouteTables& rt,
-                    const float2* cs_in, const float2* cs_out, const uint16_t* w16, float alpha,
-                    void* u, hipStream_t s) {
+                    const float2* cs_in, const float2* cs_out, const uint16_t* w16,
+                    const uint32_t* wp, float alpha, void* u, hipStream_t s) {
   hipLaunchKernelGGL(fused_kernel<D>, dim3((M + kBM - 1) / kBM), dim3(kThreads), 0, s, M, k,
                      static_cast<const uint16_t*>(x), gates, rt.perm, rt.slot_e, cs_in, cs_out,
-                     w16, alpha, static_cast<uint16_t*>(u));
+                     w16, wp, alpha, static_cast<uint16_t*>(u));
   return hipGetLastError();
 }
 
@@ -412,10 +461,11 @@ bool fused_supported(bmoe_dtype dt, int d) {
 
 hipError_t launch_fused(int M, int d, int k, const void* x, const float* gates,
                         const RouteTables& rt, const float2* cs_in, const float2* cs_out,
-                        const uint16_t* w16, float alpha, void* u, hipStream_t s) {
+                        const uint16_t* w16, const uint32_t* wp, float alpha, void* u,
+                        hipStream_t s) {
   switch (d) {
-    case 256: return launch_d<256>(M, k, x, gates, rt, cs_in, cs_out, w16, alpha, u, s);
-    case 512: return launch_d<512>(M, k, x, gates, rt, cs_in, cs_out, w16, alpha, u, s);
+    case 256: return launch_d<256>(M, k, x, gates, rt, cs_in, cs_out, w16, wp, alpha, u, s);
+    case 512: return launch_d<512>(M, k, x, gates, rt, cs_in, cs_out, w16, wp, alpha, u, s);
   }
   return hipErrorInvalidValue;
 }

@@ -29,7 +29,8 @@ bool fused_supported(bmoe_dtype dt, int d);
 // alpha * W_base * B(theta_e)^T x[t] for every routed row, in routed order.
 hipError_t launch_fused(int M, int d, int k, const void* x, const float* gates,
                         const RouteTables& rt, const float2* cs_in, const float2* cs_out,
-                        const uint16_t* w16, float alpha, void* u, hipStream_t s);
+                        const uint16_t* w16, const uint32_t* w_packed, float alpha, void* u,
+                        hipStream_t s);
 
 // Z[q] = B(theta_e)^T x[t]   (t = perm[q] / k, e = slot_e[q]).
 hipError_t launch_bfly_in(bmoe_dtype dt, int M, int d, int k, const void* x,
