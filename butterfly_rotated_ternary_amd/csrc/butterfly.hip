@@ -215,6 +215,225 @@ __global__ __launch_bounds__(kThreads) void bfly_kernel(BflyParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-d kernel (bf16, d >= 1024): 8 waves, R rows per workgroup with R*d
+// fp32 (padded) filling ~144 KiB of LDS, so each coefficient a thread loads
+// serves R rows. Every stage group's coefficients are requested in one round
+// trip up front; rows are rotated four at a time while they share an expert.
+constexpr int kBigThreads = 512;
+
+template <int D>
+struct BigCfg {
+  static_assert(D == 1024 || D == 2048 || D == 4096, "large-d kernel sizes");
+  static constexpr int L = D == 1024 ? 10 : D == 2048 ? 11 : 12;
+  static constexpr int PD = D + D / 8;
+  static constexpr int R = 147456 / (PD * 4) >= 32 ? 32 : 147456 / (PD * 4) >= 16 ? 16
+                         : 147456 / (PD * 4) >= 8 ? 8 : 4;
+  static constexpr int NG = (L + 2) / 3;
+};
+
+template <int D, bool TR>
+struct BigGroups {
+  static constexpr int L = BigCfg<D>::L;
+  static constexpr int s_hi(int g) { return TR ? L - 1 - 3 * g : (3 * g + 2 < L ? 3 * g + 2 : L - 1); }
+  static constexpr int s_lo(int g) { return TR ? (L - 3 - 3 * g > 0 ? L - 3 - 3 * g : 0) : 3 * g; }
+  static constexpr int G(int g) { return s_hi(g) - s_lo(g) + 1; }
+  // Blocks of 2^G elements per row; at these sizes there are at most as many
+  // blocks as threads, so each thread owns one block and TPB threads share it
+  // (each taking every TPB-th row).
+  static constexpr int NB(int g) { return D >> G(g); }
+  static constexpr int TPB(int g) { return kBigThreads / NB(g); }
+  static constexpr bool fits() {
+    for (int g = 0; g < BigCfg<D>::NG; ++g)
+      if (NB(g) > kBigThreads) return false;
+    return true;
+  }
+};
+
+template <int D, int G>
+__device__ __forceinline__ void big_coef(float2 (&c)[3][4], const float2* cs, int e, int s_lo,
+                                         int base) {
+  constexpr int L = BigCfg<D>::L;
+#pragma unroll
+  for (int t = 0; t < G; ++t) {
+    const int s = s_lo + t;
+    const float2* tab = cs + ((size_t)e * L + s) * (D / 2);
+#pragma unroll
+    for (int u = 0; u < (1 << (G - 1)); ++u) {
+      const int m = ((u >> t) << (t + 1)) | (u & ((1 << t) - 1));
+      c[t][u] = tab[pair_index(base + (m << s_lo), s)];
+    }
+  }
+}
+
+// One group, one block: rotate this thread's rows [ph, ph+tpb, ...) of the
+// tile; coefficients c are valid for expert ce (reloaded when a row differs).
+template <int D, int G, bool TR>
+__device__ __forceinline__ void big_rows(float* rows, const int* sh_e, int nrows, const float2* cs,
+                                         float2 (&c)[3][4], int& ce, int s_lo, int base, int ph,
+                                         int tpb) {
+  constexpr int PD = BigCfg<D>::PD;
+  int off[8];
+#pragma unroll
+  for (int m = 0; m < (1 << G); ++m) off[m] = pad(base + (m << s_lo));
+  const int rpt = (nrows - ph + tpb - 1) / tpb;  // rows of this thread
+  const int last = ph + (rpt - 1) * tpb;
+  if (rpt > 0 && sh_e[ph] == ce && sh_e[last] == ce) {
+    for (int j0 = 0; j0 < rpt; j0 += 4) {
+      float v[4][8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (j0 + q < rpt) {
+          const float* row = rows + (ph + (j0 + q) * tpb) * PD;
+#pragma unroll
+          for (int m = 0; m < (1 << G); ++m) v[q][m] = row[off[m]];
+        }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rotate_block<G, TR>(v[q], c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (j0 + q < rpt) {
+          float* row = rows + (ph + (j0 + q) * tpb) * PD;
+#pragma unroll
+          for (int m = 0; m < (1 << G); ++m) row[off[m]] = v[q][m];
+        }
+    }
+    return;
+  }
+  for (int j = 0; j < rpt; ++j) {
+    const int i = ph + j * tpb;
+    if (sh_e[i] != ce) {
+      ce = sh_e[i];
+      big_coef<D, G>(c, cs, ce, s_lo, base);
+    }
+    float* row = rows + i * PD;
+    float v[8];
+#pragma unroll
+    for (int m = 0; m < (1 << G); ++m) v[m] = row[off[m]];
+    rotate_block<G, TR>(v, c);
+#pragma unroll
+    for (int m = 0; m < (1 << G); ++m) row[off[m]] = v[m];
+  }
+}
+
+// IN_SIDE:  z[q] = B(theta_e)^T x[perm[q] / k]          (sorted order)
+// OUT_SIDE: u[perm[q]] = g * B(phi_e) h[q]               (routed order)
+template <int D, bool IN_SIDE>
+__global__ __launch_bounds__(kBigThreads) void bfly_big_kernel(BflyParams p) {
+  using C = BigCfg<D>;
+  using Gr = BigGroups<D, IN_SIDE>;
+  constexpr int PD = C::PD, R = C::R, NG = C::NG;
+  extern __shared__ float rows[];
+  __shared__ int sh_e[R], sh_r[R];
+  const int tid = threadIdx.x, lane = tid % kWave;
+  // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
+  // contiguous run of tiles so an expert's coefficient tables are fetched
+  // into one or two XCD L2s rather than all eight.
+  const int nb = gridDim.x, xcd = blockIdx.x % 8, per = nb / 8, extra = nb % 8;
+  const int tile = xcd * per + min(xcd, extra) + blockIdx.x / 8;
+  const int q0 = tile * R;
+  const int nr = min(R, p.M - q0);
+
+  // Row metadata: lane l (< R) of every wave holds row l's (expert, routed
+  // index); rows past nr repeat the last row (computed, never stored).
+  const int qm = q0 + min(lane % R, nr - 1);
+  const int my_e = p.slot_e[qm];
+  const int my_r = p.perm[qm];
+  const int my_src = IN_SIDE ? my_r / p.k : qm;
+  if (tid < R) {
+    sh_e[tid] = my_e;
+    sh_r[tid] = my_r;
+  }
+
+  // Source rows: 16-byte chunks (8 bf16) into registers.
+  constexpr int CPR = D / 8;
+  constexpr int LPT = R * CPR / kBigThreads;
+  uint4 xv[LPT];
+  const uint16_t* src = static_cast<const uint16_t*>(p.src);
+#pragma unroll
+  for (int it = 0; it < LPT; ++it) {
+    const int c = tid + it * kBigThreads;
+    const int i = c / CPR, ch = c % CPR;
+    const int sr = __shfl(my_src, i, 64);
+    xv[it] = *reinterpret_cast<const uint4*>(src + (size_t)sr * D + ch * 8);
+  }
+  // Coefficients of every group for the expert of the thread's first row.
+  float2 coef[NG][3][4];
+  int ce[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int G = Gr::G(g), s_lo = Gr::s_lo(g), nb = Gr::NB(g);
+    const int base = block_base(tid % nb, s_lo, G);
+    ce[g] = __shfl(my_e, tid / nb, 64);
+    if (G == 3) big_coef<D, 3>(coef[g], p.cs, ce[g], s_lo, base);
+    else if (G == 2) big_coef<D, 2>(coef[g], p.cs, ce[g], s_lo, base);
+    else big_coef<D, 1>(coef[g], p.cs, ce[g], s_lo, base);
+  }
+#pragma unroll
+  for (int it = 0; it < LPT; ++it) {
+    const int c = tid + it * kBigThreads;
+    const int i = c / CPR, ch = c % CPR;
+    float* dst = rows + i * PD + pad(ch * 8);
+    const uint4 v = xv[it];
+    dst[0] = bf16_lo(v.x); dst[1] = bf16_hi(v.x); dst[2] = bf16_lo(v.y); dst[3] = bf16_hi(v.y);
+    dst[4] = bf16_lo(v.z); dst[5] = bf16_hi(v.z); dst[6] = bf16_lo(v.w); dst[7] = bf16_hi(v.w);
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int G = Gr::G(g), s_lo = Gr::s_lo(g), nb = Gr::NB(g), tpb = Gr::TPB(g);
+    const int base = block_base(tid % nb, s_lo, G);
+    const int ph = tid / nb;
+    if (G == 3)
+      big_rows<D, 3, IN_SIDE>(rows, sh_e, R, p.cs, coef[g], ce[g], s_lo, base, ph, tpb);
+    else if (G == 2)
+      big_rows<D, 2, IN_SIDE>(rows, sh_e, R, p.cs, coef[g], ce[g], s_lo, base, ph, tpb);
+    else
+      big_rows<D, 1, IN_SIDE>(rows, sh_e, R, p.cs, coef[g], ce[g], s_lo, base, ph, tpb);
+    __syncthreads();
+  }
+
+  uint16_t* dst = static_cast<uint16_t*>(p.dst);
+#pragma unroll
+  for (int it = 0; it < LPT; ++it) {
+    const int c = tid + it * kBigThreads;
+    const int i = c / CPR, ch = c % CPR;
+    if (i < nr) {
+      const float* s = rows + i * PD + pad(ch * 8);
+      if (IN_SIDE) {
+        store16<uint16_t>(s, dst + (size_t)(q0 + i) * D + ch * 8, 1.0f);
+      } else {
+        const int r = sh_r[i];
+        store16<uint16_t>(s, dst + (size_t)r * D + ch * 8, p.gates[r]);
+      }
+    }
+  }
+}
+
+template <int D, bool IN_SIDE>
+hipError_t launch_big(const BflyParams& p, hipStream_t s) {
+  using C = BigCfg<D>;
+  static_assert(BigGroups<D, IN_SIDE>::fits(), "one block per thread");
+  const size_t shmem = (size_t)C::R * C::PD * sizeof(float);
+  auto kern = bfly_big_kernel<D, IN_SIDE>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((p.M + C::R - 1) / C::R), dim3(kBigThreads), shmem, s, p);
+  return hipGetLastError();
+}
+
+template <bool IN_SIDE>
+hipError_t launch_big_d(const BflyParams& p, hipStream_t s) {
+  switch (p.d) {
+    case 1024: return launch_big<1024, IN_SIDE>(p, s);
+    case 2048: return launch_big<2048, IN_SIDE>(p, s);
+    case 4096: return launch_big<4096, IN_SIDE>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 int pick_rows(int M, int d) {
   int R = 16384 / d;  // R * d * 4 bytes <= 64 KiB of LDS: two workgroups per CU
   if (R > kMaxRows) R = kMaxRows;
@@ -252,6 +471,7 @@ BflyParams make_params(int M, int d, int k, const RouteTables& rt, const float2*
 hipError_t launch_bfly_in(bmoe_dtype dt, int M, int d, int k, const void* x,
                           const RouteTables& rt, const float2* cs_in, void* z, hipStream_t s) {
   const BflyParams p = make_params(M, d, k, rt, cs_in, x, z, nullptr);
+  if (dt == BMOE_BF16 && d >= 1024 && d <= 4096) return launch_big_d<true>(p, s);
   if (dt == BMOE_BF16) return launch_rows(bfly_kernel<true, uint16_t, uint16_t>, p, s);
   return launch_rows(bfly_kernel<true, float, float>, p, s);
 }
@@ -260,6 +480,7 @@ hipError_t launch_bfly_out(bmoe_dtype dt, int M, int d, const void* h, const flo
                            const RouteTables& rt, const float2* cs_out, void* u,
                            hipStream_t s) {
   const BflyParams p = make_params(M, d, 1, rt, cs_out, h, u, gates);
+  if (dt == BMOE_BF16 && d >= 1024 && d <= 4096) return launch_big_d<false>(p, s);
   if (dt == BMOE_BF16) return launch_rows(bfly_kernel<false, uint16_t, uint16_t>, p, s);
   return launch_rows(bfly_kernel<false, float, float>, p, s);
 }
