@@ -11,6 +11,8 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -23,8 +25,11 @@ METRIC = "routed tokens/sec of ButterflyMoE layer fwd (d=512,N=64,top-2); % MFMA
 
 # MI355X published peaks
 PEAK_HBM_GBS = 8000.0
-PEAK_BF16_TFLOPS = 2500.0
-PEAK_FP32_TFLOPS = 157.3
+PEAK_BF16_TFLOPS = 2500.0        # dense bf16 MFMA
+PEAK_FP32_MFMA_TFLOPS = 157.3    # dense fp32 MFMA
+PEAK_VALU_F32_TFLOPS = 157.3     # fp32 vector (256 CU x 2.4 GHz x 256 flop/clk)
+
+GEMM_WORKLOAD = "d4096_e256_top4_bf16"
 
 
 def log(*a):
@@ -61,33 +66,100 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
-def kernel_work(name, dt_bytes, T, d, N, k):
-    """Algorithmic work of one launch of each forward kernel:
-    (bound, amount, unit) with bytes for HBM-bound kernels and flops for the
-    contraction. Counts only what the kernel must read and write once."""
+def kernel_work(name, act_bytes, T, d, N, k):
+    """Algorithmic work of one launch of a forward kernel: the bytes it must
+    move to or from HBM (each input read once, each output written once), the
+    flops of its dense contraction (MFMA) and the flops of its rotations
+    (fp32 VALU: 2 multiplies and 2 fused multiply-adds, 6 flops, per pair and
+    stage). act_bytes is the size of one activation element (x, Z, H, U, y)."""
     M = T * k
     L = d.bit_length() - 1
-    A = N * L * (d // 2)             # angles per side
-    xb = dt_bytes
-    zb = dt_bytes                    # Z stored in the activation type
+    A = N * L * (d // 2)                     # angles (pairs) per side
+    rot = M * L * (d // 2) * 6               # flops of one rotation side
+    routing = M * 4                          # one int32 per routed row
     if name.startswith("prep"):
-        return "hbm", M * 4 + 2 * A * 4 + 2 * A * 8 + 3 * M * 4 + (N + 1) * 4, "B"
+        b = M * 4 + 2 * A * 4 + 2 * A * 8 + 3 * routing + (N + 1) * 4
+        if act_bytes == 2 and d in (256, 512):
+            b += d * d // 4 + d * d * 2      # bf16 expansion of the packed substrate
+        return {"bytes": b, "mfma_flops": 0, "valu_flops": 0}
+    if name.startswith("fused"):
+        b = (T * d * act_bytes + M * d * act_bytes + d * d * 2 + 2 * A * 8
+             + 2 * routing + M * 4)
+        return {"bytes": b, "mfma_flops": 2 * M * d * d, "valu_flops": 2 * rot}
     if name.startswith("bfly_in"):
-        return "hbm", M * d * xb + M * d * zb + A * 8 + 2 * M * 4, "B"
+        b = T * d * act_bytes + M * d * act_bytes + A * 8 + 2 * routing
+        return {"bytes": b, "mfma_flops": 0, "valu_flops": rot}
     if name.startswith("gemm"):
-        return "mfma", 2 * M * d * d, "flop"
+        b = 2 * M * d * act_bytes + d * d // 4
+        return {"bytes": b, "mfma_flops": 2 * M * d * d, "valu_flops": 0}
     if name.startswith("bfly_out"):
-        return "hbm", M * d * 4 + M * d * 4 + A * 8 + 3 * M * 4, "B"
+        b = 2 * M * d * act_bytes + A * 8 + 2 * routing + M * 4
+        return {"bytes": b, "mfma_flops": 0, "valu_flops": rot}
     if name.startswith("combine"):
-        return "hbm", M * d * 4 + T * d * xb, "B"
+        return {"bytes": M * d * act_bytes + T * d * act_bytes, "mfma_flops": 0, "valu_flops": 0}
     raise KeyError(name)
 
 
-def min_hbm_bytes(dt_bytes, T, d, N, k):
+def roofline(work, dur_s, mfma_peak_tflops):
+    """The roofline of one kernel: the resource whose ideal time (work over
+    published peak) is largest bounds it; achieved = that work / measured
+    duration."""
+    t_hbm = work["bytes"] / (PEAK_HBM_GBS * 1e9)
+    t_mfma = work["mfma_flops"] / (mfma_peak_tflops * 1e12)
+    t_alu = work["valu_flops"] / (PEAK_VALU_F32_TFLOPS * 1e12)
+    bound = max((t_hbm, "hbm"), (t_mfma, "mfma"), (t_alu, "alu"))[1]
+    if bound == "hbm":
+        ach, peak, unit, amount = work["bytes"] / dur_s / 1e9, PEAK_HBM_GBS, "GB/s", work["bytes"]
+    elif bound == "mfma":
+        ach, peak, unit = work["mfma_flops"] / dur_s / 1e12, mfma_peak_tflops, "TFLOP/s"
+        amount = work["mfma_flops"]
+    else:
+        ach, peak, unit = work["valu_flops"] / dur_s / 1e12, PEAK_VALU_F32_TFLOPS, "TFLOP/s"
+        amount = work["valu_flops"]
+    return {"bound": bound, "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak,
+            "work_per_launch": amount, "duration_us": dur_s * 1e6,
+            "ideal_us": {"hbm": t_hbm * 1e6, "mfma": t_mfma * 1e6, "alu": t_alu * 1e6}}
+
+
+def min_hbm_bytes(act_bytes, T, d, N, k):
     """Bytes any forward must move: x, y, the packed substrate, both angle
     sets, ids and gates."""
     L = d.bit_length() - 1
-    return 2 * T * d * dt_bytes + d * d // 4 + 2 * N * L * (d // 2) * 4 + 2 * T * k * 4
+    return 2 * T * d * act_bytes + d * d // 4 + 2 * N * L * (d // 2) * 4 + 2 * T * k * 4
+
+
+def source_digest():
+    """sha256 over the kernel sources and the C header: a stored counter
+    figure is only valid for the sources it was taken from."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "butterfly_rotated_ternary_amd", "csrc", "*")))
+    files += sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch from the counter summary of this kernel and
+    workload under profiles/ (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel
+    calibration), or None if absent or taken from other sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith((" ", "#", "$")):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("source_sha256") != source_digest():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(inp, seconds):
@@ -123,6 +195,103 @@ def cpu_baseline(inp, seconds):
     }
 
 
+class Problem:
+    """Device-resident inputs of one workload, ready for bmoe_forward."""
+
+    def __init__(self, name):
+        import numpy as np
+        import torch
+        from butterfly_rotated_ternary_amd import bmoe
+        from butterfly_rotated_ternary_amd import workloads as W
+
+        self.name = name
+        self.inp = inp = W.make_inputs(name)
+        self.T, self.d, self.N, self.k = inp.T, inp.d, inp.N, inp.k
+        dev = torch.device("cuda:0")
+        if inp.dtype == "bf16":
+            self.x = torch.from_numpy(inp.x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+            self.dt, self.act_bytes = bmoe.BMOE_BF16, 2
+        else:
+            self.x = torch.from_numpy(inp.x).to(dev)
+            self.dt, self.act_bytes = bmoe.BMOE_F32, 4
+        self.ids = torch.from_numpy(inp.ids).to(dev)
+        self.gates = torch.from_numpy(inp.gates).to(dev)
+        self.theta = torch.from_numpy(inp.theta).to(dev)
+        self.phi = torch.from_numpy(inp.phi).to(dev)
+        self.wp = bmoe.pack_ternary(torch.from_numpy(inp.w).to(dev))
+        self.alpha = float(inp.alpha)
+        self.ws = bmoe.Workspace(self.dt, self.T, self.d, self.N, self.k, device=dev)
+        self.y = torch.empty_like(self.x)
+        self.stream = torch.cuda.current_stream()
+        self.bmoe = bmoe
+
+    def args(self):
+        return (self.dt, self.T, self.d, self.N, self.k, self.x, self.ids, self.gates, self.theta,
+                self.phi, self.wp, self.alpha, self.y, self.ws.buf, None, self.stream)
+
+    def step(self):
+        rc = self.bmoe.bmoe_forward(*self.args())
+        if rc != 0:
+            raise self.bmoe.BmoeError(rc, "bmoe_forward")
+
+    def kernel_names(self):
+        b = self.bmoe
+        nk = b.bmoe_forward_kernel_count(self.dt, self.T, self.d, self.N, self.k)
+        return [b.bmoe_forward_kernel_name(self.dt, self.T, self.d, self.N, self.k, i)
+                for i in range(nk)]
+
+    def time_steps(self, steps, warmup):
+        """Wall time per step over `steps` back-to-back forwards (ms)."""
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        if self.bmoe.bmoe_sync_status(self.ws.buf) != 0:
+            raise RuntimeError("device status not OK")
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    def time_kernels(self, steps):
+        """Average execution time of each kernel (ms), from the start/stop
+        events its own dispatch records, over `steps` forwards."""
+        import torch
+        names = self.kernel_names()
+        hip = HipEvents()
+        evsets = [hip.create(2 * len(names)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for evs in evsets:
+            rc = self.bmoe.bmoe_forward_timed(*self.args(), evs)
+            if rc != 0:
+                raise self.bmoe.BmoeError(rc, "bmoe_forward_timed")
+        torch.cuda.synchronize()
+        per = {n: 0.0 for n in names}
+        for evs in evsets:
+            for i, n in enumerate(names):
+                per[n] += hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) / steps
+        for evs in evsets:
+            hip.destroy(evs)
+        return per
+
+    def mfma_peak(self):
+        return PEAK_BF16_TFLOPS if self.dt == self.bmoe.BMOE_BF16 else PEAK_FP32_MFMA_TFLOPS
+
+
+def copy_calibration(mib, reps):
+    """Plain device-to-device copies of a known size, for scaling the HBM
+    byte counters (run under rocprofv3 --pmc)."""
+    import torch
+    n = mib << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,93 +300,44 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--gemm-steps", type=int, default=20,
+                    help="forwards of the d=4096 workload timed for its GEMM figure (0: skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run plain copies of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--print-source-digest", action="store_true")
     args = ap.parse_args()
+    if args.print_source_digest:
+        print(source_digest())
+        return
     if args.gpus != 1:
         log("bench.py measures one GPU only: the forward shards by tokens with no exchange, "
             "so a multi-GPU figure is not produced. Run with --gpus 1.")
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 10)
+        return
 
-    import numpy as np
-    import torch
-    from butterfly_rotated_ternary_amd import bmoe
     from butterfly_rotated_ternary_amd import workloads as W
 
     name = args.workload or W.HEADLINE
-    inp = W.make_inputs(name)
-    T, d, N, k = inp.T, inp.d, inp.N, inp.k
-    dev = torch.device("cuda:0")
-    if inp.dtype == "bf16":
-        x = torch.from_numpy(inp.x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-        dt, dt_bytes = bmoe.BMOE_BF16, 2
-    else:
-        x = torch.from_numpy(inp.x).to(dev)
-        dt, dt_bytes = bmoe.BMOE_F32, 4
-    ids = torch.from_numpy(inp.ids).to(dev)
-    gates = torch.from_numpy(inp.gates).to(dev)
-    theta = torch.from_numpy(inp.theta).to(dev)
-    phi = torch.from_numpy(inp.phi).to(dev)
-    wp = bmoe.pack_ternary(torch.from_numpy(inp.w).to(dev))
-    alpha = float(inp.alpha)
-    ws = bmoe.Workspace(dt, T, d, N, k, device=dev)
-    y = torch.empty_like(x)
-    stream = torch.cuda.current_stream()
-
-    def step():
-        rc = bmoe.bmoe_forward(dt, T, d, N, k, x, ids, gates, theta, phi, wp, alpha, y, ws.buf,
-                               None, stream)
-        if rc != 0:
-            raise bmoe.BmoeError(rc, "bmoe_forward")
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    if bmoe.bmoe_sync_status(ws.buf) != 0:
-        raise RuntimeError("device status not OK")
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
+    P = Problem(name)
+    T, d, N, k = P.T, P.d, P.N, P.k
+    ms = P.time_steps(args.steps, args.warmup)
     value = T / (ms * 1e-3)
     log(f"[bench] {name}: {ms * 1e3:.2f} us/step, {value:.4g} tokens/s")
 
-    # Per-kernel durations, HIP events on the library's stream, same workload.
-    nk = bmoe.bmoe_forward_kernel_count(dt, T, d, N, k)
-    names = [bmoe.bmoe_forward_kernel_name(dt, T, d, N, k, i) for i in range(nk)]
-    hip = HipEvents()
-    n_ev_steps = min(args.steps, 200)
-    evsets = [hip.create(nk + 1) for _ in range(n_ev_steps)]
-    torch.cuda.synchronize()
-    for evs in evsets:
-        rc = bmoe.bmoe_forward_timed(dt, T, d, N, k, x, ids, gates, theta, phi, wp, alpha, y,
-                                     ws.buf, None, stream, evs)
-        if rc != 0:
-            raise bmoe.BmoeError(rc, "bmoe_forward_timed")
-    torch.cuda.synchronize()
-    per_kernel = {n: 0.0 for n in names}
-    for evs in evsets:
-        for i, n in enumerate(names):
-            per_kernel[n] += hip.elapsed_ms(evs[i], evs[i + 1]) / n_ev_steps
-    for evs in evsets:
-        hip.destroy(evs)
-    log("[bench] per-kernel ms (events): " + ", ".join(f"{n}={v * 1e3:.2f}us"
-                                                        for n, v in per_kernel.items()))
-
+    per_kernel = P.time_kernels(min(args.steps, 200))
+    log("[bench] per-kernel us (dispatch events): "
+        + ", ".join(f"{n}={v * 1e3:.2f}" for n, v in per_kernel.items()))
     dom = max(per_kernel, key=per_kernel.get)
-    bound, amount, unit = kernel_work(dom, dt_bytes, T, d, N, k)
-    dur_s = per_kernel[dom] * 1e-3
-    if bound == "mfma":
-        peak = PEAK_BF16_TFLOPS if dt == bmoe.BMOE_BF16 else PEAK_FP32_TFLOPS
-        achieved = amount / dur_s / 1e12
-        runit = "TFLOP/s"
-    else:
-        peak = PEAK_HBM_GBS
-        achieved = amount / dur_s / 1e9
-        runit = "GB/s"
-    roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": runit,
-                "frac": achieved / peak, "traffic": None, "kernel": dom,
-                "work_per_launch": amount, "work_unit": unit}
+    work = kernel_work(dom, P.act_bytes, T, d, N, k)
+    roof = roofline(work, per_kernel[dom] * 1e-3, P.mfma_peak())
+    roof["traffic"] = stored_traffic(dom, name)
+    roof["kernel"] = dom
+    others = {}
+    for n, v in per_kernel.items():
+        r = roofline(kernel_work(n, P.act_bytes, T, d, N, k), v * 1e-3, P.mfma_peak())
+        others[n] = {"us": v * 1e3, "bound": r["bound"], "frac": r["frac"]}
 
     M = T * k
     out = {
@@ -231,18 +351,41 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if dt == bmoe.BMOE_BF16 else "f32",
+        "dtype": "bf16" if P.act_bytes == 2 else "f32",
         "data": "synthetic",
         "config": {"workload": name, "d": d, "n_experts": N, "top_k": k, "tokens": T,
                    "routed_rows": M},
-        "roofline": roofline,
+        "roofline": roof,
         "routed_rows_per_s": M / (ms * 1e-3),
         "e2e_frac": {"mfma_bf16": 2 * M * d * d / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
-                     "hbm": min_hbm_bytes(dt_bytes, T, d, N, k) / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9)},
-        "kernels_us": {n: v * 1e3 for n, v in per_kernel.items()},
+                     "hbm": min_hbm_bytes(P.act_bytes, T, d, N, k) / (ms * 1e-3)
+                     / (PEAK_HBM_GBS * 1e9)},
+        "kernels": others,
     }
+    del P
+
+    if args.gemm_steps > 0 and name != GEMM_WORKLOAD:
+        # The shared ternary product at d = 4096 (its own workload, same path).
+        import torch
+        G = Problem(GEMM_WORKLOAD)
+        g_ms = G.time_steps(args.gemm_steps, 3)
+        g_per = G.time_kernels(args.gemm_steps)
+        g_work = kernel_work("gemm_kernel", G.act_bytes, G.T, G.d, G.N, G.k)
+        g_roof = roofline(g_work, g_per["gemm_kernel"] * 1e-3, G.mfma_peak())
+        g_roof["traffic"] = stored_traffic("gemm_kernel", GEMM_WORKLOAD)
+        out["gemm_d4096"] = {
+            "workload": GEMM_WORKLOAD, "kernel": "gemm_kernel", "ms_per_step": g_ms,
+            "tokens_per_s": G.T / (g_ms * 1e-3), "roofline": g_roof,
+            "kernels_us": {n: v * 1e3 for n, v in g_per.items()},
+        }
+        log(f"[bench] {GEMM_WORKLOAD}: {g_ms * 1e3:.1f} us/step; gemm_kernel "
+            f"{g_roof['achieved']:.0f} TFLOP/s ({100 * g_roof['frac']:.1f}% of bf16 peak); "
+            + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in g_per.items()))
+        del G
+        torch.cuda.empty_cache()
+
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(W.make_inputs(name), args.cpu_seconds)
         log(f"[bench] cpu baseline {out['cpu_baseline']['value']:.4g} tokens/s "
             f"({out['cpu_baseline']['sample']})")
     print(json.dumps(out), flush=True)

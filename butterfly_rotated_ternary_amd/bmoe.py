@@ -115,7 +115,8 @@ def bmoe_forward(dt: int, T: int, d: int, n_experts: int, k: int, x, ids, gates,
 def bmoe_forward_timed(dt: int, T: int, d: int, n_experts: int, k: int, x, ids, gates, theta, phi,
                        w_packed, alpha: float, y, ws, route_out=None, stream=None,
                        events=None) -> int:
-    """``events``: sequence of raw hipEvent_t handles (ints), kernel count + 1."""
+    """``events``: raw hipEvent_t handles (ints), two per kernel: the start and
+    stop events of kernel i are events[2i] and events[2i+1]."""
     ev = None
     if events is not None:
         ev = (ctypes.c_void_p * len(events))(*events)

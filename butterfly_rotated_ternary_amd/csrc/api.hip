@@ -46,11 +46,14 @@ FwdLayout fwd_layout(bmoe_dtype dt, int T, int d, int N, int k) {
   l.slot_e = off;  off = align_up(off + sizeof(int32_t) * M);
   l.cs_in = off;   off = align_up(off + sizeof(float2) * N * L * (d / 2));
   l.cs_out = off;  off = align_up(off + sizeof(float2) * N * L * (d / 2));
-  l.z = off;       off = align_up(off + zel * M * d);
-  l.h = off;       off = align_up(off + zel * M * d);
+  const bool fused = fused_supported(dt, d);
+  // The fused path keeps Z and H on chip; only U (and the bf16 substrate)
+  // live in the workspace.
+  l.z = off;       if (!fused) off = align_up(off + zel * M * d);
+  l.h = off;       if (!fused) off = align_up(off + zel * M * d);
   l.u = off;       off = align_up(off + zel * M * d);
   l.w16 = off;
-  if (fused_supported(dt, d)) off = align_up(off + sizeof(uint16_t) * (size_t)d * d);
+  if (fused) off = align_up(off + sizeof(uint16_t) * (size_t)d * d);
   l.total = off;
   return l;
 }
@@ -128,33 +131,34 @@ bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   int ki = 0;
-  auto mark = [&]() -> bool {
-    if (!events) return true;
-    return hipEventRecord(static_cast<hipEvent_t>(events[ki++]), s) == hipSuccess;
+  // Timing events of the next kernel (none when events is NULL).
+  auto timing = [&]() -> KernelTiming {
+    KernelTiming t;
+    if (events) {
+      t.start = static_cast<hipEvent_t>(events[2 * ki]);
+      t.stop = static_cast<hipEvent_t>(events[2 * ki + 1]);
+      ++ki;
+    }
+    return t;
   };
   const bool fused = fused_supported(dt, d);
   uint16_t* w16 = fused ? reinterpret_cast<uint16_t*>(base + l.w16) : nullptr;
-  if (!mark()) return BMOE_E_HIP;
-  if (launch_prep(ids, M, n_experts, theta, phi, d, rt, cs_in, cs_out, status, w_packed, w16, s) !=
-      hipSuccess)
+  if (launch_prep(ids, M, n_experts, theta, phi, d, rt, cs_in, cs_out, status, w_packed, w16, s,
+                  timing()) != hipSuccess)
     return BMOE_E_HIP;
-  if (!mark()) return BMOE_E_HIP;
   if (fused) {
-    if (launch_fused(M, d, k, x, gates, rt, cs_in, cs_out, w16, w_packed, alpha, u, s) != hipSuccess)
+    if (launch_fused(M, d, k, x, gates, rt, cs_in, cs_out, w16, w_packed, alpha, u, s,
+                     timing()) != hipSuccess)
       return BMOE_E_HIP;
-    if (!mark()) return BMOE_E_HIP;
-    if (launch_combine(dt, T, d, k, u, y, s) != hipSuccess) return BMOE_E_HIP;
-    if (!mark()) return BMOE_E_HIP;
-    return BMOE_OK;
+  } else {
+    if (launch_bfly_in(dt, M, d, k, x, rt, cs_in, z, s, timing()) != hipSuccess)
+      return BMOE_E_HIP;
+    if (launch_gemm(dt, M, d, z, w_packed, alpha, h, s, timing()) != hipSuccess)
+      return BMOE_E_HIP;
+    if (launch_bfly_out(dt, M, d, h, gates, rt, cs_out, u, s, timing()) != hipSuccess)
+      return BMOE_E_HIP;
   }
-  if (launch_bfly_in(dt, M, d, k, x, rt, cs_in, z, s) != hipSuccess) return BMOE_E_HIP;
-  if (!mark()) return BMOE_E_HIP;
-  if (launch_gemm(dt, M, d, z, w_packed, alpha, h, s) != hipSuccess) return BMOE_E_HIP;
-  if (!mark()) return BMOE_E_HIP;
-  if (launch_bfly_out(dt, M, d, h, gates, rt, cs_out, u, s) != hipSuccess) return BMOE_E_HIP;
-  if (!mark()) return BMOE_E_HIP;
-  if (launch_combine(dt, T, d, k, u, y, s) != hipSuccess) return BMOE_E_HIP;
-  if (!mark()) return BMOE_E_HIP;
+  if (launch_combine(dt, T, d, k, u, y, s, timing()) != hipSuccess) return BMOE_E_HIP;
   return BMOE_OK;
 }
 

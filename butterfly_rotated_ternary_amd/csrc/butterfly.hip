@@ -412,7 +412,7 @@ __global__ __launch_bounds__(kBigThreads) void bfly_big_kernel(BflyParams p) {
 }
 
 template <int D, bool IN_SIDE>
-hipError_t launch_big(const BflyParams& p, hipStream_t s) {
+hipError_t launch_big(const BflyParams& p, hipStream_t s, const KernelTiming& t) {
   using C = BigCfg<D>;
   static_assert(BigGroups<D, IN_SIDE>::fits(), "one block per thread");
   const size_t shmem = (size_t)C::R * C::PD * sizeof(float);
@@ -420,16 +420,16 @@ hipError_t launch_big(const BflyParams& p, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((p.M + C::R - 1) / C::R), dim3(kBigThreads), shmem, s, p);
-  return hipGetLastError();
+  return launch_kernel(kern, dim3((p.M + C::R - 1) / C::R), dim3(kBigThreads), (uint32_t)shmem, s,
+                       t, p);
 }
 
 template <bool IN_SIDE>
-hipError_t launch_big_d(const BflyParams& p, hipStream_t s) {
+hipError_t launch_big_d(const BflyParams& p, hipStream_t s, const KernelTiming& t) {
   switch (p.d) {
-    case 1024: return launch_big<1024, IN_SIDE>(p, s);
-    case 2048: return launch_big<2048, IN_SIDE>(p, s);
-    case 4096: return launch_big<4096, IN_SIDE>(p, s);
+    case 1024: return launch_big<1024, IN_SIDE>(p, s, t);
+    case 2048: return launch_big<2048, IN_SIDE>(p, s, t);
+    case 4096: return launch_big<4096, IN_SIDE>(p, s, t);
   }
   return hipErrorInvalidValue;
 }
@@ -443,15 +443,15 @@ int pick_rows(int M, int d) {
 }
 
 template <typename K>
-hipError_t launch_rows(K kernel, const BflyParams& p, hipStream_t s) {
+hipError_t launch_rows(K kernel, const BflyParams& p, hipStream_t s, const KernelTiming& t) {
   const size_t shmem = (size_t)p.R * padded_row(p.d) * sizeof(float);
   if (shmem > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kernel, dim3((p.M + p.R - 1) / p.R), dim3(kThreads), shmem, s, p);
-  return hipGetLastError();
+  return launch_kernel(kernel, dim3((p.M + p.R - 1) / p.R), dim3(kThreads), (uint32_t)shmem, s, t,
+                       p);
 }
 
 BflyParams make_params(int M, int d, int k, const RouteTables& rt, const float2* cs,
@@ -469,20 +469,21 @@ BflyParams make_params(int M, int d, int k, const RouteTables& rt, const float2*
 }  // namespace
 
 hipError_t launch_bfly_in(bmoe_dtype dt, int M, int d, int k, const void* x,
-                          const RouteTables& rt, const float2* cs_in, void* z, hipStream_t s) {
+                          const RouteTables& rt, const float2* cs_in, void* z, hipStream_t s,
+                          const KernelTiming& t) {
   const BflyParams p = make_params(M, d, k, rt, cs_in, x, z, nullptr);
-  if (dt == BMOE_BF16 && d >= 1024 && d <= 4096) return launch_big_d<true>(p, s);
-  if (dt == BMOE_BF16) return launch_rows(bfly_kernel<true, uint16_t, uint16_t>, p, s);
-  return launch_rows(bfly_kernel<true, float, float>, p, s);
+  if (dt == BMOE_BF16 && d >= 1024 && d <= 4096) return launch_big_d<true>(p, s, t);
+  if (dt == BMOE_BF16) return launch_rows(bfly_kernel<true, uint16_t, uint16_t>, p, s, t);
+  return launch_rows(bfly_kernel<true, float, float>, p, s, t);
 }
 
 hipError_t launch_bfly_out(bmoe_dtype dt, int M, int d, const void* h, const float* gates,
                            const RouteTables& rt, const float2* cs_out, void* u,
-                           hipStream_t s) {
+                           hipStream_t s, const KernelTiming& t) {
   const BflyParams p = make_params(M, d, 1, rt, cs_out, h, u, gates);
-  if (dt == BMOE_BF16 && d >= 1024 && d <= 4096) return launch_big_d<false>(p, s);
-  if (dt == BMOE_BF16) return launch_rows(bfly_kernel<false, uint16_t, uint16_t>, p, s);
-  return launch_rows(bfly_kernel<false, float, float>, p, s);
+  if (dt == BMOE_BF16 && d >= 1024 && d <= 4096) return launch_big_d<false>(p, s, t);
+  if (dt == BMOE_BF16) return launch_rows(bfly_kernel<false, uint16_t, uint16_t>, p, s, t);
+  return launch_rows(bfly_kernel<false, float, float>, p, s, t);
 }
 
 }  // namespace bmoe

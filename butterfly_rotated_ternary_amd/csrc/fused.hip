@@ -446,11 +446,12 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(int M, int k, const uin
 template <int D>
 hipError_t launch_d(int M, int k, const void* x, const float* gates, const RouteTables& rt,
                     const float2* cs_in, const float2* cs_out, const uint16_t* w16,
-                    const uint32_t* wp, float alpha, void* u, hipStream_t s) {
-  hipLaunchKernelGGL(fused_kernel<D>, dim3((M + kBM - 1) / kBM), dim3(kThreads), 0, s, M, k,
-                     static_cast<const uint16_t*>(x), gates, rt.perm, rt.slot_e, cs_in, cs_out,
-                     w16, wp, alpha, static_cast<uint16_t*>(u));
-  return hipGetLastError();
+                    const uint32_t* wp, float alpha, void* u, hipStream_t s,
+                    const KernelTiming& t) {
+  return launch_kernel(fused_kernel<D>, dim3((M + kBM - 1) / kBM), dim3(kThreads), 0, s, t, M, k,
+                       static_cast<const uint16_t*>(x), gates, (const int32_t*)rt.perm,
+                       (const int32_t*)rt.slot_e, cs_in, cs_out, w16, wp, alpha,
+                       static_cast<uint16_t*>(u));
 }
 
 }  // namespace
@@ -462,10 +463,10 @@ bool fused_supported(bmoe_dtype dt, int d) {
 hipError_t launch_fused(int M, int d, int k, const void* x, const float* gates,
                         const RouteTables& rt, const float2* cs_in, const float2* cs_out,
                         const uint16_t* w16, const uint32_t* wp, float alpha, void* u,
-                        hipStream_t s) {
+                        hipStream_t s, const KernelTiming& t) {
   switch (d) {
-    case 256: return launch_d<256>(M, k, x, gates, rt, cs_in, cs_out, w16, wp, alpha, u, s);
-    case 512: return launch_d<512>(M, k, x, gates, rt, cs_in, cs_out, w16, wp, alpha, u, s);
+    case 256: return launch_d<256>(M, k, x, gates, rt, cs_in, cs_out, w16, wp, alpha, u, s, t);
+    case 512: return launch_d<512>(M, k, x, gates, rt, cs_in, cs_out, w16, wp, alpha, u, s, t);
   }
   return hipErrorInvalidValue;
 }

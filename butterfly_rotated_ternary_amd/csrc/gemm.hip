@@ -213,7 +213,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(const void* zv, const 
 
 template <class C, typename OutT>
 hipError_t launch_cfg(const void* z, const uint32_t* wp, OutT* h, int M, int d, float alpha,
-                      hipStream_t s) {
+                      hipStream_t s, const KernelTiming& t) {
   const int tm = (M + C::BM - 1) / C::BM, tn = (d + C::BN - 1) / C::BN;
   auto kern = gemm_kernel<C, OutT>;
   if (C::LDS_BYTES > 65536) {
@@ -222,9 +222,8 @@ hipError_t launch_cfg(const void* z, const uint32_t* wp, OutT* h, int M, int d, 
                                        (int)C::LDS_BYTES);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, dim3(tm * tn), dim3(C::THREADS), C::LDS_BYTES, s, z, wp, h, M, d, alpha,
-                     tm, tn);
-  return hipGetLastError();
+  return launch_kernel(kern, dim3(tm * tn), dim3(C::THREADS), (uint32_t)C::LDS_BYTES, s, t, z, wp,
+                       h, M, d, alpha, tm, tn);
 }
 
 
@@ -427,29 +426,28 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dl_kernel(const uint16_t* Z,
 
 template <class C>
 hipError_t launch_dl(const uint16_t* z, const uint32_t* wp, uint16_t* h, int M, int d,
-                     float alpha, hipStream_t s) {
+                     float alpha, hipStream_t s, const KernelTiming& t) {
   const int tm = (M + C::BM - 1) / C::BM, tn = d / C::BN;
-  hipLaunchKernelGGL(gemm_dl_kernel<C>, dim3(tm * tn), dim3(C::THREADS), 0, s, z, wp, h, M, d,
-                     alpha, tm, tn);
-  return hipGetLastError();
+  return launch_kernel(gemm_dl_kernel<C>, dim3(tm * tn), dim3(C::THREADS), 0, s, t, z, wp, h, M,
+                       d, alpha, tm, tn);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(bmoe_dtype dt, int M, int d, const void* z, const uint32_t* w_packed,
-                       float alpha, void* h, hipStream_t s) {
+                       float alpha, void* h, hipStream_t s, const KernelTiming& t) {
   if (dt == BMOE_F32)
     return launch_cfg<Cfg<64, 64, 2, 2, true>, float>(z, w_packed, static_cast<float*>(h), M, d,
-                                                      alpha, s);
+                                                      alpha, s, t);
   uint16_t* hb = static_cast<uint16_t*>(h);
   const uint16_t* zb = static_cast<const uint16_t*>(z);
   // Large problems: 256x256 tiles (4 waves of 128x128). Smaller ones: 128x128
   // tiles so that the grid still covers the 256 CUs.
   const long long big_tiles = (long long)((M + 255) / 256) * (d / 256);
   if (d >= 256 && big_tiles >= 512)
-    return launch_dl<DCfg<256, 256, 2, 4>>(zb, w_packed, hb, M, d, alpha, s);
-  if (d >= 128) return launch_dl<DCfg<128, 128, 2, 2>>(zb, w_packed, hb, M, d, alpha, s);
-  return launch_cfg<Cfg<64, 64, 2, 2, false>, uint16_t>(z, w_packed, hb, M, d, alpha, s);
+    return launch_dl<DCfg<256, 256, 2, 4>>(zb, w_packed, hb, M, d, alpha, s, t);
+  if (d >= 128) return launch_dl<DCfg<128, 128, 2, 2>>(zb, w_packed, hb, M, d, alpha, s, t);
+  return launch_cfg<Cfg<64, 64, 2, 2, false>, uint16_t>(z, w_packed, hb, M, d, alpha, s, t);
 }
 
 }  // namespace bmoe

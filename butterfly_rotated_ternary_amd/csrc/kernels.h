@@ -1,12 +1,27 @@
 // Internal launchers of the ButterflyMoE kernels (host side, not exported).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "../../include/bmoe.h"
 
 namespace bmoe {
+
+// Optional start/stop events recorded by a kernel's own dispatch.
+struct KernelTiming {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+// Launch `kernel`; with timing events set, the dispatch itself records them.
+template <typename F, typename... Args>
+hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t s,
+                         const KernelTiming& t, Args... args) {
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, t.start, t.stop, 0u, args...);
+  return hipGetLastError();
+}
 
 struct RouteTables {
   int32_t* offsets;  // [N+1]
@@ -20,7 +35,8 @@ struct RouteTables {
 // packed substrate, in one launch.
 hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, const float* phi,
                        int d, RouteTables rt, float2* cs_in, float2* cs_out, int32_t* status,
-                       const uint32_t* w_packed, uint16_t* w16, hipStream_t s);
+                       const uint32_t* w_packed, uint16_t* w16, hipStream_t s,
+                       const KernelTiming& t = {});
 
 // Whether the fused d <= 512 path handles this shape.
 bool fused_supported(bmoe_dtype dt, int d);
@@ -30,25 +46,26 @@ bool fused_supported(bmoe_dtype dt, int d);
 hipError_t launch_fused(int M, int d, int k, const void* x, const float* gates,
                         const RouteTables& rt, const float2* cs_in, const float2* cs_out,
                         const uint16_t* w16, const uint32_t* w_packed, float alpha, void* u,
-                        hipStream_t s);
+                        hipStream_t s, const KernelTiming& t = {});
 
 // Z[q] = B(theta_e)^T x[t]   (t = perm[q] / k, e = slot_e[q]).
 hipError_t launch_bfly_in(bmoe_dtype dt, int M, int d, int k, const void* x,
-                          const RouteTables& rt, const float2* cs_in, void* z, hipStream_t s);
+                          const RouteTables& rt, const float2* cs_in, void* z, hipStream_t s,
+                          const KernelTiming& t = {});
 
 // H = alpha * Z W_base^T over all M sorted rows (H bf16 on the bf16 path,
 // fp32 on the fp32 path; Z likewise).
 hipError_t launch_gemm(bmoe_dtype dt, int M, int d, const void* z, const uint32_t* w_packed,
-                       float alpha, void* h, hipStream_t s);
+                       float alpha, void* h, hipStream_t s, const KernelTiming& t = {});
 
 // U[r] = g_r * B(phi_e) H[q] for r = perm[q], written in routed order.
 hipError_t launch_bfly_out(bmoe_dtype dt, int M, int d, const void* h, const float* gates,
                            const RouteTables& rt, const float2* cs_out, void* u,
-                           hipStream_t s);
+                           hipStream_t s, const KernelTiming& t = {});
 
 // y[t] = sum_j U[t*k + j], ascending j.
 hipError_t launch_combine(bmoe_dtype dt, int T, int d, int k, const void* u, void* y,
-                          hipStream_t s);
+                          hipStream_t s, const KernelTiming& t = {});
 
 hipError_t launch_pack(const int8_t* w, int d, uint32_t* packed, int32_t* status,
                        hipStream_t s);

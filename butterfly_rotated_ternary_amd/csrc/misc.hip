@@ -89,15 +89,13 @@ int grid_for(size_t n) {
 }  // namespace
 
 hipError_t launch_combine(bmoe_dtype dt, int T, int d, int k, const void* u, void* y,
-                          hipStream_t s) {
+                          hipStream_t s, const KernelTiming& t) {
   const int g = grid_for((size_t)T * (d / 8));
   if (dt == BMOE_BF16)
-    hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t>), dim3(g), dim3(kThreads), 0, s,
-                       static_cast<const uint16_t*>(u), static_cast<uint16_t*>(y), T, d, k);
-  else
-    hipLaunchKernelGGL((combine_kernel<float, float>), dim3(g), dim3(kThreads), 0, s,
+    return launch_kernel(combine_kernel<uint16_t, uint16_t>, dim3(g), dim3(kThreads), 0, s, t,
+                         static_cast<const uint16_t*>(u), static_cast<uint16_t*>(y), T, d, k);
+  return launch_kernel(combine_kernel<float, float>, dim3(g), dim3(kThreads), 0, s, t,
                        static_cast<const float*>(u), static_cast<float*>(y), T, d, k);
-  return hipGetLastError();
 }
 
 hipError_t launch_pack(const int8_t* w, int d, uint32_t* packed, int32_t* status,

@@ -206,7 +206,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
 
 hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, const float* phi,
                        int d, RouteTables rt, float2* cs_in, float2* cs_out, int32_t* status,
-                       const uint32_t* w_packed, uint16_t* w16, hipStream_t s) {
+                       const uint32_t* w_packed, uint16_t* w16, hipStream_t s,
+                       const KernelTiming& t) {
   int L = 0;
   while ((1 << L) < d) ++L;
   PrepParams p;
@@ -242,9 +243,8 @@ hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, con
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(prep_kernel, dim3(p.n_route_blocks + p.n_trig_blocks + w_blocks), dim3(kThreads),
-                     shmem, s, p);
-  return hipGetLastError();
+  return launch_kernel(prep_kernel, dim3(p.n_route_blocks + p.n_trig_blocks + w_blocks),
+                       dim3(kThreads), (uint32_t)shmem, s, t, p);
 }
 
 }  // namespace bmoe

@@ -128,11 +128,13 @@ int bmoe_forward_kernel_count(bmoe_dtype dt, int T, int d, int n_experts, int k)
 const char* bmoe_forward_kernel_name(bmoe_dtype dt, int T, int d, int n_experts, int k, int i);
 
 /*
- * bmoe_forward, additionally recording events[i] on `stream` right before
- * kernel i is enqueued and events[count] after the last one, where count =
- * bmoe_forward_kernel_count(...). `events` holds count + 1 hipEvent_t created
- * by the caller (NULL behaves as bmoe_forward). For measuring per-kernel
- * durations with hipEventElapsedTime; results are identical to bmoe_forward.
+ * bmoe_forward, additionally timing each kernel's own dispatch: kernel i is
+ * launched with events[2i] as its start event and events[2i+1] as its stop
+ * event (hipExtLaunchKernel), so hipEventElapsedTime(events[2i],
+ * events[2i+1]) is that kernel's execution time, without launch gaps.
+ * `events` holds 2 * bmoe_forward_kernel_count(...) hipEvent_t created by the
+ * caller on the current device (NULL behaves as bmoe_forward). Results are
+ * identical to bmoe_forward.
  */
 bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
                                const int32_t* ids, const float* gates, const float* theta,

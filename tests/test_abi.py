@@ -52,9 +52,14 @@ def test_packed_words():
 
 
 def test_workspace_bytes_validates_shape():
+    # d = 512 bf16 keeps Z and H on chip: at least U (bf16) over M = T*k rows
     ok = bmoe.bmoe_workspace_bytes(bmoe.BMOE_BF16, 4096, 512, 64, 2)
-    # at least the activations: Z bf16 + H fp32 + U fp32 over M = T*k rows
-    assert ok >= 8192 * 512 * (2 + 4 + 4)
+    assert ok >= 8192 * 512 * 2
+    # split path: Z, H and U over M rows
+    big = bmoe.bmoe_workspace_bytes(bmoe.BMOE_BF16, 4096, 2048, 64, 2)
+    assert big >= 8192 * 2048 * 2 * 3
+    f32 = bmoe.bmoe_workspace_bytes(bmoe.BMOE_F32, 256, 64, 8, 2)
+    assert f32 >= 512 * 64 * 4 * 3
     assert bmoe.bmoe_workspace_bytes(bmoe.BMOE_BF16, 0, 512, 64, 2) > 0
     for args in [(bmoe.BMOE_BF16, 16, 500, 64, 2),   # d not a power of two
                  (bmoe.BMOE_BF16, 16, 512, 64, 65),  # k > N

@@ -172,3 +172,41 @@ def test_small_workspace_and_alignment_rejected():
                                  bmoe._ptr(dev["w_packed"]), 1.0, bmoe._ptr(y),
                                  bmoe.ctypes.c_void_p(ws.data_ptr() + 8), need, None, None)
     assert rc == 8
+
+
+@pytest.mark.parametrize("name", [W.HEADLINE, "d2048_e64_top2_outliers_bf16"])
+def test_timed_forward_matches_untimed(name):
+    """bmoe_forward_timed (per-dispatch start/stop events) computes exactly
+    what bmoe_forward does, and every kernel reports a positive duration."""
+    import ctypes
+    inp = W.make_inputs(name, T=300)
+    dev = to_device(inp)
+    T, d, N, k = inp.T, inp.d, inp.N, inp.k
+    y_ref, _ = run_forward(dev, inp, with_route=False)
+    dt = bmoe.BMOE_BF16 if inp.dtype == "bf16" else bmoe.BMOE_F32
+    nk = bmoe.bmoe_forward_kernel_count(dt, T, d, N, k)
+    assert nk in (3, 5)
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = []
+    for _ in range(2 * nk):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    ws = bmoe.Workspace(dt, T, d, N, k, device=dev["x"].device)
+    y = torch.empty_like(dev["x"])
+    rc = bmoe.bmoe_forward_timed(dt, T, d, N, k, dev["x"], dev["ids"], dev["gates"], dev["theta"],
+                                 dev["phi"], dev["w_packed"], dev["alpha"], y, ws.buf, None,
+                                 torch.cuda.current_stream(), evs)
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(y.float().cpu().numpy().astype(np.float64), y_ref)
+    for i in range(nk):
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), evs[2 * i], evs[2 * i + 1]) == 0
+        assert 0.0 < ms.value < 1000.0
+    for e in evs:
+        hip.hipEventDestroy(e)
