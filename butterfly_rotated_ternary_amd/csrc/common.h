@@ -27,16 +27,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
-// Packed substrate word -> 8 dwords, each two bf16 values of {-1, 0, +1}.
-// Word layout: column v = 2j has its nonzero flag at bit j and sign at bit
-// 8+j; v = 2j+1 at bits 16+j and 24+j. Dword j = (value 2j, value 2j+1):
-// shifting left by 7-j puts the two nonzero flags at bits 7 and 23 and the
-// two signs at bits 15 and 31; flag * 0x7F spreads a flag into 0x3F80 (the
-// bf16 pattern of 1.0, shifted by 0 or 16) and the signs are added on top.
+// Packed substrate word -> 8 dwords, each two bf16 values of {-2, 0, +2}:
+// twice the ternary weights, so every kernel applies alpha / 2 to its fp32
+// accumulator (a power-of-two rescale: the result is bit-identical to using
+// +-1 and alpha). Word layout: 2-bit codes (flag low bit, sign high bit);
+// column 2j at bits 2j..2j+1, column 2j+1 at bits 16+2j..17+2j. Shifting left
+// by 14 - 2j puts the pair's codes at bits 14..15 and 30..31, exactly where
+// bf16 2.0 (0x4000) has its one exponent bit and where the sign bit sits, so
+// one shift and one mask give dword j = (value 2j, value 2j+1). Plain 32-bit
+// VALU ops only: a packed (VOP3P) op writing the MFMA source registers right
+// behind an MFMA has corrupted its operands on gfx950.
 __device__ __forceinline__ uint32_t unpack_pair(uint32_t w, int j) {
-  const uint32_t t = w << (7 - j);
-  return __umul24(t & 0x00800080u, 0x7Fu) + (t & 0x80008000u);
+  return (w << (14 - 2 * j)) & 0xC000C000u;
 }
+
+// The scale kernels apply to an accumulator of expanded (+-2) substrate values.
+__host__ __device__ __forceinline__ float substrate_scale(float alpha) { return 0.5f * alpha; }
 
 // Workgroup barrier ordering LDS traffic only: waits for this wave's LDS
 // operations, then s_barrier. Unlike __syncthreads it does not wait for

@@ -245,15 +245,11 @@ __device__ __forceinline__ void ring_load(char* stage, const uint16_t* w16, int 
   }
 }
 
-// Eight bf16 {-1,0,+1} of one packed word: values 8h .. 8h+7 (h = 0, 1).
+// Eight bf16 {-2,0,+2} of one packed word: values 8h .. 8h+7 (h = 0, 1).
 __device__ __forceinline__ bf16x8 unpack_frag(uint32_t w, int h) {
-  const int s0 = 7 - 4 * h;
   u32x4 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t t = w << (s0 - i);
-    r[i] = __umul24(t & 0x00800080u, 0x7Fu) + (t & 0x80008000u);
-  }
+  for (int i = 0; i < 4; ++i) r[i] = unpack_pair(w, 4 * h + i);
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -464,9 +460,11 @@ hipError_t launch_fused(int M, int d, int k, const void* x, const float* gates,
                         const RouteTables& rt, const float2* cs_in, const float2* cs_out,
                         const uint16_t* w16, const uint32_t* wp, float alpha, void* u,
                         hipStream_t s, const KernelTiming& t) {
+  // The kernel's substrate values are +-2 (packed words and w16 alike).
+  const float a = substrate_scale(alpha);
   switch (d) {
-    case 256: return launch_d<256>(M, k, x, gates, rt, cs_in, cs_out, w16, wp, alpha, u, s, t);
-    case 512: return launch_d<512>(M, k, x, gates, rt, cs_in, cs_out, w16, wp, alpha, u, s, t);
+    case 256: return launch_d<256>(M, k, x, gates, rt, cs_in, cs_out, w16, wp, a, u, s, t);
+    case 512: return launch_d<512>(M, k, x, gates, rt, cs_in, cs_out, w16, wp, a, u, s, t);
   }
   return hipErrorInvalidValue;
 }

@@ -4,15 +4,17 @@
 // routed rows, whatever their expert).
 //
 // bf16 MFMA (v_mfma_f32_32x32x16_bf16) with fp32 accumulation. The packed
-// 2-bit substrate is expanded to exact bf16 {-1,0,+1} while it is staged in
-// LDS, so every product is exact. For fp32 activations each Z value is split
-// into three bf16 terms (hi + mid + lo represent it to within 2^-24 relative)
-// and the three partial products accumulate in fp32.
+// 2-bit substrate is expanded to exact bf16 {-2,0,+2} (twice the weights, one
+// shift and one mask per value pair), so every product is exact, and the
+// accumulator is scaled by alpha / 2. For fp32 activations each Z value is
+// split into three bf16 terms (hi + mid + lo represent it to within 2^-24
+// relative) and the three partial products accumulate in fp32.
 //
-// Tiling: BM x BN output tile per workgroup, K in steps of 64, LDS double
-// buffered (global loads for step k+1 are in flight while step k runs on the
-// matrix cores; one barrier per step). Tiles are ordered so that the
-// workgroups one XCD runs at a time share their rows of Z in that XCD's L2.
+// Generic tiling (the kernels below the large-tile one): BM x BN output tile
+// per workgroup, K in steps of 64, LDS double buffered (global loads for step
+// k+1 are in flight while step k runs on the matrix cores; one barrier per
+// step). Tiles are ordered so that the workgroups one XCD runs at a time share
+// their rows of Z in that XCD's L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -344,6 +346,9 @@ __device__ __forceinline__ void d_step(f32x16 (&acc)[C::FM][C::FN], const char* 
                                        int m0, int n0, int kt, int wm, int wn, int lane) {
   if constexpr (LOAD) {
     d_load_a<C>(anxt, Z, M, d, m0, (kt + 1) * BK);
+    // The step-end wait counts the packed-word loads as the newest B_PER
+    // vector memory ops: keep the compiler from issuing them before the DMA.
+    __asm__ volatile("" ::: "memory");
     d_load_b<C>(rl, wp, d, n0, (kt + 2) * BK);
   }
   DFrags<C> f0, f1;
@@ -432,10 +437,268 @@ hipError_t launch_dl(const uint16_t* z, const uint32_t* wp, uint16_t* h, int M, 
                        d, alpha, tm, tn);
 }
 
+// ---------------------------------------------------------------------------
+// 256x256-tile kernel for d % 256 == 0 (the large product): 4 waves, one per
+// SIMD, each owning a 256x64 block of the tile (8x2 fragments of 32x32, the
+// 16 accumulator blocks in AGPRs).
+//
+// Both operands stream global->LDS with global_load_lds_dwordx4 through a
+// 4-stage ring, three K-steps ahead: a stage holds the Z tile (256 rows x 64
+// bf16, XOR-swizzled) and the packed substrate words of the step (256 output
+// columns x 16 bytes = 4 KiB). The substrate stays packed in LDS. In the MFMA
+// B layout lane l holds output column l % 32 of a fragment and K half l / 32
+// of each 16-wide slice, so a lane reads the 16 bytes of its column once per
+// step and expands the 8 bf16 of a slice in registers (unpack_pair: two VALU
+// ops per bf16 pair) right before the MFMAs that use them. With 256 rows per
+// wave each expanded fragment feeds 8 MFMAs.
+//
+// One barrier per step, before the last slice's MFMAs: all waves are done
+// reading the step's stage (the DMA issued next step may overwrite it) and the
+// next stage has landed, so the next step's first reads overlap this step's
+// last MFMAs. sched_group_barrier fixes the order inside each slice: the next
+// slice's LDS reads go out one per MFMA at the start, the expansion VALU ops
+// are spread between MFMAs.
+template <int WM_, int WN_>
+struct RbCfg {
+  static constexpr int BM = 256, BN = 256, THREADS = 256;
+  static constexpr int WM = WM_, WN = WN_;
+  static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+  static constexpr int NSTAGE = 4, AHEAD = NSTAGE - 1;
+  static constexpr int A_BYTES = BM * kRowBytes;       // 32 KiB of Z
+  static constexpr int B_BYTES = BN * 16;              // 4 KiB of packed words
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_LOADS = A_BYTES / 1024 / 4;   // 1 KiB DMA blocks per wave
+  static constexpr int VM_PER_STEP = A_LOADS + 1;      // + one block of packed words
+  static_assert(WM * WN == 4 && FM * FN == 16, "4 waves, 256 accumulator registers each");
+  static_assert(B_BYTES == 4 * 1024, "one packed-word block per wave");
+};
+
+template <int N>
+struct RbFrag {
+  bf16x8 v[N];
+};
+
+// Issue step kt's DMA into `stg`: first this wave's block of packed words
+// (columns n0 + 64 * wave + lane), then its share of the Z tile.
+template <class C>
+__device__ __forceinline__ void rb_load(char* stg, const uint16_t* Z, const uint32_t* wp, int M,
+                                        int d, int m0, int n0, int kt, int lane, int wave) {
+  const uint32_t* g = wp + (size_t)(n0 + wave * 64 + lane) * (d / 16) + kt * 4;
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)(stg + C::A_BYTES +
+                                                                            wave * 1024),
+                                   16, 0, 0);
+  __asm__ volatile("" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < C::A_LOADS; ++j) {
+    const int blk = wave * C::A_LOADS + j;  // 8 rows
+    const int row = blk * 8 + lane / 8;
+    const int chunk = (lane % 8) ^ ((row >> 1) & 7);
+    const int grow = min(m0 + row, M - 1);
+    const uint16_t* z = Z + (size_t)grow * d + kt * BK + chunk * 8;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)z,
+                                     (__attribute__((address_space(3))) void*)(stg + blk * 1024),
+                                     16, 0, 0);
+  }
+}
+
+// A fragments of slice kk (0..3) for this wave's rows.
+template <class C>
+__device__ __forceinline__ void rb_read_a(RbFrag<C::FM>& a, const char* stg, int wm, int lane,
+                                          int kk) {
+  const int chunk = 2 * kk + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+    a.v[i] = *reinterpret_cast<const bf16x8*>(stg + swz(wm * C::TM + i * 32 + (lane & 31), chunk));
+}
+
+// Packed words of this lane's columns for the whole step.
+template <class C>
+__device__ __forceinline__ void rb_read_w(uint4 (&w)[C::FN], const char* stg, int wn, int lane) {
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j)
+    w[j] = *reinterpret_cast<const uint4*>(stg + C::A_BYTES +
+                                           16 * (wn * C::TN + j * 32 + (lane & 31)));
+}
+
+// B fragments of slice kk from the packed words (shifted by this lane's half).
+template <class C>
+__device__ __forceinline__ void rb_expand_b(RbFrag<C::FN>& b, const uint4 (&w)[C::FN], int hshift,
+                                            int kk) {
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) {
+    const uint32_t word = (kk == 0 ? w[j].x : kk == 1 ? w[j].y : kk == 2 ? w[j].z : w[j].w) >> hshift;
+    u32x4 u;
+    u[0] = unpack_pair(word, 0);
+    u[1] = unpack_pair(word, 1);
+    u[2] = unpack_pair(word, 2);
+    u[3] = unpack_pair(word, 3);
+    b.v[j] = __builtin_bit_cast(bf16x8, u);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void rb_mfma(f32x16 (&acc)[C::FM][C::FN], const RbFrag<C::FM>& a,
+                                        const RbFrag<C::FN>& b) {
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v[i], b.v[j], acc[i][j], 0, 0, 0);
+}
+
+// Order inside one slice section: the FM*FN MFMAs, with `nds` LDS reads and
+// `nvm` DMA issues one per MFMA from the start, VALU ops spread between them.
+// The closing sched_barrier keeps sections apart.
+template <class C>
+__device__ __forceinline__ void rb_interleave(int nds, int nvm) {
+  constexpr int NMF = C::FM * C::FN;
+#pragma unroll
+  for (int i = 0; i < NMF; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+    if (i < nds) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
+    if (i < nvm) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM read
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);                  // VALU
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One K-step in ring slot S. On entry `a` holds slice 0 and `w` the packed
+// words of this step. LOAD: issue step kt+3 into slot S+3. WAIT: vector memory
+// ops allowed in flight once step kt+1 has landed. NEXT: after the barrier,
+// read slice 0 and the packed words of step kt+1.
+template <class C, int S, bool LOAD, int WAIT, bool NEXT>
+__device__ __forceinline__ void rb_step(f32x16 (&acc)[C::FM][C::FN], RbFrag<C::FM>& a,
+                                        uint4 (&w)[C::FN], char* const (&ring)[C::NSTAGE],
+                                        const uint16_t* Z, const uint32_t* wp, int M, int d,
+                                        int m0, int n0, int kt, int wm, int wn, int lane, int wave,
+                                        int hshift) {
+  const char* cur = ring[S];
+  if constexpr (LOAD)
+    rb_load<C>(ring[(S + C::AHEAD) % C::NSTAGE], Z, wp, M, d, m0, n0, kt + C::AHEAD, lane, wave);
+  RbFrag<C::FN> b0, b1;
+  RbFrag<C::FM> a1;
+  rb_expand_b<C>(b0, w, hshift, 0);
+  rb_read_a<C>(a1, cur, wm, lane, 1);
+  rb_mfma<C>(acc, a, b0);
+  rb_interleave<C>(C::FM, LOAD ? C::VM_PER_STEP : 0);
+  rb_expand_b<C>(b1, w, hshift, 1);
+  rb_read_a<C>(a, cur, wm, lane, 2);
+  rb_mfma<C>(acc, a1, b1);
+  rb_interleave<C>(C::FM, 0);
+  rb_expand_b<C>(b0, w, hshift, 2);
+  rb_read_a<C>(a1, cur, wm, lane, 3);
+  rb_mfma<C>(acc, a, b0);
+  rb_interleave<C>(C::FM, 0);
+  rb_expand_b<C>(b1, w, hshift, 3);
+  if constexpr (NEXT) {
+    wait_vmcnt<WAIT>();
+    lds_barrier();
+    const char* nxt = ring[(S + 1) % C::NSTAGE];
+    rb_read_w<C>(w, nxt, wn, lane);
+    rb_read_a<C>(a, nxt, wm, lane, 0);
+  }
+  rb_mfma<C>(acc, a1, b1);
+  rb_interleave<C>(NEXT ? C::FM + C::FN : 0, 0);
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void gemm_rb_kernel(const uint16_t* Z,
+                                                             const uint32_t* wp, uint16_t* H,
+                                                             int M, int d, float alpha,
+                                                             int tiles_m, int tiles_n) {
+  // One array per stage: the compiler can then tell a stage being read from
+  // the stages the DMA still writes, and does not wait for all loads.
+  __shared__ __attribute__((aligned(1024))) char st0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st3[C::STAGE];
+  static_assert(C::NSTAGE == 4, "four stage arrays");
+  char* ring[4];
+  ring[0] = st0;
+  ring[1] = st1;
+  ring[2] = st2;
+  ring[3] = st3;
+
+  const int ntiles = tiles_m * tiles_n;
+  const int bid = blockIdx.x;
+  // XCD-contiguous tile ranges (workgroups are dealt round-robin to 8 XCDs).
+  const int xcd = bid % 8, per = ntiles / 8, extra = ntiles % 8;
+  const int tile = xcd * per + min(xcd, extra) + bid / 8;
+  const int m0 = (tile / tiles_n) * C::BM, n0 = (tile % tiles_n) * C::BN;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int hshift = 8 * (lane >> 5);  // K half of the slice -> its 4 code pairs
+
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = d / BK;  // multiple of 4
+#pragma unroll
+  for (int s = 0; s < C::AHEAD; ++s) {
+    rb_load<C>(ring[s], Z, wp, M, d, m0, n0, s, lane, wave);
+    __asm__ volatile("" ::: "memory");
+  }
+  wait_vmcnt<(C::AHEAD - 1) * C::VM_PER_STEP>();
+  lds_barrier();
+  uint4 w[C::FN];
+  RbFrag<C::FM> a;
+  rb_read_w<C>(w, ring[0], wn, lane);
+  rb_read_a<C>(a, ring[0], wm, lane, 0);
+
+  constexpr int W3 = 2 * C::VM_PER_STEP;  // steady state: steps kt+2, kt+3 in flight
+  int kt = 0;
+  for (; kt + 4 < nk; kt += 4) {
+    rb_step<C, 0, true, W3, true>(acc, a, w, ring, Z, wp, M, d, m0, n0, kt, wm, wn, lane, wave,
+                                  hshift);
+    rb_step<C, 1, true, W3, true>(acc, a, w, ring, Z, wp, M, d, m0, n0, kt + 1, wm, wn, lane,
+                                  wave, hshift);
+    rb_step<C, 2, true, W3, true>(acc, a, w, ring, Z, wp, M, d, m0, n0, kt + 2, wm, wn, lane,
+                                  wave, hshift);
+    rb_step<C, 3, true, W3, true>(acc, a, w, ring, Z, wp, M, d, m0, n0, kt + 3, wm, wn, lane,
+                                  wave, hshift);
+  }
+  // Last four steps: only the first still issues a load (step nk-1).
+  rb_step<C, 0, true, W3, true>(acc, a, w, ring, Z, wp, M, d, m0, n0, kt, wm, wn, lane, wave,
+                                hshift);
+  rb_step<C, 1, false, C::VM_PER_STEP, true>(acc, a, w, ring, Z, wp, M, d, m0, n0, kt + 1, wm, wn,
+                                             lane, wave, hshift);
+  rb_step<C, 2, false, 0, true>(acc, a, w, ring, Z, wp, M, d, m0, n0, kt + 2, wm, wn, lane, wave,
+                                hshift);
+  rb_step<C, 3, false, 0, false>(acc, a, w, ring, Z, wp, M, d, m0, n0, kt + 3, wm, wn, lane, wave,
+                                 hshift);
+
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int c = n0 + wn * C::TN + j * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * C::TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row < M) H[(size_t)row * d + c] = (uint16_t)f32_to_bf16_bits(alpha * acc[i][j][r]);
+      }
+    }
+}
+
+template <class C>
+hipError_t launch_rb(const uint16_t* z, const uint32_t* wp, uint16_t* h, int M, int d,
+                     float alpha, hipStream_t s, const KernelTiming& t) {
+  const int tm = (M + C::BM - 1) / C::BM, tn = d / C::BN;
+  return launch_kernel(gemm_rb_kernel<C>, dim3(tm * tn), dim3(C::THREADS), 0, s, t, z, wp, h, M,
+                       d, alpha, tm, tn);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(bmoe_dtype dt, int M, int d, const void* z, const uint32_t* w_packed,
                        float alpha, void* h, hipStream_t s, const KernelTiming& t) {
+  alpha = substrate_scale(alpha);  // the expanded substrate holds +-2
   if (dt == BMOE_F32)
     return launch_cfg<Cfg<64, 64, 2, 2, true>, float>(z, w_packed, static_cast<float*>(h), M, d,
                                                       alpha, s, t);
@@ -445,7 +708,7 @@ hipError_t launch_gemm(bmoe_dtype dt, int M, int d, const void* z, const uint32_
   // tiles so that the grid still covers the 256 CUs.
   const long long big_tiles = (long long)((M + 255) / 256) * (d / 256);
   if (d >= 256 && big_tiles >= 512)
-    return launch_dl<DCfg<256, 256, 2, 4>>(zb, w_packed, hb, M, d, alpha, s, t);
+    return launch_rb<RbCfg<1, 4>>(zb, w_packed, hb, M, d, alpha, s, t);
   if (d >= 128) return launch_dl<DCfg<128, 128, 2, 2>>(zb, w_packed, hb, M, d, alpha, s, t);
   return launch_cfg<Cfg<64, 64, 2, 2, false>, uint16_t>(z, w_packed, hb, M, d, alpha, s, t);
 }

@@ -64,8 +64,8 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const int8_t* w, int d, 
     for (int v = 0; v < 16; ++v) {
       const int8_t val = (int8_t)((parts[v >> 2] >> (8 * (v & 3))) & 0xFFu);
       const int j = v >> 1;
-      const int nz_bit = (v & 1) ? 16 + j : j;
-      const int sg_bit = nz_bit + 8;
+      const int nz_bit = (v & 1) ? 16 + 2 * j : 2 * j;
+      const int sg_bit = nz_bit + 1;
       if (val == 1) {
         word |= 1u << nz_bit;
       } else if (val == -1) {

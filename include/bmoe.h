@@ -86,9 +86,10 @@ size_t bmoe_pack_workspace_bytes(void);
  * per entry.
  *   w        int8 [d][d], row o = output, column c = input.
  *   packed   uint32 [d][ceil(d/16)] (output). Row o, word g holds columns
- *            c = 16g .. 16g+15: column v = c - 16g with v = 2j keeps its
- *            nonzero flag at bit j and its sign at bit 8+j; v = 2j+1 at bits
- *            16+j and 24+j. +1 = (nz 1, sign 0), -1 = (1, 1), 0 = (0, 0).
+ *            c = 16g .. 16g+15 as 2-bit codes, nonzero flag in the low bit
+ *            and sign in the high bit (+1 = 01, -1 = 11, 0 = 00): column
+ *            v = c - 16g with v = 2j uses bits 2j and 2j+1, v = 2j+1 uses
+ *            bits 16+2j and 17+2j.
  *   ws       at least bmoe_pack_workspace_bytes(); receives the status word.
  * Invalid entries are packed as 0 and reported as BMOE_E_TERNARY by
  * bmoe_sync_status(ws, stream).

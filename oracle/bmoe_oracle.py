@@ -159,16 +159,17 @@ def route(ids, n_experts: int):
 # Packed W_base layout (a storage reading: the pages give 1.58 bit/weight as
 # the information content, §2.1; the stored form here uses 2 bits/weight).
 # Row o (output), group g of 16 input columns c = 16g .. 16g+15 -> one uint32
-# at [o][g]. For v = c - 16g: v = 2j puts its nonzero flag at bit j and its
-# sign flag at bit 8+j; v = 2j+1 puts them at bits 16+j and 24+j. +1 is
-# (nz=1, sign=0), -1 is (nz=1, sign=1), 0 is (0, 0). Rows with d < 16 pad
-# with zeros.
+# at [o][g]. Each weight is a 2-bit code, nonzero flag in the low bit and
+# sign in the high bit: +1 -> 01, -1 -> 11, 0 -> 00 (10 never occurs). For
+# v = c - 16g: v = 2j takes bits 2j (flag) and 2j+1 (sign); v = 2j+1 takes
+# bits 16+2j and 17+2j, so even columns fill the low half-word and odd columns
+# the high one. Rows with d < 16 pad with zeros.
 
 def _bit_positions(v: int):
     j = v >> 1
     if v & 1:
-        return 16 + j, 24 + j
-    return j, 8 + j
+        return 16 + 2 * j, 17 + 2 * j
+    return 2 * j, 2 * j + 1
 
 
 def pack_ternary(w) -> np.ndarray:

@@ -24,7 +24,7 @@ MUTANTS = {
     "sides_swapped": [("Z = apply_butterfly(theta[e]", "Z = apply_butterfly(phi[e]"),
                       ("U[a:b] = apply_butterfly(phi[e]", "U[a:b] = apply_butterfly(theta[e]")],
     "route_unstable": [("for r, e in enumerate(flat):", "for r, e in reversed(list(enumerate(flat))):")],
-    "pack_bits": [("return 16 + j, 24 + j", "return 24 + j, 16 + j")],
+    "pack_bits": [("return 16 + 2 * j, 17 + 2 * j", "return 17 + 2 * j, 16 + 2 * j")],
     "token_of_row": [("x[rows // k]", "x[rows % x.shape[0]]")],
 }
 

@@ -69,6 +69,33 @@ def test_forward_full_size_sampled(name):
     assert np.isfinite(y).all()
 
 
+# Shapes whose routed-row count is large enough for the 256x256-tile product
+# kernel while M = T*k is ragged against its tiles (the last row tile is
+# partly past M). The token sample includes every token routed to the last
+# expert, whose rows sit in that last tile.
+LARGE_TILE_CASES = [
+    (1024, 8, 4, 8200),   # M = 32800 = 128 * 256 + 32
+    (4096, 16, 2, 4001),  # M = 8002 = 31 * 256 + 66
+]
+
+
+@pytest.mark.parametrize("d,N,k,T", LARGE_TILE_CASES)
+def test_large_tile_product_ragged(d, N, k, T):
+    inp = W.make_inputs(W.HEADLINE, d=d, N=N, k=k, T=T, seed=77 + d)
+    _announce(f"[parity large tiles] T={T} d={d} N={N} k={k} M={T * k}")
+    dev = to_device(inp)
+    y, route = run_forward(dev, inp)
+    check_route(inp, route)
+    rng = np.random.default_rng(1)
+    last = np.nonzero((inp.ids == N - 1).any(axis=1))[0]
+    toks = np.unique(np.concatenate([[0, T - 1], last[-40:], rng.choice(T, 60, replace=False)]))
+    ref = O.forward_tokens(toks, inp.x, inp.ids, inp.gates, inp.theta, inp.phi, inp.w, inp.alpha)
+    err = O.max_rel_err(y[toks], ref)
+    _announce(f"  max rel err {err:.3e} on {toks.size} sampled tokens")
+    assert err <= TOL[inp.dtype]
+    assert np.isfinite(y).all()
+
+
 @pytest.mark.parametrize("d", [16, 64, 512, 4096])
 def test_pack_bit_exact(d):
     inp = W.make_inputs("custom", d=d, N=1, k=1, T=1, seed=d)
