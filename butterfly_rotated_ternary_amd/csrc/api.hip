@@ -23,7 +23,7 @@ int log2i(int d) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct FwdLayout {
-  size_t status, offsets, perm, inv, slot_e, cs_in, cs_out, z, h, u, w16, total;
+  size_t status, offsets, perm, inv, slot_e, cs_in, cs_out, z, h, u, w16, wt, total;
 };
 
 bool shape_ok(bmoe_dtype dt, int T, int d, int N, int k) {
@@ -54,6 +54,9 @@ FwdLayout fwd_layout(bmoe_dtype dt, int T, int d, int N, int k) {
   l.u = off;       off = align_up(off + zel * M * d);
   l.w16 = off;
   if (fused) off = align_up(off + sizeof(uint16_t) * (size_t)d * d);
+  // Tile-major copy of the packed substrate for the large-tile product.
+  l.wt = off;
+  if (gemm_tiled_w_block(dt, (int)M, d)) off = align_up(off + sizeof(uint32_t) * (size_t)d * (d / 16));
   l.total = off;
   return l;
 }
@@ -143,8 +146,10 @@ bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k
   };
   const bool fused = fused_supported(dt, d);
   uint16_t* w16 = fused ? reinterpret_cast<uint16_t*>(base + l.w16) : nullptr;
-  if (launch_prep(ids, M, n_experts, theta, phi, d, rt, cs_in, cs_out, status, w_packed, w16, s,
-                  timing()) != hipSuccess)
+  const int wt_block = gemm_tiled_w_block(dt, M, d);
+  uint32_t* wt = wt_block ? reinterpret_cast<uint32_t*>(base + l.wt) : nullptr;
+  if (launch_prep(ids, M, n_experts, theta, phi, d, rt, cs_in, cs_out, status, w_packed, w16, wt,
+                  wt_block, s, timing()) != hipSuccess)
     return BMOE_E_HIP;
   if (fused) {
     if (launch_fused(M, d, k, x, gates, rt, cs_in, cs_out, w16, w_packed, alpha, u, s,
@@ -153,7 +158,7 @@ bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k
   } else {
     if (launch_bfly_in(dt, M, d, k, x, rt, cs_in, z, s, timing()) != hipSuccess)
       return BMOE_E_HIP;
-    if (launch_gemm(dt, M, d, z, w_packed, alpha, h, s, timing()) != hipSuccess)
+    if (launch_gemm(dt, M, d, z, w_packed, wt, alpha, h, s, timing()) != hipSuccess)
       return BMOE_E_HIP;
     if (launch_bfly_out(dt, M, d, h, gates, rt, cs_out, u, s, timing()) != hipSuccess)
       return BMOE_E_HIP;

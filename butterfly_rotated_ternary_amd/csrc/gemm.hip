@@ -458,19 +458,22 @@ hipError_t launch_dl(const uint16_t* z, const uint32_t* wp, uint16_t* h, int M, 
 // last MFMAs. sched_group_barrier fixes the order inside each slice: the next
 // slice's LDS reads go out one per MFMA at the start, the expansion VALU ops
 // are spread between MFMAs.
-template <int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_>
 struct RbCfg {
-  static constexpr int BM = 256, BN = 256, THREADS = 256;
+  static constexpr int BM = BM_, BN = BN_, THREADS = 256;
   static constexpr int WM = WM_, WN = WN_;
   static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   static constexpr int NSTAGE = 4, AHEAD = NSTAGE - 1;
-  static constexpr int A_BYTES = BM * kRowBytes;       // 32 KiB of Z
-  static constexpr int B_BYTES = BN * 16;              // 4 KiB of packed words
+  static constexpr int A_BYTES = BM * kRowBytes;       // Z: BM rows x 64 bf16
+  static constexpr int B_BYTES = BN * 16;              // packed words: BN columns x 16 B
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int A_LOADS = A_BYTES / 1024 / 4;   // 1 KiB DMA blocks per wave
-  static constexpr int VM_PER_STEP = A_LOADS + 1;      // + one block of packed words
+  static constexpr int B_LOADS = B_BYTES / 1024 / 4;
+  static constexpr int VM_PER_STEP = A_LOADS + B_LOADS;
+  static constexpr int OUT_BYTES = 16 * TN * 2;        // per-wave epilogue staging: 16 rows
   static_assert(WM * WN == 4 && FM * FN == 16, "4 waves, 256 accumulator registers each");
-  static_assert(B_BYTES == 4 * 1024, "one packed-word block per wave");
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1, "whole DMA blocks per wave");
+  static_assert(NSTAGE * STAGE + 4 * OUT_BYTES <= 160 * 1024, "LDS budget");
 };
 
 template <int N>
@@ -478,16 +481,22 @@ struct RbFrag {
   bf16x8 v[N];
 };
 
-// Issue step kt's DMA into `stg`: first this wave's block of packed words
-// (columns n0 + 64 * wave + lane), then its share of the Z tile.
+// Issue step kt's DMA into `stg`: first this wave's blocks of packed words
+// (each one contiguous KiB of the tile-major copy wt: 64 columns x 16 B),
+// then its share of the Z tile.
 template <class C>
-__device__ __forceinline__ void rb_load(char* stg, const uint16_t* Z, const uint32_t* wp, int M,
+__device__ __forceinline__ void rb_load(char* stg, const uint16_t* Z, const uint32_t* wt, int M,
                                         int d, int m0, int n0, int kt, int lane, int wave) {
-  const uint32_t* g = wp + (size_t)(n0 + wave * 64 + lane) * (d / 16) + kt * 4;
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)(stg + C::A_BYTES +
-                                                                            wave * 1024),
-                                   16, 0, 0);
+#pragma unroll
+  for (int b = 0; b < C::B_LOADS; ++b) {
+    const int blk = wave * C::B_LOADS + b;  // 64 columns
+    const uint32_t* g =
+        wt + (((size_t)(n0 / C::BN) * (d / BK) + kt) * C::BN + blk * 64 + lane) * 4;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)(stg + C::A_BYTES +
+                                                                              blk * 1024),
+                                     16, 0, 0);
+  }
   __asm__ volatile("" ::: "memory");
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j) {
@@ -537,14 +546,18 @@ __device__ __forceinline__ void rb_expand_b(RbFrag<C::FN>& b, const uint4 (&w)[C
   }
 }
 
-template <class C>
+// INIT: start the accumulators from zero (the tile's first slice), so they
+// are not live across tiles.
+template <class C, bool INIT = false>
 __device__ __forceinline__ void rb_mfma(f32x16 (&acc)[C::FM][C::FN], const RbFrag<C::FM>& a,
                                         const RbFrag<C::FN>& b) {
+  const f32x16 zero = {};
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v[i], b.v[j], acc[i][j], 0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v[i], b.v[j], INIT ? zero : acc[i][j],
+                                                          0, 0, 0);
 }
 
 // Order inside one slice section: the FM*FN MFMAs, with `nds` LDS reads and
@@ -563,34 +576,56 @@ __device__ __forceinline__ void rb_interleave(int nds, int nvm) {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// What a step issues at its start.
+enum RbLoad { kNoLoad = 0, kOwnStep = 1, kNextTile = 2 };
+
+struct RbTile {
+  int m0, n0;
+};
+
 // One K-step in ring slot S. On entry `a` holds slice 0 and `w` the packed
-// words of this step. LOAD: issue step kt+3 into slot S+3. WAIT: vector memory
+// words of this step. LOAD kOwnStep: issue step kt+3 of this tile into slot
+// S+3; kNextTile: issue steps 0..2 of tile `nt` into slots 0..2 (only legal in
+// the last step, once every wave has left slots 0..2). WAIT: vector memory
 // ops allowed in flight once step kt+1 has landed. NEXT: after the barrier,
 // read slice 0 and the packed words of step kt+1.
-template <class C, int S, bool LOAD, int WAIT, bool NEXT>
+template <class C, int S, int LOAD, int WAIT, bool NEXT, bool INIT = false>
 __device__ __forceinline__ void rb_step(f32x16 (&acc)[C::FM][C::FN], RbFrag<C::FM>& a,
                                         uint4 (&w)[C::FN], char* const (&ring)[C::NSTAGE],
-                                        const uint16_t* Z, const uint32_t* wp, int M, int d,
-                                        int m0, int n0, int kt, int wm, int wn, int lane, int wave,
-                                        int hshift) {
+                                        const uint16_t* Z, const uint32_t* wt, int M, int d,
+                                        RbTile tl, RbTile nt, int kt, int wm, int wn, int lane,
+                                        int wave, int hshift) {
   const char* cur = ring[S];
-  if constexpr (LOAD)
-    rb_load<C>(ring[(S + C::AHEAD) % C::NSTAGE], Z, wp, M, d, m0, n0, kt + C::AHEAD, lane, wave);
+  if constexpr (LOAD == kOwnStep) {
+    rb_load<C>(ring[(S + C::AHEAD) % C::NSTAGE], Z, wt, M, d, tl.m0, tl.n0, kt + C::AHEAD, lane,
+               wave);
+  } else if constexpr (LOAD == kNextTile) {
+#pragma unroll
+    for (int s = 0; s < C::AHEAD; ++s) {
+      rb_load<C>(ring[s], Z, wt, M, d, nt.m0, nt.n0, s, lane, wave);
+      __asm__ volatile("" ::: "memory");
+    }
+  }
+  constexpr int NVM = LOAD == kOwnStep ? C::VM_PER_STEP : LOAD == kNextTile ? 3 * C::VM_PER_STEP : 0;
   RbFrag<C::FN> b0, b1;
   RbFrag<C::FM> a1;
   rb_expand_b<C>(b0, w, hshift, 0);
   rb_read_a<C>(a1, cur, wm, lane, 1);
-  rb_mfma<C>(acc, a, b0);
-  rb_interleave<C>(C::FM, LOAD ? C::VM_PER_STEP : 0);
+  rb_mfma<C, INIT>(acc, a, b0);
+  rb_interleave<C>(C::FM, NVM < 16 ? NVM : 16);
   rb_expand_b<C>(b1, w, hshift, 1);
   rb_read_a<C>(a, cur, wm, lane, 2);
   rb_mfma<C>(acc, a1, b1);
-  rb_interleave<C>(C::FM, 0);
+  rb_interleave<C>(C::FM, NVM > 16 ? NVM - 16 : 0);
   rb_expand_b<C>(b0, w, hshift, 2);
   rb_read_a<C>(a1, cur, wm, lane, 3);
   rb_mfma<C>(acc, a, b0);
   rb_interleave<C>(C::FM, 0);
   rb_expand_b<C>(b1, w, hshift, 3);
+  // The last expansion happens before the barrier, so this step's packed
+  // words are dead before the next step reloads their registers.
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) __asm__ volatile("" : "+v"(b1.v[j]));
   if constexpr (NEXT) {
     wait_vmcnt<WAIT>();
     lds_barrier();
@@ -602,9 +637,50 @@ __device__ __forceinline__ void rb_step(f32x16 (&acc)[C::FM][C::FN], RbFrag<C::F
   rb_interleave<C>(NEXT ? C::FM + C::FN : 0, 0);
 }
 
+// Epilogue of one tile: alpha * acc -> bf16 H through this wave's staging
+// LDS, 16 rows at a time (registers 8h .. 8h+7 of a 32x32 block are its rows
+// 16h .. 16h+15), so the global stores are 16 bytes per lane over whole row
+// segments of TN columns (8 stores per 32 rows).
+template <class C>
+__device__ __forceinline__ void rb_store(const f32x16 (&acc)[C::FM][C::FN], char* stg,
+                                         uint16_t* H, int M, int d, RbTile tl, int wm, int wn,
+                                         int lane, float alpha) {
+  constexpr int PITCH = C::TN * 2, CHUNKS = C::TN / 8, RPQ = 64 / CHUNKS;
+  static_assert((CHUNKS & (CHUNKS - 1)) == 0 && CHUNKS <= 64, "chunk swizzle");
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // 16 rows x TN bf16; 16-byte chunks XOR-swizzled by row.
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int r = 8 * h; r < 8 * h + 8; ++r) {
+          const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) - 16 * h;
+          const int col = j * 32 + (lane & 31);
+          const int off = row * PITCH + 16 * ((col >> 3) ^ (row & (CHUNKS - 1))) + 2 * (col & 7);
+          *reinterpret_cast<uint16_t*>(stg + off) =
+              (uint16_t)f32_to_bf16_bits(alpha * acc[i][j][r]);
+        }
+#pragma unroll
+      for (int q = 0; q < 16 / RPQ; ++q) {
+        const int row = q * RPQ + lane / CHUNKS, ch = lane % CHUNKS;
+        const uint4 v =
+            *reinterpret_cast<const uint4*>(stg + row * PITCH + 16 * (ch ^ (row & (CHUNKS - 1))));
+        const int grow = tl.m0 + wm * C::TM + i * 32 + 16 * h + row;
+        if (grow < M)
+          *reinterpret_cast<uint4*>(H + (size_t)grow * d + tl.n0 + wn * C::TN + ch * 8) = v;
+      }
+    }
+}
+
+// Persistent: one workgroup per CU walks every nw-th tile of its XCD's
+// contiguous tile range. The next tile's first three K-steps are issued in the
+// current tile's last K-step (ring slots 0..2 are free once every wave has
+// passed step nk-2's barrier), so they land while the epilogue stores run.
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void gemm_rb_kernel(const uint16_t* Z,
-                                                             const uint32_t* wp, uint16_t* H,
+                                                             const uint32_t* wt, uint16_t* H,
                                                              int M, int d, float alpha,
                                                              int tiles_m, int tiles_n) {
   // One array per stage: the compiler can then tell a stage being read from
@@ -613,6 +689,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_rb_kernel(const uint16_t* Z,
   __shared__ __attribute__((aligned(1024))) char st1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) char st2[C::STAGE];
   __shared__ __attribute__((aligned(1024))) char st3[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage_out[4 * C::OUT_BYTES];
   static_assert(C::NSTAGE == 4, "four stage arrays");
   char* ring[4];
   ring[0] = st0;
@@ -620,95 +697,137 @@ __global__ __launch_bounds__(C::THREADS) void gemm_rb_kernel(const uint16_t* Z,
   ring[2] = st2;
   ring[3] = st3;
 
-  const int ntiles = tiles_m * tiles_n;
-  const int bid = blockIdx.x;
-  // XCD-contiguous tile ranges (workgroups are dealt round-robin to 8 XCDs).
-  const int xcd = bid % 8, per = ntiles / 8, extra = ntiles % 8;
-  const int tile = xcd * per + min(xcd, extra) + bid / 8;
-  const int m0 = (tile / tiles_n) * C::BM, n0 = (tile % tiles_n) * C::BN;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int hshift = 8 * (lane >> 5);  // K half of the slice -> its 4 code pairs
 
-  f32x16 acc[C::FM][C::FN];
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // Workgroups are dealt round-robin to the 8 XCDs (gridDim.x is a multiple
+  // of 8): XCD x owns tiles [t0, t1) and its nw workgroups interleave on them.
+  const int ntiles = tiles_m * tiles_n;
+  const int xcd = blockIdx.x % 8, nw = gridDim.x / 8;
+  const int per = ntiles / 8, extra = ntiles % 8;
+  const int t0 = xcd * per + min(xcd, extra), t1 = t0 + per + (xcd < extra ? 1 : 0);
+  int tile = t0 + blockIdx.x / 8;
+  if (tile >= t1) return;  // whole workgroup
+  RbTile tl;
+  tl.m0 = (tile / tiles_n) * C::BM;
+  tl.n0 = (tile % tiles_n) * C::BN;
 
   const int nk = d / BK;  // multiple of 4
 #pragma unroll
   for (int s = 0; s < C::AHEAD; ++s) {
-    rb_load<C>(ring[s], Z, wp, M, d, m0, n0, s, lane, wave);
+    rb_load<C>(ring[s], Z, wt, M, d, tl.m0, tl.n0, s, lane, wave);
     __asm__ volatile("" ::: "memory");
   }
   wait_vmcnt<(C::AHEAD - 1) * C::VM_PER_STEP>();
   lds_barrier();
-  uint4 w[C::FN];
-  RbFrag<C::FM> a;
-  rb_read_w<C>(w, ring[0], wn, lane);
-  rb_read_a<C>(a, ring[0], wm, lane, 0);
 
   constexpr int W3 = 2 * C::VM_PER_STEP;  // steady state: steps kt+2, kt+3 in flight
-  int kt = 0;
-  for (; kt + 4 < nk; kt += 4) {
-    rb_step<C, 0, true, W3, true>(acc, a, w, ring, Z, wp, M, d, m0, n0, kt, wm, wn, lane, wave,
-                                  hshift);
-    rb_step<C, 1, true, W3, true>(acc, a, w, ring, Z, wp, M, d, m0, n0, kt + 1, wm, wn, lane,
-                                  wave, hshift);
-    rb_step<C, 2, true, W3, true>(acc, a, w, ring, Z, wp, M, d, m0, n0, kt + 2, wm, wn, lane,
-                                  wave, hshift);
-    rb_step<C, 3, true, W3, true>(acc, a, w, ring, Z, wp, M, d, m0, n0, kt + 3, wm, wn, lane,
-                                  wave, hshift);
-  }
-  // Last four steps: only the first still issues a load (step nk-1).
-  rb_step<C, 0, true, W3, true>(acc, a, w, ring, Z, wp, M, d, m0, n0, kt, wm, wn, lane, wave,
-                                hshift);
-  rb_step<C, 1, false, C::VM_PER_STEP, true>(acc, a, w, ring, Z, wp, M, d, m0, n0, kt + 1, wm, wn,
-                                             lane, wave, hshift);
-  rb_step<C, 2, false, 0, true>(acc, a, w, ring, Z, wp, M, d, m0, n0, kt + 2, wm, wn, lane, wave,
-                                hshift);
-  rb_step<C, 3, false, 0, false>(acc, a, w, ring, Z, wp, M, d, m0, n0, kt + 3, wm, wn, lane, wave,
-                                 hshift);
+  for (;;) {
+    const int next = tile + nw;
+    const bool has_next = next < t1;
+    // Without a next tile the last step re-issues this tile's first steps (a
+    // few wasted loads, no branch around the accumulators); they are drained
+    // before the workgroup exits.
+    const int nx = has_next ? next : tile;
+    RbTile nt;
+    nt.m0 = (nx / tiles_n) * C::BM;
+    nt.n0 = (nx % tiles_n) * C::BN;
 
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const int c = n0 + wn * C::TN + j * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * C::TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < M) H[(size_t)row * d + c] = (uint16_t)f32_to_bf16_bits(alpha * acc[i][j][r]);
-      }
+    uint4 w[C::FN];
+    RbFrag<C::FM> a;
+    rb_read_w<C>(w, ring[0], wn, lane);
+    rb_read_a<C>(a, ring[0], wm, lane, 0);
+    f32x16 acc[C::FM][C::FN];
+    // The first four steps (the first slice sets the accumulators).
+    rb_step<C, 0, kOwnStep, W3, true, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, 0, wm, wn, lane,
+                                            wave, hshift);
+    rb_step<C, 1, kOwnStep, W3, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, 1, wm, wn, lane, wave,
+                                      hshift);
+    rb_step<C, 2, kOwnStep, W3, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, 2, wm, wn, lane, wave,
+                                      hshift);
+    rb_step<C, 3, kOwnStep, W3, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, 3, wm, wn, lane, wave,
+                                      hshift);
+    int kt = 4;
+    for (; kt + 4 < nk; kt += 4) {
+      rb_step<C, 0, kOwnStep, W3, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, kt, wm, wn, lane,
+                                        wave, hshift);
+      rb_step<C, 1, kOwnStep, W3, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, kt + 1, wm, wn,
+                                        lane, wave, hshift);
+      rb_step<C, 2, kOwnStep, W3, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, kt + 2, wm, wn,
+                                        lane, wave, hshift);
+      rb_step<C, 3, kOwnStep, W3, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, kt + 3, wm, wn,
+                                        lane, wave, hshift);
     }
+    rb_step<C, 0, kOwnStep, W3, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, kt, wm, wn, lane,
+                                      wave, hshift);
+    rb_step<C, 1, kNoLoad, C::VM_PER_STEP, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, kt + 1,
+                                                 wm, wn, lane, wave, hshift);
+    rb_step<C, 2, kNoLoad, 0, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, kt + 2, wm, wn, lane,
+                                    wave, hshift);
+    rb_step<C, 3, kNextTile, 0, false>(acc, a, w, ring, Z, wt, M, d, tl, nt, kt + 3, wm, wn, lane,
+                                       wave, hshift);
+
+    rb_store<C>(acc, stage_out + wave * C::OUT_BYTES, H, M, d, tl, wm, wn, lane, alpha);
+    if (!has_next) {
+      wait_vmcnt<0>();  // no DMA may land in LDS after the workgroup ends
+      break;
+    }
+    tile = next;
+    tl = nt;
+    // Step 0 of the new tile was issued before the epilogue's stores; steps 1
+    // and 2 and the stores (8 per 32 rows) may still be in flight.
+    wait_vmcnt<2 * C::VM_PER_STEP + 8 * C::FM>();
+    lds_barrier();
+  }
 }
 
 template <class C>
-hipError_t launch_rb(const uint16_t* z, const uint32_t* wp, uint16_t* h, int M, int d,
+hipError_t launch_rb(const uint16_t* z, const uint32_t* wt, uint16_t* h, int M, int d,
                      float alpha, hipStream_t s, const KernelTiming& t) {
   const int tm = (M + C::BM - 1) / C::BM, tn = d / C::BN;
-  return launch_kernel(gemm_rb_kernel<C>, dim3(tm * tn), dim3(C::THREADS), 0, s, t, z, wp, h, M,
-                       d, alpha, tm, tn);
+  // One workgroup per CU (the LDS use allows no second one), a multiple of 8.
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        n >= 8)
+      cus = n;
+    else
+      cus = 256;
+  }
+  int grid = tm * tn < cus ? tm * tn : cus;
+  grid = (grid + 7) / 8 * 8;
+  return launch_kernel(gemm_rb_kernel<C>, dim3(grid), dim3(C::THREADS), 0, s, t, z, wt, h, M, d,
+                       alpha, tm, tn);
 }
 
 }  // namespace
 
+using LargeCfg = RbCfg<128, 512, 1, 4>;
+
+int gemm_tiled_w_block(bmoe_dtype dt, int M, int d) {
+  if (dt != BMOE_BF16 || d % LargeCfg::BN != 0) return 0;
+  const long long tiles = (long long)((M + LargeCfg::BM - 1) / LargeCfg::BM) * (d / LargeCfg::BN);
+  return tiles >= 512 ? LargeCfg::BN : 0;
+}
+
 hipError_t launch_gemm(bmoe_dtype dt, int M, int d, const void* z, const uint32_t* w_packed,
-                       float alpha, void* h, hipStream_t s, const KernelTiming& t) {
+                       const uint32_t* wt, float alpha, void* h, hipStream_t s,
+                       const KernelTiming& t) {
   alpha = substrate_scale(alpha);  // the expanded substrate holds +-2
   if (dt == BMOE_F32)
     return launch_cfg<Cfg<64, 64, 2, 2, true>, float>(z, w_packed, static_cast<float*>(h), M, d,
                                                       alpha, s, t);
   uint16_t* hb = static_cast<uint16_t*>(h);
   const uint16_t* zb = static_cast<const uint16_t*>(z);
-  // Large problems: 256x256 tiles (4 waves of 128x128). Smaller ones: 128x128
-  // tiles so that the grid still covers the 256 CUs.
-  const long long big_tiles = (long long)((M + 255) / 256) * (d / 256);
-  if (d >= 256 && big_tiles >= 512)
-    return launch_rb<RbCfg<1, 4>>(zb, w_packed, hb, M, d, alpha, s, t);
+  // Large problems: 128x512 tiles (4 waves of 128x128, tile-major substrate
+  // copy). Smaller ones: 128x128 tiles so that the grid still covers the CUs.
+  if (gemm_tiled_w_block(dt, M, d)) {
+    if (!wt) return hipErrorInvalidValue;
+    return launch_rb<LargeCfg>(zb, wt, hb, M, d, alpha, s, t);
+  }
   if (d >= 128) return launch_dl<DCfg<128, 128, 2, 2>>(zb, w_packed, hb, M, d, alpha, s, t);
   return launch_cfg<Cfg<64, 64, 2, 2, false>, uint16_t>(z, w_packed, hb, M, d, alpha, s, t);
 }

@@ -31,12 +31,19 @@ struct RouteTables {
 };
 
 // Routing (histogram, scan, stable scatter), the per-call cos/sin tables of
-// both rotation sides and (if w16 is not NULL) the bf16 expansion of the
-// packed substrate, in one launch.
+// both rotation sides and, optionally, a per-call copy of the packed
+// substrate for the product: w16 (bf16 expansion, d <= 512 fused path) or wt
+// (tile-major packed words for the large-tile GEMM), in one launch.
 hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, const float* phi,
                        int d, RouteTables rt, float2* cs_in, float2* cs_out, int32_t* status,
-                       const uint32_t* w_packed, uint16_t* w16, hipStream_t s,
-                       const KernelTiming& t = {});
+                       const uint32_t* w_packed, uint16_t* w16, uint32_t* wt, int wt_block,
+                       hipStream_t s, const KernelTiming& t = {});
+
+// Column block CB of the tile-major substrate copy `wt` the large-tile GEMM
+// reads, or 0 when launch_gemm does not use that kernel. For output-column
+// block ob = o / CB and K-step kt (64 columns), the 16 bytes of row o sit at
+// uint4 index (ob * (d/64) + kt) * CB + o % CB of `wt`.
+int gemm_tiled_w_block(bmoe_dtype dt, int M, int d);
 
 // Whether the fused d <= 512 path handles this shape.
 bool fused_supported(bmoe_dtype dt, int d);
@@ -56,7 +63,8 @@ hipError_t launch_bfly_in(bmoe_dtype dt, int M, int d, int k, const void* x,
 // H = alpha * Z W_base^T over all M sorted rows (H bf16 on the bf16 path,
 // fp32 on the fp32 path; Z likewise).
 hipError_t launch_gemm(bmoe_dtype dt, int M, int d, const void* z, const uint32_t* w_packed,
-                       float alpha, void* h, hipStream_t s, const KernelTiming& t = {});
+                       const uint32_t* wt, float alpha, void* h, hipStream_t s,
+                       const KernelTiming& t = {});
 
 // U[r] = g_r * B(phi_e) H[q] for r = perm[q], written in routed order.
 hipError_t launch_bfly_out(bmoe_dtype dt, int M, int d, const void* h, const float* gates,

@@ -27,9 +27,12 @@ struct PrepParams {
   float2* cs_in;
   float2* cs_out;
   long long n_ang;  // angles per side: N * L * d/2
-  // Optional expansion of the packed substrate to bf16 [d][d] (NULL: none).
+  // Optional per-call copy of the packed substrate (both NULL: none): bf16
+  // expansion [d][d], or tile-major packed words.
   const uint32_t* w_packed;
   uint16_t* w16;
+  uint32_t* wt;
+  int wt_block;
   int d, n_trig_blocks;
 };
 
@@ -59,6 +62,24 @@ __device__ int block_exclusive_scan(int v, int* scratch) {
 }
 
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
+  if ((int)blockIdx.x >= p.n_route_blocks + p.n_trig_blocks && p.wt) {
+    // ---- packed substrate -> tile-major order ---------------------------
+    // Destination-ordered: uint4 u = (ob * nk + kt) * CB + oo holds the 16
+    // bytes of row ob * CB + oo for K-step kt.
+    const int nk = p.d / 64;
+    const size_t cb = (size_t)p.wt_block;
+    const size_t n = (size_t)p.d * nk;
+    const int b = blockIdx.x - p.n_route_blocks - p.n_trig_blocks;
+    const int nb = gridDim.x - p.n_route_blocks - p.n_trig_blocks;
+    for (size_t u = (size_t)b * kThreads + threadIdx.x; u < n; u += (size_t)nb * kThreads) {
+      const size_t oo = u % cb, rest = u / cb;
+      const size_t kt = rest % nk, ob = rest / nk;
+      const size_t o = ob * cb + oo;
+      reinterpret_cast<uint4*>(p.wt)[u] =
+          *reinterpret_cast<const uint4*>(p.w_packed + o * (p.d / 16) + kt * 4);
+    }
+    return;
+  }
   if ((int)blockIdx.x >= p.n_route_blocks + p.n_trig_blocks) {
     // ---- packed substrate -> bf16 rows ----------------------------------
     const int G = p.d / 16;
@@ -206,8 +227,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
 
 hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, const float* phi,
                        int d, RouteTables rt, float2* cs_in, float2* cs_out, int32_t* status,
-                       const uint32_t* w_packed, uint16_t* w16, hipStream_t s,
-                       const KernelTiming& t) {
+                       const uint32_t* w_packed, uint16_t* w16, uint32_t* wt, int wt_block,
+                       hipStream_t s, const KernelTiming& t) {
   int L = 0;
   while ((1 << L) < d) ++L;
   PrepParams p;
@@ -231,11 +252,16 @@ hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, con
   p.n_trig_blocks = (int)trig_blocks;
   p.w_packed = w_packed;
   p.w16 = w16;
+  p.wt = (w16 || wt_block <= 0 || d % wt_block != 0) ? nullptr : wt;
+  p.wt_block = wt_block;
   p.d = d;
   int w_blocks = 0;
   if (w16) {
     const long long words = (long long)d * (d / 16);
     w_blocks = (int)((words + kThreads * 4 - 1) / (kThreads * 4));
+  } else if (p.wt) {
+    const long long quads = (long long)d * (d / 64);
+    w_blocks = (int)((quads + kThreads * 4 - 1) / (kThreads * 4));
   }
   const size_t shmem = sizeof(int) * ((size_t)(2 + kWaves) * N + p.chunk);
   if (shmem > 65536) {

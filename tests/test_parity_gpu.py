@@ -69,13 +69,14 @@ def test_forward_full_size_sampled(name):
     assert np.isfinite(y).all()
 
 
-# Shapes whose routed-row count is large enough for the 256x256-tile product
-# kernel while M = T*k is ragged against its tiles (the last row tile is
-# partly past M). The token sample includes every token routed to the last
-# expert, whose rows sit in that last tile.
+# Shapes whose routed-row count is large enough for the large-tile product
+# kernel (128 x 512 tiles, at least 512 of them) while M = T*k is ragged
+# against its tiles (the last row tile is partly past M). The token sample
+# includes the last 40 tokens routed to the last expert, whose rows sit in
+# that last tile.
 LARGE_TILE_CASES = [
-    (1024, 8, 4, 8200),   # M = 32800 = 128 * 256 + 32
-    (4096, 16, 2, 4001),  # M = 8002 = 31 * 256 + 66
+    (1024, 8, 4, 8200),   # M = 32800 = 256 * 128 + 32
+    (4096, 16, 2, 4200),  # M = 8400 = 65 * 128 + 80
 ]
 
 
