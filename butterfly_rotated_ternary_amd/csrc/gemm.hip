@@ -585,38 +585,36 @@ struct RbTile {
 
 // One K-step in ring slot S. On entry `a` holds slice 0 and `w` the packed
 // words of this step. LOAD kOwnStep: issue step kt+3 of this tile into slot
-// S+3; kNextTile: issue steps 0..2 of tile `nt` into slots 0..2 (only legal in
-// the last step, once every wave has left slots 0..2). WAIT: vector memory
-// ops allowed in flight once step kt+1 has landed. NEXT: after the barrier,
-// read slice 0 and the packed words of step kt+1.
-template <class C, int S, int LOAD, int WAIT, bool NEXT, bool INIT = false>
+// S+3; kNextTile: issue step kt+3-nk of the next tile `nt` there instead (the
+// ring runs on across the tile boundary). WAIT: vector memory ops allowed in
+// flight once step kt+1 has landed; `strict` (runtime, uniform) adds a wait
+// down to WSTRICT first. NEXT: after the barrier, read slice 0 and the packed
+// words of the following step.
+template <class C, int S, int LOAD, int WAIT, bool NEXT, bool INIT = false, int WSTRICT = WAIT>
 __device__ __forceinline__ void rb_step(f32x16 (&acc)[C::FM][C::FN], RbFrag<C::FM>& a,
                                         uint4 (&w)[C::FN], char* const (&ring)[C::NSTAGE],
                                         const uint16_t* Z, const uint32_t* wt, int M, int d,
                                         RbTile tl, RbTile nt, int kt, int wm, int wn, int lane,
-                                        int wave, int hshift) {
+                                        int wave, int hshift, bool strict = false) {
   const char* cur = ring[S];
   if constexpr (LOAD == kOwnStep) {
     rb_load<C>(ring[(S + C::AHEAD) % C::NSTAGE], Z, wt, M, d, tl.m0, tl.n0, kt + C::AHEAD, lane,
                wave);
   } else if constexpr (LOAD == kNextTile) {
-#pragma unroll
-    for (int s = 0; s < C::AHEAD; ++s) {
-      rb_load<C>(ring[s], Z, wt, M, d, nt.m0, nt.n0, s, lane, wave);
-      __asm__ volatile("" ::: "memory");
-    }
+    rb_load<C>(ring[(S + C::AHEAD) % C::NSTAGE], Z, wt, M, d, nt.m0, nt.n0,
+               kt + C::AHEAD - d / BK, lane, wave);
   }
-  constexpr int NVM = LOAD == kOwnStep ? C::VM_PER_STEP : LOAD == kNextTile ? 3 * C::VM_PER_STEP : 0;
+  constexpr int NVM = LOAD != kNoLoad ? C::VM_PER_STEP : 0;
   RbFrag<C::FN> b0, b1;
   RbFrag<C::FM> a1;
   rb_expand_b<C>(b0, w, hshift, 0);
   rb_read_a<C>(a1, cur, wm, lane, 1);
   rb_mfma<C, INIT>(acc, a, b0);
-  rb_interleave<C>(C::FM, NVM < 16 ? NVM : 16);
+  rb_interleave<C>(C::FM, NVM);
   rb_expand_b<C>(b1, w, hshift, 1);
   rb_read_a<C>(a, cur, wm, lane, 2);
   rb_mfma<C>(acc, a1, b1);
-  rb_interleave<C>(C::FM, NVM > 16 ? NVM - 16 : 0);
+  rb_interleave<C>(C::FM, 0);
   rb_expand_b<C>(b0, w, hshift, 2);
   rb_read_a<C>(a1, cur, wm, lane, 3);
   rb_mfma<C>(acc, a, b0);
@@ -627,6 +625,9 @@ __device__ __forceinline__ void rb_step(f32x16 (&acc)[C::FM][C::FN], RbFrag<C::F
 #pragma unroll
   for (int j = 0; j < C::FN; ++j) __asm__ volatile("" : "+v"(b1.v[j]));
   if constexpr (NEXT) {
+    if constexpr (WSTRICT != WAIT) {
+      if (strict) wait_vmcnt<WSTRICT>();
+    }
     wait_vmcnt<WAIT>();
     lds_barrier();
     const char* nxt = ring[(S + 1) % C::NSTAGE];
@@ -713,7 +714,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_rb_kernel(const uint16_t* Z,
   tl.m0 = (tile / tiles_n) * C::BM;
   tl.n0 = (tile % tiles_n) * C::BN;
 
-  const int nk = d / BK;  // multiple of 4
+  const int nk = d / BK;  // multiple of 4, at least 8
 #pragma unroll
   for (int s = 0; s < C::AHEAD; ++s) {
     rb_load<C>(ring[s], Z, wt, M, d, tl.m0, tl.n0, s, lane, wave);
@@ -721,12 +722,22 @@ __global__ __launch_bounds__(C::THREADS) void gemm_rb_kernel(const uint16_t* Z,
   }
   wait_vmcnt<(C::AHEAD - 1) * C::VM_PER_STEP>();
   lds_barrier();
+  uint4 w[C::FN];
+  RbFrag<C::FM> a;
+  rb_read_w<C>(w, ring[0], wn, lane);
+  rb_read_a<C>(a, ring[0], wm, lane, 0);
 
-  constexpr int W3 = 2 * C::VM_PER_STEP;  // steady state: steps kt+2, kt+3 in flight
+  // Steady state: steps kt+2, kt+3 in flight. A tile's first two steps also
+  // have the previous tile's epilogue stores (8 per 32 rows) in flight; the
+  // first tile has none, so it waits strictly there.
+  constexpr int W3 = 2 * C::VM_PER_STEP;
+  constexpr int WS = W3 + 8 * C::FM;
+  static_assert(WS <= 63, "vmcnt range");
+  bool first = true;
   for (;;) {
     const int next = tile + nw;
     const bool has_next = next < t1;
-    // Without a next tile the last step re-issues this tile's first steps (a
+    // Without a next tile the last steps re-issue this tile's first steps (a
     // few wasted loads, no branch around the accumulators); they are drained
     // before the workgroup exits.
     const int nx = has_next ? next : tile;
@@ -734,16 +745,12 @@ __global__ __launch_bounds__(C::THREADS) void gemm_rb_kernel(const uint16_t* Z,
     nt.m0 = (nx / tiles_n) * C::BM;
     nt.n0 = (nx % tiles_n) * C::BN;
 
-    uint4 w[C::FN];
-    RbFrag<C::FM> a;
-    rb_read_w<C>(w, ring[0], wn, lane);
-    rb_read_a<C>(a, ring[0], wm, lane, 0);
     f32x16 acc[C::FM][C::FN];
     // The first four steps (the first slice sets the accumulators).
-    rb_step<C, 0, kOwnStep, W3, true, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, 0, wm, wn, lane,
-                                            wave, hshift);
-    rb_step<C, 1, kOwnStep, W3, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, 1, wm, wn, lane, wave,
-                                      hshift);
+    rb_step<C, 0, kOwnStep, WS, true, true, W3>(acc, a, w, ring, Z, wt, M, d, tl, nt, 0, wm, wn,
+                                                lane, wave, hshift, first);
+    rb_step<C, 1, kOwnStep, WS, true, false, W3>(acc, a, w, ring, Z, wt, M, d, tl, nt, 1, wm, wn,
+                                                 lane, wave, hshift, first);
     rb_step<C, 2, kOwnStep, W3, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, 2, wm, wn, lane, wave,
                                       hshift);
     rb_step<C, 3, kOwnStep, W3, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, 3, wm, wn, lane, wave,
@@ -759,13 +766,14 @@ __global__ __launch_bounds__(C::THREADS) void gemm_rb_kernel(const uint16_t* Z,
       rb_step<C, 3, kOwnStep, W3, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, kt + 3, wm, wn,
                                         lane, wave, hshift);
     }
+    // Last four steps: the ring runs on into the next tile's steps 0..2.
     rb_step<C, 0, kOwnStep, W3, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, kt, wm, wn, lane,
                                       wave, hshift);
-    rb_step<C, 1, kNoLoad, C::VM_PER_STEP, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, kt + 1,
-                                                 wm, wn, lane, wave, hshift);
-    rb_step<C, 2, kNoLoad, 0, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, kt + 2, wm, wn, lane,
-                                    wave, hshift);
-    rb_step<C, 3, kNextTile, 0, false>(acc, a, w, ring, Z, wt, M, d, tl, nt, kt + 3, wm, wn, lane,
+    rb_step<C, 1, kNextTile, W3, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, kt + 1, wm, wn, lane,
+                                       wave, hshift);
+    rb_step<C, 2, kNextTile, W3, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, kt + 2, wm, wn, lane,
+                                       wave, hshift);
+    rb_step<C, 3, kNextTile, W3, true>(acc, a, w, ring, Z, wt, M, d, tl, nt, kt + 3, wm, wn, lane,
                                        wave, hshift);
 
     rb_store<C>(acc, stage_out + wave * C::OUT_BYTES, H, M, d, tl, wm, wn, lane, alpha);
@@ -775,10 +783,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_rb_kernel(const uint16_t* Z,
     }
     tile = next;
     tl = nt;
-    // Step 0 of the new tile was issued before the epilogue's stores; steps 1
-    // and 2 and the stores (8 per 32 rows) may still be in flight.
-    wait_vmcnt<2 * C::VM_PER_STEP + 8 * C::FM>();
-    lds_barrier();
+    first = false;
   }
 }
 
