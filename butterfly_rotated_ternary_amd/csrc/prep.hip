@@ -127,31 +127,42 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
   __syncthreads();
 
   // Histogram of every id (all blocks need the global offsets), 4 ids per
-  // load, several loads in flight per thread.
+  // load, a whole batch of loads in flight per thread (one round trip for
+  // M <= 4 * kBatch * kThreads). The ids of this block's chunk go to LDS
+  // from the same loads.
   bool bad = false;
   const int M4 = M / 4;
   const int4* ids4 = reinterpret_cast<const int4*>(p.ids);
-#pragma unroll 4
-  for (int i = tid; i < M4; i += kThreads) {
-    const int4 v = ids4[i];
-    const int r = 4 * i;
-    const int e0 = clamp_expert(v.x, N, bad), e1 = clamp_expert(v.y, N, bad);
-    const int e2 = clamp_expert(v.z, N, bad), e3 = clamp_expert(v.w, N, bad);
-    atomicAdd(&cnt[e0], 1); atomicAdd(&cnt[e1], 1);
-    atomicAdd(&cnt[e2], 1); atomicAdd(&cnt[e3], 1);
-    if (r < r0) {  // chunks start at multiples of 4
-      atomicAdd(&before[e0], 1); atomicAdd(&before[e1], 1);
-      atomicAdd(&before[e2], 1); atomicAdd(&before[e3], 1);
+  constexpr int kBatch = 16;
+  for (int i0 = 0; i0 < M4; i0 += kBatch * kThreads) {
+    int4 v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = i0 + tid + j * kThreads;
+      v[j] = i < M4 ? ids4[i] : make_int4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = i0 + tid + j * kThreads;
+      if (i >= M4) break;
+      const int r = 4 * i;
+      const int e0 = clamp_expert(v[j].x, N, bad), e1 = clamp_expert(v[j].y, N, bad);
+      const int e2 = clamp_expert(v[j].z, N, bad), e3 = clamp_expert(v[j].w, N, bad);
+      atomicAdd(&cnt[e0], 1); atomicAdd(&cnt[e1], 1);
+      atomicAdd(&cnt[e2], 1); atomicAdd(&cnt[e3], 1);
+      if (r < r0) {  // chunks start at multiples of 4
+        atomicAdd(&before[e0], 1); atomicAdd(&before[e1], 1);
+        atomicAdd(&before[e2], 1); atomicAdd(&before[e3], 1);
+      } else if (r < r1) {  // r1 - r0 is a multiple of 4 except at M
+        cid[r - r0] = e0; cid[r - r0 + 1] = e1; cid[r - r0 + 2] = e2; cid[r - r0 + 3] = e3;
+      }
     }
   }
-  for (int r = 4 * M4 + tid; r < M; r += kThreads) {
+  for (int r = 4 * M4 + tid; r < M; r += kThreads) {  // the last M % 4 ids
     const int e = clamp_expert(p.ids[r], N, bad);
     atomicAdd(&cnt[e], 1);
     if (r < r0) atomicAdd(&before[e], 1);
-  }
-  for (int r = r0 + tid; r < r1; r += kThreads) {
-    bool dummy = false;
-    cid[r - r0] = clamp_expert(p.ids[r], N, dummy);
+    else if (r < r1) cid[r - r0] = e;
   }
   __syncthreads();
 
