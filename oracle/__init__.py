@@ -1,4 +1,4 @@
-"""Plain fp64 CPU oracle for the ButterflyMoE expert-layer forward.
+"""Plain fp64 CPU oracle for the ButterflyMoE expert layer (forward and backward).
 
 TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import it. The HIP library never
@@ -6,3 +6,4 @@ calls into it, and it shares no code, table or constant generator with the
 HIP path.
 """
 from .bmoe_oracle import *  # noqa: F401,F403
+from .bmoe_backward import backward, loss as backward_loss  # noqa: F401
