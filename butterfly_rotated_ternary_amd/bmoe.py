@@ -63,6 +63,11 @@ def lib():
         L.bmoe_sync_status.restype = c_int
         L.bmoe_status_str.argtypes = [c_int]
         L.bmoe_status_str.restype = ctypes.c_char_p
+        L.bmoe_backward_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
+        L.bmoe_backward_workspace_bytes.restype = c_sz
+        L.bmoe_backward.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
+                                    c_f, vp, vp, vp, vp, vp, vp, vp, c_sz, vp]
+        L.bmoe_backward.restype = c_int
         _lib = L
     return _lib
 
@@ -142,6 +147,19 @@ def bmoe_status_str(code: int) -> str:
     return lib().bmoe_status_str(code).decode()
 
 
+def bmoe_backward_workspace_bytes(dt: int, T: int, d: int, n_experts: int, k: int) -> int:
+    return lib().bmoe_backward_workspace_bytes(dt, T, d, n_experts, k)
+
+
+def bmoe_backward(dt: int, T: int, d: int, n_experts: int, k: int, x, ids, gates, theta, phi,
+                  w_packed, alpha: float, dy, dx, dgates, dtheta, dphi, dw, ws,
+                  stream=None) -> int:
+    return lib().bmoe_backward(dt, T, d, n_experts, k, _ptr(x), _ptr(ids), _ptr(gates),
+                               _ptr(theta), _ptr(phi), _ptr(w_packed), float(alpha), _ptr(dy),
+                               _ptr(dx), _ptr(dgates), _ptr(dtheta), _ptr(dphi), _ptr(dw),
+                               _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+
+
 # ---- conveniences over the entry points (allocation + error checks) -------
 
 def dtype_code(t: torch.Tensor) -> int:
@@ -190,3 +208,29 @@ def forward(x: torch.Tensor, ids: torch.Tensor, gates: torch.Tensor, theta: torc
     _check(bmoe_forward(dt, T, d, N, k, x, ids, gates, theta, phi, w_packed, alpha, y, ws.buf,
                         route_out, stream), "bmoe_forward")
     return y
+
+
+def backward(x: torch.Tensor, ids: torch.Tensor, gates: torch.Tensor, theta: torch.Tensor,
+             phi: torch.Tensor, w_packed: torch.Tensor, alpha: float, dy: torch.Tensor, *,
+             want_dw: bool = True, stream=None) -> dict:
+    """Gradients of sum(dy * y) for the layer bmoe_forward computes: dict of
+    dx (dtype of x), dgates, dtheta, dphi and (want_dw) dw, all fp32 but dx."""
+    T, d = x.shape
+    k = ids.shape[1]
+    N = theta.shape[0]
+    dt = dtype_code(x)
+    n = bmoe_backward_workspace_bytes(dt, T, d, N, k)
+    if n == 0:
+        raise BmoeError(2, "bmoe_backward_workspace_bytes")
+    ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+    out = {
+        "dx": torch.empty_like(x),
+        "dgates": torch.empty(T, k, dtype=torch.float32, device=x.device),
+        "dtheta": torch.empty_like(theta),
+        "dphi": torch.empty_like(phi),
+        "dw": torch.empty(d, d, dtype=torch.float32, device=x.device) if want_dw else None,
+    }
+    _check(bmoe_backward(dt, T, d, N, k, x, ids, gates, theta, phi, w_packed, alpha, dy,
+                         out["dx"], out["dgates"], out["dtheta"], out["dphi"], out["dw"], ws,
+                         stream), "bmoe_backward")
+    return out

@@ -2,6 +2,9 @@
 // launch sequence of the forward. Every step of the forward runs in the HIP
 // kernels of this library; nothing here touches element data.
 #include <climits>
+#include <mutex>
+
+#include <rocblas/rocblas.h>
 
 #include "common.h"
 #include "kernels.h"
@@ -59,6 +62,66 @@ FwdLayout fwd_layout(bmoe_dtype dt, int T, int d, int N, int k) {
   if (gemm_tiled_w_block(dt, (int)M, d)) off = align_up(off + sizeof(uint32_t) * (size_t)d * (d / 16));
   l.total = off;
   return l;
+}
+
+struct BwdLayout {
+  size_t status, offsets, perm, inv, slot_e, cs_in, cs_out, z, h, dh, dx, wt, wpt, wtt, tiles,
+      tile_base, part_in, part_out, total;
+  int max_tiles, wt_block;
+};
+
+BwdLayout bwd_layout(bmoe_dtype dt, int T, int d, int N, int k) {
+  BwdLayout l{};
+  const size_t M = (size_t)T * k;
+  const size_t L = (size_t)log2i(d);
+  const size_t zel = dt == BMOE_BF16 ? 2 : 4;
+  const size_t wwords = (size_t)d * (d / 16);
+  l.wt_block = gemm_tiled_w_block(dt, (int)M, d);
+  l.max_tiles = bwd_max_tiles((int)M, N);
+  size_t off = 0;
+  l.status = off;    off = align_up(off + sizeof(int32_t));
+  l.offsets = off;   off = align_up(off + sizeof(int32_t) * (N + 1));
+  l.perm = off;      off = align_up(off + sizeof(int32_t) * M);
+  l.inv = off;       off = align_up(off + sizeof(int32_t) * M);
+  l.slot_e = off;    off = align_up(off + sizeof(int32_t) * M);
+  l.cs_in = off;     off = align_up(off + sizeof(float2) * N * L * (d / 2));
+  l.cs_out = off;    off = align_up(off + sizeof(float2) * N * L * (d / 2));
+  l.z = off;         off = align_up(off + zel * M * d);
+  l.h = off;         off = align_up(off + zel * M * d);  // H, then dZ
+  l.dh = off;        off = align_up(off + zel * M * d);
+  l.dx = off;        off = align_up(off + zel * M * d);  // per routed row
+  l.wt = off;        if (l.wt_block) off = align_up(off + sizeof(uint32_t) * wwords);
+  l.wpt = off;       off = align_up(off + sizeof(uint32_t) * wwords);
+  l.wtt = off;       if (l.wt_block) off = align_up(off + sizeof(uint32_t) * wwords);
+  l.tiles = off;     off = align_up(off + sizeof(int4) * l.max_tiles);
+  l.tile_base = off; off = align_up(off + sizeof(int32_t) * (N + 1));
+  l.part_in = off;   off = align_up(off + sizeof(float) * l.max_tiles * L * (d / 2));
+  l.part_out = off;  off = align_up(off + sizeof(float) * l.max_tiles * L * (d / 2));
+  l.total = off;
+  return l;
+}
+
+bool bwd_shape_ok(bmoe_dtype dt, int T, int d, int N, int k) {
+  return shape_ok(dt, T, d, N, k) && d <= 4096;
+}
+
+// dW = alpha * dH^T Z (row-major [d][d], fp32): the column-major product
+// Z_cm * dH_cm^T of the row-major [M][d] matrices viewed column-major.
+bmoe_status substrate_grad(bmoe_dtype dt, int M, int d, const void* dh, const void* z,
+                           float alpha, float* dw, hipStream_t s) {
+  static std::once_flag once;
+  static rocblas_handle handle = nullptr;
+  static rocblas_status created = rocblas_status_internal_error;
+  std::call_once(once, [] { created = rocblas_create_handle(&handle); });
+  if (created != rocblas_status_success) return BMOE_E_HIP;
+  if (rocblas_set_stream(handle, s) != rocblas_status_success) return BMOE_E_HIP;
+  const float beta = 0.f;
+  const rocblas_datatype at = dt == BMOE_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
+  const rocblas_status st = rocblas_gemm_ex(
+      handle, rocblas_operation_none, rocblas_operation_transpose, d, d, M, &alpha, z, at, d, dh,
+      at, d, &beta, dw, rocblas_datatype_f32_r, d, dw, rocblas_datatype_f32_r, d,
+      rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+  return st == rocblas_status_success ? BMOE_OK : BMOE_E_HIP;
 }
 
 }  // namespace
@@ -197,6 +260,80 @@ bmoe_status bmoe_sync_status(const void* ws, void* stream) {
   if (v == BMOE_E_EXPERT) return BMOE_E_EXPERT;
   if (v == BMOE_E_TERNARY) return BMOE_E_TERNARY;
   return v == BMOE_OK ? BMOE_OK : BMOE_E_HIP;
+}
+
+size_t bmoe_backward_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts, int k) {
+  if (!bwd_shape_ok(dt, T, d, n_experts, k)) return 0;
+  return bwd_layout(dt, T, d, n_experts, k).total;
+}
+
+bmoe_status bmoe_backward(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
+                          const int32_t* ids, const float* gates, const float* theta,
+                          const float* phi, const uint32_t* w_packed, float alpha,
+                          const void* dy, void* dx, float* dgates, float* dtheta, float* dphi,
+                          float* dw, void* ws, size_t ws_bytes, void* stream) {
+  if (dt != BMOE_F32 && dt != BMOE_BF16) return BMOE_E_DTYPE;
+  if (!bwd_shape_ok(dt, T, d, n_experts, k)) return BMOE_E_SHAPE;
+  if (T == 0) return BMOE_OK;
+  if (!x || !ids || !gates || !theta || !phi || !w_packed || !dy || !dx || !dgates || !dtheta ||
+      !dphi)
+    return BMOE_E_NULL;
+  const BwdLayout l = bwd_layout(dt, T, d, n_experts, k);
+  if (!ws || ws_bytes < l.total) return BMOE_E_WORKSPACE;
+  const void* ptrs[] = {x, ids, gates, theta, phi, w_packed, dy, dx, dgates, dtheta, dphi, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return BMOE_E_ALIGN;
+  if (dw && !aligned16(dw)) return BMOE_E_ALIGN;
+
+  char* base = static_cast<char*>(ws);
+  const int M = T * k;
+  RouteTables rt;
+  rt.offsets = reinterpret_cast<int32_t*>(base + l.offsets);
+  rt.perm = reinterpret_cast<int32_t*>(base + l.perm);
+  rt.inv = reinterpret_cast<int32_t*>(base + l.inv);
+  rt.slot_e = reinterpret_cast<int32_t*>(base + l.slot_e);
+  int32_t* status = reinterpret_cast<int32_t*>(base + l.status);
+  float2* cs_in = reinterpret_cast<float2*>(base + l.cs_in);
+  float2* cs_out = reinterpret_cast<float2*>(base + l.cs_out);
+  void* z = base + l.z;
+  void* h = base + l.h;
+  void* dh = base + l.dh;
+  void* dxr = base + l.dx;
+  uint32_t* wt = l.wt_block ? reinterpret_cast<uint32_t*>(base + l.wt) : nullptr;
+  uint32_t* wpt = reinterpret_cast<uint32_t*>(base + l.wpt);
+  uint32_t* wtt = l.wt_block ? reinterpret_cast<uint32_t*>(base + l.wtt) : nullptr;
+  int4* tiles = reinterpret_cast<int4*>(base + l.tiles);
+  int32_t* tile_base = reinterpret_cast<int32_t*>(base + l.tile_base);
+  float* part_in = reinterpret_cast<float*>(base + l.part_in);
+  float* part_out = reinterpret_cast<float*>(base + l.part_out);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  // Forward recompute: routing, cos/sin, Z = B^T x, H = alpha Z W^T.
+  if (launch_prep(ids, M, n_experts, theta, phi, d, rt, cs_in, cs_out, status, w_packed, nullptr,
+                  wt, l.wt_block, s) != hipSuccess)
+    return BMOE_E_HIP;
+  if (launch_pack_transpose(w_packed, d, wpt, wtt, l.wt_block, s) != hipSuccess) return BMOE_E_HIP;
+  if (launch_tiles(rt.offsets, n_experts, tiles, tile_base, l.max_tiles, s) != hipSuccess)
+    return BMOE_E_HIP;
+  if (launch_bfly_in(dt, M, d, k, x, rt, cs_in, z, s) != hipSuccess) return BMOE_E_HIP;
+  if (launch_gemm(dt, M, d, z, w_packed, wt, alpha, h, s) != hipSuccess) return BMOE_E_HIP;
+  // Output side: dH, dgates, dphi partials.
+  if (launch_bfly_bwd(false, dt, M, d, k, tiles, l.max_tiles, rt.perm, cs_out, gates, h, dy, dh,
+                      dgates, part_out, s) != hipSuccess)
+    return BMOE_E_HIP;
+  if (dw && substrate_grad(dt, M, d, dh, z, alpha, dw, s) != BMOE_OK) return BMOE_E_HIP;
+  // dZ = alpha dH W (the product with the transposed substrate), into H's space.
+  if (launch_gemm(dt, M, d, dh, wpt, wtt, alpha, h, s) != hipSuccess) return BMOE_E_HIP;
+  // Input side: dX per routed row, dtheta partials; dx_t = sum_j dX[t k + j].
+  if (launch_bfly_bwd(true, dt, M, d, k, tiles, l.max_tiles, rt.perm, cs_in, gates, x, h, dxr,
+                      nullptr, part_in, s) != hipSuccess)
+    return BMOE_E_HIP;
+  if (launch_combine(dt, T, d, k, dxr, dx, s) != hipSuccess) return BMOE_E_HIP;
+  if (launch_angle_reduce(part_out, tile_base, n_experts, d, dphi, s) != hipSuccess)
+    return BMOE_E_HIP;
+  if (launch_angle_reduce(part_in, tile_base, n_experts, d, dtheta, s) != hipSuccess)
+    return BMOE_E_HIP;
+  return BMOE_OK;
 }
 
 const char* bmoe_status_str(bmoe_status s) {

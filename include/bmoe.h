@@ -148,6 +148,36 @@ bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k
  * BMOE_E_HIP if the wait itself failed. */
 bmoe_status bmoe_sync_status(const void* ws, void* stream);
 
+/* Workspace bytes bmoe_backward needs for this shape (0 if the shape is not
+ * supported: as bmoe_forward, and d <= 4096). */
+size_t bmoe_backward_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts, int k);
+
+/*
+ * Backward of the layer computed by bmoe_forward, for training the rotations
+ * (gist.science summary, §2.4; the map itself §2.1/§2.3). Given dy = dL/dy
+ * (same dtype and layout as y), writes the gradients of L:
+ *   dx      [T][d], dtype dt       sum over j of B(theta_e) dz
+ *   dgates  fp32 [T][k]            <dy_t, B(phi_e) h> for routed row (t, j)
+ *   dtheta, dphi  fp32 [N][L][d/2] per-stage, per-pair angle gradients
+ *                                  (experts without rows get 0)
+ *   dw      fp32 [d][d] or NULL    alpha * sum over routed rows of dh z^T:
+ *                                  the substrate's gradient taken as a real
+ *                                  matrix (the straight-through reading),
+ *                                  row o = output, column c = input
+ * with z = B(theta_e)^T x_t, h = alpha W_base z, dh = B(phi_e)^T (g dy_t).
+ * The other arguments are bmoe_forward's (same routing and rounding points;
+ * the forward is recomputed inside). All outputs are overwritten; dtheta and
+ * dphi are summed per expert in a fixed order (run-to-run bit-identical). The
+ * dw product is a plain library GEMM (rocBLAS): the first call with dw != NULL
+ * creates a rocBLAS handle kept for the life of the process. ws: at least
+ * bmoe_backward_workspace_bytes(), 16-byte aligned. Errors as bmoe_forward.
+ */
+bmoe_status bmoe_backward(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
+                          const int32_t* ids, const float* gates, const float* theta,
+                          const float* phi, const uint32_t* w_packed, float alpha,
+                          const void* dy, void* dx, float* dgates, float* dtheta, float* dphi,
+                          float* dw, void* ws, size_t ws_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* bmoe_status_str(bmoe_status s);
 
