@@ -100,6 +100,39 @@ def kernel_work(name, act_bytes, T, d, N, k):
     raise KeyError(name)
 
 
+def backward_work(name, act_bytes, T, d, N, k):
+    """Algorithmic work of one launch of the backward (same conventions as
+    kernel_work). A butterfly-backward stage costs 22 flops per pair and row:
+    6 to recompute the forward rotation, 6 each to invert it on the values and
+    on the gradients, 4 for the angle gradient and its sum."""
+    M = T * k
+    L = d.bit_length() - 1
+    A = N * L * (d // 2)
+    tiles = -(-M // 64) + N                  # upper bound on expert-aligned row tiles
+    partial = tiles * L * (d // 2) * 4
+    routing = M * 4
+    if name in ("prep_kernel", "bfly_in_kernel", "gemm_kernel", "combine_kernel"):
+        return kernel_work(name, act_bytes, T, d, N, k)
+    if name == "pack_transpose_kernel":
+        return {"bytes": d * d // 4 * (3 if d % 512 == 0 else 2), "mfma_flops": 0,
+                "valu_flops": 0}
+    if name == "tiles_kernel":
+        return {"bytes": (N + 1) * 4 * 2 + tiles * 16, "mfma_flops": 0, "valu_flops": 0}
+    if name == "gemm_t_kernel":
+        return kernel_work("gemm_kernel", act_bytes, T, d, N, k)
+    if name == "substrate_grad_gemm":
+        return {"bytes": 2 * M * d * act_bytes + d * d * 4, "mfma_flops": 2 * M * d * d,
+                "valu_flops": 0}
+    if name in ("bfly_bwd_out_kernel", "bfly_bwd_in_kernel"):
+        b = (2 * M * d + T * d) * act_bytes + A * 8 + routing + partial
+        if name == "bfly_bwd_out_kernel":
+            b += 2 * M * 4                   # gates in, dgates out
+        return {"bytes": b, "mfma_flops": 0, "valu_flops": M * L * (d // 2) * 22}
+    if name.startswith("angle_reduce"):
+        return {"bytes": partial + A * 4, "mfma_flops": 0, "valu_flops": 0}
+    raise KeyError(name)
+
+
 def roofline(work, dur_s, mfma_peak_tflops):
     """The roofline of one kernel: the resource whose ideal time (work over
     published peak) is largest bounds it; achieved = that work / measured
@@ -275,8 +308,84 @@ class Problem:
             hip.destroy(evs)
         return per
 
+    def backward_setup(self):
+        import numpy as np
+        import torch
+        rng = np.random.default_rng(5)
+        dy = torch.from_numpy(rng.standard_normal((self.T, self.d)).astype(np.float32))
+        self.dy = dy.to(self.x.device).to(self.x.dtype)
+        b = self.bmoe
+        n = b.bmoe_backward_workspace_bytes(self.dt, self.T, self.d, self.N, self.k)
+        if n == 0:
+            raise ValueError(f"backward does not support {self.name}")
+        self.bws = torch.empty(n, dtype=torch.uint8, device=self.x.device)
+        self.g = {"dx": torch.empty_like(self.x),
+                  "dgates": torch.empty_like(self.gates),
+                  "dtheta": torch.empty_like(self.theta),
+                  "dphi": torch.empty_like(self.phi),
+                  "dw": torch.empty(self.d, self.d, dtype=torch.float32, device=self.x.device)}
+
+    def backward_args(self):
+        g = self.g
+        return (self.dt, self.T, self.d, self.N, self.k, self.x, self.ids, self.gates, self.theta,
+                self.phi, self.wp, self.alpha, self.dy, g["dx"], g["dgates"], g["dtheta"],
+                g["dphi"], g["dw"], self.bws, self.stream)
+
+    def time_backward(self, steps, warmup):
+        """Wall time per backward over `steps` back-to-back calls (ms), then
+        each launch's average time from its own events (ms)."""
+        import torch
+        b = self.bmoe
+        for _ in range(warmup):
+            rc = b.bmoe_backward(*self.backward_args())
+            if rc != 0:
+                raise b.BmoeError(rc, "bmoe_backward")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            b.bmoe_backward(*self.backward_args())
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        nk = b.bmoe_backward_kernel_count(self.dt, self.T, self.d, self.N, self.k)
+        names = [b.bmoe_backward_kernel_name(self.dt, self.T, self.d, self.N, self.k, i)
+                 for i in range(nk)]
+        hip = HipEvents()
+        evsets = [hip.create(2 * nk) for _ in range(steps)]
+        for evs in evsets:
+            rc = b.bmoe_backward_timed(*self.backward_args(), events=evs)
+            if rc != 0:
+                raise b.BmoeError(rc, "bmoe_backward_timed")
+        torch.cuda.synchronize()
+        per = {n: 0.0 for n in names}
+        for evs in evsets:
+            for i, n in enumerate(names):
+                per[n] += hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) / steps
+        for evs in evsets:
+            hip.destroy(evs)
+        return ms, per
+
     def mfma_peak(self):
         return PEAK_BF16_TFLOPS if self.dt == self.bmoe.BMOE_BF16 else PEAK_FP32_MFMA_TFLOPS
+
+
+def backward_section(P, steps):
+    """The backward (all gradients, forward recomputed inside) on the same
+    workload: tokens/s and the roofline of its longest launch."""
+    P.backward_setup()
+    ms, per = P.time_backward(steps, max(3, steps // 10))
+    T, d, N, k = P.T, P.d, P.N, P.k
+    dom = max(per, key=per.get)
+    roof = roofline(backward_work(dom, P.act_bytes, T, d, N, k), per[dom] * 1e-3, P.mfma_peak())
+    roof["traffic"] = stored_traffic(dom, P.name)
+    roof["kernel"] = dom
+    kern = {}
+    for n, v in per.items():
+        r = roofline(backward_work(n, P.act_bytes, T, d, N, k), v * 1e-3, P.mfma_peak())
+        kern[n] = {"us": v * 1e3, "bound": r["bound"], "frac": r["frac"]}
+    log(f"[bench] backward {P.name}: {ms * 1e3:.1f} us/step; "
+        + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in per.items()))
+    return {"workload": P.name, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+            "steps": steps, "roofline": roof, "kernels": kern}
 
 
 def copy_calibration(mib, reps):
@@ -302,6 +411,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--gemm-steps", type=int, default=20,
                     help="forwards of the d=4096 workload timed for its GEMM figure (0: skip)")
+    ap.add_argument("--bwd-steps", type=int, default=100,
+                    help="backward passes timed on the same workload (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain copies of MIB MiB (counter calibration) and exit")
     ap.add_argument("--print-source-digest", action="store_true")
@@ -362,6 +473,8 @@ def main():
                      / (PEAK_HBM_GBS * 1e9)},
         "kernels": others,
     }
+    if args.bwd_steps > 0:
+        out["backward"] = backward_section(P, args.bwd_steps)
     del P
 
     if args.gemm_steps > 0 and name != GEMM_WORKLOAD:

@@ -68,6 +68,12 @@ def lib():
         L.bmoe_backward.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
                                     c_f, vp, vp, vp, vp, vp, vp, vp, c_sz, vp]
         L.bmoe_backward.restype = c_int
+        L.bmoe_backward_timed.argtypes = L.bmoe_backward.argtypes + [vp]
+        L.bmoe_backward_timed.restype = c_int
+        L.bmoe_backward_kernel_count.argtypes = [c_int, c_int, c_int, c_int, c_int]
+        L.bmoe_backward_kernel_count.restype = c_int
+        L.bmoe_backward_kernel_name.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int]
+        L.bmoe_backward_kernel_name.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
@@ -158,6 +164,28 @@ def bmoe_backward(dt: int, T: int, d: int, n_experts: int, k: int, x, ids, gates
                                _ptr(theta), _ptr(phi), _ptr(w_packed), float(alpha), _ptr(dy),
                                _ptr(dx), _ptr(dgates), _ptr(dtheta), _ptr(dphi), _ptr(dw),
                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+
+
+def bmoe_backward_timed(dt: int, T: int, d: int, n_experts: int, k: int, x, ids, gates, theta,
+                        phi, w_packed, alpha: float, dy, dx, dgates, dtheta, dphi, dw, ws,
+                        stream=None, events=None) -> int:
+    """``events``: raw hipEvent_t handles (ints), two per launch (start, stop)."""
+    ev = None
+    if events is not None:
+        ev = (ctypes.c_void_p * len(events))(*events)
+    return lib().bmoe_backward_timed(dt, T, d, n_experts, k, _ptr(x), _ptr(ids), _ptr(gates),
+                                     _ptr(theta), _ptr(phi), _ptr(w_packed), float(alpha),
+                                     _ptr(dy), _ptr(dx), _ptr(dgates), _ptr(dtheta), _ptr(dphi),
+                                     _ptr(dw), _ptr(ws), ws.numel() * ws.element_size(),
+                                     _stream(stream), ev)
+
+
+def bmoe_backward_kernel_count(dt: int, T: int, d: int, n_experts: int, k: int) -> int:
+    return lib().bmoe_backward_kernel_count(dt, T, d, n_experts, k)
+
+
+def bmoe_backward_kernel_name(dt: int, T: int, d: int, n_experts: int, k: int, i: int) -> str:
+    return lib().bmoe_backward_kernel_name(dt, T, d, n_experts, k, i).decode()
 
 
 # ---- conveniences over the entry points (allocation + error checks) -------

@@ -77,7 +77,7 @@ BwdLayout bwd_layout(bmoe_dtype dt, int T, int d, int N, int k) {
   const size_t zel = dt == BMOE_BF16 ? 2 : 4;
   const size_t wwords = (size_t)d * (d / 16);
   l.wt_block = gemm_tiled_w_block(dt, (int)M, d);
-  l.max_tiles = bwd_max_tiles((int)M, N);
+  l.max_tiles = bwd_max_tiles((int)M, N, d);
   size_t off = 0;
   l.status = off;    off = align_up(off + sizeof(int32_t));
   l.offsets = off;   off = align_up(off + sizeof(int32_t) * (N + 1));
@@ -267,11 +267,12 @@ size_t bmoe_backward_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts,
   return bwd_layout(dt, T, d, n_experts, k).total;
 }
 
-bmoe_status bmoe_backward(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
-                          const int32_t* ids, const float* gates, const float* theta,
-                          const float* phi, const uint32_t* w_packed, float alpha,
-                          const void* dy, void* dx, float* dgates, float* dtheta, float* dphi,
-                          float* dw, void* ws, size_t ws_bytes, void* stream) {
+bmoe_status bmoe_backward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k,
+                                const void* x, const int32_t* ids, const float* gates,
+                                const float* theta, const float* phi, const uint32_t* w_packed,
+                                float alpha, const void* dy, void* dx, float* dgates,
+                                float* dtheta, float* dphi, float* dw, void* ws, size_t ws_bytes,
+                                void* stream, void* const* events) {
   if (dt != BMOE_F32 && dt != BMOE_BF16) return BMOE_E_DTYPE;
   if (!bwd_shape_ok(dt, T, d, n_experts, k)) return BMOE_E_SHAPE;
   if (T == 0) return BMOE_OK;
@@ -307,33 +308,77 @@ bmoe_status bmoe_backward(bmoe_dtype dt, int T, int d, int n_experts, int k, con
   float* part_in = reinterpret_cast<float*>(base + l.part_in);
   float* part_out = reinterpret_cast<float*>(base + l.part_out);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  int ki = 0;
+  // Timing events of the next launch (none when events is NULL).
+  auto timing = [&]() -> KernelTiming {
+    KernelTiming t;
+    if (events) {
+      t.start = static_cast<hipEvent_t>(events[2 * ki]);
+      t.stop = static_cast<hipEvent_t>(events[2 * ki + 1]);
+      ++ki;
+    }
+    return t;
+  };
 
   // Forward recompute: routing, cos/sin, Z = B^T x, H = alpha Z W^T.
   if (launch_prep(ids, M, n_experts, theta, phi, d, rt, cs_in, cs_out, status, w_packed, nullptr,
-                  wt, l.wt_block, s) != hipSuccess)
+                  wt, l.wt_block, s, timing()) != hipSuccess)
     return BMOE_E_HIP;
-  if (launch_pack_transpose(w_packed, d, wpt, wtt, l.wt_block, s) != hipSuccess) return BMOE_E_HIP;
-  if (launch_tiles(rt.offsets, n_experts, tiles, tile_base, l.max_tiles, s) != hipSuccess)
+  if (launch_pack_transpose(w_packed, d, wpt, wtt, l.wt_block, s, timing()) != hipSuccess) return BMOE_E_HIP;
+  if (launch_tiles(rt.offsets, n_experts, d, tiles, tile_base, l.max_tiles, s, timing()) != hipSuccess)
     return BMOE_E_HIP;
-  if (launch_bfly_in(dt, M, d, k, x, rt, cs_in, z, s) != hipSuccess) return BMOE_E_HIP;
-  if (launch_gemm(dt, M, d, z, w_packed, wt, alpha, h, s) != hipSuccess) return BMOE_E_HIP;
+  if (launch_bfly_in(dt, M, d, k, x, rt, cs_in, z, s, timing()) != hipSuccess) return BMOE_E_HIP;
+  if (launch_gemm(dt, M, d, z, w_packed, wt, alpha, h, s, timing()) != hipSuccess) return BMOE_E_HIP;
   // Output side: dH, dgates, dphi partials.
   if (launch_bfly_bwd(false, dt, M, d, k, tiles, l.max_tiles, rt.perm, cs_out, gates, h, dy, dh,
-                      dgates, part_out, s) != hipSuccess)
+                      dgates, part_out, s, timing()) != hipSuccess)
     return BMOE_E_HIP;
-  if (dw && substrate_grad(dt, M, d, dh, z, alpha, dw, s) != BMOE_OK) return BMOE_E_HIP;
+  {
+    const KernelTiming t = timing();
+    if (t.start && hipEventRecord(t.start, s) != hipSuccess) return BMOE_E_HIP;
+    if (dw && substrate_grad(dt, M, d, dh, z, alpha, dw, s) != BMOE_OK) return BMOE_E_HIP;
+    if (t.stop && hipEventRecord(t.stop, s) != hipSuccess) return BMOE_E_HIP;
+  }
   // dZ = alpha dH W (the product with the transposed substrate), into H's space.
-  if (launch_gemm(dt, M, d, dh, wpt, wtt, alpha, h, s) != hipSuccess) return BMOE_E_HIP;
+  if (launch_gemm(dt, M, d, dh, wpt, wtt, alpha, h, s, timing()) != hipSuccess) return BMOE_E_HIP;
   // Input side: dX per routed row, dtheta partials; dx_t = sum_j dX[t k + j].
   if (launch_bfly_bwd(true, dt, M, d, k, tiles, l.max_tiles, rt.perm, cs_in, gates, x, h, dxr,
-                      nullptr, part_in, s) != hipSuccess)
+                      nullptr, part_in, s, timing()) != hipSuccess)
     return BMOE_E_HIP;
-  if (launch_combine(dt, T, d, k, dxr, dx, s) != hipSuccess) return BMOE_E_HIP;
-  if (launch_angle_reduce(part_out, tile_base, n_experts, d, dphi, s) != hipSuccess)
+  if (launch_combine(dt, T, d, k, dxr, dx, s, timing()) != hipSuccess) return BMOE_E_HIP;
+  if (launch_angle_reduce(part_out, tile_base, n_experts, d, dphi, s, timing()) != hipSuccess)
     return BMOE_E_HIP;
-  if (launch_angle_reduce(part_in, tile_base, n_experts, d, dtheta, s) != hipSuccess)
+  if (launch_angle_reduce(part_in, tile_base, n_experts, d, dtheta, s, timing()) != hipSuccess)
     return BMOE_E_HIP;
   return BMOE_OK;
+}
+
+bmoe_status bmoe_backward(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
+                          const int32_t* ids, const float* gates, const float* theta,
+                          const float* phi, const uint32_t* w_packed, float alpha,
+                          const void* dy, void* dx, float* dgates, float* dtheta, float* dphi,
+                          float* dw, void* ws, size_t ws_bytes, void* stream) {
+  return bmoe_backward_timed(dt, T, d, n_experts, k, x, ids, gates, theta, phi, w_packed, alpha,
+                             dy, dx, dgates, dtheta, dphi, dw, ws, ws_bytes, stream, nullptr);
+}
+
+namespace {
+const char* const kBackwardNames[] = {
+    "prep_kernel",      "pack_transpose_kernel", "tiles_kernel",         "bfly_in_kernel",
+    "gemm_kernel",      "bfly_bwd_out_kernel",   "substrate_grad_gemm",  "gemm_t_kernel",
+    "bfly_bwd_in_kernel", "combine_kernel",      "angle_reduce_out_kernel",
+    "angle_reduce_in_kernel"};
+constexpr int kBackwardLaunches = sizeof(kBackwardNames) / sizeof(kBackwardNames[0]);
+}  // namespace
+
+int bmoe_backward_kernel_count(bmoe_dtype dt, int T, int d, int n_experts, int k) {
+  if (!bwd_shape_ok(dt, T, d, n_experts, k) || T == 0) return 0;
+  return kBackwardLaunches;
+}
+
+const char* bmoe_backward_kernel_name(bmoe_dtype dt, int T, int d, int n_experts, int k, int i) {
+  if (i < 0 || i >= bmoe_backward_kernel_count(dt, T, d, n_experts, k)) return "";
+  return kBackwardNames[i];
 }
 
 const char* bmoe_status_str(bmoe_status s) {

@@ -10,35 +10,29 @@
 // A stage maps a pair (x_i, x_j) to (c x_i - s x_j, s x_i + c x_j). Written
 // with its OUTPUT v and the gradient G of the output, the angle gradient is
 // G_j v_i - G_i v_j and the input gradient and input are S^T G and S^T v.
-// So the kernels below first run a row forward through its butterfly (in
-// LDS, fp32), then walk the stages backward from the outputs: no per-stage
-// activations are stored. On the input side each stage runs with angle -a, so
-// its angle gradient changes sign and its inverse is S(a).
+// So the kernels below hold a few rows in LDS (fp32), run them forward
+// through their butterfly, then walk the stages backward from the outputs: no
+// per-stage activations are stored. On the input side each stage runs with
+// angle -a, so its angle gradient changes sign and its inverse is S(a).
 //
 // Angle gradients are summed per expert without atomics: rows are cut into
-// tiles of at most kTileRows sorted rows of one expert, each tile keeps its
-// sums in registers and writes one partial, and a second kernel adds an
-// expert's partials in tile order (bit-reproducible).
+// tiles of a few sorted rows of one expert, each tile keeps its sums in
+// registers and writes one partial, and a second kernel adds an expert's
+// partials in tile order (bit-reproducible).
 #include "common.h"
 #include "kernels.h"
 
 namespace bmoe {
 namespace {
 
-constexpr int kTileRows = 64;
-
 __device__ __forceinline__ int pad(int i) { return i + (i >> 3); }
 
-__device__ __forceinline__ float ld_act(const uint16_t* p) { return bf16_lo(*p); }
-__device__ __forceinline__ float ld_act(const float* p) { return *p; }
-__device__ __forceinline__ void st_act(uint16_t* p, float v) { *p = (uint16_t)f32_to_bf16_bits(v); }
-__device__ __forceinline__ void st_act(float* p, float v) { *p = v; }
-
 // ---- expert-aligned row tiles ------------------------------------------------
-// tiles[i] = (expert, first sorted row, end row, 0); tile_base[e] = first tile
+// tiles[i] = (expert, first sorted row, end row, 0), at most tr rows each; tile_base[e] = first tile
 // of expert e, tile_base[N] = number of tiles. One workgroup.
-__global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* offsets, int N, int4* tiles,
-                                                     int32_t* tile_base, int max_tiles) {
+__global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* offsets, int N, int tr,
+                                                     int4* tiles, int32_t* tile_base,
+                                                     int max_tiles) {
   __shared__ int scan[1024];
   __shared__ int carry;
   const int tid = threadIdx.x;
@@ -47,7 +41,7 @@ __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* offsets, int
   for (int e0 = 0; e0 < N; e0 += 1024) {
     const int e = e0 + tid;
     const int cnt = e < N ? offsets[e + 1] - offsets[e] : 0;
-    const int nt = (cnt + kTileRows - 1) / kTileRows;
+    const int nt = (cnt + tr - 1) / tr;
     scan[tid] = nt;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
@@ -61,7 +55,7 @@ __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* offsets, int
       tile_base[e] = base;
       const int q0 = offsets[e];
       for (int i = 0; i < nt; ++i)
-        tiles[base + i] = make_int4(e, q0 + i * kTileRows, min(q0 + (i + 1) * kTileRows, q0 + cnt), 0);
+        tiles[base + i] = make_int4(e, q0 + i * tr, min(q0 + (i + 1) * tr, q0 + cnt), 0);
     }
     __syncthreads();
     if (tid == 1023) carry += scan[1023];
@@ -101,19 +95,32 @@ __global__ __launch_bounds__(256) void pack_transpose_kernel(const uint32_t* wp,
 }
 
 // ---- butterfly backward --------------------------------------------------------
+// Stages are grouped three at a time as in the forward kernels: group g holds
+// stages 3g .. min(3g + 3, L) - 1. A thread owns register blocks of a group
+// (the 2^G elements whose indices differ only in the group's stage bits) for
+// a fixed set of rows of the tile, so the angle gradients of its blocks'
+// pairs sum in registers over those rows, and each element crosses LDS once
+// per group and pass.
+constexpr int bwd_rows(int d) { return d >= 4096 ? 2 : (8192 / d > 32 ? 32 : 8192 / d); }
+constexpr int bwd_tile_rows(int d) { return d >= 1024 ? 64 : bwd_rows(d); }
+
 template <int D>
 struct BwdCfg {
   static_assert(D >= 16 && D <= 4096, "backward sizes");
   static constexpr int L = D == 16 ? 4 : D == 32 ? 5 : D == 64 ? 6 : D == 128 ? 7 : D == 256 ? 8
                          : D == 512 ? 9 : D == 1024 ? 10 : D == 2048 ? 11 : 12;
-  // Each thread keeps cos/sin and gradient sums for L * P pairs in registers.
+  static constexpr int NG = (L + 2) / 3;
   static constexpr int NTHR = D >= 4096 ? 512 : 256;
-  static constexpr int NPAIR = D / 2;
-  static constexpr int P = NPAIR >= NTHR ? NPAIR / NTHR : 1;   // pairs per thread per stage
-  static constexpr int RB = NPAIR >= NTHR ? 1 : NTHR / NPAIR;  // rows per batch
-  static constexpr int TPR = NTHR / RB;                        // threads per row
-  static constexpr int EPT = D / TPR;                          // elements per thread
-  static constexpr int PD = D + D / 8;
+  static constexpr int R = bwd_rows(D);        // rows held in LDS at a time
+  static constexpr int PD = D + D / 8;         // padded LDS row
+  static constexpr int TPR = NTHR / R;         // threads per row (gate dot products)
+  static constexpr int gsize(int g) { return L - 3 * g < 3 ? L - 3 * g : 3; }
+  static constexpr int nblk(int g) { return D >> gsize(g); }
+  // threads sharing a block (each takes every tpb-th row) and blocks per thread
+  static constexpr int tpb(int g) { return nblk(g) >= NTHR ? 1 : NTHR / nblk(g); }
+  static constexpr int slots(int g) { return nblk(g) >= NTHR ? nblk(g) / NTHR : 1; }
+  static constexpr int npairs(int g) { return gsize(g) << (gsize(g) - 1); }
+  static constexpr int VSZ = R * PD > 12 * NTHR ? R * PD : 12 * NTHR;
 };
 
 struct BwdParams {
@@ -129,207 +136,186 @@ struct BwdParams {
   float* partial;       // [tiles][L][D/2]
 };
 
-// Row batch load: zeros past the tile end.
-template <int D, bool IN_SIDE, typename XT, typename AT>
-__device__ __forceinline__ void bwd_load(const BwdParams& p, float* v, float* g, int q, bool valid,
-                                         int t, int ec) {
+// Element offsets of pair u of stage t within a block of 2^G elements.
+__device__ __forceinline__ int pair_lo(int t, int u) {
+  return ((u >> t) << (t + 1)) | (u & ((1 << t) - 1));
+}
+
+template <int D, int G>
+__device__ __forceinline__ void block_of(int g, int sl, int tid, int& base, int& ph) {
   using C = BwdCfg<D>;
+  const int bstride = C::NTHR / C::tpb(g);
+  ph = tid / bstride;
+  base = block_base(tid % bstride + sl * bstride, 3 * g, G);
+}
+
+// Forward rotation of one register block through its stages (IN_SIDE: stages
+// descending, each by -angle).
+template <int G, bool IN_SIDE>
+__device__ __forceinline__ void fwd_block(float (&v)[8], const float2 (&c)[12]) {
 #pragma unroll
-  for (int m = 0; m < C::EPT; ++m) {
-    const int c = ec + m * C::TPR;
-    float vv = 0.f, gg = 0.f;
-    if (valid) {
+  for (int tt = 0; tt < G; ++tt) {
+    const int t = IN_SIDE ? G - 1 - tt : tt;
+#pragma unroll
+    for (int u = 0; u < (1 << (G - 1)); ++u) {
+      const int m = pair_lo(t, u), n = m + (1 << t);
+      const float a = v[m], b = v[n], cc = c[t * 4 + u].x, ss = c[t * 4 + u].y;
       if (IN_SIDE) {
-        vv = ld_act(static_cast<const XT*>(p.src) + (size_t)t * D + c);
-        gg = ld_act(static_cast<const AT*>(p.grad) + (size_t)q * D + c);
+        v[m] = cc * a + ss * b;
+        v[n] = cc * b - ss * a;
       } else {
-        vv = ld_act(static_cast<const AT*>(p.src) + (size_t)q * D + c);
-        gg = ld_act(static_cast<const XT*>(p.grad) + (size_t)t * D + c);
+        v[m] = cc * a - ss * b;
+        v[n] = ss * a + cc * b;
       }
     }
-    v[pad(c)] = vv;
-    g[pad(c)] = gg;
   }
 }
 
-// Output side, after the forward pass: dg_r = <dy_t, u>, then G = g_r * dy_t.
-template <int D>
-__device__ __forceinline__ void bwd_gates(const BwdParams& p, float* v, float* g, float* red,
-                                          bool valid, int r, int tid, int ec) {
-  using C = BwdCfg<D>;
-  float dot = 0.f;
+// Backward through one register block: v holds the block's stage outputs and
+// gr their gradients; walks the stages in reverse, adding each pair's angle
+// gradient to acc and leaving the block's inputs and their gradients.
+template <int G, bool IN_SIDE>
+__device__ __forceinline__ void bwd_block(float (&v)[8], float (&gr)[8], const float2 (&c)[12],
+                                          float (&acc)[12]) {
 #pragma unroll
-  for (int m = 0; m < C::EPT; ++m) {
-    const int c = ec + m * C::TPR;
-    dot += g[pad(c)] * v[pad(c)];
-  }
-  if (C::TPR >= 64) {
-    // a row spans TPR / 64 whole waves: wave sums, then the row's first thread
-    constexpr int WPR = C::TPR / 64;
+  for (int tt = 0; tt < G; ++tt) {
+    const int t = IN_SIDE ? tt : G - 1 - tt;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
-    if (tid % 64 == 0) red[tid / 64] = dot;
-    __syncthreads();
-    if (ec == 0 && valid) {
-      float s = 0.f;
-      for (int w = 0; w < WPR; ++w) s += red[(tid / 64) + w];
-      p.dgates[r] = s;
+    for (int u = 0; u < (1 << (G - 1)); ++u) {
+      const int m = pair_lo(t, u), n = m + (1 << t);
+      const float cc = c[t * 4 + u].x, ss = IN_SIDE ? -c[t * 4 + u].y : c[t * 4 + u].y;
+      const float vm = v[m], vn = v[n], gm = gr[m], gn = gr[n];
+      const float da = gn * vm - gm * vn;   // d L / d (applied angle)
+      acc[t * 4 + u] += IN_SIDE ? -da : da;
+      v[m] = cc * vm + ss * vn;
+      v[n] = cc * vn - ss * vm;
+      gr[m] = cc * gm + ss * gn;
+      gr[n] = cc * gn - ss * gm;
     }
-  } else {
-#pragma unroll
-    for (int off = C::TPR / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, C::TPR);
-    if (ec == 0 && valid) p.dgates[r] = dot;
-  }
-  const float gate = valid ? p.gates[r] : 0.f;
-#pragma unroll
-  for (int m = 0; m < C::EPT; ++m) {
-    const int c = ec + m * C::TPR;
-    g[pad(c)] *= gate;
   }
 }
 
-template <int D, bool IN_SIDE, typename AT>
-__device__ __forceinline__ void bwd_store(const BwdParams& p, const float* g, int q, int r,
-                                          bool valid, int ec) {
+template <int D, int g, bool IN_SIDE, bool BWD>
+__device__ __forceinline__ void run_group(float* V, float* Gs, int nr, int tid,
+                                          const float2 (&cf)[BwdCfg<D>::NG][2][12],
+                                          float (&acc)[BwdCfg<D>::NG][2][12], bool keep_v) {
   using C = BwdCfg<D>;
-  if (!valid) return;
-  AT* dst = static_cast<AT*>(p.dst) + (size_t)(IN_SIDE ? r : q) * D;
+  constexpr int G = C::gsize(g), TPB = C::tpb(g);
 #pragma unroll
-  for (int m = 0; m < C::EPT; ++m) {
-    const int c = ec + m * C::TPR;
-    st_act(dst + c, g[pad(c)]);
+  for (int sl = 0; sl < C::slots(g); ++sl) {
+    int base, ph;
+    block_of<D, G>(g, sl, tid, base, ph);
+    int off[8];
+#pragma unroll
+    for (int m = 0; m < (1 << G); ++m) off[m] = pad(base + (m << (3 * g)));
+    for (int i = ph; i < nr; i += TPB) {
+      float* vr = V + i * C::PD;
+      float v[8];
+#pragma unroll
+      for (int m = 0; m < (1 << G); ++m) v[m] = vr[off[m]];
+      if (BWD) {
+        float* gp = Gs + i * C::PD;
+        float gr[8];
+#pragma unroll
+        for (int m = 0; m < (1 << G); ++m) gr[m] = gp[off[m]];
+        bwd_block<G, IN_SIDE>(v, gr, cf[g][sl], acc[g][sl]);
+#pragma unroll
+        for (int m = 0; m < (1 << G); ++m) gp[off[m]] = gr[m];
+        if (keep_v) {
+#pragma unroll
+          for (int m = 0; m < (1 << G); ++m) vr[off[m]] = v[m];
+        }
+      } else {
+        fwd_block<G, IN_SIDE>(v, cf[g][sl]);
+#pragma unroll
+        for (int m = 0; m < (1 << G); ++m) vr[off[m]] = v[m];
+      }
+    }
   }
 }
 
-// Forward rotation of one pair (angle as applied: sn already signed).
-__device__ __forceinline__ void rot_fwd(float* vr, int i, int j, float cs, float sn) {
-  const float xi = vr[pad(i)], xj = vr[pad(j)];
-  vr[pad(i)] = cs * xi - sn * xj;
-  vr[pad(j)] = sn * xi + cs * xj;
+// Groups in forward order (out side ascending, in side descending), or in
+// backward order; a barrier after each group.
+template <int D, bool IN_SIDE, bool BWD, int I = 0>
+__device__ __forceinline__ void run_groups(float* V, float* Gs, int nr, int tid,
+                                           const float2 (&cf)[BwdCfg<D>::NG][2][12],
+                                           float (&acc)[BwdCfg<D>::NG][2][12]) {
+  using C = BwdCfg<D>;
+  if constexpr (I < C::NG) {
+    constexpr bool ascending = IN_SIDE == BWD;
+    constexpr int g = ascending ? I : C::NG - 1 - I;
+    // the values are dead after the last group of the backward walk
+    run_group<D, g, IN_SIDE, BWD>(V, Gs, nr, tid, cf, acc, !(BWD && I == C::NG - 1));
+    __syncthreads();
+    run_groups<D, IN_SIDE, BWD, I + 1>(V, Gs, nr, tid, cf, acc);
+  }
 }
 
-// Backward step of one pair from the stage outputs: returns dL/d(applied angle).
-__device__ __forceinline__ float rot_bwd(float* vr, float* gr, int i, int j, float cs, float sn) {
-  const float vi = vr[pad(i)], vj = vr[pad(j)], gi = gr[pad(i)], gj = gr[pad(j)];
-  vr[pad(i)] = cs * vi + sn * vj;
-  vr[pad(j)] = -sn * vi + cs * vj;
-  gr[pad(i)] = cs * gi + sn * gj;
-  gr[pad(j)] = -sn * gi + cs * gj;
-  return gj * vi - gi * vj;
+// This tile's angle-gradient partial for group g: blocks shared by several
+// threads (each over its own rows) are summed in thread order through LDS.
+template <int D, int g>
+__device__ __forceinline__ void write_partial(float* red, float* out, int tid,
+                                              const float (&acc)[BwdCfg<D>::NG][2][12]) {
+  using C = BwdCfg<D>;
+  constexpr int G = C::gsize(g), TPB = C::tpb(g), NP = C::npairs(g);
+  constexpr int bstride = C::NTHR / TPB;
+#pragma unroll
+  for (int sl = 0; sl < C::slots(g); ++sl) {
+    int base, ph;
+    block_of<D, G>(g, sl, tid, base, ph);
+    float sum[12];
+    if (TPB > 1) {
+#pragma unroll
+      for (int t = 0; t < G; ++t)
+#pragma unroll
+        for (int u = 0; u < (1 << (G - 1)); ++u) red[(t * 4 + u) * C::NTHR + tid] = acc[g][sl][t * 4 + u];
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < G; ++t)
+#pragma unroll
+        for (int u = 0; u < (1 << (G - 1)); ++u) {
+          float a = 0.f;
+#pragma unroll 2
+          for (int q = 0; q < TPB; ++q) a += red[(t * 4 + u) * C::NTHR + q * bstride + tid % bstride];
+          sum[t * 4 + u] = a;
+        }
+      __syncthreads();
+    } else {
+#pragma unroll
+      for (int j = 0; j < 12; ++j) sum[j] = acc[g][sl][j];
+    }
+    if (ph == 0) {
+#pragma unroll
+      for (int t = 0; t < G; ++t) {
+        const int s = 3 * g + t;
+#pragma unroll
+        for (int u = 0; u < (1 << (G - 1)); ++u)
+          out[s * (D / 2) + pair_index(base + (pair_lo(t, u) << (3 * g)), s)] = sum[t * 4 + u];
+      }
+    }
+  }
+  (void)NP;
 }
 
-__device__ __forceinline__ void pair_ij(int pp, int s, int& i, int& j) {
-  i = ((pp >> s) << (s + 1)) | (pp & ((1 << s) - 1));
-  j = i + (1 << s);
+template <int D, int I = 0>
+__device__ __forceinline__ void write_partials(float* red, float* out, int tid,
+                                               const float (&acc)[BwdCfg<D>::NG][2][12]) {
+  if constexpr (I < BwdCfg<D>::NG) {
+    write_partial<D, I>(red, out, tid, acc);
+    write_partials<D, I + 1>(red, out, tid, acc);
+  }
 }
 
 // IN_SIDE = false: from H and dy to dH, dgates and dphi partials.
 // IN_SIDE = true:  from x and dZ to dX (routed order) and dtheta partials.
-// XT: element type of x / dy; AT: element type of H, dH, dZ, dX.
-// d <= 512: several rows per batch, cos/sin and gradient sums in registers.
-template <int D, bool IN_SIDE, typename XT, typename AT>
+// T: element type of every activation (x, dy, H, dH, dZ, dX).
+template <int D, bool IN_SIDE, typename T>
 __global__ __launch_bounds__(BwdCfg<D>::NTHR) void bfly_bwd_kernel(BwdParams p) {
   using C = BwdCfg<D>;
-  constexpr int L = C::L, P = C::P, RB = C::RB, TPR = C::TPR, PD = C::PD;
-  static_assert(D <= 512, "small-d variant");
-  __shared__ float V[RB * PD];
-  __shared__ float G[RB * PD];
-  __shared__ float red[C::NTHR / 64];
-
-  const int4 tile = p.tiles[blockIdx.x];
-  const int e = tile.x;
-  if (e < 0) return;  // past the last tile (whole workgroup)
-  const int q0 = tile.y, q1 = tile.z;
-  const int tid = threadIdx.x;
-  // Stage work: thread -> (row slot, pairs). Element work: thread -> (row slot, elements).
-  const int prs = RB > 1 ? tid / C::NPAIR : 0;
-  const int ers = tid / TPR, ec = tid % TPR;
-
-  float2 cf[L][P];
-  float acc[L][P];
-#pragma unroll
-  for (int s = 0; s < L; ++s)
-#pragma unroll
-    for (int m = 0; m < P; ++m) {
-      const int pp = RB > 1 ? tid % C::NPAIR : tid + m * C::NTHR;
-      cf[s][m] = p.cs[((size_t)e * L + s) * C::NPAIR + pp];
-      acc[s][m] = 0.f;
-    }
-
-  for (int qb = q0; qb < q1; qb += RB) {
-    const int q = qb + ers;
-    const bool valid = q < q1;
-    const int r = valid ? p.perm[q] : 0;
-    float* v = V + ers * PD;
-    float* g = G + ers * PD;
-    bwd_load<D, IN_SIDE, XT, AT>(p, v, g, q, valid, r / p.k, ec);
-    __syncthreads();
-#pragma unroll
-    for (int ss = 0; ss < L; ++ss) {
-      const int s = IN_SIDE ? L - 1 - ss : ss;
-#pragma unroll
-      for (int m = 0; m < P; ++m) {
-        const int pp = RB > 1 ? tid % C::NPAIR : tid + m * C::NTHR;
-        int i, j;
-        pair_ij(pp, s, i, j);
-        rot_fwd(V + prs * PD, i, j, cf[s][m].x, IN_SIDE ? -cf[s][m].y : cf[s][m].y);
-      }
-      __syncthreads();
-    }
-    if (!IN_SIDE) {
-      bwd_gates<D>(p, v, g, red, valid, r, tid, ec);
-      __syncthreads();
-    }
-#pragma unroll
-    for (int ss = 0; ss < L; ++ss) {
-      const int s = IN_SIDE ? ss : L - 1 - ss;
-#pragma unroll
-      for (int m = 0; m < P; ++m) {
-        const int pp = RB > 1 ? tid % C::NPAIR : tid + m * C::NTHR;
-        int i, j;
-        pair_ij(pp, s, i, j);
-        const float da = rot_bwd(V + prs * PD, G + prs * PD, i, j, cf[s][m].x,
-                                 IN_SIDE ? -cf[s][m].y : cf[s][m].y);
-        acc[s][m] += IN_SIDE ? -da : da;
-      }
-      __syncthreads();
-    }
-    bwd_store<D, IN_SIDE, AT>(p, g, q, r, valid, ec);
-    __syncthreads();
-  }
-
-  // This tile's angle-gradient partial (row slots summed in slot order).
-  float* out = p.partial + (size_t)blockIdx.x * L * C::NPAIR;
-  if (RB == 1) {
-#pragma unroll
-    for (int s = 0; s < L; ++s)
-#pragma unroll
-      for (int m = 0; m < P; ++m) out[s * C::NPAIR + tid + m * C::NTHR] = acc[s][m];
-  } else {
-#pragma unroll
-    for (int s = 0; s < L; ++s) {
-      V[tid] = acc[s][0];
-      __syncthreads();
-      if (tid < C::NPAIR) {
-        float sum = 0.f;
-        for (int rs = 0; rs < RB; ++rs) sum += V[rs * C::NPAIR + tid];
-        out[s * C::NPAIR + tid] = sum;
-      }
-      __syncthreads();
-    }
-  }
-}
-
-// d >= 1024: one row per batch; gradient sums in LDS (one slot per stage and
-// pair, owned by one thread), cos/sin streamed one stage ahead.
-template <int D, bool IN_SIDE, typename XT, typename AT>
-__global__ __launch_bounds__(BwdCfg<D>::NTHR) void bfly_bwd_big_kernel(BwdParams p) {
-  using C = BwdCfg<D>;
-  constexpr int L = C::L, P = C::P, PD = C::PD, NPAIR = C::NPAIR, NTHR = C::NTHR;
-  static_assert(D >= 1024 && C::RB == 1, "large-d variant");
-  __shared__ float V[PD];
-  __shared__ float G[PD];
-  __shared__ float A[L * NPAIR];
+  constexpr int L = C::L, NG = C::NG, R = C::R, PD = C::PD, NTHR = C::NTHR, TPR = C::TPR;
+  __shared__ float V[C::VSZ];
+  __shared__ float Gs[R * PD];
+  __shared__ int rowr[R];
   __shared__ float red[NTHR / 64];
 
   const int4 tile = p.tiles[blockIdx.x];
@@ -337,63 +323,89 @@ __global__ __launch_bounds__(BwdCfg<D>::NTHR) void bfly_bwd_big_kernel(BwdParams
   if (e < 0) return;  // past the last tile (whole workgroup)
   const int q0 = tile.y, q1 = tile.z;
   const int tid = threadIdx.x;
-  const float2* cse = p.cs + (size_t)e * L * NPAIR;
-  for (int u = tid; u < L * NPAIR; u += NTHR) A[u] = 0.f;
+  const float2* cse = p.cs + (size_t)e * L * (D / 2);
 
-  for (int q = q0; q < q1; ++q) {
-    const int r = p.perm[q];
-    bwd_load<D, IN_SIDE, XT, AT>(p, V, G, q, true, r / p.k, tid);
-    float2 cf[P], nf[P];
-    {
-      const int s = IN_SIDE ? L - 1 : 0;
+  // cos/sin of every block this thread owns, and its gradient sums
+  float2 cf[NG][2][12];
+  float acc[NG][2][12];
 #pragma unroll
-      for (int m = 0; m < P; ++m) cf[m] = cse[s * NPAIR + tid + m * NTHR];
-    }
-    __syncthreads();
-#pragma unroll 1
-    for (int ss = 0; ss < L; ++ss) {
-      const int s = IN_SIDE ? L - 1 - ss : ss;
-      const int sn_next = IN_SIDE ? L - 2 - ss : ss + 1;  // forward stage after this one
-      const int s_next = ss + 1 < L ? sn_next : (IN_SIDE ? 0 : L - 1);  // then backward's first
+  for (int g = 0; g < NG; ++g) {
+    const int G = C::gsize(g);
 #pragma unroll
-      for (int m = 0; m < P; ++m) nf[m] = cse[s_next * NPAIR + tid + m * NTHR];
+    for (int sl = 0; sl < 2; ++sl) {
 #pragma unroll
-      for (int m = 0; m < P; ++m) {
-        int i, j;
-        pair_ij(tid + m * NTHR, s, i, j);
-        rot_fwd(V, i, j, cf[m].x, IN_SIDE ? -cf[m].y : cf[m].y);
+      for (int j = 0; j < 12; ++j) {
+        acc[g][sl][j] = 0.f;
+        cf[g][sl][j] = make_float2(1.f, 0.f);
       }
+      if (sl < C::slots(g)) {
+        const int bstride = NTHR / C::tpb(g);
+        const int base = block_base(tid % bstride + sl * bstride, 3 * g, G);
 #pragma unroll
-      for (int m = 0; m < P; ++m) cf[m] = nf[m];
-      __syncthreads();
-    }
-    if (!IN_SIDE) {
-      bwd_gates<D>(p, V, G, red, true, r, tid, tid);
-      __syncthreads();
-    }
-#pragma unroll 1
-    for (int ss = 0; ss < L; ++ss) {
-      const int s = IN_SIDE ? ss : L - 1 - ss;
-      const int s_next = IN_SIDE ? (ss + 1 < L ? ss + 1 : L - 1) : (ss + 1 < L ? L - 2 - ss : 0);
+        for (int t = 0; t < 3; ++t)
 #pragma unroll
-      for (int m = 0; m < P; ++m) nf[m] = cse[s_next * NPAIR + tid + m * NTHR];
-#pragma unroll
-      for (int m = 0; m < P; ++m) {
-        int i, j;
-        pair_ij(tid + m * NTHR, s, i, j);
-        const float da = rot_bwd(V, G, i, j, cf[m].x, IN_SIDE ? -cf[m].y : cf[m].y);
-        A[s * NPAIR + tid + m * NTHR] += IN_SIDE ? -da : da;
+          for (int u = 0; u < 4; ++u)
+            if (t < G && u < (1 << (G - 1))) {
+              const int s = 3 * g + t;
+              cf[g][sl][t * 4 + u] = cse[s * (D / 2) + pair_index(base + (pair_lo(t, u) << (3 * g)), s)];
+            }
       }
-#pragma unroll
-      for (int m = 0; m < P; ++m) cf[m] = nf[m];
-      __syncthreads();
     }
-    bwd_store<D, IN_SIDE, AT>(p, G, q, r, true, tid);
-    __syncthreads();
   }
 
-  float* out = p.partial + (size_t)blockIdx.x * L * NPAIR;
-  for (int u = tid; u < L * NPAIR; u += NTHR) out[u] = A[u];
+  constexpr int VS = 16 / sizeof(T), CPR = D / VS;  // 16-byte chunks per row
+  const T* src = static_cast<const T*>(p.src);
+  const T* grad = static_cast<const T*>(p.grad);
+  T* dst = static_cast<T*>(p.dst);
+  for (int qb = q0; qb < q1; qb += R) {
+    const int nr = min(R, q1 - qb);
+    if (tid < nr) rowr[tid] = p.perm[qb + tid];
+    __syncthreads();
+    for (int c = tid; c < nr * CPR; c += NTHR) {
+      const int i = c / CPR, off = (c % CPR) * VS;
+      const size_t tok = (size_t)(rowr[i] / p.k), sorted = (size_t)(qb + i);
+      load16<T>(src + (IN_SIDE ? tok : sorted) * D + off, V + i * PD + pad(off));
+      load16<T>(grad + (IN_SIDE ? sorted : tok) * D + off, Gs + i * PD + pad(off));
+    }
+    __syncthreads();
+    run_groups<D, IN_SIDE, false>(V, Gs, nr, tid, cf, acc);
+    if (!IN_SIDE) {
+      // dg_r = <dy_t, u_r>, then G = g_r dy_t (each thread scales what it read)
+      const int i = tid / TPR, c0 = tid % TPR;
+      float dot = 0.f;
+      if (i < nr) {
+#pragma unroll 4
+        for (int c = c0; c < D; c += TPR) dot += V[i * PD + pad(c)] * Gs[i * PD + pad(c)];
+        const float gate = p.gates[rowr[i]];
+#pragma unroll 4
+        for (int c = c0; c < D; c += TPR) Gs[i * PD + pad(c)] *= gate;
+      }
+      if (TPR <= 64) {
+#pragma unroll
+        for (int o = TPR / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, TPR);
+        if (c0 == 0 && i < nr) p.dgates[rowr[i]] = dot;
+      } else {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, 64);
+        if (tid % 64 == 0) red[tid / 64] = dot;
+        __syncthreads();
+        if (c0 == 0 && i < nr) {
+          float sum = 0.f;
+          for (int w = 0; w < TPR / 64; ++w) sum += red[tid / 64 + w];
+          p.dgates[rowr[i]] = sum;
+        }
+      }
+      __syncthreads();
+    }
+    run_groups<D, IN_SIDE, true>(V, Gs, nr, tid, cf, acc);
+    for (int c = tid; c < nr * CPR; c += NTHR) {
+      const int i = c / CPR, off = (c % CPR) * VS;
+      const size_t row = IN_SIDE ? (size_t)rowr[i] : (size_t)(qb + i);
+      store16<T>(Gs + i * PD + pad(off), dst + row * D + off, 1.0f);
+    }
+    __syncthreads();
+  }
+  write_partials<D>(V, p.partial + (size_t)blockIdx.x * L * (D / 2), tid, acc);
 }
 
 // dA[e][s][p] = sum of expert e's tile partials, in tile order (0 if no rows).
@@ -417,59 +429,57 @@ int grid_for(size_t n) {
 }
 
 template <int D, bool IN_SIDE>
-hipError_t launch_bwd_d(bmoe_dtype dt, int max_tiles, const BwdParams& p, hipStream_t s) {
+hipError_t launch_bwd_d(bmoe_dtype dt, int max_tiles, const BwdParams& p, hipStream_t s,
+                        const KernelTiming& t) {
   using C = BwdCfg<D>;
-  if constexpr (D >= 1024) {
-    if (dt == BMOE_BF16)
-      return launch_kernel(bfly_bwd_big_kernel<D, IN_SIDE, uint16_t, uint16_t>, dim3(max_tiles),
-                           dim3(C::NTHR), 0, s, KernelTiming{}, p);
-    return launch_kernel(bfly_bwd_big_kernel<D, IN_SIDE, float, float>, dim3(max_tiles),
-                         dim3(C::NTHR), 0, s, KernelTiming{}, p);
-  } else {
-    if (dt == BMOE_BF16)
-      return launch_kernel(bfly_bwd_kernel<D, IN_SIDE, uint16_t, uint16_t>, dim3(max_tiles),
-                           dim3(C::NTHR), 0, s, KernelTiming{}, p);
-    return launch_kernel(bfly_bwd_kernel<D, IN_SIDE, float, float>, dim3(max_tiles),
-                         dim3(C::NTHR), 0, s, KernelTiming{}, p);
-  }
+  if (dt == BMOE_BF16)
+    return launch_kernel(bfly_bwd_kernel<D, IN_SIDE, uint16_t>, dim3(max_tiles), dim3(C::NTHR), 0,
+                         s, t, p);
+  return launch_kernel(bfly_bwd_kernel<D, IN_SIDE, float>, dim3(max_tiles), dim3(C::NTHR), 0, s,
+                       t, p);
 }
 
 template <bool IN_SIDE>
-hipError_t launch_bwd(bmoe_dtype dt, int d, int max_tiles, const BwdParams& p, hipStream_t s) {
+hipError_t launch_bwd(bmoe_dtype dt, int d, int max_tiles, const BwdParams& p, hipStream_t s,
+                      const KernelTiming& t) {
   switch (d) {
-    case 16: return launch_bwd_d<16, IN_SIDE>(dt, max_tiles, p, s);
-    case 32: return launch_bwd_d<32, IN_SIDE>(dt, max_tiles, p, s);
-    case 64: return launch_bwd_d<64, IN_SIDE>(dt, max_tiles, p, s);
-    case 128: return launch_bwd_d<128, IN_SIDE>(dt, max_tiles, p, s);
-    case 256: return launch_bwd_d<256, IN_SIDE>(dt, max_tiles, p, s);
-    case 512: return launch_bwd_d<512, IN_SIDE>(dt, max_tiles, p, s);
-    case 1024: return launch_bwd_d<1024, IN_SIDE>(dt, max_tiles, p, s);
-    case 2048: return launch_bwd_d<2048, IN_SIDE>(dt, max_tiles, p, s);
-    case 4096: return launch_bwd_d<4096, IN_SIDE>(dt, max_tiles, p, s);
+    case 16: return launch_bwd_d<16, IN_SIDE>(dt, max_tiles, p, s, t);
+    case 32: return launch_bwd_d<32, IN_SIDE>(dt, max_tiles, p, s, t);
+    case 64: return launch_bwd_d<64, IN_SIDE>(dt, max_tiles, p, s, t);
+    case 128: return launch_bwd_d<128, IN_SIDE>(dt, max_tiles, p, s, t);
+    case 256: return launch_bwd_d<256, IN_SIDE>(dt, max_tiles, p, s, t);
+    case 512: return launch_bwd_d<512, IN_SIDE>(dt, max_tiles, p, s, t);
+    case 1024: return launch_bwd_d<1024, IN_SIDE>(dt, max_tiles, p, s, t);
+    case 2048: return launch_bwd_d<2048, IN_SIDE>(dt, max_tiles, p, s, t);
+    case 4096: return launch_bwd_d<4096, IN_SIDE>(dt, max_tiles, p, s, t);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int bwd_max_tiles(int M, int N) { return (M + kTileRows - 1) / kTileRows + N; }
+int bwd_max_tiles(int M, int N, int d) {
+  const int tr = bwd_tile_rows(d);
+  return (M + tr - 1) / tr + N;
+}
 
-hipError_t launch_tiles(const int32_t* offsets, int N, int4* tiles, int32_t* tile_base,
-                        int max_tiles, hipStream_t s) {
-  return launch_kernel(tiles_kernel, dim3(1), dim3(1024), 0, s, KernelTiming{}, offsets, N, tiles,
-                       tile_base, max_tiles);
+hipError_t launch_tiles(const int32_t* offsets, int N, int d, int4* tiles, int32_t* tile_base,
+                        int max_tiles, hipStream_t s, const KernelTiming& t) {
+  return launch_kernel(tiles_kernel, dim3(1), dim3(1024), 0, s, t, offsets, N, bwd_tile_rows(d),
+                       tiles, tile_base, max_tiles);
 }
 
 hipError_t launch_pack_transpose(const uint32_t* wp, int d, uint32_t* wpt, uint32_t* wtt, int cb,
-                                 hipStream_t s) {
+                                 hipStream_t s, const KernelTiming& t) {
   return launch_kernel(pack_transpose_kernel, dim3(grid_for((size_t)d * (d / 16))), dim3(256), 0,
-                       s, KernelTiming{}, wp, d, wpt, wtt, cb);
+                       s, t, wp, d, wpt, wtt, cb);
 }
 
 hipError_t launch_bfly_bwd(bool in_side, bmoe_dtype dt, int M, int d, int k, const int4* tiles,
                            int max_tiles, const int32_t* perm, const float2* cs,
                            const float* gates, const void* src, const void* grad, void* dst,
-                           float* dgates, float* partial, hipStream_t s) {
+                           float* dgates, float* partial, hipStream_t s,
+                           const KernelTiming& t) {
   BwdParams p;
   p.M = M;
   p.k = k;
@@ -482,17 +492,17 @@ hipError_t launch_bfly_bwd(bool in_side, bmoe_dtype dt, int M, int d, int k, con
   p.dst = dst;
   p.dgates = dgates;
   p.partial = partial;
-  return in_side ? launch_bwd<true>(dt, d, max_tiles, p, s)
-                 : launch_bwd<false>(dt, d, max_tiles, p, s);
+  return in_side ? launch_bwd<true>(dt, d, max_tiles, p, s, t)
+                 : launch_bwd<false>(dt, d, max_tiles, p, s, t);
 }
 
 hipError_t launch_angle_reduce(const float* partial, const int32_t* tile_base, int N, int d,
-                               float* out, hipStream_t s) {
+                               float* out, hipStream_t s, const KernelTiming& t) {
   int L = 0;
   while ((1 << L) < d) ++L;
   const int per = L * (d / 2);
   return launch_kernel(angle_reduce_kernel, dim3(grid_for((size_t)N * per)), dim3(256), 0, s,
-                       KernelTiming{}, partial, tile_base, N, per, out);
+                       t, partial, tile_base, N, per, out);
 }
 
 }  // namespace bmoe

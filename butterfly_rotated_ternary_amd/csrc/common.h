@@ -54,6 +54,39 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// 16 bytes of a row (8 bf16 or 4 fp32) to fp32 in LDS.
+template <typename T>
+__device__ __forceinline__ void load16(const T* src, float* dst) {
+  const uint4 v = *reinterpret_cast<const uint4*>(src);
+  if constexpr (sizeof(T) == 2) {
+    dst[0] = bf16_lo(v.x); dst[1] = bf16_hi(v.x);
+    dst[2] = bf16_lo(v.y); dst[3] = bf16_hi(v.y);
+    dst[4] = bf16_lo(v.z); dst[5] = bf16_hi(v.z);
+    dst[6] = bf16_lo(v.w); dst[7] = bf16_hi(v.w);
+  } else {  // padded LDS rows are only 4-byte aligned here
+    dst[0] = __uint_as_float(v.x); dst[1] = __uint_as_float(v.y);
+    dst[2] = __uint_as_float(v.z); dst[3] = __uint_as_float(v.w);
+  }
+}
+
+// fp32 values from LDS (times `scale`) to 16 bytes of a row.
+template <typename T>
+__device__ __forceinline__ void store16(const float* s, T* dst, float scale) {
+  uint4 v;
+  if constexpr (sizeof(T) == 2) {
+    v.x = pack_bf16x2(s[0] * scale, s[1] * scale);
+    v.y = pack_bf16x2(s[2] * scale, s[3] * scale);
+    v.z = pack_bf16x2(s[4] * scale, s[5] * scale);
+    v.w = pack_bf16x2(s[6] * scale, s[7] * scale);
+  } else {
+    v.x = __float_as_uint(s[0] * scale);
+    v.y = __float_as_uint(s[1] * scale);
+    v.z = __float_as_uint(s[2] * scale);
+    v.w = __float_as_uint(s[3] * scale);
+  }
+  *reinterpret_cast<uint4*>(dst) = v;
+}
+
 // Index of the j-th element of a block of 2^g elements whose varying index
 // bits start at bit s_lo; `b` enumerates blocks (all other index bits).
 __device__ __forceinline__ int block_base(int b, int s_lo, int g) {

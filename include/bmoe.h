@@ -178,6 +178,28 @@ bmoe_status bmoe_backward(bmoe_dtype dt, int T, int d, int n_experts, int k, con
                           const void* dy, void* dx, float* dgates, float* dtheta, float* dphi,
                           float* dw, void* ws, size_t ws_bytes, void* stream);
 
+/* Number and names of the launches of one bmoe_backward (0 / "" when the
+ * shape is unsupported or T == 0, or i is out of range). The substrate
+ * gradient is a library GEMM that may run as several kernels; its slot
+ * covers all of them (and is empty when dw is NULL). */
+int bmoe_backward_kernel_count(bmoe_dtype dt, int T, int d, int n_experts, int k);
+const char* bmoe_backward_kernel_name(bmoe_dtype dt, int T, int d, int n_experts, int k, int i);
+
+/*
+ * bmoe_backward, additionally timing each launch: launch i records
+ * events[2i] and events[2i+1] around its own execution, as in
+ * bmoe_forward_timed (the library-GEMM slot with hipEventRecord on `stream`
+ * before and after it). `events` holds 2 * bmoe_backward_kernel_count(...)
+ * hipEvent_t created by the caller on the current device; NULL behaves as
+ * bmoe_backward. Results are identical to bmoe_backward.
+ */
+bmoe_status bmoe_backward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k,
+                                const void* x, const int32_t* ids, const float* gates,
+                                const float* theta, const float* phi, const uint32_t* w_packed,
+                                float alpha, const void* dy, void* dx, float* dgates,
+                                float* dtheta, float* dphi, float* dw, void* ws, size_t ws_bytes,
+                                void* stream, void* const* events);
+
 /* Static description of a status code. */
 const char* bmoe_status_str(bmoe_status s);
 

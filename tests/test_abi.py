@@ -87,3 +87,22 @@ def test_host_validation_needs_no_gpu():
     assert lib.bmoe_forward(1, 0, 512, 8, 2, None, None, None, None, None, None, 1.0, None, None,
                             0, None, None) == 0     # T = 0 is a no-op
     assert lib.bmoe_pack_ternary(None, 16, None, None, 0, None) == 1
+
+
+def test_backward_launch_table_and_validation():
+    bf = bmoe.BMOE_BF16
+    names = [bmoe.bmoe_backward_kernel_name(bf, 64, 512, 8, 2, i)
+             for i in range(bmoe.bmoe_backward_kernel_count(bf, 64, 512, 8, 2))]
+    assert len(names) == 12 and len(set(names)) == 12
+    assert "bfly_bwd_out_kernel" in names and "gemm_t_kernel" in names
+    assert bmoe.bmoe_backward_kernel_count(bf, 64, 8192, 8, 2) == 0   # d > 4096
+    assert bmoe.bmoe_backward_kernel_count(bf, 0, 512, 8, 2) == 0
+    assert bmoe.bmoe_backward_kernel_name(bf, 64, 512, 8, 2, 12) == ""
+    assert bmoe.bmoe_backward_workspace_bytes(bf, 64, 8192, 8, 2) == 0
+    assert bmoe.bmoe_backward_workspace_bytes(bf, 64, 4096, 8, 2) > 0
+    lib = bmoe.lib()
+    a = [None] * 10
+    assert lib.bmoe_backward(9, 4, 512, 8, 2, *a[:6], 1.0, *a[:7], 0, None) == 3
+    assert lib.bmoe_backward(1, 4, 8192, 8, 2, *a[:6], 1.0, *a[:7], 0, None) == 2
+    assert lib.bmoe_backward(1, 4, 512, 8, 2, *a[:6], 1.0, *a[:7], 0, None) == 1
+    assert lib.bmoe_backward(1, 0, 512, 8, 2, *a[:6], 1.0, *a[:7], 0, None) == 0

@@ -93,3 +93,39 @@ def test_backward_is_deterministic():
 
 def test_backward_rejects_d8192():
     assert bmoe.bmoe_backward_workspace_bytes(bmoe.BMOE_BF16, 4, 8192, 2, 1) == 0
+
+
+def test_timed_backward_matches_untimed():
+    import ctypes
+    inp = W.make_inputs(W.HEADLINE, T=300)
+    dev = to_device(inp)
+    dy = torch.randn(inp.T, inp.d, device="cuda").to(torch.bfloat16)
+    a = bmoe.backward(dev["x"], dev["ids"], dev["gates"], dev["theta"], dev["phi"],
+                      dev["w_packed"], dev["alpha"], dy)
+    b = {k: torch.empty_like(v) for k, v in a.items()}
+    dt, T, d, N, k = bmoe.BMOE_BF16, inp.T, inp.d, inp.N, inp.k
+    ws = torch.empty(bmoe.bmoe_backward_workspace_bytes(dt, T, d, N, k), dtype=torch.uint8,
+                     device="cuda")
+    hip = ctypes.CDLL("libamdhip64.so")
+    nk = bmoe.bmoe_backward_kernel_count(dt, T, d, N, k)
+    evs = []
+    for _ in range(2 * nk):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    rc = bmoe.bmoe_backward_timed(dt, T, d, N, k, dev["x"], dev["ids"], dev["gates"],
+                                  dev["theta"], dev["phi"], dev["w_packed"], dev["alpha"], dy,
+                                  b["dx"], b["dgates"], b["dtheta"], b["dphi"], b["dw"], ws,
+                                  events=evs)
+    assert rc == 0
+    torch.cuda.synchronize()
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    for i in range(nk):
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), evs[2 * i], evs[2 * i + 1]) == 0
+        assert ms.value >= 0.0
+    for e in evs:
+        hip.hipEventDestroy(ctypes.c_void_p(e))
+    for key in ("dx", "dgates", "dtheta", "dphi", "dw"):
+        assert torch.equal(a[key], b[key]), key
