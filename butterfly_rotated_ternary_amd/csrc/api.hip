@@ -66,9 +66,25 @@ FwdLayout fwd_layout(bmoe_dtype dt, int T, int d, int N, int k) {
 
 struct BwdLayout {
   size_t status, offsets, perm, inv, slot_e, cs_in, cs_out, z, h, dh, dx, wt, wpt, wtt, tiles,
-      tile_base, part_in, part_out, total;
+      tile_base, part_in, part_out, dw_part, total;
   int max_tiles, wt_block;
 };
+
+// The substrate gradient's reduction over M routed rows is split into
+// dw_splits() equal row ranges (plus one for the remainder) when d is small,
+// so the library GEMM has enough output tiles to fill the chip; the fp32
+// partial products are then summed in a fixed order.
+int dw_splits(int M, int d) {
+  if (d >= 2048) return 1;
+  const int tiles = d >= 128 ? (d / 128) * (d / 128) : 1;
+  int S = (256 + tiles - 1) / tiles;
+  if (S > M / 256) S = M / 256;
+  return S < 1 ? 1 : S;
+}
+int dw_slots(int M, int d) {
+  const int S = dw_splits(M, d);
+  return S == 1 ? 0 : S + (M % S != 0 ? 1 : 0);
+}
 
 BwdLayout bwd_layout(bmoe_dtype dt, int T, int d, int N, int k) {
   BwdLayout l{};
@@ -97,6 +113,7 @@ BwdLayout bwd_layout(bmoe_dtype dt, int T, int d, int N, int k) {
   l.tile_base = off; off = align_up(off + sizeof(int32_t) * (N + 1));
   l.part_in = off;   off = align_up(off + sizeof(float) * l.max_tiles * L * (d / 2));
   l.part_out = off;  off = align_up(off + sizeof(float) * l.max_tiles * L * (d / 2));
+  l.dw_part = off;   off = align_up(off + sizeof(float) * dw_slots((int)M, d) * d * d);
   l.total = off;
   return l;
 }
@@ -106,9 +123,11 @@ bool bwd_shape_ok(bmoe_dtype dt, int T, int d, int N, int k) {
 }
 
 // dW = alpha * dH^T Z (row-major [d][d], fp32): the column-major product
-// Z_cm * dH_cm^T of the row-major [M][d] matrices viewed column-major.
+// Z_cm * dH_cm^T of the row-major [M][d] matrices viewed column-major. With
+// S > 1 splits, batch b takes rows b*Kb .. (b+1)*Kb - 1 into part[b], the
+// remainder rows go to part[S], and a kernel sums the slices in order.
 bmoe_status substrate_grad(bmoe_dtype dt, int M, int d, const void* dh, const void* z,
-                           float alpha, float* dw, hipStream_t s) {
+                           float alpha, float* dw, float* part, hipStream_t s) {
   static std::once_flag once;
   static rocblas_handle handle = nullptr;
   static rocblas_status created = rocblas_status_internal_error;
@@ -117,11 +136,34 @@ bmoe_status substrate_grad(bmoe_dtype dt, int M, int d, const void* dh, const vo
   if (rocblas_set_stream(handle, s) != rocblas_status_success) return BMOE_E_HIP;
   const float beta = 0.f;
   const rocblas_datatype at = dt == BMOE_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
-  const rocblas_status st = rocblas_gemm_ex(
-      handle, rocblas_operation_none, rocblas_operation_transpose, d, d, M, &alpha, z, at, d, dh,
-      at, d, &beta, dw, rocblas_datatype_f32_r, d, dw, rocblas_datatype_f32_r, d,
-      rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-  return st == rocblas_status_success ? BMOE_OK : BMOE_E_HIP;
+  const rocblas_datatype f32 = rocblas_datatype_f32_r;
+  const size_t el = dt == BMOE_BF16 ? 2 : 4;
+  const int S = dw_splits(M, d);
+  if (S == 1) {
+    const rocblas_status st = rocblas_gemm_ex(
+        handle, rocblas_operation_none, rocblas_operation_transpose, d, d, M, &alpha, z, at, d,
+        dh, at, d, &beta, dw, f32, d, dw, f32, d, f32, rocblas_gemm_algo_standard, 0, 0);
+    return st == rocblas_status_success ? BMOE_OK : BMOE_E_HIP;
+  }
+  const int kb = M / S, rest = M - S * kb;
+  const rocblas_stride sab = (rocblas_stride)kb * d, sc = (rocblas_stride)d * d;
+  rocblas_status st = rocblas_gemm_strided_batched_ex(
+      handle, rocblas_operation_none, rocblas_operation_transpose, d, d, kb, &alpha, z, at, d, sab,
+      dh, at, d, sab, &beta, part, f32, d, sc, part, f32, d, sc, S, f32,
+      rocblas_gemm_algo_standard, 0, 0);
+  if (st != rocblas_status_success) return BMOE_E_HIP;
+  if (rest > 0) {
+    const char* z1 = static_cast<const char*>(z) + el * (size_t)S * kb * d;
+    const char* dh1 = static_cast<const char*>(dh) + el * (size_t)S * kb * d;
+    float* p1 = part + (size_t)S * d * d;
+    st = rocblas_gemm_ex(handle, rocblas_operation_none, rocblas_operation_transpose, d, d, rest,
+                         &alpha, z1, at, d, dh1, at, d, &beta, p1, f32, d, p1, f32, d, f32,
+                         rocblas_gemm_algo_standard, 0, 0);
+    if (st != rocblas_status_success) return BMOE_E_HIP;
+  }
+  return launch_sum_slices(part, S + (rest > 0 ? 1 : 0), (size_t)d * d, dw, s) == hipSuccess
+             ? BMOE_OK
+             : BMOE_E_HIP;
 }
 
 }  // namespace
@@ -336,7 +378,9 @@ bmoe_status bmoe_backward_timed(bmoe_dtype dt, int T, int d, int n_experts, int 
   {
     const KernelTiming t = timing();
     if (t.start && hipEventRecord(t.start, s) != hipSuccess) return BMOE_E_HIP;
-    if (dw && substrate_grad(dt, M, d, dh, z, alpha, dw, s) != BMOE_OK) return BMOE_E_HIP;
+    if (dw && substrate_grad(dt, M, d, dh, z, alpha, dw,
+                             reinterpret_cast<float*>(base + l.dw_part), s) != BMOE_OK)
+      return BMOE_E_HIP;
     if (t.stop && hipEventRecord(t.stop, s) != hipSuccess) return BMOE_E_HIP;
   }
   // dZ = alpha dH W (the product with the transposed substrate), into H's space.

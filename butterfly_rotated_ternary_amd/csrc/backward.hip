@@ -421,6 +421,21 @@ __global__ __launch_bounds__(256) void angle_reduce_kernel(const float* partial,
   }
 }
 
+__global__ __launch_bounds__(256) void sum_slices_kernel(const float4* part, int S, size_t n4,
+                                                         float4* out) {
+  for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < n4; u += (size_t)gridDim.x * 256) {
+    float4 a = part[u];
+    for (int b = 1; b < S; ++b) {
+      const float4 v = part[(size_t)b * n4 + u];
+      a.x += v.x;
+      a.y += v.y;
+      a.z += v.z;
+      a.w += v.w;
+    }
+    out[u] = a;
+  }
+}
+
 int grid_for(size_t n) {
   size_t b = (n + 255) / 256;
   if (b > 65536) b = 65536;
@@ -494,6 +509,12 @@ hipError_t launch_bfly_bwd(bool in_side, bmoe_dtype dt, int M, int d, int k, con
   p.partial = partial;
   return in_side ? launch_bwd<true>(dt, d, max_tiles, p, s, t)
                  : launch_bwd<false>(dt, d, max_tiles, p, s, t);
+}
+
+hipError_t launch_sum_slices(const float* part, int S, size_t n, float* out, hipStream_t s) {
+  return launch_kernel(sum_slices_kernel, dim3(grid_for(n / 4)), dim3(256), 0, s, KernelTiming{},
+                       reinterpret_cast<const float4*>(part), S, n / 4,
+                       reinterpret_cast<float4*>(out));
 }
 
 hipError_t launch_angle_reduce(const float* partial, const int32_t* tile_base, int N, int d,

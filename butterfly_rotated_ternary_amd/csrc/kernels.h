@@ -98,6 +98,8 @@ hipError_t launch_bfly_bwd(bool in_side, bmoe_dtype dt, int M, int d, int k, con
                            int max_tiles, const int32_t* perm, const float2* cs,
                            const float* gates, const void* src, const void* grad, void* dst,
                            float* dgates, float* partial, hipStream_t s, const KernelTiming& t = {});
+// out[i] = sum over b < S of part[b * n + i], in order of b (n % 4 == 0).
+hipError_t launch_sum_slices(const float* part, int S, size_t n, float* out, hipStream_t s);
 // out[e][s][p] = sum over expert e's tiles of partial[tile][s][p], in tile order.
 hipError_t launch_angle_reduce(const float* partial, const int32_t* tile_base, int N, int d,
                                float* out, hipStream_t s, const KernelTiming& t = {});

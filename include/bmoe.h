@@ -1,6 +1,6 @@
 /*
- * bmoe.h — C ABI of libbmoe.so: the ButterflyMoE expert-layer forward on
- * AMD Instinct MI355X (gfx950).
+ * bmoe.h — C ABI of libbmoe.so: the ButterflyMoE expert-layer forward and
+ * its backward on AMD Instinct MI355X (gfx950).
  *
  * Method (ButterflyMoE: Sub-Linear Ternary Experts via Structured Butterfly
  * Orbits, gist.science technical summary):
@@ -25,7 +25,10 @@
  * Conventions for every entry point:
  *   - All array pointers are DEVICE pointers owned by the caller, 16-byte
  *     aligned. The library allocates nothing on the call path and keeps no
- *     state between calls besides the loaded code object.
+ *     state between calls besides the loaded code object, with one
+ *     exception: bmoe_backward with dw != NULL creates, on its first such
+ *     call, a rocBLAS handle (which holds device memory of its own) that
+ *     lives until the process ends.
  *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *     asynchronously; a call returns before the GPU finishes.
  *   - A non-BMOE_OK return comes from host-side validation, before anything
@@ -168,8 +171,9 @@ size_t bmoe_backward_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts,
  * The other arguments are bmoe_forward's (same routing and rounding points;
  * the forward is recomputed inside). All outputs are overwritten; dtheta and
  * dphi are summed per expert in a fixed order (run-to-run bit-identical). The
- * dw product is a plain library GEMM (rocBLAS): the first call with dw != NULL
- * creates a rocBLAS handle kept for the life of the process. ws: at least
+ * dw product is a plain library GEMM (rocBLAS; for d < 2048 split into row
+ * ranges whose fp32 products are summed in a fixed order): the first call
+ * with dw != NULL creates a rocBLAS handle kept for the life of the process. ws: at least
  * bmoe_backward_workspace_bytes(), 16-byte aligned. Errors as bmoe_forward.
  */
 bmoe_status bmoe_backward(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
