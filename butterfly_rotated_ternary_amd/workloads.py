@@ -26,6 +26,12 @@ this fixed order):
 7. gate logits ~ N(0, 1), shape ``[T][k]``; gates are their softmax over the
    ``k`` entries of each token, taken in fp64 and stored as fp32.
 
+Router weights (for the router in front of the layer) come from a separate
+generator, ``PCG64(seed + 1_000_000)``, so the draws above do not change:
+``w_router`` ~ N(0, 1/d), shape ``[N][d]`` (one row per expert), which gives
+logits of unit variance for N(0, 1) inputs; rounded to bf16 like ``x`` for
+bf16 workloads.
+
 ``alpha = fp32(1/sqrt(d))``. For bf16 workloads ``x`` is rounded to bf16 with
 round-to-nearest-even; ``x`` then holds the exact bf16 values as fp32 and
 ``x_bits`` their raw 16-bit patterns.
@@ -184,3 +190,20 @@ def make_inputs(name: str = HEADLINE, *, T: Optional[int] = None, seed: Optional
     return Inputs(name=name, d=d, N=N, k=k, T=T, dtype=cfg["dtype"], x=x, x_bits=x_bits,
                   ids=ids, gates=gates, theta=theta, phi=phi, w=w,
                   alpha=np.float32(1.0 / math.sqrt(d)), outlier_channels=outl)
+
+
+@dataclasses.dataclass
+class RouterWeights:
+    w: np.ndarray                  # [N][d] fp32: the exact values the kernel receives
+    w_bits: Optional[np.ndarray]   # [N][d] uint16 bf16 patterns (bf16 only)
+
+
+def make_router_weights(inp: Inputs, seed: Optional[int] = None) -> RouterWeights:
+    """Router weights for a drawn workload (own generator; see the recipe)."""
+    base = WORKLOADS[inp.name]["seed"] if seed is None and inp.name in WORKLOADS else (seed or 1)
+    rng = np.random.Generator(np.random.PCG64(base + 1_000_000))
+    w = (rng.standard_normal((inp.N, inp.d)) / math.sqrt(inp.d)).astype(np.float32)
+    if inp.dtype == "bf16":
+        bits = bf16_round_bits(w)
+        return RouterWeights(w=bf16_bits_to_f32(bits), w_bits=bits)
+    return RouterWeights(w=w, w_bits=None)

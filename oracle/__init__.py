@@ -1,4 +1,5 @@
-"""Plain fp64 CPU oracle for the ButterflyMoE expert layer (forward and backward).
+"""Plain fp64 CPU oracle for the ButterflyMoE expert layer (forward, backward
+and the top-k router in front of it).
 
 TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import it. The HIP library never
@@ -7,3 +8,4 @@ HIP path.
 """
 from .bmoe_oracle import *  # noqa: F401,F403
 from .bmoe_backward import backward, loss as backward_loss  # noqa: F401
+from .bmoe_router import router, router_logits  # noqa: F401
