@@ -68,6 +68,13 @@ def lib():
         L.bmoe_backward.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
                                     c_f, vp, vp, vp, vp, vp, vp, vp, c_sz, vp]
         L.bmoe_backward.restype = c_int
+        L.bmoe_router_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
+        L.bmoe_router_workspace_bytes.restype = c_sz
+        L.bmoe_router.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp, c_sz,
+                                  vp]
+        L.bmoe_router.restype = c_int
+        L.bmoe_router_timed.argtypes = L.bmoe_router.argtypes + [vp]
+        L.bmoe_router_timed.restype = c_int
         L.bmoe_backward_timed.argtypes = L.bmoe_backward.argtypes + [vp]
         L.bmoe_backward_timed.restype = c_int
         L.bmoe_backward_kernel_count.argtypes = [c_int, c_int, c_int, c_int, c_int]
@@ -188,6 +195,29 @@ def bmoe_backward_kernel_name(dt: int, T: int, d: int, n_experts: int, k: int, i
     return lib().bmoe_backward_kernel_name(dt, T, d, n_experts, k, i).decode()
 
 
+def bmoe_router_workspace_bytes(dt: int, T: int, d: int, n_experts: int, k: int) -> int:
+    return lib().bmoe_router_workspace_bytes(dt, T, d, n_experts, k)
+
+
+def bmoe_router(dt: int, T: int, d: int, n_experts: int, k: int, x, w_router, ids, gates,
+                logits=None, ws=None, stream=None) -> int:
+    nb = 0 if ws is None else ws.numel() * ws.element_size()
+    return lib().bmoe_router(dt, T, d, n_experts, k, _ptr(x), _ptr(w_router), _ptr(ids),
+                             _ptr(gates), _ptr(logits), _ptr(ws), nb, _stream(stream))
+
+
+def bmoe_router_timed(dt: int, T: int, d: int, n_experts: int, k: int, x, w_router, ids, gates,
+                      logits=None, ws=None, stream=None, events=None) -> int:
+    """``events``: 4 raw hipEvent_t handles (start/stop of the logits and
+    top-k launches)."""
+    ev = None
+    if events is not None:
+        ev = (ctypes.c_void_p * len(events))(*events)
+    nb = 0 if ws is None else ws.numel() * ws.element_size()
+    return lib().bmoe_router_timed(dt, T, d, n_experts, k, _ptr(x), _ptr(w_router), _ptr(ids),
+                                   _ptr(gates), _ptr(logits), _ptr(ws), nb, _stream(stream), ev)
+
+
 # ---- conveniences over the entry points (allocation + error checks) -------
 
 def dtype_code(t: torch.Tensor) -> int:
@@ -262,3 +292,26 @@ def backward(x: torch.Tensor, ids: torch.Tensor, gates: torch.Tensor, theta: tor
                          out["dx"], out["dgates"], out["dtheta"], out["dphi"], out["dw"], ws,
                          stream), "bmoe_backward")
     return out
+
+
+def route(x: torch.Tensor, w_router: torch.Tensor, k: int, *, want_logits: bool = False,
+          stream=None):
+    """Router: (ids int32 [T][k], gates fp32 [T][k]) for bmoe_forward, plus
+    the fp32 [T][N] logits when want_logits."""
+    T, d = x.shape
+    N = w_router.shape[0]
+    dt = dtype_code(x)
+    if w_router.dtype != x.dtype or w_router.shape[1] != d:
+        raise ValueError("w_router must be [N][d] in x's dtype")
+    ids = torch.empty(T, k, dtype=torch.int32, device=x.device)
+    gates = torch.empty(T, k, dtype=torch.float32, device=x.device)
+    logits = torch.empty(T, N, dtype=torch.float32, device=x.device) if want_logits else None
+    ws = None
+    if logits is None:
+        n = bmoe_router_workspace_bytes(dt, T, d, N, k)
+        if n == 0:
+            raise BmoeError(2, "bmoe_router_workspace_bytes")
+        ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+    _check(bmoe_router(dt, T, d, N, k, x, w_router, ids, gates, logits, ws, stream),
+           "bmoe_router")
+    return (ids, gates, logits) if want_logits else (ids, gates)

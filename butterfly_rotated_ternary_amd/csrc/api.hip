@@ -118,6 +118,11 @@ BwdLayout bwd_layout(bmoe_dtype dt, int T, int d, int N, int k) {
   return l;
 }
 
+constexpr int kRouterMaxK = 64;
+bool router_shape_ok(bmoe_dtype dt, int T, int d, int N, int k) {
+  return shape_ok(dt, T, d, N, k) && k <= kRouterMaxK;
+}
+
 bool bwd_shape_ok(bmoe_dtype dt, int T, int d, int N, int k) {
   return shape_ok(dt, T, d, N, k) && d <= 4096;
 }
@@ -414,6 +419,48 @@ const char* const kBackwardNames[] = {
     "angle_reduce_in_kernel"};
 constexpr int kBackwardLaunches = sizeof(kBackwardNames) / sizeof(kBackwardNames[0]);
 }  // namespace
+
+size_t bmoe_router_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts, int k) {
+  if (!router_shape_ok(dt, T, d, n_experts, k)) return 0;
+  return align_up(sizeof(float) * (size_t)T * n_experts + 1);
+}
+
+bmoe_status bmoe_router_timed(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
+                              const void* w_router, int32_t* ids, float* gates, float* logits,
+                              void* ws, size_t ws_bytes, void* stream, void* const* events) {
+  if (dt != BMOE_F32 && dt != BMOE_BF16) return BMOE_E_DTYPE;
+  if (!router_shape_ok(dt, T, d, n_experts, k)) return BMOE_E_SHAPE;
+  if (T == 0) return BMOE_OK;
+  if (!x || !w_router || !ids || !gates) return BMOE_E_NULL;
+  float* lg = logits;
+  if (!lg) {
+    if (!ws || ws_bytes < bmoe_router_workspace_bytes(dt, T, d, n_experts, k))
+      return BMOE_E_WORKSPACE;
+    lg = static_cast<float*>(ws);
+  }
+  const void* ptrs[] = {x, w_router, ids, gates, lg};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return BMOE_E_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  KernelTiming t0, t1;
+  if (events) {
+    t0.start = static_cast<hipEvent_t>(events[0]);
+    t0.stop = static_cast<hipEvent_t>(events[1]);
+    t1.start = static_cast<hipEvent_t>(events[2]);
+    t1.stop = static_cast<hipEvent_t>(events[3]);
+  }
+  if (launch_router_logits(dt, T, d, n_experts, x, w_router, lg, s, t0) != hipSuccess)
+    return BMOE_E_HIP;
+  if (launch_topk(lg, T, n_experts, k, ids, gates, s, t1) != hipSuccess) return BMOE_E_HIP;
+  return BMOE_OK;
+}
+
+bmoe_status bmoe_router(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
+                        const void* w_router, int32_t* ids, float* gates, float* logits, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return bmoe_router_timed(dt, T, d, n_experts, k, x, w_router, ids, gates, logits, ws, ws_bytes,
+                           stream, nullptr);
+}
 
 int bmoe_backward_kernel_count(bmoe_dtype dt, int T, int d, int n_experts, int k) {
   if (!bwd_shape_ok(dt, T, d, n_experts, k) || T == 0) return 0;

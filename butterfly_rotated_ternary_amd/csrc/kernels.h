@@ -104,4 +104,14 @@ hipError_t launch_sum_slices(const float* part, int S, size_t n, float* out, hip
 hipError_t launch_angle_reduce(const float* partial, const int32_t* tile_base, int N, int d,
                                float* out, hipStream_t s, const KernelTiming& t = {});
 
+// ---- router ------------------------------------------------------------------
+// logits[t][e] = sum_c x[t][c] w[e][c] (fp32), x [T][d] and w [N][d] of dtype dt.
+hipError_t launch_router_logits(bmoe_dtype dt, int T, int d, int N, const void* x,
+                                const void* w, float* logits, hipStream_t s,
+                                const KernelTiming& t = {});
+// Top-k (k <= 64) of each logits row, ties to the lower id; softmax gates over
+// the chosen logits.
+hipError_t launch_topk(const float* logits, int T, int N, int k, int32_t* ids, float* gates,
+                       hipStream_t s, const KernelTiming& t = {});
+
 }  // namespace bmoe

@@ -204,6 +204,39 @@ bmoe_status bmoe_backward_timed(bmoe_dtype dt, int T, int d, int n_experts, int 
                                 float* dtheta, float* dphi, float* dw, void* ws, size_t ws_bytes,
                                 void* stream, void* const* events);
 
+/*
+ * Router: the top-k gate that picks each token's experts and gates (the
+ * layer is a top-k mixture of experts, ButterflyMoE abstract and summary
+ * §2.3; the pages give no router formula, so this is the plain top-k
+ * softmax gate). For token t:
+ *   logits[t][e] = sum_c x[t][c] * w_router[e][c]     (fp32 accumulation)
+ *   ids[t][0..k)  the k experts with the largest logits, in descending
+ *                 order of logit; equal logits go to the lower expert id
+ *   gates[t][j]   softmax over the k chosen logits (they sum to 1)
+ * The outputs are laid out exactly as bmoe_forward's ids and gates inputs.
+ *   dt        element type of x and w_router (bf16: products on bf16 MFMA,
+ *             fp32 accumulation; fp32: fp32 FMA).
+ *   x         [T][d].
+ *   w_router  [N][d]: one row per expert (W_r stored transposed).
+ *   ids       int32 [T][k] (output).
+ *   gates     fp32 [T][k] (output).
+ *   logits    optional fp32 [T][N] output; NULL keeps the logits in ws.
+ *   ws        needed only when logits is NULL: at least
+ *             bmoe_router_workspace_bytes() bytes.
+ * Shapes as bmoe_forward, and k <= 64 (BMOE_E_SHAPE otherwise). Logits that
+ * are NaN give unspecified ids.
+ */
+size_t bmoe_router_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts, int k);
+bmoe_status bmoe_router(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
+                        const void* w_router, int32_t* ids, float* gates, float* logits,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* bmoe_router, timing its two launches (logits, then top-k): events holds 4
+ * hipEvent_t (start/stop of each), or NULL. Results identical to bmoe_router. */
+bmoe_status bmoe_router_timed(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
+                              const void* w_router, int32_t* ids, float* gates, float* logits,
+                              void* ws, size_t ws_bytes, void* stream, void* const* events);
+
 /* Static description of a status code. */
 const char* bmoe_status_str(bmoe_status s);
 

@@ -106,3 +106,15 @@ def test_backward_launch_table_and_validation():
     assert lib.bmoe_backward(1, 4, 8192, 8, 2, *a[:6], 1.0, *a[:7], 0, None) == 2
     assert lib.bmoe_backward(1, 4, 512, 8, 2, *a[:6], 1.0, *a[:7], 0, None) == 1
     assert lib.bmoe_backward(1, 0, 512, 8, 2, *a[:6], 1.0, *a[:7], 0, None) == 0
+
+
+def test_router_validation_needs_no_gpu():
+    bf = bmoe.BMOE_BF16
+    assert bmoe.bmoe_router_workspace_bytes(bf, 100, 512, 64, 2) >= 100 * 64 * 4
+    assert bmoe.bmoe_router_workspace_bytes(bf, 100, 512, 128, 65) == 0   # k > 64
+    assert bmoe.bmoe_router_workspace_bytes(bf, 100, 500, 64, 2) == 0
+    lib = bmoe.lib()
+    assert lib.bmoe_router(9, 4, 512, 8, 2, None, None, None, None, None, None, 0, None) == 3
+    assert lib.bmoe_router(1, 4, 512, 80, 65, None, None, None, None, None, None, 0, None) == 2
+    assert lib.bmoe_router(1, 4, 512, 8, 2, None, None, None, None, None, None, 0, None) == 1
+    assert lib.bmoe_router(1, 0, 512, 8, 2, None, None, None, None, None, None, 0, None) == 0
