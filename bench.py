@@ -133,6 +133,21 @@ def backward_work(name, act_bytes, T, d, N, k):
     raise KeyError(name)
 
 
+def router_work(name, act_bytes, T, d, N, k):
+    """Algorithmic work of one router launch: the logits product reads x and
+    the router weights once and writes fp32 logits (2 T d N flops, MFMA on
+    bf16, VALU on fp32); the top-k reads the logits and writes ids and gates."""
+    if name == "router_logits_kernel":
+        b = T * d * act_bytes + N * d * act_bytes + T * N * 4
+        f = 2 * T * d * N
+        if act_bytes == 2:
+            return {"bytes": b, "mfma_flops": f, "valu_flops": 0}
+        return {"bytes": b, "mfma_flops": 0, "valu_flops": f}
+    if name == "topk_kernel":
+        return {"bytes": T * N * 4 + T * k * 8, "mfma_flops": 0, "valu_flops": 0}
+    raise KeyError(name)
+
+
 def roofline(work, dur_s, mfma_peak_tflops):
     """The roofline of one kernel: the resource whose ideal time (work over
     published peak) is largest bounds it; achieved = that work / measured
@@ -364,6 +379,69 @@ class Problem:
             hip.destroy(evs)
         return ms, per
 
+    def router_setup(self):
+        import numpy as np
+        import torch
+        from butterfly_rotated_ternary_amd import workloads as W
+        rw = W.make_router_weights(self.inp)
+        if self.act_bytes == 2:
+            self.wr = torch.from_numpy(rw.w_bits.view(np.int16)).view(torch.bfloat16).to(
+                self.x.device)
+        else:
+            self.wr = torch.from_numpy(rw.w).to(self.x.device)
+        b = self.bmoe
+        self.r_ids = torch.empty_like(self.ids)
+        self.r_gates = torch.empty_like(self.gates)
+        n = b.bmoe_router_workspace_bytes(self.dt, self.T, self.d, self.N, self.k)
+        self.rws = torch.empty(n, dtype=torch.uint8, device=self.x.device)
+
+    def router_args(self):
+        return (self.dt, self.T, self.d, self.N, self.k, self.x, self.wr, self.r_ids,
+                self.r_gates, None, self.rws, self.stream)
+
+    def time_router(self, steps, warmup):
+        """(router ms, router + forward ms per step, per-launch router ms)."""
+        import torch
+        b = self.bmoe
+        fwd = (self.dt, self.T, self.d, self.N, self.k, self.x, self.r_ids, self.r_gates,
+               self.theta, self.phi, self.wp, self.alpha, self.y, self.ws.buf, None, self.stream)
+        for _ in range(warmup):
+            rc = b.bmoe_router(*self.router_args())
+            if rc != 0:
+                raise b.BmoeError(rc, "bmoe_router")
+            rc = b.bmoe_forward(*fwd)
+            if rc != 0:
+                raise b.BmoeError(rc, "bmoe_forward")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            b.bmoe_router(*self.router_args())
+        torch.cuda.synchronize()
+        r_ms = (time.perf_counter() - t0) * 1e3 / steps
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            b.bmoe_router(*self.router_args())
+            b.bmoe_forward(*fwd)
+        torch.cuda.synchronize()
+        rf_ms = (time.perf_counter() - t0) * 1e3 / steps
+        if b.bmoe_sync_status(self.ws.buf) != 0:
+            raise RuntimeError("device status not OK after routed forwards")
+        names = ["router_logits_kernel", "topk_kernel"]
+        hip = HipEvents()
+        evsets = [hip.create(4) for _ in range(steps)]
+        for evs in evsets:
+            rc = b.bmoe_router_timed(*self.router_args(), events=evs)
+            if rc != 0:
+                raise b.BmoeError(rc, "bmoe_router_timed")
+        torch.cuda.synchronize()
+        per = {n: 0.0 for n in names}
+        for evs in evsets:
+            for i, n in enumerate(names):
+                per[n] += hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) / steps
+        for evs in evsets:
+            hip.destroy(evs)
+        return r_ms, rf_ms, per
+
     def mfma_peak(self):
         return PEAK_BF16_TFLOPS if self.dt == self.bmoe.BMOE_BF16 else PEAK_FP32_MFMA_TFLOPS
 
@@ -386,6 +464,23 @@ def backward_section(P, steps):
         + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in per.items()))
     return {"workload": P.name, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
             "steps": steps, "roofline": roof, "kernels": kern}
+
+
+def router_section(P, steps):
+    """The router on the same workload (synthetic router weights), alone and
+    followed by the forward on its ids and gates."""
+    P.router_setup()
+    r_ms, rf_ms, per = P.time_router(steps, max(3, steps // 10))
+    T, d, N, k = P.T, P.d, P.N, P.k
+    kern = {}
+    for n, v in per.items():
+        r = roofline(router_work(n, P.act_bytes, T, d, N, k), v * 1e-3, P.mfma_peak())
+        kern[n] = {"us": v * 1e3, "bound": r["bound"], "frac": r["frac"],
+                   "achieved": r["achieved"], "unit": r["unit"]}
+    log(f"[bench] router {P.name}: {r_ms * 1e3:.1f} us; router + forward {rf_ms * 1e3:.1f} us; "
+        + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in per.items()))
+    return {"workload": P.name, "ms_per_step": r_ms, "routed_forward_ms_per_step": rf_ms,
+            "routed_forward_tokens_per_s": T / (rf_ms * 1e-3), "steps": steps, "kernels": kern}
 
 
 def copy_calibration(mib, reps):
@@ -413,6 +508,8 @@ def main():
                     help="forwards of the d=4096 workload timed for its GEMM figure (0: skip)")
     ap.add_argument("--bwd-steps", type=int, default=100,
                     help="backward passes timed on the same workload (0: skip)")
+    ap.add_argument("--router-steps", type=int, default=200,
+                    help="router passes timed on the same workload (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain copies of MIB MiB (counter calibration) and exit")
     ap.add_argument("--print-source-digest", action="store_true")
@@ -473,6 +570,8 @@ def main():
                      / (PEAK_HBM_GBS * 1e9)},
         "kernels": others,
     }
+    if args.router_steps > 0:
+        out["router"] = router_section(P, args.router_steps)
     if args.bwd_steps > 0:
         out["backward"] = backward_section(P, args.bwd_steps)
     del P

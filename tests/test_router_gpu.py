@@ -85,6 +85,8 @@ def test_router_matches_oracle(name, T):
 @pytest.mark.parametrize("d,N,k,T,dtype", [
     (16, 8, 3, 5, "bf16"), (32, 70, 5, 65, "bf16"), (64, 1, 1, 3, "f32"), (128, 130, 64, 70, "bf16"),
     (256, 4096, 64, 20, "bf16"), (512, 100, 7, 1, "f32"), (1024, 600, 8, 64, "bf16"),
+    # large enough for the LDS-tiled logits (ragged in tokens and experts)
+    (512, 130, 4, 32700, "bf16"), (64, 257, 2, 16390, "bf16"), (128, 33, 3, 33000, "bf16"),
 ])
 def test_router_edge_shapes(d, N, k, T, dtype):
     inp = W.make_inputs("tiny_d64_e8_top2_f32", T=T, d=d, N=N, k=min(k, N), dtype=dtype,
