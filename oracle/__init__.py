@@ -1,5 +1,5 @@
-"""Plain fp64 CPU oracle for the ButterflyMoE expert layer (forward, backward
-and the top-k router in front of it).
+"""Plain fp64 CPU oracle for the ButterflyMoE expert layer (forward, backward,
+the top-k router in front of it, and the base-3 storage of the substrate).
 
 TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import it. The HIP library never
@@ -9,3 +9,4 @@ HIP path.
 from .bmoe_oracle import *  # noqa: F401,F403
 from .bmoe_backward import backward, loss as backward_loss  # noqa: F401
 from .bmoe_router import router, router_logits  # noqa: F401
+from .bmoe_pack3 import pack_ternary_b3, packed3_bytes, unpack_ternary_b3  # noqa: F401
