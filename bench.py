@@ -483,6 +483,34 @@ def router_section(P, steps):
             "routed_forward_tokens_per_s": T / (rf_ms * 1e-3), "steps": steps, "kernels": kern}
 
 
+def base3_section(P, steps, fwd_ms):
+    """Base-3 storage of the substrate (five ternary digits per byte): bytes at
+    rest, and the kernel that decodes it into the 2-bit words the forward
+    reads (HBM-bound: d*d/5 bytes read, d*d/4 written)."""
+    import torch
+    b, d = P.bmoe, P.d
+    w8 = torch.from_numpy(P.inp.w).to(P.x.device)
+    p3 = b.pack_ternary_b3(w8)
+    out = torch.empty(d, d // 16, dtype=torch.int32, device=P.x.device)
+    ws = torch.empty(b.bmoe_pack_workspace_bytes(), dtype=torch.uint8, device=P.x.device)
+    hip = HipEvents()
+    evsets = [hip.create(2) for _ in range(steps)]
+    for evs in [hip.create(2) for _ in range(3)] + evsets:
+        rc = b.bmoe_unpack_ternary_b3_timed(p3, d, out, ws, events=evs)
+        if rc != 0:
+            raise b.BmoeError(rc, "bmoe_unpack_ternary_b3")
+    torch.cuda.synchronize()
+    if b.bmoe_sync_status(ws) != 0 or not torch.equal(out.reshape(-1), P.wp.reshape(-1)):
+        raise RuntimeError("base-3 decoding differs from the 2-bit pack")
+    us = sum(hip.elapsed_ms(e[0], e[1]) for e in evsets) / steps * 1e3
+    nbytes = p3.numel() + d * d // 4
+    log(f"[bench] base-3 d={d}: {p3.numel()} B at rest vs {d * d // 4} B (2-bit); "
+        f"decode {us:.2f} us ({nbytes / us / 1e3:.0f} GB/s)")
+    return {"d": d, "bytes_base3": p3.numel(), "bytes_2bit": d * d // 4,
+            "bits_per_weight": 8 * p3.numel() / (d * d), "decode_us": us,
+            "decode_gbs": nbytes / us / 1e3, "decode_frac_of_forward": us * 1e-3 / fwd_ms}
+
+
 def copy_calibration(mib, reps):
     """Plain device-to-device copies of a known size, for scaling the HBM
     byte counters (run under rocprofv3 --pmc)."""
@@ -572,6 +600,7 @@ def main():
     }
     if args.router_steps > 0:
         out["router"] = router_section(P, args.router_steps)
+        out["base3"] = base3_section(P, 50, ms)
     if args.bwd_steps > 0:
         out["backward"] = backward_section(P, args.bwd_steps)
     del P

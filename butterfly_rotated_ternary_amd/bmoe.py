@@ -17,6 +17,8 @@ _lib = None
 
 BMOE_F32 = 0
 BMOE_BF16 = 1
+BMOE_E_TERNARY = 4
+BMOE_E_EXPERT = 5
 
 STATUS = {
     0: "BMOE_OK", 1: "BMOE_E_NULL", 2: "BMOE_E_SHAPE", 3: "BMOE_E_DTYPE",
@@ -50,6 +52,14 @@ def lib():
         L.bmoe_pack_workspace_bytes.restype = c_sz
         L.bmoe_pack_ternary.argtypes = [vp, c_int, vp, vp, c_sz, vp]
         L.bmoe_pack_ternary.restype = c_int
+        L.bmoe_packed3_bytes.argtypes = [c_int]
+        L.bmoe_packed3_bytes.restype = c_sz
+        L.bmoe_pack_ternary_b3.argtypes = [vp, c_int, vp, vp, c_sz, vp]
+        L.bmoe_pack_ternary_b3.restype = c_int
+        L.bmoe_unpack_ternary_b3.argtypes = [vp, c_int, vp, vp, c_sz, vp]
+        L.bmoe_unpack_ternary_b3.restype = c_int
+        L.bmoe_unpack_ternary_b3_timed.argtypes = [vp, c_int, vp, vp, c_sz, vp, vp]
+        L.bmoe_unpack_ternary_b3_timed.restype = c_int
         L.bmoe_forward.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp, c_f,
                                    vp, vp, c_sz, vp, vp]
         L.bmoe_forward.restype = c_int
@@ -121,6 +131,31 @@ def bmoe_pack_ternary(w: torch.Tensor, d: int, packed: torch.Tensor, ws: torch.T
                       stream=None) -> int:
     return lib().bmoe_pack_ternary(_ptr(w), d, _ptr(packed), _ptr(ws), ws.numel() * ws.element_size(),
                                    _stream(stream))
+
+
+def bmoe_packed3_bytes(d: int) -> int:
+    return lib().bmoe_packed3_bytes(d)
+
+
+def bmoe_pack_ternary_b3(w: torch.Tensor, d: int, packed3: torch.Tensor, ws: torch.Tensor,
+                         stream=None) -> int:
+    return lib().bmoe_pack_ternary_b3(_ptr(w), d, _ptr(packed3), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream))
+
+
+def bmoe_unpack_ternary_b3(packed3: torch.Tensor, d: int, packed: torch.Tensor,
+                           ws: torch.Tensor, stream=None) -> int:
+    return lib().bmoe_unpack_ternary_b3(_ptr(packed3), d, _ptr(packed), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream))
+
+
+def bmoe_unpack_ternary_b3_timed(packed3: torch.Tensor, d: int, packed: torch.Tensor,
+                                 ws: torch.Tensor, stream=None, events=None) -> int:
+    ev = None
+    if events is not None:
+        ev = (ctypes.c_void_p * len(events))(*events)
+    return lib().bmoe_unpack_ternary_b3_timed(_ptr(packed3), d, _ptr(packed), _ptr(ws),
+                                              ws.numel() * ws.element_size(), _stream(stream), ev)
 
 
 def bmoe_forward(dt: int, T: int, d: int, n_experts: int, k: int, x, ids, gates, theta, phi,
@@ -315,3 +350,27 @@ def route(x: torch.Tensor, w_router: torch.Tensor, k: int, *, want_logits: bool 
     _check(bmoe_router(dt, T, d, N, k, x, w_router, ids, gates, logits, ws, stream),
            "bmoe_router")
     return (ids, gates, logits) if want_logits else (ids, gates)
+
+
+def pack_ternary_b3(w: torch.Tensor) -> torch.Tensor:
+    """int8 [d][d] in {-1,0,+1} on the GPU -> uint8 base-3 stream (raises on
+    a bad entry)."""
+    d = w.shape[0]
+    n = bmoe_packed3_bytes(d)
+    if n == 0 or w.shape != (d, d) or w.dtype != torch.int8:
+        raise ValueError("w must be int8 [d][d] with a supported d")
+    out = torch.empty((n + 15) // 16 * 16, dtype=torch.uint8, device=w.device)
+    ws = torch.empty(bmoe_pack_workspace_bytes(), dtype=torch.uint8, device=w.device)
+    _check(bmoe_pack_ternary_b3(w, d, out, ws), "bmoe_pack_ternary_b3")
+    _check(bmoe_sync_status(ws), "bmoe_pack_ternary_b3 (device)")
+    return out[:n]
+
+
+def unpack_ternary_b3(packed3: torch.Tensor, d: int) -> torch.Tensor:
+    """Base-3 stream -> the 2-bit words bmoe_forward takes (raises on a byte
+    above 242)."""
+    out = torch.empty(d, d // 16, dtype=torch.int32, device=packed3.device)
+    ws = torch.empty(bmoe_pack_workspace_bytes(), dtype=torch.uint8, device=packed3.device)
+    _check(bmoe_unpack_ternary_b3(packed3, d, out, ws), "bmoe_unpack_ternary_b3")
+    _check(bmoe_sync_status(ws), "bmoe_unpack_ternary_b3 (device)")
+    return out

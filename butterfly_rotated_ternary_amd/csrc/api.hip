@@ -206,6 +206,46 @@ bmoe_status bmoe_pack_ternary(const int8_t* w, int d, uint32_t* packed, void* ws
   return BMOE_OK;
 }
 
+size_t bmoe_packed3_bytes(int d) {
+  if (!valid_d(d)) return 0;
+  return ((size_t)d * d + 4) / 5;
+}
+
+bmoe_status bmoe_pack_ternary_b3(const int8_t* w, int d, uint8_t* packed3, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (!w || !packed3) return BMOE_E_NULL;
+  if (!valid_d(d)) return BMOE_E_SHAPE;
+  if (!ws || ws_bytes < bmoe_pack_workspace_bytes()) return BMOE_E_WORKSPACE;
+  if (!aligned16(w) || !aligned16(packed3) || !aligned16(ws)) return BMOE_E_ALIGN;
+  if (launch_pack_b3(w, d, packed3, static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return BMOE_E_HIP;
+  return BMOE_OK;
+}
+
+bmoe_status bmoe_unpack_ternary_b3_timed(const uint8_t* packed3, int d, uint32_t* packed,
+                                         void* ws, size_t ws_bytes, void* stream,
+                                         void* const* events) {
+  if (!packed3 || !packed) return BMOE_E_NULL;
+  if (!valid_d(d)) return BMOE_E_SHAPE;
+  if (!ws || ws_bytes < bmoe_pack_workspace_bytes()) return BMOE_E_WORKSPACE;
+  if (!aligned16(packed3) || !aligned16(packed) || !aligned16(ws)) return BMOE_E_ALIGN;
+  KernelTiming t;
+  if (events) {
+    t.start = static_cast<hipEvent_t>(events[0]);
+    t.stop = static_cast<hipEvent_t>(events[1]);
+  }
+  if (launch_unpack_b3(packed3, d, packed, static_cast<int32_t*>(ws),
+                       static_cast<hipStream_t>(stream), t) != hipSuccess)
+    return BMOE_E_HIP;
+  return BMOE_OK;
+}
+
+bmoe_status bmoe_unpack_ternary_b3(const uint8_t* packed3, int d, uint32_t* packed, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  return bmoe_unpack_ternary_b3_timed(packed3, d, packed, ws, ws_bytes, stream, nullptr);
+}
+
 bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
                                const int32_t* ids, const float* gates, const float* theta,
                                const float* phi, const uint32_t* w_packed, float alpha, void* y,

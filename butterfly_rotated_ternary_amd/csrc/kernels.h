@@ -75,6 +75,14 @@ hipError_t launch_bfly_out(bmoe_dtype dt, int M, int d, const void* h, const flo
 hipError_t launch_combine(bmoe_dtype dt, int T, int d, int k, const void* u, void* y,
                           hipStream_t s, const KernelTiming& t = {});
 
+// Base-3 storage: five ternary digits per byte over the row-major entries
+// (ceil(d*d/5) bytes), and its decoding into the 2-bit words launch_pack
+// writes. Both reset *status first and set BMOE_E_TERNARY on a bad entry or a
+// byte above 242.
+hipError_t launch_pack_b3(const int8_t* w, int d, uint8_t* packed3, int32_t* status,
+                          hipStream_t s);
+hipError_t launch_unpack_b3(const uint8_t* packed3, int d, uint32_t* packed, int32_t* status,
+                            hipStream_t s, const KernelTiming& t = {});
 hipError_t launch_pack(const int8_t* w, int d, uint32_t* packed, int32_t* status,
                        hipStream_t s);
 

@@ -79,6 +79,77 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const int8_t* w, int d, 
   }
 }
 
+// ---- base-3 storage (summary §2.1: 1.58 bits per weight) --------------------
+// Five ternary digits per byte over the row-major entries n = o*d + c:
+// byte j = sum_i (w[5j+i] + 1) * 3^i, digits past d*d equal to 1 (value 0).
+__global__ __launch_bounds__(kThreads) void pack_b3_kernel(const int8_t* w, size_t nw,
+                                                           uint8_t* out, size_t nb,
+                                                           int32_t* status) {
+  for (size_t j = (size_t)blockIdx.x * kThreads + threadIdx.x; j < nb;
+       j += (size_t)gridDim.x * kThreads) {
+    uint32_t byte = 0, scale = 1;
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const size_t n = 5 * j + i;
+      const int v = n < nw ? (int)w[n] : 0;
+      if (v < -1 || v > 1) bad = true;
+      byte += (uint32_t)(v < -1 || v > 1 ? 1 : v + 1) * scale;
+      scale *= 3;
+    }
+    if (bad) *status = BMOE_E_TERNARY;  // every writer stores the same value
+    out[j] = (uint8_t)byte;
+  }
+}
+
+// One thread per 2-bit word (row o, columns 16g .. 16g+15): its 16 entries
+// lie in at most 4 consecutive bytes. An LDS table maps each byte value to
+// its five digits as 2-bit codes in entry order (digit t = 0, 1, 2, i.e.
+// -1, 0, +1, becomes code 3, 0, 1; byte values above 242 map to 0xFFFF).
+// The four bytes' codes are concatenated, shifted to the word's first entry,
+// and split into the word layout: even columns in the low half, odd columns
+// in the high half.
+__global__ __launch_bounds__(kThreads) void unpack_b3_kernel(const uint8_t* in, size_t nb,
+                                                             uint32_t* packed, size_t nwords,
+                                                             int32_t* status) {
+  __shared__ uint16_t lut[256];
+  for (int v = threadIdx.x; v < 256; v += kThreads) {
+    uint32_t codes = 0xFFFFu, rest = (uint32_t)v;
+    if (v <= 242) {
+      codes = 0;
+      for (int i = 0; i < 5; ++i) {
+        const uint32_t t = rest % 3u;
+        rest /= 3u;
+        codes |= (t == 0 ? 3u : t == 2 ? 1u : 0u) << (2 * i);
+      }
+    }
+    lut[v] = (uint16_t)codes;
+  }
+  __syncthreads();
+  for (size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x; idx < nwords;
+       idx += (size_t)gridDim.x * kThreads) {
+    const size_t e0 = idx * 16, b0 = e0 / 5;
+    const int pos = (int)(e0 - 5 * b0);
+    uint64_t seq = 0;
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t c = b0 + i < nb ? lut[in[b0 + i]] : 0u;
+      bad |= c == 0xFFFFu;
+      seq |= (uint64_t)(c & 0x3FFu) << (10 * i);
+    }
+    const uint32_t codes = (uint32_t)(seq >> (2 * pos));  // code of entry v at bits 2v, 2v+1
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      word |= ((codes >> (4 * j)) & 3u) << (2 * j);             // column 2j
+      word |= ((codes >> (4 * j + 2)) & 3u) << (16 + 2 * j);    // column 2j + 1
+    }
+    if (bad) *status = BMOE_E_TERNARY;
+    packed[idx] = word;
+  }
+}
+
 int grid_for(size_t n) {
   size_t b = (n + kThreads - 1) / kThreads;
   if (b > 8192) b = 8192;
@@ -104,6 +175,24 @@ hipError_t launch_pack(const int8_t* w, int d, uint32_t* packed, int32_t* status
   hipLaunchKernelGGL(pack_kernel, dim3(grid_for((size_t)d * (d / 16))), dim3(kThreads), 0, s, w, d,
                      packed, status);
   return hipGetLastError();
+}
+
+hipError_t launch_pack_b3(const int8_t* w, int d, uint8_t* packed3, int32_t* status,
+                          hipStream_t s) {
+  const size_t nw = (size_t)d * d, nb = (nw + 4) / 5;
+  hipLaunchKernelGGL(set_status_kernel, dim3(1), dim3(1), 0, s, status, (int32_t)BMOE_OK);
+  hipLaunchKernelGGL(pack_b3_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, s, w, nw, packed3, nb,
+                     status);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_b3(const uint8_t* packed3, int d, uint32_t* packed, int32_t* status,
+                            hipStream_t s, const KernelTiming& t) {
+  hipLaunchKernelGGL(set_status_kernel, dim3(1), dim3(1), 0, s, status, (int32_t)BMOE_OK);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  const size_t nw = (size_t)d * (d / 16), nb = ((size_t)d * d + 4) / 5;
+  return launch_kernel(unpack_b3_kernel, dim3(grid_for(nw)), dim3(kThreads), 0, s, t, packed3, nb,
+                       packed, nw, status);
 }
 
 }  // namespace bmoe

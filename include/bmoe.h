@@ -101,6 +101,34 @@ bmoe_status bmoe_pack_ternary(const int8_t* w, int d, uint32_t* packed, void* ws
                               size_t ws_bytes, void* stream);
 
 /*
+ * Base-3 storage of the substrate: the summary (§2.1) stores W_base at 1.58
+ * bits per weight (log2 3); this is the byte-aligned form, five ternary
+ * digits per byte, 1.6 bits per weight. The d*d entries are taken row-major
+ * (entry n = o*d + c); byte j = sum over i < 5 of (w[5j+i] + 1) * 3^i, entry
+ * 5j being the least significant digit; digits past d*d are 1 (the value 0).
+ * bmoe_packed3_bytes(d) = ceil(d*d / 5) (0 for an invalid d).
+ *
+ * bmoe_pack_ternary_b3: int8 w [d][d] -> packed3. Invalid entries are stored
+ * as 0 and reported as BMOE_E_TERNARY by bmoe_sync_status(ws, stream).
+ * bmoe_unpack_ternary_b3: packed3 -> the 2-bit words of bmoe_pack_ternary
+ * (bit-identical to packing the same w directly), which bmoe_forward and
+ * bmoe_backward take. A byte above 242 is decoded as zeros and reported as
+ * BMOE_E_TERNARY. Decoding is one pass that reads d*d/5 bytes and writes
+ * d*d/4: it runs once per weight set, or before each forward into a small
+ * buffer, rather than inside the product's inner loop.
+ * ws: at least bmoe_pack_workspace_bytes() (the status word). The _timed
+ * variant records events[0] / events[1] around the decoding kernel.
+ */
+size_t bmoe_packed3_bytes(int d);
+bmoe_status bmoe_pack_ternary_b3(const int8_t* w, int d, uint8_t* packed3, void* ws,
+                                 size_t ws_bytes, void* stream);
+bmoe_status bmoe_unpack_ternary_b3(const uint8_t* packed3, int d, uint32_t* packed, void* ws,
+                                   size_t ws_bytes, void* stream);
+bmoe_status bmoe_unpack_ternary_b3_timed(const uint8_t* packed3, int d, uint32_t* packed,
+                                         void* ws, size_t ws_bytes, void* stream,
+                                         void* const* events);
+
+/*
  * Forward of one ButterflyMoE expert layer for T tokens (§2.3 order).
  *   dt        BMOE_F32 or BMOE_BF16: element type of x and y.
  *   x         [T][d] tokens.
