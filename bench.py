@@ -511,6 +511,53 @@ def base3_section(P, steps, fwd_ms):
             "decode_gbs": nbytes / us / 1e3, "decode_frac_of_forward": us * 1e-3 / fwd_ms}
 
 
+OUTLIER_WORKLOAD = "d2048_e64_top2_outliers_bf16"
+QUANTISERS = [("int8_absmax", 127, 0), ("int4_absmax", 7, 0), ("ternary_absmax", 1, 0),
+              ("ternary_absmean", 1, 1)]
+
+
+def outliers_section():
+    """Outlier spreading on the workload with outlier channels: per-token
+    quantisation error and crest factor of x and of z = B(theta_e)^T x (the
+    workload's random angles), each averaged over rows."""
+    import numpy as np
+    import torch
+    from butterfly_rotated_ternary_amd import bmoe
+    from butterfly_rotated_ternary_amd import workloads as W
+    inp = W.make_inputs(OUTLIER_WORKLOAD)
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(inp.x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    ids = torch.from_numpy(inp.ids).to(dev)
+    theta = torch.from_numpy(inp.theta).to(dev)
+    z = bmoe.rotate_in(x, ids, theta)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        z = bmoe.rotate_in(x, ids, theta)
+    torch.cuda.synchronize()
+    rot_ms = (time.perf_counter() - t0) * 1e3 / 5
+    out = {"workload": OUTLIER_WORKLOAD, "rows_x": inp.T, "rows_z": inp.T * inp.k,
+           "rotate_in_ms": rot_ms, "angles": "random U(-pi, pi), not learned"}
+    # the fully spread limit: iid N(0, 1) rows of the same shape
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    gauss = torch.randn(inp.T, inp.d, device=dev, generator=gen).to(torch.bfloat16)
+    for tag, v in (("x", x), ("z", z), ("gaussian_reference", gauss)):
+        res = {}
+        for name, m, mode in QUANTISERS:
+            err, crest = bmoe.quant_error(v, m, mode)
+            res[name] = float(err.double().mean())
+        res["crest"] = float(crest.double().mean())
+        out[tag] = res
+    log(f"[bench] outliers {OUTLIER_WORKLOAD}: "
+        + "; ".join(f"{q}: x {out['x'][q]:.4f} -> z {out['z'][q]:.4f} "
+                    f"(iid normal {out['gaussian_reference'][q]:.4f})"
+                    for q in [n for n, _, _ in QUANTISERS] + ["crest"]))
+    del x, z, ids, theta, gauss
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration(mib, reps):
     """Plain device-to-device copies of a known size, for scaling the HBM
     byte counters (run under rocprofv3 --pmc)."""
@@ -538,6 +585,8 @@ def main():
                     help="backward passes timed on the same workload (0: skip)")
     ap.add_argument("--router-steps", type=int, default=200,
                     help="router passes timed on the same workload (0: skip)")
+    ap.add_argument("--no-outliers", action="store_true",
+                    help="skip the outlier-spreading measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain copies of MIB MiB (counter calibration) and exit")
     ap.add_argument("--print-source-digest", action="store_true")
@@ -624,6 +673,9 @@ def main():
             + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in g_per.items()))
         del G
         torch.cuda.empty_cache()
+
+    if not args.no_outliers:
+        out["outliers"] = outliers_section()
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W.make_inputs(name), args.cpu_seconds)

@@ -78,6 +78,13 @@ def lib():
         L.bmoe_backward.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
                                     c_f, vp, vp, vp, vp, vp, vp, vp, c_sz, vp]
         L.bmoe_backward.restype = c_int
+        L.bmoe_rotate_in_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
+        L.bmoe_rotate_in_workspace_bytes.restype = c_sz
+        L.bmoe_rotate_in.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, c_sz,
+                                     vp]
+        L.bmoe_rotate_in.restype = c_int
+        L.bmoe_quant_error.argtypes = [c_int, c_int, c_int, vp, c_int, c_int, vp, vp, vp]
+        L.bmoe_quant_error.restype = c_int
         L.bmoe_router_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
         L.bmoe_router_workspace_bytes.restype = c_sz
         L.bmoe_router.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp, c_sz,
@@ -230,6 +237,22 @@ def bmoe_backward_kernel_name(dt: int, T: int, d: int, n_experts: int, k: int, i
     return lib().bmoe_backward_kernel_name(dt, T, d, n_experts, k, i).decode()
 
 
+def bmoe_rotate_in_workspace_bytes(dt: int, T: int, d: int, n_experts: int, k: int) -> int:
+    return lib().bmoe_rotate_in_workspace_bytes(dt, T, d, n_experts, k)
+
+
+def bmoe_rotate_in(dt: int, T: int, d: int, n_experts: int, k: int, x, ids, theta, z, ws,
+                   stream=None) -> int:
+    return lib().bmoe_rotate_in(dt, T, d, n_experts, k, _ptr(x), _ptr(ids), _ptr(theta), _ptr(z),
+                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+
+
+def bmoe_quant_error(dt: int, rows: int, d: int, src, m: int, mode: int, err, crest=None,
+                     stream=None) -> int:
+    return lib().bmoe_quant_error(dt, rows, d, _ptr(src), m, mode, _ptr(err), _ptr(crest),
+                                  _stream(stream))
+
+
 def bmoe_router_workspace_bytes(dt: int, T: int, d: int, n_experts: int, k: int) -> int:
     return lib().bmoe_router_workspace_bytes(dt, T, d, n_experts, k)
 
@@ -374,3 +397,28 @@ def unpack_ternary_b3(packed3: torch.Tensor, d: int) -> torch.Tensor:
     _check(bmoe_unpack_ternary_b3(packed3, d, out, ws), "bmoe_unpack_ternary_b3")
     _check(bmoe_sync_status(ws), "bmoe_unpack_ternary_b3 (device)")
     return out
+
+
+def rotate_in(x: torch.Tensor, ids: torch.Tensor, theta: torch.Tensor) -> torch.Tensor:
+    """z [T*k][d] (x's dtype), row t*k + j = B(theta_{ids[t][j]})^T x[t]."""
+    T, d = x.shape
+    k = ids.shape[1]
+    N = theta.shape[0]
+    dt = dtype_code(x)
+    n = bmoe_rotate_in_workspace_bytes(dt, T, d, N, k)
+    if n == 0:
+        raise BmoeError(2, "bmoe_rotate_in_workspace_bytes")
+    ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+    z = torch.empty(T * k, d, dtype=x.dtype, device=x.device)
+    _check(bmoe_rotate_in(dt, T, d, N, k, x, ids, theta, z, ws), "bmoe_rotate_in")
+    _check(bmoe_sync_status(ws), "bmoe_rotate_in (device)")
+    return z
+
+
+def quant_error(v: torch.Tensor, m: int, mode: int = 0):
+    """(err, crest) fp32 [rows] for the rows of v (bf16 or fp32)."""
+    rows, d = v.shape
+    err = torch.empty(rows, dtype=torch.float32, device=v.device)
+    crest = torch.empty(rows, dtype=torch.float32, device=v.device)
+    _check(bmoe_quant_error(dtype_code(v), rows, d, v, m, mode, err, crest), "bmoe_quant_error")
+    return err, crest

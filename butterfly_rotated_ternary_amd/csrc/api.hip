@@ -64,6 +64,25 @@ FwdLayout fwd_layout(bmoe_dtype dt, int T, int d, int N, int k) {
   return l;
 }
 
+// Workspace of bmoe_rotate_in: the routing tables and the input-side cos/sin.
+struct RotLayout {
+  size_t status, offsets, perm, inv, slot_e, cs_in, total;
+};
+
+RotLayout rot_layout(int T, int d, int N, int k) {
+  RotLayout l{};
+  const size_t M = (size_t)T * k;
+  size_t off = 0;
+  l.status = off;  off = align_up(off + sizeof(int32_t));
+  l.offsets = off; off = align_up(off + sizeof(int32_t) * (N + 1));
+  l.perm = off;    off = align_up(off + sizeof(int32_t) * M);
+  l.inv = off;     off = align_up(off + sizeof(int32_t) * M);
+  l.slot_e = off;  off = align_up(off + sizeof(int32_t) * M);
+  l.cs_in = off;   off = align_up(off + sizeof(float2) * N * log2i(d) * (d / 2));
+  l.total = off;
+  return l;
+}
+
 struct BwdLayout {
   size_t status, offsets, perm, inv, slot_e, cs_in, cs_out, z, h, dh, dx, wt, wpt, wtt, tiles,
       tile_base, part_in, part_out, dw_part, total;
@@ -459,6 +478,54 @@ const char* const kBackwardNames[] = {
     "angle_reduce_in_kernel"};
 constexpr int kBackwardLaunches = sizeof(kBackwardNames) / sizeof(kBackwardNames[0]);
 }  // namespace
+
+size_t bmoe_rotate_in_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts, int k) {
+  if (!shape_ok(dt, T, d, n_experts, k)) return 0;
+  return rot_layout(T, d, n_experts, k).total;
+}
+
+bmoe_status bmoe_rotate_in(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
+                           const int32_t* ids, const float* theta, void* z, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (dt != BMOE_F32 && dt != BMOE_BF16) return BMOE_E_DTYPE;
+  if (!shape_ok(dt, T, d, n_experts, k)) return BMOE_E_SHAPE;
+  if (T == 0) return BMOE_OK;
+  if (!x || !ids || !theta || !z) return BMOE_E_NULL;
+  const RotLayout l = rot_layout(T, d, n_experts, k);
+  if (!ws || ws_bytes < l.total) return BMOE_E_WORKSPACE;
+  const void* ptrs[] = {x, ids, theta, z, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return BMOE_E_ALIGN;
+  char* base = static_cast<char*>(ws);
+  RouteTables rt;
+  rt.offsets = reinterpret_cast<int32_t*>(base + l.offsets);
+  rt.perm = reinterpret_cast<int32_t*>(base + l.perm);
+  rt.inv = reinterpret_cast<int32_t*>(base + l.inv);
+  rt.slot_e = reinterpret_cast<int32_t*>(base + l.slot_e);
+  float2* cs_in = reinterpret_cast<float2*>(base + l.cs_in);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int M = T * k;
+  if (launch_prep(ids, M, n_experts, theta, nullptr, d, rt, cs_in, nullptr,
+                  reinterpret_cast<int32_t*>(base + l.status), nullptr, nullptr, nullptr, 0,
+                  s) != hipSuccess)
+    return BMOE_E_HIP;
+  if (launch_bfly_in(dt, M, d, k, x, rt, cs_in, z, s, KernelTiming{}, true) != hipSuccess)
+    return BMOE_E_HIP;
+  return BMOE_OK;
+}
+
+bmoe_status bmoe_quant_error(bmoe_dtype dt, int rows, int d, const void* src, int m, int mode,
+                             float* err, float* crest, void* stream) {
+  if (dt != BMOE_F32 && dt != BMOE_BF16) return BMOE_E_DTYPE;
+  if (rows < 0 || !valid_d(d) || m < 1 || (mode != 0 && mode != 1)) return BMOE_E_SHAPE;
+  if (rows == 0) return BMOE_OK;
+  if (!src || !err) return BMOE_E_NULL;
+  if (!aligned16(src) || !aligned16(err) || (crest && !aligned16(crest))) return BMOE_E_ALIGN;
+  if (launch_quant_error(dt, rows, d, src, m, mode, err, crest,
+                         static_cast<hipStream_t>(stream)) != hipSuccess)
+    return BMOE_E_HIP;
+  return BMOE_OK;
+}
 
 size_t bmoe_router_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts, int k) {
   if (!router_shape_ok(dt, T, d, n_experts, k)) return 0;

@@ -34,6 +34,7 @@ struct BflyParams {
   void* dst;
   const float2* cs;     // [N][L][d/2] (cos, sin)
   const float* gates;   // output side only, [M] in routed order
+  int routed_out;       // input side: write row r = perm[q] instead of q
 };
 
 // Rotate the 2^G register values of one block through its G stages.
@@ -145,7 +146,8 @@ __device__ int setup_rows(const BflyParams& p, int q0, int nr, int* sh_e, int* s
   return nruns_sh;
 }
 
-// IN_SIDE:  dst[q] = B(theta_e)^T x[perm[q] / k]          (sorted order)
+// IN_SIDE:  dst[q] = B(theta_e)^T x[perm[q] / k]          (sorted order, or
+//           dst[perm[q]] with routed_out)
 // OUT_SIDE: dst[perm[q]] = g_{perm[q]} * B(phi_e) src[q]   (routed order)
 template <bool IN_SIDE, typename SrcT, typename DstT>
 __global__ __launch_bounds__(kThreads) void bfly_kernel(BflyParams p) {
@@ -174,7 +176,8 @@ __global__ __launch_bounds__(kThreads) void bfly_kernel(BflyParams p) {
   for (int c = threadIdx.x; c < nr * cd; c += kThreads) {
     const int i = c / cd, off = (c % cd) * VD;
     if (IN_SIDE) {
-      store16<DstT>(rows + (size_t)i * padded_row(d) + pad(off), dst + (size_t)(q0 + i) * d + off, 1.0f);
+      const size_t row = p.routed_out ? (size_t)sh_r[i] : (size_t)(q0 + i);
+      store16<DstT>(rows + (size_t)i * padded_row(d) + pad(off), dst + row * d + off, 1.0f);
     } else {
       const int r = sh_r[i];
       store16<DstT>(rows + (size_t)i * padded_row(d) + pad(off), dst + (size_t)r * d + off, p.gates[r]);
@@ -369,7 +372,8 @@ __global__ __launch_bounds__(kBigThreads) void bfly_big_kernel(BflyParams p) {
     if (i < nr) {
       const float* s = rows + i * PD + pad(ch * 8);
       if (IN_SIDE) {
-        store16<uint16_t>(s, dst + (size_t)(q0 + i) * D + ch * 8, 1.0f);
+        const size_t row = p.routed_out ? (size_t)sh_r[i] : (size_t)(q0 + i);
+        store16<uint16_t>(s, dst + row * D + ch * 8, 1.0f);
       } else {
         const int r = sh_r[i];
         store16<uint16_t>(s, dst + (size_t)r * D + ch * 8, p.gates[r]);
@@ -437,8 +441,9 @@ BflyParams make_params(int M, int d, int k, const RouteTables& rt, const float2*
 
 hipError_t launch_bfly_in(bmoe_dtype dt, int M, int d, int k, const void* x,
                           const RouteTables& rt, const float2* cs_in, void* z, hipStream_t s,
-                          const KernelTiming& t) {
-  const BflyParams p = make_params(M, d, k, rt, cs_in, x, z, nullptr);
+                          const KernelTiming& t, bool routed_out) {
+  BflyParams p = make_params(M, d, k, rt, cs_in, x, z, nullptr);
+  p.routed_out = routed_out ? 1 : 0;
   if (dt == BMOE_BF16 && d >= 1024 && d <= 4096) return launch_big_d<true>(p, s, t);
   if (dt == BMOE_BF16) return launch_rows(bfly_kernel<true, uint16_t, uint16_t>, p, s, t);
   return launch_rows(bfly_kernel<true, float, float>, p, s, t);

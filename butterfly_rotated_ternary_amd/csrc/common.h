@@ -54,7 +54,7 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// 16 bytes of a row (8 bf16 or 4 fp32) to fp32 in LDS.
+// 16 bytes of a row (8 bf16 or 4 fp32) to fp32 (in LDS or registers).
 template <typename T>
 __device__ __forceinline__ void load16(const T* src, float* dst) {
   const uint4 v = *reinterpret_cast<const uint4*>(src);

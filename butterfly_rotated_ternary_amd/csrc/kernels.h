@@ -56,9 +56,10 @@ hipError_t launch_fused(int M, int d, int k, const void* x, const float* gates,
                         hipStream_t s, const KernelTiming& t = {});
 
 // Z[q] = B(theta_e)^T x[t]   (t = perm[q] / k, e = slot_e[q]).
+// routed_out: row perm[q] of z instead of row q (routed order).
 hipError_t launch_bfly_in(bmoe_dtype dt, int M, int d, int k, const void* x,
                           const RouteTables& rt, const float2* cs_in, void* z, hipStream_t s,
-                          const KernelTiming& t = {});
+                          const KernelTiming& t = {}, bool routed_out = false);
 
 // H = alpha * Z W_base^T over all M sorted rows (H bf16 on the bf16 path,
 // fp32 on the fp32 path; Z likewise).
@@ -111,6 +112,14 @@ hipError_t launch_sum_slices(const float* part, int S, size_t n, float* out, hip
 // out[e][s][p] = sum over expert e's tiles of partial[tile][s][p], in tile order.
 hipError_t launch_angle_reduce(const float* partial, const int32_t* tile_base, int N, int d,
                                float* out, hipStream_t s, const KernelTiming& t = {});
+
+// ---- outlier measurement ---------------------------------------------------------
+// Per row of src [rows][d] (dtype dt): err = ||v - q|| / ||v|| with
+// q = s * clip(rint(v / s), -m, m), s = max|v| / m (mode 0) or mean|v|
+// (mode 1); crest (optional) = max|v| / rms(v). Zero rows give 0.
+hipError_t launch_quant_error(bmoe_dtype dt, int rows, int d, const void* src, int m, int mode,
+                              float* err, float* crest, hipStream_t s,
+                              const KernelTiming& t = {});
 
 // ---- router ------------------------------------------------------------------
 // logits[t][e] = sum_c x[t][c] w[e][c] (fp32), x [T][d] and w [N][d] of dtype dt.

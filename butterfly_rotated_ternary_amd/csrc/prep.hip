@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
   }
   if ((int)blockIdx.x >= p.n_route_blocks) {
     // ---- cos/sin tables -------------------------------------------------
-    const long long total = 2 * p.n_ang;
+    const long long total = p.phi ? 2 * p.n_ang : p.n_ang;  // no phi: input side only
     const long long stride = (long long)p.n_trig_blocks * kThreads;
     for (long long i = (long long)(blockIdx.x - p.n_route_blocks) * kThreads + threadIdx.x;
          i < total; i += stride) {
@@ -258,7 +258,7 @@ hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, con
   p.cs_in = cs_in;
   p.cs_out = cs_out;
   p.n_ang = (long long)N * L * (d / 2);
-  long long trig_blocks = (2 * p.n_ang + kThreads * 8 - 1) / (kThreads * 8);
+  long long trig_blocks = ((phi ? 2 : 1) * p.n_ang + kThreads * 8 - 1) / (kThreads * 8);
   if (trig_blocks > 65536) trig_blocks = 65536;
   p.n_trig_blocks = (int)trig_blocks;
   p.w_packed = w_packed;

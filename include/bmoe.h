@@ -233,6 +233,35 @@ bmoe_status bmoe_backward_timed(bmoe_dtype dt, int T, int d, int n_experts, int 
                                 void* stream, void* const* events);
 
 /*
+ * Input-side rotation alone (§2.3, first step): z[r] = B(theta_e)^T x[t] for
+ * every routed row r = t*k + j, e = ids[t][j], written in routed order
+ * ([T*k][d], dtype dt; the same rounding point as the forward's Z). Used to
+ * measure how the rotation spreads activation outliers (§2.4). ws: at least
+ * bmoe_rotate_in_workspace_bytes() (routing tables and cos/sin; its status
+ * word reports bad expert ids through bmoe_sync_status). Shapes and errors
+ * as bmoe_forward.
+ */
+size_t bmoe_rotate_in_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts, int k);
+bmoe_status bmoe_rotate_in(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
+                           const int32_t* ids, const float* theta, void* z, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
+ * Per-row quantisation error of src [rows][d] (dtype dt), for the
+ * outlier-spreading measurement (§2.4, §4: the rotation lowers the activation
+ * quantisation error; the pages name no quantiser, so this is the plain
+ * per-token symmetric one). For row v:
+ *   s = max|v| / m (mode 0, absmax; m = 127 for int8, 7 for int4, 1 for
+ *       ternary) or s = mean|v| (mode 1, absmean),
+ *   q = s * clip(rint(v / s), -m, m),
+ *   err[row]   = ||v - q|| / ||v||        (fp32; 0 for a zero row),
+ *   crest[row] = max|v| / rms(v)          (fp32; optional, may be NULL).
+ * d as bmoe_forward, rows >= 0, m >= 1, mode 0 or 1 (BMOE_E_SHAPE otherwise).
+ */
+bmoe_status bmoe_quant_error(bmoe_dtype dt, int rows, int d, const void* src, int m, int mode,
+                             float* err, float* crest, void* stream);
+
+/*
  * Router: the top-k gate that picks each token's experts and gates (the
  * layer is a top-k mixture of experts, ButterflyMoE abstract and summary
  * §2.3; the pages give no router formula, so this is the plain top-k

@@ -1,0 +1,96 @@
+"""GPU parity of the outlier-measurement pieces: the input-side rotation
+against the oracle's rotate_in (per routed row, the forward's bar), and the
+per-row quantisation error and crest factor against the oracle on seeded
+inputs (closed-form rows included)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from butterfly_rotated_ternary_amd import bmoe
+from butterfly_rotated_ternary_amd import workloads as W
+from devinputs import to_device
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.mark.parametrize("name,T", [
+    ("tiny_d64_e8_top2_f32", 256), ("d512_e64_top2_bf16", 300), ("d512_e256_top2_zipf_bf16", 300),
+    ("d2048_e64_top2_outliers_bf16", 200), ("d4096_e256_top4_bf16", 40),
+])
+def test_rotate_in_matches_oracle(name, T):
+    inp = W.make_inputs(name, T=T)
+    print(f"[rotate_in] {name} T={T}", flush=True)
+    dev = to_device(inp)
+    z = bmoe.rotate_in(dev["x"], dev["ids"], dev["theta"])
+    torch.cuda.synchronize()
+    ref = O.rotate_in(inp.x, inp.ids, inp.theta)
+    assert O.max_rel_err(z.float().cpu().numpy().astype(np.float64), ref) <= TOL[inp.dtype]
+
+
+@pytest.mark.parametrize("d,N,k,T,dtype", [(16, 3, 2, 9, "f32"), (1024, 5, 3, 50, "bf16"),
+                                           (8192, 2, 1, 5, "bf16"), (256, 70, 1, 130, "f32")])
+def test_rotate_in_edge_shapes(d, N, k, T, dtype):
+    inp = W.make_inputs("tiny_d64_e8_top2_f32", T=T, d=d, N=N, k=k, dtype=dtype, seed=d + N)
+    dev = to_device(inp)
+    z = bmoe.rotate_in(dev["x"], dev["ids"], dev["theta"])
+    torch.cuda.synchronize()
+    ref = O.rotate_in(inp.x, inp.ids, inp.theta)
+    assert O.max_rel_err(z.float().cpu().numpy().astype(np.float64), ref) <= TOL[dtype]
+
+
+def test_rotate_in_full_size_sampled():
+    inp = W.make_inputs("d2048_e64_top2_outliers_bf16")
+    dev = to_device(inp)
+    z = bmoe.rotate_in(dev["x"], dev["ids"], dev["theta"])
+    torch.cuda.synchronize()
+    toks = np.unique(np.concatenate([np.random.default_rng(3).choice(inp.T, 300, replace=False),
+                                     np.arange(inp.T - 20, inp.T)]))
+    rows = (toks[:, None] * inp.k + np.arange(inp.k)[None, :]).reshape(-1)
+    ref = O.rotate_in(inp.x[toks], inp.ids[toks], inp.theta)
+    got = z[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    assert O.max_rel_err(got, ref) <= 2e-2
+
+
+def _rows(dtype, d, seed):
+    """Seeded rows: normal, outlier-heavy, on-grid, constant and zero."""
+    rng = np.random.default_rng(seed)
+    V = rng.standard_normal((40, d)).astype(np.float32)
+    V[5:10, :3] *= 50.0
+    g = rng.integers(-7, 8, size=(5, d)).astype(np.float32)
+    g[:, 0] = 7.0
+    V[10:15] = 0.25 * g               # on the m = 7 grid, s = 0.25 exactly
+    V[15:18] = -1.5                   # constant rows
+    V[18:20] = 0.0                    # zero rows
+    if dtype == "bf16":
+        bits = W.bf16_round_bits(V)
+        return W.bf16_bits_to_f32(bits), torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    return V, torch.from_numpy(V)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [16, 512, 2048])
+def test_quant_error_matches_oracle(dtype, d):
+    V, Vt = _rows(dtype, d, 100 + d)
+    Vg = Vt.cuda()
+    for m, mode in [(127, 0), (7, 0), (1, 0), (1, 1)]:
+        err, crest = bmoe.quant_error(Vg, m, mode)
+        torch.cuda.synchronize()
+        ref = O.quant_error(V, m, mode)
+        got = err.cpu().numpy().astype(np.float64)
+        assert np.allclose(got, ref, rtol=1e-4, atol=1e-6), (m, mode, np.abs(got - ref).max())
+        assert np.all(got[18:20] == 0.0)
+        c = crest.cpu().numpy().astype(np.float64)
+        assert np.allclose(c, O.crest_factor(V), rtol=1e-5, atol=1e-6)
+    err, _ = bmoe.quant_error(Vg, 7, 0)
+    assert np.all(err.cpu().numpy()[10:15] < 1e-6)   # on-grid rows quantise exactly
+
+
+def test_quant_error_rejects_bad_arguments():
+    v = torch.zeros(4, 64, device="cuda")
+    e = torch.empty(4, device="cuda")
+    assert bmoe.bmoe_quant_error(bmoe.BMOE_F32, 4, 64, v, 0, 0, e) == 2
+    assert bmoe.bmoe_quant_error(bmoe.BMOE_F32, 4, 64, v, 7, 2, e) == 2
+    assert bmoe.bmoe_quant_error(bmoe.BMOE_F32, 4, 60, v, 7, 0, e) == 2
