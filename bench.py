@@ -113,11 +113,9 @@ def backward_work(name, act_bytes, T, d, N, k):
     routing = M * 4
     if name in ("prep_kernel", "bfly_in_kernel", "gemm_kernel", "combine_kernel"):
         return kernel_work(name, act_bytes, T, d, N, k)
-    if name == "pack_transpose_kernel":
-        return {"bytes": d * d // 4 * (3 if d % 512 == 0 else 2), "mfma_flops": 0,
-                "valu_flops": 0}
-    if name == "tiles_kernel":
-        return {"bytes": (N + 1) * 4 * 2 + tiles * 16, "mfma_flops": 0, "valu_flops": 0}
+    if name == "bwd_setup_kernel":          # tile list + packed W_base^T (1 or 2 copies)
+        return {"bytes": d * d // 4 * (3 if d % 512 == 0 else 2) + (N + 1) * 4 * 2 + tiles * 16,
+                "mfma_flops": 0, "valu_flops": 0}
     if name == "gemm_t_kernel":
         return kernel_work("gemm_kernel", act_bytes, T, d, N, k)
     if name == "substrate_grad_gemm":
@@ -128,8 +126,8 @@ def backward_work(name, act_bytes, T, d, N, k):
         if name == "bfly_bwd_out_kernel":
             b += 2 * M * 4                   # gates in, dgates out
         return {"bytes": b, "mfma_flops": 0, "valu_flops": M * L * (d // 2) * 22}
-    if name.startswith("angle_reduce"):
-        return {"bytes": partial + A * 4, "mfma_flops": 0, "valu_flops": 0}
+    if name == "angle_reduce_kernel":       # both sides
+        return {"bytes": 2 * (partial + A * 4), "mfma_flops": 0, "valu_flops": 0}
     raise KeyError(name)
 
 

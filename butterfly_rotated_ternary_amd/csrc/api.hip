@@ -430,8 +430,8 @@ bmoe_status bmoe_backward_timed(bmoe_dtype dt, int T, int d, int n_experts, int 
   if (launch_prep(ids, M, n_experts, theta, phi, d, rt, cs_in, cs_out, status, w_packed, nullptr,
                   wt, l.wt_block, s, timing()) != hipSuccess)
     return BMOE_E_HIP;
-  if (launch_pack_transpose(w_packed, d, wpt, wtt, l.wt_block, s, timing()) != hipSuccess) return BMOE_E_HIP;
-  if (launch_tiles(rt.offsets, n_experts, d, tiles, tile_base, l.max_tiles, s, timing()) != hipSuccess)
+  if (launch_bwd_setup(rt.offsets, n_experts, d, tiles, tile_base, l.max_tiles, w_packed, wpt, wtt,
+                       l.wt_block, s, timing()) != hipSuccess)
     return BMOE_E_HIP;
   if (launch_bfly_in(dt, M, d, k, x, rt, cs_in, z, s, timing()) != hipSuccess) return BMOE_E_HIP;
   if (launch_gemm(dt, M, d, z, w_packed, wt, alpha, h, s, timing()) != hipSuccess) return BMOE_E_HIP;
@@ -454,9 +454,8 @@ bmoe_status bmoe_backward_timed(bmoe_dtype dt, int T, int d, int n_experts, int 
                       nullptr, part_in, s, timing()) != hipSuccess)
     return BMOE_E_HIP;
   if (launch_combine(dt, T, d, k, dxr, dx, s, timing()) != hipSuccess) return BMOE_E_HIP;
-  if (launch_angle_reduce(part_out, tile_base, n_experts, d, dphi, s, timing()) != hipSuccess)
-    return BMOE_E_HIP;
-  if (launch_angle_reduce(part_in, tile_base, n_experts, d, dtheta, s, timing()) != hipSuccess)
+  if (launch_angle_reduce(part_out, part_in, tile_base, n_experts, d, dphi, dtheta, s,
+                          timing()) != hipSuccess)
     return BMOE_E_HIP;
   return BMOE_OK;
 }
@@ -472,10 +471,9 @@ bmoe_status bmoe_backward(bmoe_dtype dt, int T, int d, int n_experts, int k, con
 
 namespace {
 const char* const kBackwardNames[] = {
-    "prep_kernel",      "pack_transpose_kernel", "tiles_kernel",         "bfly_in_kernel",
-    "gemm_kernel",      "bfly_bwd_out_kernel",   "substrate_grad_gemm",  "gemm_t_kernel",
-    "bfly_bwd_in_kernel", "combine_kernel",      "angle_reduce_out_kernel",
-    "angle_reduce_in_kernel"};
+    "prep_kernel",         "bwd_setup_kernel",    "bfly_in_kernel",     "gemm_kernel",
+    "bfly_bwd_out_kernel", "substrate_grad_gemm", "gemm_t_kernel",      "bfly_bwd_in_kernel",
+    "combine_kernel",      "angle_reduce_kernel"};
 constexpr int kBackwardLaunches = sizeof(kBackwardNames) / sizeof(kBackwardNames[0]);
 }  // namespace
 

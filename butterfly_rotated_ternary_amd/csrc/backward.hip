@@ -27,24 +27,32 @@ namespace {
 
 __device__ __forceinline__ int pad(int i) { return i + (i >> 3); }
 
-// ---- expert-aligned row tiles ------------------------------------------------
-// tiles[i] = (expert, first sorted row, end row, 0), at most tr rows each; tile_base[e] = first tile
-// of expert e, tile_base[N] = number of tiles. One workgroup.
-__global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* offsets, int N, int tr,
-                                                     int4* tiles, int32_t* tile_base,
-                                                     int max_tiles) {
-  __shared__ int scan[1024];
+// ---- backward setup: expert-aligned row tiles + packed W_base^T -------------
+// Block 0: tiles[i] = (expert, first sorted row, end row, 0), at most tr rows
+// each; tile_base[e] = first tile of expert e, tile_base[N] = number of
+// tiles; unused entries get expert -1.
+// Blocks 1..: one thread per word of W^T: row c, columns o = 16 g .. 16 g + 15
+// (the codes W[o][c]), written row-major (wpt) and, when cb > 0, into the
+// tile-major copy the large-tile GEMM reads (wtt: 4-word K-steps of 64
+// columns, cb rows each).
+__device__ __forceinline__ int code_pos(int v) { return (v & 1) ? 16 + 2 * (v >> 1) : 2 * (v >> 1); }
+
+constexpr int kSetupThreads = 256;
+
+__device__ void tiles_role(const int32_t* offsets, int N, int tr, int4* tiles, int32_t* tile_base,
+                           int max_tiles) {
+  __shared__ int scan[kSetupThreads];
   __shared__ int carry;
   const int tid = threadIdx.x;
   if (tid == 0) carry = 0;
   __syncthreads();
-  for (int e0 = 0; e0 < N; e0 += 1024) {
+  for (int e0 = 0; e0 < N; e0 += kSetupThreads) {
     const int e = e0 + tid;
     const int cnt = e < N ? offsets[e + 1] - offsets[e] : 0;
     const int nt = (cnt + tr - 1) / tr;
     scan[tid] = nt;
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
+    for (int off = 1; off < kSetupThreads; off <<= 1) {
       const int v = tid >= off ? scan[tid - off] : 0;
       __syncthreads();
       scan[tid] += v;
@@ -58,26 +66,25 @@ __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* offsets, int
         tiles[base + i] = make_int4(e, q0 + i * tr, min(q0 + (i + 1) * tr, q0 + cnt), 0);
     }
     __syncthreads();
-    if (tid == 1023) carry += scan[1023];
+    if (tid == kSetupThreads - 1) carry += scan[kSetupThreads - 1];
     __syncthreads();
   }
   const int total = carry;
   if (tid == 0) tile_base[N] = total;
-  for (int i = total + tid; i < max_tiles; i += 1024) tiles[i] = make_int4(-1, 0, 0, 0);
+  for (int i = total + tid; i < max_tiles; i += kSetupThreads) tiles[i] = make_int4(-1, 0, 0, 0);
 }
 
-// ---- packed W_base^T ---------------------------------------------------------
-// One thread per word of W^T: row c, columns o = 16 g .. 16 g + 15 (the codes
-// W[o][c]), written row-major (wpt) and, when cb > 0, into the tile-major copy
-// the large-tile GEMM reads (wtt: 4-word K-steps of 64 columns, cb rows each).
-__device__ __forceinline__ int code_pos(int v) { return (v & 1) ? 16 + 2 * (v >> 1) : 2 * (v >> 1); }
-
-__global__ __launch_bounds__(256) void pack_transpose_kernel(const uint32_t* wp, int d,
-                                                             uint32_t* wpt, uint32_t* wtt,
-                                                             int cb) {
+__global__ __launch_bounds__(kSetupThreads) void bwd_setup_kernel(
+    const int32_t* offsets, int N, int tr, int4* tiles, int32_t* tile_base, int max_tiles,
+    const uint32_t* wp, int d, uint32_t* wpt, uint32_t* wtt, int cb) {
+  if (blockIdx.x == 0) {
+    tiles_role(offsets, N, tr, tiles, tile_base, max_tiles);
+    return;
+  }
   const int G = d / 16;
   const size_t n = (size_t)d * G;
-  for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < n; u += (size_t)gridDim.x * 256) {
+  for (size_t u = (size_t)(blockIdx.x - 1) * kSetupThreads + threadIdx.x; u < n;
+       u += (size_t)(gridDim.x - 1) * kSetupThreads) {
     const int c = (int)(u / G), g = (int)(u % G);
     const int cw = c / 16, cpos = code_pos(c % 16);
     uint32_t out = 0u;
@@ -408,16 +415,24 @@ __global__ __launch_bounds__(BwdCfg<D>::NTHR) void bfly_bwd_kernel(BwdParams p) 
   write_partials<D>(V, p.partial + (size_t)blockIdx.x * L * (D / 2), tid, acc);
 }
 
-// dA[e][s][p] = sum of expert e's tile partials, in tile order (0 if no rows).
-__global__ __launch_bounds__(256) void angle_reduce_kernel(const float* partial,
+// dA[e][s][p] = sum of expert e's tile partials, in tile order (0 if no rows),
+// for both sides in one launch: indices below N * per_expert reduce the
+// output side into out0, the rest the input side into out1.
+__global__ __launch_bounds__(256) void angle_reduce_kernel(const float* partial0,
+                                                           const float* partial1,
                                                            const int32_t* tile_base, int N,
-                                                           int per_expert, float* out) {
+                                                           int per_expert, float* out0,
+                                                           float* out1) {
   const size_t n = (size_t)N * per_expert;
-  for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < n; u += (size_t)gridDim.x * 256) {
+  for (size_t v = (size_t)blockIdx.x * 256 + threadIdx.x; v < 2 * n;
+       v += (size_t)gridDim.x * 256) {
+    const bool second = v >= n;
+    const size_t u = second ? v - n : v;
+    const float* partial = second ? partial1 : partial0;
     const int e = (int)(u / per_expert), off = (int)(u % per_expert);
     float s = 0.f;
     for (int t = tile_base[e]; t < tile_base[e + 1]; ++t) s += partial[(size_t)t * per_expert + off];
-    out[u] = s;
+    (second ? out1 : out0)[u] = s;
   }
 }
 
@@ -478,16 +493,12 @@ int bwd_max_tiles(int M, int N, int d) {
   return (M + tr - 1) / tr + N;
 }
 
-hipError_t launch_tiles(const int32_t* offsets, int N, int d, int4* tiles, int32_t* tile_base,
-                        int max_tiles, hipStream_t s, const KernelTiming& t) {
-  return launch_kernel(tiles_kernel, dim3(1), dim3(1024), 0, s, t, offsets, N, bwd_tile_rows(d),
-                       tiles, tile_base, max_tiles);
-}
-
-hipError_t launch_pack_transpose(const uint32_t* wp, int d, uint32_t* wpt, uint32_t* wtt, int cb,
-                                 hipStream_t s, const KernelTiming& t) {
-  return launch_kernel(pack_transpose_kernel, dim3(grid_for((size_t)d * (d / 16))), dim3(256), 0,
-                       s, t, wp, d, wpt, wtt, cb);
+hipError_t launch_bwd_setup(const int32_t* offsets, int N, int d, int4* tiles,
+                           int32_t* tile_base, int max_tiles, const uint32_t* wp, uint32_t* wpt,
+                           uint32_t* wtt, int cb, hipStream_t s, const KernelTiming& t) {
+  return launch_kernel(bwd_setup_kernel, dim3(1 + grid_for((size_t)d * (d / 16))),
+                       dim3(kSetupThreads), 0, s, t, offsets, N, bwd_tile_rows(d), tiles,
+                       tile_base, max_tiles, wp, d, wpt, wtt, cb);
 }
 
 hipError_t launch_bfly_bwd(bool in_side, bmoe_dtype dt, int M, int d, int k, const int4* tiles,
@@ -517,13 +528,14 @@ hipError_t launch_sum_slices(const float* part, int S, size_t n, float* out, hip
                        reinterpret_cast<float4*>(out));
 }
 
-hipError_t launch_angle_reduce(const float* partial, const int32_t* tile_base, int N, int d,
-                               float* out, hipStream_t s, const KernelTiming& t) {
+hipError_t launch_angle_reduce(const float* partial_out, const float* partial_in,
+                               const int32_t* tile_base, int N, int d, float* dphi, float* dtheta,
+                               hipStream_t s, const KernelTiming& t) {
   int L = 0;
   while ((1 << L) < d) ++L;
   const int per = L * (d / 2);
-  return launch_kernel(angle_reduce_kernel, dim3(grid_for((size_t)N * per)), dim3(256), 0, s,
-                       t, partial, tile_base, N, per, out);
+  return launch_kernel(angle_reduce_kernel, dim3(grid_for(2 * (size_t)N * per)), dim3(256), 0, s,
+                       t, partial_out, partial_in, tile_base, N, per, dphi, dtheta);
 }
 
 }  // namespace bmoe

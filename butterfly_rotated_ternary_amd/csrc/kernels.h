@@ -90,15 +90,14 @@ hipError_t launch_pack(const int8_t* w, int d, uint32_t* packed, int32_t* status
 // ---- backward ----------------------------------------------------------------
 // Upper bound on the expert-aligned row tiles of the backward kernels.
 int bwd_max_tiles(int M, int N, int d);
-// Tile list from the routing offsets: tiles[i] = (expert, q0, q1, 0) with at
-// most a d-dependent number of sorted rows each; tile_base[e] = first tile of expert e,
-// tile_base[N] = count; unused entries have expert -1.
-hipError_t launch_tiles(const int32_t* offsets, int N, int d, int4* tiles, int32_t* tile_base,
-                        int max_tiles, hipStream_t s, const KernelTiming& t = {});
-// Packed W_base^T (row c holds the codes of column c), row-major into wpt and,
-// when cb > 0, also in the large-tile GEMM's tile-major order into wtt.
-hipError_t launch_pack_transpose(const uint32_t* wp, int d, uint32_t* wpt, uint32_t* wtt, int cb,
-                                 hipStream_t s, const KernelTiming& t = {});
+// One launch: the tile list from the routing offsets (tiles[i] = (expert, q0,
+// q1, 0) with at most a d-dependent number of sorted rows each; tile_base[e] =
+// first tile of expert e, tile_base[N] = count; unused entries have expert
+// -1), and packed W_base^T (row c holds the codes of column c) row-major into
+// wpt and, when cb > 0, in the large-tile GEMM's tile-major order into wtt.
+hipError_t launch_bwd_setup(const int32_t* offsets, int N, int d, int4* tiles,
+                           int32_t* tile_base, int max_tiles, const uint32_t* wp, uint32_t* wpt,
+                           uint32_t* wtt, int cb, hipStream_t s, const KernelTiming& t = {});
 // Butterfly backward over the tiles. Output side (in_side = false): src = H
 // (sorted), grad = dy (token rows) -> dst = dH (sorted), dgates, partials of
 // dphi. Input side: src = x (token rows), grad = dZ (sorted) -> dst = dX
@@ -109,9 +108,11 @@ hipError_t launch_bfly_bwd(bool in_side, bmoe_dtype dt, int M, int d, int k, con
                            float* dgates, float* partial, hipStream_t s, const KernelTiming& t = {});
 // out[i] = sum over b < S of part[b * n + i], in order of b (n % 4 == 0).
 hipError_t launch_sum_slices(const float* part, int S, size_t n, float* out, hipStream_t s);
-// out[e][s][p] = sum over expert e's tiles of partial[tile][s][p], in tile order.
-hipError_t launch_angle_reduce(const float* partial, const int32_t* tile_base, int N, int d,
-                               float* out, hipStream_t s, const KernelTiming& t = {});
+// dphi / dtheta [N][L][d/2] = sums over each expert's tiles of the output /
+// input side partials [tiles][L][d/2], in tile order (one launch).
+hipError_t launch_angle_reduce(const float* partial_out, const float* partial_in,
+                               const int32_t* tile_base, int N, int d, float* dphi, float* dtheta,
+                               hipStream_t s, const KernelTiming& t = {});
 
 // ---- outlier measurement ---------------------------------------------------------
 // Per row of src [rows][d] (dtype dt): err = ||v - q|| / ||v|| with
