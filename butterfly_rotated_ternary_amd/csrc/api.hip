@@ -155,8 +155,13 @@ bmoe_status substrate_grad(bmoe_dtype dt, int M, int d, const void* dh, const vo
   static std::once_flag once;
   static rocblas_handle handle = nullptr;
   static rocblas_status created = rocblas_status_internal_error;
+  // One handle for the process: the stream it is bound to and the GEMMs
+  // enqueued on it are set under one lock, so concurrent callers on other
+  // streams cannot interleave (only host-side enqueueing is serialised).
+  static std::mutex mu;
   std::call_once(once, [] { created = rocblas_create_handle(&handle); });
   if (created != rocblas_status_success) return BMOE_E_HIP;
+  std::lock_guard<std::mutex> lock(mu);
   if (rocblas_set_stream(handle, s) != rocblas_status_success) return BMOE_E_HIP;
   const float beta = 0.f;
   const rocblas_datatype at = dt == BMOE_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
