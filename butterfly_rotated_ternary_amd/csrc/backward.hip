@@ -215,7 +215,52 @@ __device__ __forceinline__ void run_group(float* V, float* Gs, int nr, int tid,
     int off[8];
 #pragma unroll
     for (int m = 0; m < (1 << G); ++m) off[m] = pad(base + (m << (3 * g)));
-    for (int i = ph; i < nr; i += TPB) {
+    // Two rows at a time (loads of both in flight before either is rotated),
+    // then the odd row out.
+    int i = ph;
+    for (; i + TPB < nr; i += 2 * TPB) {
+      float* vr0 = V + i * C::PD;
+      float* vr1 = V + (i + TPB) * C::PD;
+      float v0[8], v1[8];
+#pragma unroll
+      for (int m = 0; m < (1 << G); ++m) {
+        v0[m] = vr0[off[m]];
+        v1[m] = vr1[off[m]];
+      }
+      if (BWD) {
+        float* gp0 = Gs + i * C::PD;
+        float* gp1 = Gs + (i + TPB) * C::PD;
+        float g0[8], g1[8];
+#pragma unroll
+        for (int m = 0; m < (1 << G); ++m) {
+          g0[m] = gp0[off[m]];
+          g1[m] = gp1[off[m]];
+        }
+        bwd_block<G, IN_SIDE>(v0, g0, cf[g][sl], acc[g][sl]);
+        bwd_block<G, IN_SIDE>(v1, g1, cf[g][sl], acc[g][sl]);
+#pragma unroll
+        for (int m = 0; m < (1 << G); ++m) {
+          gp0[off[m]] = g0[m];
+          gp1[off[m]] = g1[m];
+        }
+        if (keep_v) {
+#pragma unroll
+          for (int m = 0; m < (1 << G); ++m) {
+            vr0[off[m]] = v0[m];
+            vr1[off[m]] = v1[m];
+          }
+        }
+      } else {
+        fwd_block<G, IN_SIDE>(v0, cf[g][sl]);
+        fwd_block<G, IN_SIDE>(v1, cf[g][sl]);
+#pragma unroll
+        for (int m = 0; m < (1 << G); ++m) {
+          vr0[off[m]] = v0[m];
+          vr1[off[m]] = v1[m];
+        }
+      }
+    }
+    if (i < nr) {
       float* vr = V + i * C::PD;
       float v[8];
 #pragma unroll
