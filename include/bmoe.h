@@ -174,9 +174,10 @@ bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k
                                void* ws, size_t ws_bytes, int32_t* route_out, void* stream,
                                void* const* events);
 
-/* Wait for `stream`, then return the device-side status of the last forward
- * or pack that used `ws` (BMOE_OK, BMOE_E_EXPERT or BMOE_E_TERNARY), or
- * BMOE_E_HIP if the wait itself failed. */
+/* Wait for `stream`, then return the device-side status of the last call
+ * that used `ws` (bmoe_forward, bmoe_backward, bmoe_rotate_in, or a pack or
+ * base-3 unpack): BMOE_OK, BMOE_E_EXPERT or BMOE_E_TERNARY, or BMOE_E_HIP if
+ * the wait itself failed. */
 bmoe_status bmoe_sync_status(const void* ws, void* stream);
 
 /* Workspace bytes bmoe_backward needs for this shape (0 if the shape is not
@@ -201,8 +202,9 @@ size_t bmoe_backward_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts,
  * dphi are summed per expert in a fixed order (run-to-run bit-identical). The
  * dw product is a plain library GEMM (rocBLAS; for d < 2048 split into row
  * ranges whose fp32 products are summed in a fixed order): the first call
- * with dw != NULL creates a rocBLAS handle kept for the life of the process. ws: at least
- * bmoe_backward_workspace_bytes(), 16-byte aligned. Errors as bmoe_forward.
+ * with dw != NULL creates a rocBLAS handle kept for the life of the process.
+ * ws: at least bmoe_backward_workspace_bytes(), 16-byte aligned. Errors as
+ * bmoe_forward.
  */
 bmoe_status bmoe_backward(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
                           const int32_t* ids, const float* gates, const float* theta,
