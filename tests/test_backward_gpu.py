@@ -31,9 +31,13 @@ def _global_err(a, ref):
 
 
 def _run(name, T, seed=11, **override):
-    inp = W.make_inputs(name, T=T, **override)
+    return _check_case(W.make_inputs(name, T=T, **override), seed)
+
+
+def _check_case(inp, seed):
+    name = inp.name
     dy, dy_bits = _dy(inp, seed)
-    print(f"[backward] {name} T={inp.T} d={inp.d} N={inp.N} k={inp.k} {override}", flush=True)
+    print(f"[backward] {name} T={inp.T} d={inp.d} N={inp.N} k={inp.k}", flush=True)
     dev = to_device(inp)
     if inp.dtype == "bf16":
         dyt = torch.from_numpy(dy_bits.view(np.int16)).view(torch.bfloat16).cuda()
@@ -130,3 +134,35 @@ def test_timed_backward_matches_untimed():
         hip.hipEventDestroy(ctypes.c_void_p(e))
     for key in ("dx", "dgates", "dtheta", "dphi", "dw"):
         assert torch.equal(a[key], b[key]), key
+
+
+def test_backward_one_expert_takes_every_row():
+    inp = W.make_inputs("d512_e64_top2_bf16", T=333)
+    inp.ids[:, 0] = 5                       # every token's first pick is expert 5
+    inp.ids[:, 1] = np.where(inp.ids[:, 1] == 5, 6, inp.ids[:, 1])
+    _check_case(inp, seed=21)
+
+
+def test_backward_many_empty_experts():
+    # 4096 experts, 9 tokens: almost every expert has no rows (zero angle gradients)
+    inp = W.make_inputs("tiny_d64_e8_top2_f32", T=9, d=128, N=4096, k=3, dtype="bf16", seed=5)
+    got = _check_case(inp, seed=22)
+    used = np.unique(inp.ids)
+    unused = np.setdiff1d(np.arange(4096), used)
+    assert np.all(got["dtheta"][unused] == 0.0) and np.all(got["dphi"][unused] == 0.0)
+
+
+def test_backward_single_token_all_experts():
+    inp = W.make_inputs("tiny_d64_e8_top2_f32", T=1, d=4096, N=3, k=3, dtype="bf16", seed=6)
+    _check_case(inp, seed=23)
+
+
+def test_backward_empty_batch_is_a_noop():
+    dev = torch.device("cuda")
+    x = torch.empty(0, 256, dtype=torch.bfloat16, device=dev)
+    g = bmoe.backward(x, torch.empty(0, 2, dtype=torch.int32, device=dev),
+                      torch.empty(0, 2, device=dev), torch.zeros(4, 8, 128, device=dev),
+                      torch.zeros(4, 8, 128, device=dev),
+                      bmoe.pack_ternary(torch.zeros(256, 256, dtype=torch.int8, device=dev)),
+                      1.0, torch.empty(0, 256, dtype=torch.bfloat16, device=dev))
+    assert g["dx"].shape == (0, 256)
