@@ -440,6 +440,49 @@ class Problem:
             hip.destroy(evs)
         return r_ms, rf_ms, per
 
+    def time_training_step(self, steps, warmup):
+        """Per-step ms of forward + backward (the backward recomputes the
+        forward) and of keep-forward + kept backward, and of the kept
+        backward alone."""
+        import torch
+        b = self.bmoe
+        kept = torch.empty(b.bmoe_forward_keep_workspace_bytes(self.dt, self.T, self.d, self.N,
+                                                               self.k),
+                           dtype=torch.uint8, device=self.x.device)
+        g = self.g
+        fwd_keep = (self.dt, self.T, self.d, self.N, self.k, self.x, self.ids, self.gates,
+                    self.theta, self.phi, self.wp, self.alpha, self.y, kept, self.stream)
+        bwd_kept = (self.dt, self.T, self.d, self.N, self.k, self.x, self.gates, self.wp,
+                    self.alpha, self.dy, g["dx"], g["dgates"], g["dtheta"], g["dphi"], g["dw"],
+                    kept, self.bws, self.stream)
+
+        def run(fn, n):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(n):
+                fn()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t0) * 1e3 / n
+
+        def recompute():
+            if b.bmoe_forward(*self.args()) != 0 or b.bmoe_backward(*self.backward_args()) != 0:
+                raise RuntimeError("forward/backward failed")
+
+        def kept_step():
+            if b.bmoe_forward_keep(*fwd_keep) != 0 or b.bmoe_backward_kept(*bwd_kept) != 0:
+                raise RuntimeError("kept forward/backward failed")
+
+        def kept_bwd():
+            if b.bmoe_backward_kept(*bwd_kept) != 0:
+                raise RuntimeError("kept backward failed")
+
+        out = {"recompute_ms": run(recompute, steps), "kept_ms": run(kept_step, steps)}
+        out["kept_backward_ms"] = run(kept_bwd, steps)
+        del kept
+        return out
+
     def mfma_peak(self):
         return PEAK_BF16_TFLOPS if self.dt == self.bmoe.BMOE_BF16 else PEAK_FP32_MFMA_TFLOPS
 
@@ -460,8 +503,12 @@ def backward_section(P, steps):
         kern[n] = {"us": v * 1e3, "bound": r["bound"], "frac": r["frac"]}
     log(f"[bench] backward {P.name}: {ms * 1e3:.1f} us/step; "
         + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in per.items()))
+    train = P.time_training_step(steps, max(3, steps // 10))
+    log(f"[bench] training step {P.name}: forward + backward {train['recompute_ms'] * 1e3:.1f} us; "
+        f"keep-forward + kept backward {train['kept_ms'] * 1e3:.1f} us "
+        f"(kept backward alone {train['kept_backward_ms'] * 1e3:.1f} us)")
     return {"workload": P.name, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
-            "steps": steps, "roofline": roof, "kernels": kern}
+            "steps": steps, "roofline": roof, "kernels": kern, "training_step": train}
 
 
 def router_section(P, steps):

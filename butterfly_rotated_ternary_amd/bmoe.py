@@ -78,6 +78,16 @@ def lib():
         L.bmoe_backward.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp,
                                     c_f, vp, vp, vp, vp, vp, vp, vp, c_sz, vp]
         L.bmoe_backward.restype = c_int
+        L.bmoe_forward_keep_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
+        L.bmoe_forward_keep_workspace_bytes.restype = c_sz
+        L.bmoe_forward_keep.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp,
+                                        vp, c_f, vp, vp, c_sz, vp]
+        L.bmoe_forward_keep.restype = c_int
+        L.bmoe_backward_kept.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, c_f, vp,
+                                         vp, vp, vp, vp, vp, vp, c_sz, vp, c_sz, vp]
+        L.bmoe_backward_kept.restype = c_int
+        L.bmoe_backward_kept_timed.argtypes = L.bmoe_backward_kept.argtypes + [vp]
+        L.bmoe_backward_kept_timed.restype = c_int
         L.bmoe_rotate_in_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
         L.bmoe_rotate_in_workspace_bytes.restype = c_sz
         L.bmoe_rotate_in.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, c_sz,
@@ -235,6 +245,41 @@ def bmoe_backward_kernel_count(dt: int, T: int, d: int, n_experts: int, k: int) 
 
 def bmoe_backward_kernel_name(dt: int, T: int, d: int, n_experts: int, k: int, i: int) -> str:
     return lib().bmoe_backward_kernel_name(dt, T, d, n_experts, k, i).decode()
+
+
+def bmoe_forward_keep_workspace_bytes(dt: int, T: int, d: int, n_experts: int, k: int) -> int:
+    return lib().bmoe_forward_keep_workspace_bytes(dt, T, d, n_experts, k)
+
+
+def bmoe_forward_keep(dt: int, T: int, d: int, n_experts: int, k: int, x, ids, gates, theta, phi,
+                      w_packed, alpha: float, y, ws, stream=None) -> int:
+    return lib().bmoe_forward_keep(dt, T, d, n_experts, k, _ptr(x), _ptr(ids), _ptr(gates),
+                                   _ptr(theta), _ptr(phi), _ptr(w_packed), float(alpha), _ptr(y),
+                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+
+
+def bmoe_backward_kept(dt: int, T: int, d: int, n_experts: int, k: int, x, gates, w_packed,
+                       alpha: float, dy, dx, dgates, dtheta, dphi, dw, fwd_ws, ws,
+                       stream=None) -> int:
+    return lib().bmoe_backward_kept(dt, T, d, n_experts, k, _ptr(x), _ptr(gates),
+                                    _ptr(w_packed), float(alpha), _ptr(dy), _ptr(dx),
+                                    _ptr(dgates), _ptr(dtheta), _ptr(dphi), _ptr(dw),
+                                    _ptr(fwd_ws), fwd_ws.numel() * fwd_ws.element_size(),
+                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+
+
+def bmoe_backward_kept_timed(dt: int, T: int, d: int, n_experts: int, k: int, x, gates,
+                             w_packed, alpha: float, dy, dx, dgates, dtheta, dphi, dw, fwd_ws,
+                             ws, stream=None, events=None) -> int:
+    ev = None
+    if events is not None:
+        ev = (ctypes.c_void_p * len(events))(*events)
+    return lib().bmoe_backward_kept_timed(dt, T, d, n_experts, k, _ptr(x), _ptr(gates),
+                                          _ptr(w_packed), float(alpha), _ptr(dy), _ptr(dx),
+                                          _ptr(dgates), _ptr(dtheta), _ptr(dphi), _ptr(dw),
+                                          _ptr(fwd_ws), fwd_ws.numel() * fwd_ws.element_size(),
+                                          _ptr(ws), ws.numel() * ws.element_size(),
+                                          _stream(stream), ev)
 
 
 def bmoe_rotate_in_workspace_bytes(dt: int, T: int, d: int, n_experts: int, k: int) -> int:
@@ -422,3 +467,49 @@ def quant_error(v: torch.Tensor, m: int, mode: int = 0):
     crest = torch.empty(rows, dtype=torch.float32, device=v.device)
     _check(bmoe_quant_error(dtype_code(v), rows, d, v, m, mode, err, crest), "bmoe_quant_error")
     return err, crest
+
+
+def forward_keep(x: torch.Tensor, ids: torch.Tensor, gates: torch.Tensor, theta: torch.Tensor,
+                 phi: torch.Tensor, w_packed: torch.Tensor, alpha: float, stream=None):
+    """(y, kept workspace): the forward on the unfused path, with its routing
+    tables, cos/sin tables, Z and H left in the returned workspace for
+    backward_kept."""
+    T, d = x.shape
+    k = ids.shape[1]
+    N = theta.shape[0]
+    dt = dtype_code(x)
+    n = bmoe_forward_keep_workspace_bytes(dt, T, d, N, k)
+    if n == 0:
+        raise BmoeError(2, "bmoe_forward_keep_workspace_bytes")
+    ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+    y = torch.empty_like(x)
+    _check(bmoe_forward_keep(dt, T, d, N, k, x, ids, gates, theta, phi, w_packed, alpha, y, ws,
+                             stream), "bmoe_forward_keep")
+    return y, ws
+
+
+def backward_kept(x: torch.Tensor, gates: torch.Tensor, n_experts: int, w_packed: torch.Tensor,
+                  alpha: float, dy: torch.Tensor, kept: torch.Tensor, *, want_dw: bool = True,
+                  stream=None) -> dict:
+    """As backward(), reading the forward's intermediates from forward_keep's
+    workspace instead of recomputing them."""
+    T, d = x.shape
+    k = gates.shape[1]
+    N = n_experts
+    dt = dtype_code(x)
+    L = int(d).bit_length() - 1
+    n = bmoe_backward_workspace_bytes(dt, T, d, N, k)
+    if n == 0:
+        raise BmoeError(2, "bmoe_backward_workspace_bytes")
+    ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+    out = {
+        "dx": torch.empty_like(x),
+        "dgates": torch.empty(T, k, dtype=torch.float32, device=x.device),
+        "dtheta": torch.empty(N, L, d // 2, dtype=torch.float32, device=x.device),
+        "dphi": torch.empty(N, L, d // 2, dtype=torch.float32, device=x.device),
+        "dw": torch.empty(d, d, dtype=torch.float32, device=x.device) if want_dw else None,
+    }
+    _check(bmoe_backward_kept(dt, T, d, N, k, x, gates, w_packed, alpha, dy, out["dx"],
+                              out["dgates"], out["dtheta"], out["dphi"], out["dw"], kept, ws,
+                              stream), "bmoe_backward_kept")
+    return out

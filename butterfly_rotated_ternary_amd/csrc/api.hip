@@ -36,7 +36,9 @@ bool shape_ok(bmoe_dtype dt, int T, int d, int N, int k) {
   return true;
 }
 
-FwdLayout fwd_layout(bmoe_dtype dt, int T, int d, int N, int k) {
+// keep: the unfused path, with Z and H left in the workspace (with the
+// routing and cos/sin tables) for a later bmoe_backward_kept.
+FwdLayout fwd_layout(bmoe_dtype dt, int T, int d, int N, int k, bool keep = false) {
   FwdLayout l{};
   const size_t M = (size_t)T * k;
   const size_t L = (size_t)log2i(d);
@@ -49,7 +51,7 @@ FwdLayout fwd_layout(bmoe_dtype dt, int T, int d, int N, int k) {
   l.slot_e = off;  off = align_up(off + sizeof(int32_t) * M);
   l.cs_in = off;   off = align_up(off + sizeof(float2) * N * L * (d / 2));
   l.cs_out = off;  off = align_up(off + sizeof(float2) * N * L * (d / 2));
-  const bool fused = fused_supported(dt, d);
+  const bool fused = !keep && fused_supported(dt, d);
   // The fused path keeps Z and H on chip; only U (and the bf16 substrate)
   // live in the workspace.
   l.z = off;       if (!fused) off = align_up(off + zel * M * d);
@@ -270,16 +272,17 @@ bmoe_status bmoe_unpack_ternary_b3(const uint8_t* packed3, int d, uint32_t* pack
   return bmoe_unpack_ternary_b3_timed(packed3, d, packed, ws, ws_bytes, stream, nullptr);
 }
 
-bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
-                               const int32_t* ids, const float* gates, const float* theta,
-                               const float* phi, const uint32_t* w_packed, float alpha, void* y,
-                               void* ws, size_t ws_bytes, int32_t* route_out, void* stream,
-                               void* const* events) {
+namespace {
+bmoe_status forward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
+                         const int32_t* ids, const float* gates, const float* theta,
+                         const float* phi, const uint32_t* w_packed, float alpha, void* y,
+                         void* ws, size_t ws_bytes, int32_t* route_out, void* stream,
+                         void* const* events, bool keep) {
   if (dt != BMOE_F32 && dt != BMOE_BF16) return BMOE_E_DTYPE;
   if (!shape_ok(dt, T, d, n_experts, k)) return BMOE_E_SHAPE;
   if (T == 0) return BMOE_OK;
   if (!x || !ids || !gates || !theta || !phi || !w_packed || !y) return BMOE_E_NULL;
-  const FwdLayout l = fwd_layout(dt, T, d, n_experts, k);
+  const FwdLayout l = fwd_layout(dt, T, d, n_experts, k, keep);
   if (!ws || ws_bytes < l.total) return BMOE_E_WORKSPACE;
   const void* ptrs[] = {x, ids, gates, theta, phi, w_packed, y, ws};
   for (const void* p : ptrs)
@@ -318,7 +321,7 @@ bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k
     }
     return t;
   };
-  const bool fused = fused_supported(dt, d);
+  const bool fused = !keep && fused_supported(dt, d);
   uint16_t* w16 = fused ? reinterpret_cast<uint16_t*>(base + l.w16) : nullptr;
   const int wt_block = gemm_tiled_w_block(dt, M, d);
   uint32_t* wt = wt_block ? reinterpret_cast<uint32_t*>(base + l.wt) : nullptr;
@@ -339,6 +342,29 @@ bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k
   }
   if (launch_combine(dt, T, d, k, u, y, s, timing()) != hipSuccess) return BMOE_E_HIP;
   return BMOE_OK;
+}
+}  // namespace
+
+bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
+                               const int32_t* ids, const float* gates, const float* theta,
+                               const float* phi, const uint32_t* w_packed, float alpha, void* y,
+                               void* ws, size_t ws_bytes, int32_t* route_out, void* stream,
+                               void* const* events) {
+  return forward_impl(dt, T, d, n_experts, k, x, ids, gates, theta, phi, w_packed, alpha, y, ws,
+                      ws_bytes, route_out, stream, events, false);
+}
+
+size_t bmoe_forward_keep_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts, int k) {
+  if (!shape_ok(dt, T, d, n_experts, k)) return 0;
+  return fwd_layout(dt, T, d, n_experts, k, true).total;
+}
+
+bmoe_status bmoe_forward_keep(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
+                              const int32_t* ids, const float* gates, const float* theta,
+                              const float* phi, const uint32_t* w_packed, float alpha, void* y,
+                              void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(dt, T, d, n_experts, k, x, ids, gates, theta, phi, w_packed, alpha, y, ws,
+                      ws_bytes, nullptr, stream, nullptr, true);
 }
 
 bmoe_status bmoe_forward(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
@@ -378,37 +404,53 @@ size_t bmoe_backward_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts,
   return bwd_layout(dt, T, d, n_experts, k).total;
 }
 
-bmoe_status bmoe_backward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k,
-                                const void* x, const int32_t* ids, const float* gates,
-                                const float* theta, const float* phi, const uint32_t* w_packed,
-                                float alpha, const void* dy, void* dx, float* dgates,
-                                float* dtheta, float* dphi, float* dw, void* ws, size_t ws_bytes,
-                                void* stream, void* const* events) {
+namespace {
+// kept: the workspace of a bmoe_forward_keep call (routing and cos/sin
+// tables, Z and H are read from it and not recomputed), or NULL.
+bmoe_status backward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
+                          const int32_t* ids, const float* gates, const float* theta,
+                          const float* phi, const uint32_t* w_packed, float alpha,
+                          const void* dy, void* dx, float* dgates, float* dtheta, float* dphi,
+                          float* dw, const void* kept, size_t kept_bytes, void* ws,
+                          size_t ws_bytes, void* stream, void* const* events) {
   if (dt != BMOE_F32 && dt != BMOE_BF16) return BMOE_E_DTYPE;
   if (!bwd_shape_ok(dt, T, d, n_experts, k)) return BMOE_E_SHAPE;
   if (T == 0) return BMOE_OK;
-  if (!x || !ids || !gates || !theta || !phi || !w_packed || !dy || !dx || !dgates || !dtheta ||
-      !dphi)
-    return BMOE_E_NULL;
+  if (!x || !gates || !w_packed || !dy || !dx || !dgates || !dtheta || !dphi) return BMOE_E_NULL;
+  if (!kept && (!ids || !theta || !phi)) return BMOE_E_NULL;
   const BwdLayout l = bwd_layout(dt, T, d, n_experts, k);
   if (!ws || ws_bytes < l.total) return BMOE_E_WORKSPACE;
-  const void* ptrs[] = {x, ids, gates, theta, phi, w_packed, dy, dx, dgates, dtheta, dphi, ws};
+  const FwdLayout fl = fwd_layout(dt, T, d, n_experts, k, true);
+  if (kept && kept_bytes < fl.total) return BMOE_E_WORKSPACE;
+  const void* ptrs[] = {x, gates, w_packed, dy, dx, dgates, dtheta, dphi, ws};
   for (const void* p : ptrs)
     if (!aligned16(p)) return BMOE_E_ALIGN;
-  if (dw && !aligned16(dw)) return BMOE_E_ALIGN;
+  if (!kept) {
+    const void* rec[] = {ids, theta, phi};
+    for (const void* p : rec)
+      if (!aligned16(p)) return BMOE_E_ALIGN;
+  }
+  if ((dw && !aligned16(dw)) || (kept && !aligned16(kept))) return BMOE_E_ALIGN;
 
   char* base = static_cast<char*>(ws);
+  // Tables, Z and H: this workspace (recomputed below) or the kept forward's.
+  char* src = kept ? const_cast<char*>(static_cast<const char*>(kept)) : base;
+  const size_t o_off = kept ? fl.offsets : l.offsets, o_perm = kept ? fl.perm : l.perm;
+  const size_t o_inv = kept ? fl.inv : l.inv, o_slot = kept ? fl.slot_e : l.slot_e;
+  const size_t o_csi = kept ? fl.cs_in : l.cs_in, o_cso = kept ? fl.cs_out : l.cs_out;
+  const size_t o_z = kept ? fl.z : l.z, o_h = kept ? fl.h : l.h;
   const int M = T * k;
   RouteTables rt;
-  rt.offsets = reinterpret_cast<int32_t*>(base + l.offsets);
-  rt.perm = reinterpret_cast<int32_t*>(base + l.perm);
-  rt.inv = reinterpret_cast<int32_t*>(base + l.inv);
-  rt.slot_e = reinterpret_cast<int32_t*>(base + l.slot_e);
+  rt.offsets = reinterpret_cast<int32_t*>(src + o_off);
+  rt.perm = reinterpret_cast<int32_t*>(src + o_perm);
+  rt.inv = reinterpret_cast<int32_t*>(src + o_inv);
+  rt.slot_e = reinterpret_cast<int32_t*>(src + o_slot);
   int32_t* status = reinterpret_cast<int32_t*>(base + l.status);
-  float2* cs_in = reinterpret_cast<float2*>(base + l.cs_in);
-  float2* cs_out = reinterpret_cast<float2*>(base + l.cs_out);
-  void* z = base + l.z;
-  void* h = base + l.h;
+  float2* cs_in = reinterpret_cast<float2*>(src + o_csi);
+  float2* cs_out = reinterpret_cast<float2*>(src + o_cso);
+  void* z = src + o_z;
+  void* h = src + o_h;
+  void* dz = base + l.h;  // dZ: this workspace's H region (the kept H stays intact)
   void* dh = base + l.dh;
   void* dxr = base + l.dx;
   uint32_t* wt = l.wt_block ? reinterpret_cast<uint32_t*>(base + l.wt) : nullptr;
@@ -431,15 +473,31 @@ bmoe_status bmoe_backward_timed(bmoe_dtype dt, int T, int d, int n_experts, int 
     return t;
   };
 
+  // An empty timing slot for a launch the kept forward already did.
+  auto skip = [&]() -> bool {
+    const KernelTiming t = timing();
+    return (!t.start || hipEventRecord(t.start, s) == hipSuccess) &&
+           (!t.stop || hipEventRecord(t.stop, s) == hipSuccess);
+  };
   // Forward recompute: routing, cos/sin, Z = B^T x, H = alpha Z W^T.
-  if (launch_prep(ids, M, n_experts, theta, phi, d, rt, cs_in, cs_out, status, w_packed, nullptr,
-                  wt, l.wt_block, s, timing()) != hipSuccess)
+  if (kept) {
+    // Bad ids were the forward's to report; the setup kernel below clears
+    // this workspace's status word.
+    if (!skip()) return BMOE_E_HIP;
+  } else if (launch_prep(ids, M, n_experts, theta, phi, d, rt, cs_in, cs_out, status, w_packed,
+                         nullptr, wt, l.wt_block, s, timing()) != hipSuccess) {
     return BMOE_E_HIP;
+  }
   if (launch_bwd_setup(rt.offsets, n_experts, d, tiles, tile_base, l.max_tiles, w_packed, wpt, wtt,
-                       l.wt_block, s, timing()) != hipSuccess)
+                       l.wt_block, kept ? status : nullptr, s, timing()) != hipSuccess)
     return BMOE_E_HIP;
-  if (launch_bfly_in(dt, M, d, k, x, rt, cs_in, z, s, timing()) != hipSuccess) return BMOE_E_HIP;
-  if (launch_gemm(dt, M, d, z, w_packed, wt, alpha, h, s, timing()) != hipSuccess) return BMOE_E_HIP;
+  if (kept) {
+    if (!skip() || !skip()) return BMOE_E_HIP;
+  } else {
+    if (launch_bfly_in(dt, M, d, k, x, rt, cs_in, z, s, timing()) != hipSuccess) return BMOE_E_HIP;
+    if (launch_gemm(dt, M, d, z, w_packed, wt, alpha, h, s, timing()) != hipSuccess)
+      return BMOE_E_HIP;
+  }
   // Output side: dH, dgates, dphi partials.
   if (launch_bfly_bwd(false, dt, M, d, k, tiles, l.max_tiles, rt.perm, cs_out, gates, h, dy, dh,
                       dgates, part_out, s, timing()) != hipSuccess)
@@ -452,10 +510,10 @@ bmoe_status bmoe_backward_timed(bmoe_dtype dt, int T, int d, int n_experts, int 
       return BMOE_E_HIP;
     if (t.stop && hipEventRecord(t.stop, s) != hipSuccess) return BMOE_E_HIP;
   }
-  // dZ = alpha dH W (the product with the transposed substrate), into H's space.
-  if (launch_gemm(dt, M, d, dh, wpt, wtt, alpha, h, s, timing()) != hipSuccess) return BMOE_E_HIP;
+  // dZ = alpha dH W (the product with the transposed substrate).
+  if (launch_gemm(dt, M, d, dh, wpt, wtt, alpha, dz, s, timing()) != hipSuccess) return BMOE_E_HIP;
   // Input side: dX per routed row, dtheta partials; dx_t = sum_j dX[t k + j].
-  if (launch_bfly_bwd(true, dt, M, d, k, tiles, l.max_tiles, rt.perm, cs_in, gates, x, h, dxr,
+  if (launch_bfly_bwd(true, dt, M, d, k, tiles, l.max_tiles, rt.perm, cs_in, gates, x, dz, dxr,
                       nullptr, part_in, s, timing()) != hipSuccess)
     return BMOE_E_HIP;
   if (launch_combine(dt, T, d, k, dxr, dx, s, timing()) != hipSuccess) return BMOE_E_HIP;
@@ -463,6 +521,39 @@ bmoe_status bmoe_backward_timed(bmoe_dtype dt, int T, int d, int n_experts, int 
                           timing()) != hipSuccess)
     return BMOE_E_HIP;
   return BMOE_OK;
+}
+}  // namespace
+
+bmoe_status bmoe_backward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k,
+                                const void* x, const int32_t* ids, const float* gates,
+                                const float* theta, const float* phi, const uint32_t* w_packed,
+                                float alpha, const void* dy, void* dx, float* dgates,
+                                float* dtheta, float* dphi, float* dw, void* ws, size_t ws_bytes,
+                                void* stream, void* const* events) {
+  return backward_impl(dt, T, d, n_experts, k, x, ids, gates, theta, phi, w_packed, alpha, dy, dx,
+                       dgates, dtheta, dphi, dw, nullptr, 0, ws, ws_bytes, stream, events);
+}
+
+bmoe_status bmoe_backward_kept_timed(bmoe_dtype dt, int T, int d, int n_experts, int k,
+                                     const void* x, const float* gates,
+                                     const uint32_t* w_packed, float alpha, const void* dy,
+                                     void* dx, float* dgates, float* dtheta, float* dphi,
+                                     float* dw, const void* fwd_ws, size_t fwd_ws_bytes, void* ws,
+                                     size_t ws_bytes, void* stream, void* const* events) {
+  if (!fwd_ws) return BMOE_E_NULL;
+  return backward_impl(dt, T, d, n_experts, k, x, nullptr, gates, nullptr, nullptr, w_packed,
+                       alpha, dy, dx, dgates, dtheta, dphi, dw, fwd_ws, fwd_ws_bytes, ws, ws_bytes,
+                       stream, events);
+}
+
+bmoe_status bmoe_backward_kept(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
+                               const float* gates, const uint32_t* w_packed, float alpha,
+                               const void* dy, void* dx, float* dgates, float* dtheta,
+                               float* dphi, float* dw, const void* fwd_ws, size_t fwd_ws_bytes,
+                               void* ws, size_t ws_bytes, void* stream) {
+  return bmoe_backward_kept_timed(dt, T, d, n_experts, k, x, gates, w_packed, alpha, dy, dx,
+                                  dgates, dtheta, dphi, dw, fwd_ws, fwd_ws_bytes, ws, ws_bytes,
+                                  stream, nullptr);
 }
 
 bmoe_status bmoe_backward(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,

@@ -76,8 +76,9 @@ __device__ void tiles_role(const int32_t* offsets, int N, int tr, int4* tiles, i
 
 __global__ __launch_bounds__(kSetupThreads) void bwd_setup_kernel(
     const int32_t* offsets, int N, int tr, int4* tiles, int32_t* tile_base, int max_tiles,
-    const uint32_t* wp, int d, uint32_t* wpt, uint32_t* wtt, int cb) {
+    const uint32_t* wp, int d, uint32_t* wpt, uint32_t* wtt, int cb, int32_t* status) {
   if (blockIdx.x == 0) {
+    if (status && threadIdx.x == 0) *status = BMOE_OK;
     tiles_role(offsets, N, tr, tiles, tile_base, max_tiles);
     return;
   }
@@ -540,10 +541,11 @@ int bwd_max_tiles(int M, int N, int d) {
 
 hipError_t launch_bwd_setup(const int32_t* offsets, int N, int d, int4* tiles,
                            int32_t* tile_base, int max_tiles, const uint32_t* wp, uint32_t* wpt,
-                           uint32_t* wtt, int cb, hipStream_t s, const KernelTiming& t) {
+                           uint32_t* wtt, int cb, int32_t* status, hipStream_t s,
+                           const KernelTiming& t) {
   return launch_kernel(bwd_setup_kernel, dim3(1 + grid_for((size_t)d * (d / 16))),
                        dim3(kSetupThreads), 0, s, t, offsets, N, bwd_tile_rows(d), tiles,
-                       tile_base, max_tiles, wp, d, wpt, wtt, cb);
+                       tile_base, max_tiles, wp, d, wpt, wtt, cb, status);
 }
 
 hipError_t launch_bfly_bwd(bool in_side, bmoe_dtype dt, int M, int d, int k, const int4* tiles,

@@ -95,9 +95,11 @@ int bwd_max_tiles(int M, int N, int d);
 // first tile of expert e, tile_base[N] = count; unused entries have expert
 // -1), and packed W_base^T (row c holds the codes of column c) row-major into
 // wpt and, when cb > 0, in the large-tile GEMM's tile-major order into wtt.
+// status (may be NULL): set to BMOE_OK.
 hipError_t launch_bwd_setup(const int32_t* offsets, int N, int d, int4* tiles,
                            int32_t* tile_base, int max_tiles, const uint32_t* wp, uint32_t* wpt,
-                           uint32_t* wtt, int cb, hipStream_t s, const KernelTiming& t = {});
+                           uint32_t* wtt, int cb, int32_t* status, hipStream_t s,
+                           const KernelTiming& t = {});
 // Butterfly backward over the tiles. Output side (in_side = false): src = H
 // (sorted), grad = dy (token rows) -> dst = dH (sorted), dgates, partials of
 // dphi. Input side: src = x (token rows), grad = dZ (sorted) -> dst = dX

@@ -235,6 +235,42 @@ bmoe_status bmoe_backward_timed(bmoe_dtype dt, int T, int d, int n_experts, int 
                                 void* stream, void* const* events);
 
 /*
+ * Forward that keeps its intermediates for the backward (a training step):
+ * as bmoe_forward, but always on the unfused path, so that after the call
+ * the workspace holds the routing tables, both cos/sin tables, Z and H.
+ * bmoe_backward_kept then reads them instead of recomputing the forward.
+ * No route_out (the tables stay in the workspace). ws: at least
+ * bmoe_forward_keep_workspace_bytes(). y is identical to the unfused
+ * forward's.
+ */
+size_t bmoe_forward_keep_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts, int k);
+bmoe_status bmoe_forward_keep(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
+                              const int32_t* ids, const float* gates, const float* theta,
+                              const float* phi, const uint32_t* w_packed, float alpha, void* y,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * bmoe_backward after a bmoe_forward_keep: fwd_ws (fwd_ws_bytes) is that
+ * call's workspace, unchanged since; x, gates, w_packed and alpha are the
+ * same as in that call (ids, theta and phi live on in its tables). Skips the
+ * forward recompute (routing, cos/sin, Z, H); the results are bit-identical
+ * to bmoe_backward's. fwd_ws is only read. ws: at least
+ * bmoe_backward_workspace_bytes(). The _timed variant has the same launch
+ * slots as bmoe_backward_timed; the slots of the skipped launches are empty.
+ */
+bmoe_status bmoe_backward_kept(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
+                               const float* gates, const uint32_t* w_packed, float alpha,
+                               const void* dy, void* dx, float* dgates, float* dtheta,
+                               float* dphi, float* dw, const void* fwd_ws, size_t fwd_ws_bytes,
+                               void* ws, size_t ws_bytes, void* stream);
+bmoe_status bmoe_backward_kept_timed(bmoe_dtype dt, int T, int d, int n_experts, int k,
+                                     const void* x, const float* gates,
+                                     const uint32_t* w_packed, float alpha, const void* dy,
+                                     void* dx, float* dgates, float* dtheta, float* dphi,
+                                     float* dw, const void* fwd_ws, size_t fwd_ws_bytes, void* ws,
+                                     size_t ws_bytes, void* stream, void* const* events);
+
+/*
  * Input-side rotation alone (§2.3, first step): z[r] = B(theta_e)^T x[t] for
  * every routed row r = t*k + j, e = ids[t][j], written in routed order
  * ([T*k][d], dtype dt; the same rounding point as the forward's Z). Used to

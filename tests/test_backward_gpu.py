@@ -166,3 +166,43 @@ def test_backward_empty_batch_is_a_noop():
                       bmoe.pack_ternary(torch.zeros(256, 256, dtype=torch.int8, device=dev)),
                       1.0, torch.empty(0, 256, dtype=torch.bfloat16, device=dev))
     assert g["dx"].shape == (0, 256)
+
+
+@pytest.mark.parametrize("name,T", [("tiny_d64_e8_top2_f32", 200), ("d512_e64_top2_bf16", 301),
+                                    ("d2048_e64_top2_outliers_bf16", 90),
+                                    ("d4096_e256_top4_bf16", 30)])
+def test_backward_after_kept_forward_is_bit_identical(name, T):
+    """bmoe_forward_keep + bmoe_backward_kept gives exactly bmoe_backward's
+    gradients (same kernels on the same inputs), and the kept forward's y
+    matches the oracle."""
+    inp = W.make_inputs(name, T=T)
+    print(f"[kept] {name} T={T}", flush=True)
+    dev = to_device(inp)
+    dy = torch.randn(inp.T, inp.d, device="cuda").to(dev["x"].dtype)
+    y, kept = bmoe.forward_keep(dev["x"], dev["ids"], dev["gates"], dev["theta"], dev["phi"],
+                                dev["w_packed"], dev["alpha"])
+    kept_copy = kept.clone()
+    a = bmoe.backward_kept(dev["x"], dev["gates"], inp.N, dev["w_packed"], dev["alpha"], dy, kept)
+    b = bmoe.backward(dev["x"], dev["ids"], dev["gates"], dev["theta"], dev["phi"],
+                      dev["w_packed"], dev["alpha"], dy)
+    torch.cuda.synchronize()
+    for key in ("dx", "dgates", "dtheta", "dphi", "dw"):
+        assert torch.equal(a[key], b[key]), key
+    assert torch.equal(kept, kept_copy)      # the kept workspace is only read
+    ref = O.forward(inp.x, inp.ids, inp.gates, inp.theta, inp.phi, inp.w, inp.alpha)
+    assert O.max_rel_err(y.float().cpu().numpy().astype(np.float64), ref) <= TOL[inp.dtype]
+
+
+def test_backward_kept_rejects_a_short_forward_workspace():
+    inp = W.make_inputs("d512_e64_top2_bf16", T=64)
+    dev = to_device(inp)
+    dt, T, d, N, k = bmoe.BMOE_BF16, inp.T, inp.d, inp.N, inp.k
+    n = bmoe.bmoe_forward_keep_workspace_bytes(dt, T, d, N, k)
+    short = torch.empty(n - 256, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(bmoe.bmoe_backward_workspace_bytes(dt, T, d, N, k), dtype=torch.uint8,
+                     device="cuda")
+    o = {key: torch.empty(1024 * 1024, device="cuda") for key in ("dg", "dth", "dph", "dw")}
+    dx = torch.empty_like(dev["x"])
+    rc = bmoe.bmoe_backward_kept(dt, T, d, N, k, dev["x"], dev["gates"], dev["w_packed"], 1.0,
+                                 dev["x"], dx, o["dg"], o["dth"], o["dph"], o["dw"], short, ws)
+    assert rc == 6  # BMOE_E_WORKSPACE
