@@ -206,3 +206,28 @@ def test_backward_kept_rejects_a_short_forward_workspace():
     rc = bmoe.bmoe_backward_kept(dt, T, d, N, k, dev["x"], dev["gates"], dev["w_packed"], 1.0,
                                  dev["x"], dx, o["dg"], o["dth"], o["dph"], o["dw"], short, ws)
     assert rc == 6  # BMOE_E_WORKSPACE
+
+
+@pytest.mark.parametrize("name", ["d512_e64_top2_bf16", "d4096_e256_top4_bf16"])
+def test_backward_full_size_sampled_tokens(name):
+    """At the full workload size: dx and dgates of a token depend only on that
+    token's rows, so the oracle computes them exactly for a sample of tokens
+    (the angle and substrate gradients sum over every row and are covered at
+    reduced sizes)."""
+    inp = W.make_inputs(name)
+    print(f"[backward] full {name}", flush=True)
+    dy, dy_bits = _dy(inp, 31)
+    dev = to_device(inp)
+    dyt = torch.from_numpy(dy_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    g = bmoe.backward(dev["x"], dev["ids"], dev["gates"], dev["theta"], dev["phi"],
+                      dev["w_packed"], dev["alpha"], dyt, want_dw=False)
+    torch.cuda.synchronize()
+    toks = np.unique(np.concatenate([np.random.default_rng(4).choice(inp.T, 160, replace=False),
+                                     np.arange(inp.T - 16, inp.T)]))
+    ref = O.backward(inp.x[toks], inp.ids[toks], inp.gates[toks], inp.theta, inp.phi, inp.w,
+                     inp.alpha, dy[toks])
+    t = torch.from_numpy(toks).cuda()
+    dx = g["dx"][t].float().cpu().numpy().astype(np.float64)
+    dgt = g["dgates"][t].cpu().numpy().astype(np.float64)
+    assert O.max_rel_err(dx, ref["dx"]) <= TOL["bf16"]
+    assert _global_err(dgt, ref["dgates"]) <= TOL["bf16"]
