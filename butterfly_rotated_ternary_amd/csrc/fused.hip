@@ -5,17 +5,19 @@
 //
 //   gather x rows -> LDS (fp32)        butterfly-in, register blocks of 3 stages
 //   -> bf16 A tile in LDS              substrate GEMM on MFMA 32x32x16, the bf16
-//                                      substrate streamed through a 4-stage
-//                                      global->LDS ring
+//                                      substrate of the last K-steps streamed
+//                                      through a global->LDS ring
 //   -> alpha * H back into LDS (fp32)  butterfly-out
 //   -> g_r * row, bf16, in routed order (the combine kernel sums the k rows).
 //
-// LDS (160 KiB at d = 512): four ring stages and the A tile, each its own
+// LDS (160 KiB at d = 512): four stage arrays and the A tile, each its own
 // array so the compiler can tell the stage being read from the stages the
-// DMA is filling. The fp32 rows live inside ring stages 1..3 (14 rows per
-// stage; they are used only before and after the GEMM). The first K-steps of
-// the GEMM take the substrate from packed words in registers, which leaves
-// time for the ring to fill after the rows are dead.
+// DMA is filling. The fp32 rows live inside stages 1..3 (14 rows per stage;
+// they are used only before and after the GEMM). The ring uses stages 0..2;
+// stage 3 keeps the last rows, the row metadata and, for a tile of more than
+// one expert, the last expert's coefficient table. The first K-steps of the
+// GEMM take the substrate from packed words in registers, which leaves time
+// for the ring to fill after the rows are dead.
 #include "common.h"
 #include "kernels.h"
 
@@ -35,26 +37,32 @@ struct FCfg {
   static constexpr int KS = 32;                     // K per GEMM step
   static constexpr int NSTEP = D / KS;
   // The first NP steps take B from the packed 2-bit words (registers, VALU
-  // expansion); the remaining NR steps from the bf16 substrate via the ring.
+  // expansion); the last NR steps from the bf16 substrate via the ring.
   // Splitting K balances VALU against L2 bandwidth: with every CU streaming
   // the substrate at once, bf16 alone is L2-bound, packed alone VALU-bound.
-  static constexpr int NP = NSTEP * 3 / 4;
-  static constexpr int NR = NSTEP - NP;  // <= 4: every ring stage is prefetched
+  // At most three ring steps, so ring stage 3 is never used by the ring: it
+  // keeps the last rows, the row metadata and one expert's coefficient table.
+  static constexpr int NR = NSTEP / 4 < 3 ? NSTEP / 4 : 3;
+  static constexpr int NP = NSTEP - NR;
   static constexpr int STAGE_BYTES = D * KS * 2;    // D rows of 64 bytes
   static constexpr int NSTAGE = 4;
   static constexpr int ZT_BYTES = kBM * D * 2;
   static constexpr int ROW_BYTES = PD * 4;
   static constexpr int RPS = STAGE_BYTES / ROW_BYTES;  // rows per stage array
-  // Row metadata (expert, routed index) after the last row in stage 3; it is
-  // reloaded after the GEMM has overwritten it.
+  // Row metadata (expert, routed index) after the last row in stage 3.
   static constexpr int META_OFF = (kBM - 2 * RPS) * ROW_BYTES;
+  // One side's cos/sin table of one expert (L * D/2 pairs), in stage 3 after
+  // the metadata: the tile's last expert when the tile holds more than one.
+  static constexpr int TAB_BYTES = L * (D / 2) * 8;
+  static constexpr int TAB_OFF = (META_OFF + 2 * kBM * 4 + 1023) / 1024 * 1024;
   static constexpr int WN = D / kWavesF;            // output columns per wave
   static constexpr int FN = WN / 32;
   static constexpr int LPW = STAGE_BYTES / 1024 / kWavesF;  // 1 KiB wave loads per wave per stage
   static_assert(FN >= 1 && LPW >= 1, "d too small for this tiling");
   static_assert(3 * RPS >= kBM && 2 * RPS < kBM, "rows must end in ring stage 3");
-  static_assert(NR >= 1 && NR <= NSTAGE, "ring steps must fit the four stages");
-  static_assert(META_OFF + 2 * kBM * 4 <= STAGE_BYTES, "metadata must fit in stage 3");
+  static_assert(NR >= 1 && NR <= 3, "ring steps must leave stage 3 free");
+  static_assert(TAB_OFF + TAB_BYTES <= STAGE_BYTES && TAB_BYTES % 1024 == 0,
+                "metadata and one coefficient table must fit in stage 3");
 };
 
 // fp32 row i inside ring stages 1..3.
@@ -120,10 +128,39 @@ __device__ __forceinline__ void load_coef(float2 (&c)[3][4], const float2* cs, i
   }
 }
 
+// The same coefficients from an expert's table copied to LDS (pair order).
+template <int D, int G>
+__device__ __forceinline__ void load_coef_lds(float2 (&c)[3][4], const float2* tab, int s_lo,
+                                              int base) {
+#pragma unroll
+  for (int t = 0; t < G; ++t) {
+    const int s = s_lo + t;
+#pragma unroll
+    for (int u = 0; u < (1 << (G - 1)); ++u) {
+      const int m = ((u >> t) << (t + 1)) | (u & ((1 << t) - 1));
+      c[t][u] = tab[s * (D / 2) + pair_index(base + (m << s_lo), s)];
+    }
+  }
+}
+
+// Expert e's table of one side (contiguous) -> LDS at dst, 1 KiB per wave
+// instruction (global->LDS DMA; completion is tracked by vmcnt).
+template <int D>
+__device__ __forceinline__ void table_load(char* dst, const float2* cs, int e) {
+  using C = FCfg<D>;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const char* src = reinterpret_cast<const char*>(cs + (size_t)e * C::L * (D / 2));
+  for (int ch = wave; ch < C::TAB_BYTES / 1024; ch += kWavesF)
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(src + ch * 1024 + lane * 16),
+        (__attribute__((address_space(3))) void*)(dst + ch * 1024), 16, 0, 0);
+}
+
 // Butterfly side over the kBM rows in LDS. Each thread owns one block per
 // group and every tpb-th row; its coefficients are fetched up front for the
 // expert of its first row (prefetch) and reloaded only when the expert of a
-// later row differs (rows are sorted by expert).
+// later row differs (rows are sorted by expert): from the LDS copy of expert
+// e_tab's table when the row belongs to it, else from global memory.
 template <int D, bool TR>
 struct BflyCoef {
   using Gr = Groups<D, TR>;
@@ -159,7 +196,8 @@ struct BflyCoef {
 
   template <int G>
   __device__ __forceinline__ void rotate_rows(const RowMap<D>& rows, const int* sh_e,
-                                              const float2* cs, int g, int s_lo, int base,
+                                              const float2* cs, const float2* tab, int e_tab,
+                                              int g, int s_lo, int base,
                                               const int (&off)[8], int ph, int tpb) {
     constexpr int RPT_MAX = kBM;  // loop bound; actual rows per thread = kBM / tpb
     const int rpt = kBM / tpb;
@@ -196,7 +234,8 @@ struct BflyCoef {
       const int ei = sh_e[i];
       if (ei != e[g]) {
         e[g] = ei;
-        load_coef<D, G>(c[g], cs, ei, s_lo, base);
+        if (ei == e_tab) load_coef_lds<D, G>(c[g], tab, s_lo, base);
+        else load_coef<D, G>(c[g], cs, ei, s_lo, base);
       }
       float* row = rows.row(i);
       float v[8];
@@ -209,7 +248,7 @@ struct BflyCoef {
   }
 
   __device__ __forceinline__ void apply(const RowMap<D>& rows, const float2* cs,
-                                        const int* sh_e) {
+                                        const int* sh_e, const float2* tab, int e_tab) {
 #pragma unroll
     for (int g = 0; g < Gr::N; ++g) {
       const int G = Gr::G(g), s_lo = Gr::s_lo(g);
@@ -220,9 +259,9 @@ struct BflyCoef {
       int off[8];
 #pragma unroll
       for (int m = 0; m < 8; ++m) off[m] = padi(base + ((m & ((1 << G) - 1)) << s_lo));
-      if (G == 3) rotate_rows<3>(rows, sh_e, cs, g, s_lo, base, off, ph, tpb);
-      else if (G == 2) rotate_rows<2>(rows, sh_e, cs, g, s_lo, base, off, ph, tpb);
-      else rotate_rows<1>(rows, sh_e, cs, g, s_lo, base, off, ph, tpb);
+      if (G == 3) rotate_rows<3>(rows, sh_e, cs, tab, e_tab, g, s_lo, base, off, ph, tpb);
+      else if (G == 2) rotate_rows<2>(rows, sh_e, cs, tab, e_tab, g, s_lo, base, off, ph, tpb);
+      else rotate_rows<1>(rows, sh_e, cs, tab, e_tab, g, s_lo, base, off, ph, tpb);
       lds_barrier();
     }
   }
@@ -285,8 +324,8 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(int M, int k, const uin
   const int q0 = blockIdx.x * kBM;
   const int nr = min(kBM, M - q0);
   // Lane l < 32 of every wave keeps row l's (expert, routed index) in
-  // registers: the LDS copy is overwritten by the GEMM ring. Rows past the end
-  // repeat the last row's expert (their values are zero).
+  // registers (an LDS copy serves the butterflies). Rows past the end repeat
+  // the last row's expert (their values are zero).
   const int q_meta = q0 + min(lane & 31, nr - 1);
   const int my_e = slot_e[q_meta];
   const int my_r = perm[q_meta];
@@ -295,11 +334,19 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(int M, int k, const uin
     sh_e[tid] = my_e;
     sh_r[tid] = my_r;
   }
+  // A tile holding more than one expert copies its last expert's tables to
+  // LDS (each side before that side's butterfly), so the rows of that expert
+  // reload their coefficients from LDS rather than from global memory.
+  const int e_tab = __shfl(my_e, 0, 64) != __shfl(my_e, kBM - 1, 64) ? __shfl(my_e, kBM - 1, 64)
+                                                                     : -1;
+  const float2* const tab = reinterpret_cast<const float2*>(st3 + C::TAB_OFF);
+  if (e_tab >= 0) table_load<D>(st3 + C::TAB_OFF, cs_in, e_tab);
+  __asm__ volatile("" ::: "memory");
 
-  // Gather x rows (8 bf16 per 16-byte chunk) into registers, fetch the
-  // butterfly-in coefficients and the packed substrate words of the first NP
-  // K-steps. Token indices come from the lanes holding them (no LDS round
-  // trip). Tail rows past nr repeat the last row: computed, never stored.
+  // Gather x rows (8 bf16 per 16-byte chunk) into registers and fetch the
+  // butterfly-in coefficients. Token indices come from the lanes holding them
+  // (no LDS round trip). Tail rows past nr repeat the last row: computed,
+  // never stored.
   constexpr int CPR = D / 8;
   constexpr int XPT = kBM * CPR / kThreads;
   uint4 xv[XPT];
@@ -312,15 +359,6 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(int M, int k, const uin
   }
   BflyCoef<D, true> cin;
   cin.prefetch_from_lanes(cs_in, my_e);
-  // lane l needs W rows o = wave*WN + 32j + (l & 31), two words per K-step.
-  uint2 pw[C::NP][C::FN];
-#pragma unroll
-  for (int ks = 0; ks < C::NP; ++ks)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const int o = wave * C::WN + j * 32 + (lane & 31);
-      pw[ks][j] = *reinterpret_cast<const uint2*>(wp + (size_t)o * (D / 16) + 2 * ks);
-    }
 #pragma unroll
   for (int it = 0; it < XPT; ++it) {
     const int c = tid + it * kThreads;
@@ -330,9 +368,20 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(int M, int k, const uin
     dst[0] = bf16_lo(v.x); dst[1] = bf16_hi(v.x); dst[2] = bf16_lo(v.y); dst[3] = bf16_hi(v.y);
     dst[4] = bf16_lo(v.z); dst[5] = bf16_hi(v.z); dst[6] = bf16_lo(v.w); dst[7] = bf16_hi(v.w);
   }
+  if (e_tab >= 0) wait_vm<0>();  // this wave's part of the table has landed
   __syncthreads();
+  // The packed substrate words of the first NP K-steps, for the GEMM.
+  // Lane l needs W rows o = wave*WN + 32j + (l & 31), two words per K-step.
+  uint2 pw[C::NP][C::FN];
+#pragma unroll
+  for (int ks = 0; ks < C::NP; ++ks)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int o = wave * C::WN + j * 32 + (lane & 31);
+      pw[ks][j] = *reinterpret_cast<const uint2*>(wp + (size_t)o * (D / 16) + 2 * ks);
+    }
 
-  cin.apply(rows, cs_in, sh_e);
+  cin.apply(rows, cs_in, sh_e, tab, e_tab);
 
   // fp32 rows -> bf16 A tile, 16-byte chunk c of row r at chunk c ^ (r & 15).
 #pragma unroll
@@ -350,10 +399,13 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(int M, int k, const uin
   // they land. Loads complete in issue order, so the coefficients go first.
   BflyCoef<D, false> cout;
   cout.prefetch_from_lanes(cs_out, my_e);
+  // The output side's table replaces the input side's (that butterfly is
+  // done); it goes out before the ring, so it has landed once the ring has.
+  if (e_tab >= 0) table_load<D>(st3 + C::TAB_OFF, cs_out, e_tab);
+  __asm__ volatile("" ::: "memory");
   ring_load<D>(st0, w16, C::NP);
   if (C::NR > 1) ring_load<D>(st1, w16, C::NP + 1);
   if (C::NR > 2) ring_load<D>(st2, w16, C::NP + 2);
-  if (C::NR > 3) ring_load<D>(st3, w16, C::NP + 3);
 
   // ---- substrate GEMM: wave w computes rows 0..31 x columns [w*WN, (w+1)*WN)
   f32x16 acc[C::FN];
@@ -382,8 +434,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(int M, int k, const uin
   for (int rs = 0; rs < C::NR; ++rs) {
     // Stages requested after stage rs: rs+1 .. NR-1.
     const int after = C::NR - 1 - rs;
-    if (after == 3) wait_vm<3 * C::LPW>();
-    else if (after == 2) wait_vm<2 * C::LPW>();
+    if (after == 2) wait_vm<2 * C::LPW>();
     else if (after == 1) wait_vm<C::LPW>();
     else wait_vm<0>();
     lds_barrier();  // every wave's part of stage rs has landed
@@ -403,10 +454,6 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(int M, int k, const uin
     }
   }
   __syncthreads();  // every wave is done with the ring: rows may be rewritten
-  if (tid < kBM) {
-    sh_e[tid] = my_e;
-    sh_r[tid] = my_r;
-  }
 
   // alpha * H -> fp32 rows. 32x32 block layout: lane l, register r ->
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
@@ -421,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(int M, int k, const uin
   }
   __syncthreads();
 
-  cout.apply(rows, cs_out, sh_e);
+  cout.apply(rows, cs_out, sh_e, tab, e_tab);
 
   // g_r * row -> bf16, routed order.
 #pragma unroll

@@ -148,6 +148,25 @@ def test_edge_shapes(d, N, k, T):
     assert O.max_rel_err(y, ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("d", [256, 512])
+def test_fused_tiles_holding_several_experts(d):
+    """Sorted rows are cut into 32-row tiles regardless of expert: one tile
+    splits two experts (its last expert's coefficients are reloaded from an
+    LDS copy of the table), one holds five (the middle ones reload from global
+    memory), one a single expert, and the last ends on an empty expert."""
+    counts = [13, 19, 3, 1, 2, 70, 0, 20]  # rows 0..127 by expert: tiles 0..3
+    labels = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    inp = W.make_inputs("custom", d=d, N=len(counts), k=2, T=64, seed=d + 11, dtype="bf16")
+    inp.ids[:] = np.random.default_rng(d).permutation(labels).reshape(64, 2)
+    _announce(f"[tiles] d={d} counts={counts}")
+    dev = to_device(inp)
+    y, route = run_forward(dev, inp)
+    check_route(inp, route)
+    assert np.array_equal(np.diff(route[0]), counts)
+    ref = O.forward(inp.x, inp.ids, inp.gates, inp.theta, inp.phi, inp.w, inp.alpha)
+    assert O.max_rel_err(y, ref) <= TOL["bf16"]
+
+
 def test_duplicate_experts_in_a_token():
     inp = W.make_inputs("custom", d=64, N=4, k=3, T=50, seed=5, dtype="f32")
     inp.ids[:, 1] = inp.ids[:, 0]
