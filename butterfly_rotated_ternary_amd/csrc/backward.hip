@@ -110,7 +110,10 @@ __global__ __launch_bounds__(kSetupThreads) void bwd_setup_kernel(
 // pairs sum in registers over those rows, and each element crosses LDS once
 // per group and pass.
 constexpr int bwd_rows(int d) { return d >= 4096 ? 2 : (8192 / d > 32 ? 32 : 8192 / d); }
-constexpr int bwd_tile_rows(int d) { return d >= 1024 ? 64 : bwd_rows(d); }
+// Rows per tile (a workgroup walks them bwd_rows at a time). Two passes per
+// tile at d = 512 keep the grid within one round of two workgroups per CU at
+// the usual row counts; more passes per tile measured slower.
+constexpr int bwd_tile_rows(int d) { return d >= 1024 ? 64 : d == 512 ? 32 : bwd_rows(d); }
 
 template <int D>
 struct BwdCfg {
