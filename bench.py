@@ -30,6 +30,7 @@ PEAK_FP32_MFMA_TFLOPS = 157.3    # dense fp32 MFMA
 PEAK_VALU_F32_TFLOPS = 157.3     # fp32 vector (256 CU x 2.4 GHz x 256 flop/clk)
 
 GEMM_WORKLOAD = "d4096_e256_top4_bf16"
+SHARD_TOKENS = 4096
 
 
 def log(*a):
@@ -244,14 +245,14 @@ def cpu_baseline(inp, seconds):
 class Problem:
     """Device-resident inputs of one workload, ready for bmoe_forward."""
 
-    def __init__(self, name):
+    def __init__(self, name, T=None):
         import numpy as np
         import torch
         from butterfly_rotated_ternary_amd import bmoe
         from butterfly_rotated_ternary_amd import workloads as W
 
         self.name = name
-        self.inp = inp = W.make_inputs(name)
+        self.inp = inp = W.make_inputs(name, T=T)
         self.T, self.d, self.N, self.k = inp.T, inp.d, inp.N, inp.k
         dev = torch.device("cuda:0")
         if inp.dtype == "bf16":
@@ -717,6 +718,24 @@ def main():
             f"{g_roof['achieved']:.0f} TFLOP/s ({100 * g_roof['frac']:.1f}% of bf16 peak); "
             + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in g_per.items()))
         del G
+        torch.cuda.empty_cache()
+        # One GPU's share when the same workload is split by tokens over 8
+        # GPUs (the forward needs no exchange): T = 4096 tokens per GPU.
+        S = Problem(GEMM_WORKLOAD, T=SHARD_TOKENS)
+        s_ms = S.time_steps(args.gemm_steps, 3)
+        s_per = S.time_kernels(args.gemm_steps)
+        s_roof = roofline(kernel_work("gemm_kernel", S.act_bytes, S.T, S.d, S.N, S.k),
+                          s_per["gemm_kernel"] * 1e-3, S.mfma_peak())
+        out["shard_d4096"] = {
+            "workload": GEMM_WORKLOAD, "tokens": S.T, "split": "tokens over 8 GPUs",
+            "ms_per_step": s_ms, "tokens_per_s": S.T / (s_ms * 1e-3), "gemm_roofline": s_roof,
+            "kernels_us": {n: v * 1e3 for n, v in s_per.items()},
+        }
+        log(f"[bench] {GEMM_WORKLOAD} at T={S.T} (one GPU of 8): {s_ms * 1e3:.1f} us/step, "
+            f"{S.T / (s_ms * 1e-3):.4g} tokens/s; gemm_kernel {s_roof['achieved']:.0f} TFLOP/s "
+            f"({100 * s_roof['frac']:.1f}%); "
+            + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in s_per.items()))
+        del S
         torch.cuda.empty_cache()
 
     if not args.no_outliers:
