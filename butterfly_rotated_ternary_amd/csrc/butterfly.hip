@@ -192,14 +192,18 @@ __global__ __launch_bounds__(kThreads) void bfly_kernel(BflyParams p) {
 // trip up front; rows are rotated four at a time while they share an expert.
 constexpr int kBigThreads = 512;
 
+// Two workgroups per CU: R fp32 rows each (74 KiB of LDS) and at most 128
+// registers per lane (four waves per SIMD), so one workgroup's row loads and
+// stores overlap the other's rotations. A thread holds the coefficients of
+// the group it rotates and of the next one (fetched during the current one).
 template <int D>
 struct BigCfg {
   static_assert(D == 1024 || D == 2048 || D == 4096, "large-d kernel sizes");
   static constexpr int L = D == 1024 ? 10 : D == 2048 ? 11 : 12;
   static constexpr int PD = D + D / 8;
-  static constexpr int R = 147456 / (PD * 4) >= 32 ? 32 : 147456 / (PD * 4) >= 16 ? 16
-                         : 147456 / (PD * 4) >= 8 ? 8 : 4;
+  static constexpr int R = D == 1024 ? 16 : D == 2048 ? 8 : 4;
   static constexpr int NG = (L + 2) / 3;
+  static_assert(R * PD * 4 <= 80 * 1024, "two workgroups per CU");
 };
 
 template <int D, bool TR>
@@ -286,13 +290,44 @@ __device__ __forceinline__ void big_rows(float* rows, const int* sh_e, int nrows
   }
 }
 
+// Group g's coefficients for the expert of this thread's first row in that
+// group (lane l < R of each wave holds row l's expert in my_e).
+template <int D, bool IN_SIDE, int g>
+__device__ __forceinline__ void big_group_coef(float2 (&c)[3][4], int& ce, const float2* cs,
+                                               int my_e, int tid) {
+  using Gr = BigGroups<D, IN_SIDE>;
+  constexpr int G = Gr::G(g), NB = Gr::NB(g);
+  const int base = block_base(tid % NB, Gr::s_lo(g), G);
+  ce = __shfl(my_e, tid / NB, 64);
+  big_coef<D, G>(c, cs, ce, Gr::s_lo(g), base);
+}
+
+// Groups g.. in application order, a barrier after each; group g+1's
+// coefficients are requested before group g's rotations.
+template <int D, bool IN_SIDE, int g>
+__device__ __forceinline__ void big_groups(float* rows, const int* sh_e, const float2* cs,
+                                           float2 (&coef)[2][3][4], int (&ce)[2], int my_e,
+                                           int tid) {
+  using Gr = BigGroups<D, IN_SIDE>;
+  if constexpr (g < BigCfg<D>::NG) {
+    if constexpr (g + 1 < BigCfg<D>::NG)
+      big_group_coef<D, IN_SIDE, g + 1>(coef[(g + 1) & 1], ce[(g + 1) & 1], cs, my_e, tid);
+    constexpr int G = Gr::G(g), NB = Gr::NB(g);
+    const int base = block_base(tid % NB, Gr::s_lo(g), G);
+    big_rows<D, G, IN_SIDE>(rows, sh_e, BigCfg<D>::R, cs, coef[g & 1], ce[g & 1], Gr::s_lo(g),
+                            base, tid / NB, Gr::TPB(g));
+    __syncthreads();
+    big_groups<D, IN_SIDE, g + 1>(rows, sh_e, cs, coef, ce, my_e, tid);
+  }
+}
+
 // IN_SIDE:  z[q] = B(theta_e)^T x[perm[q] / k]          (sorted order)
 // OUT_SIDE: u[perm[q]] = g * B(phi_e) h[q]               (routed order)
 template <int D, bool IN_SIDE>
-__global__ __launch_bounds__(kBigThreads) void bfly_big_kernel(BflyParams p) {
+__global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void bfly_big_kernel(BflyParams p) {
   using C = BigCfg<D>;
-  using Gr = BigGroups<D, IN_SIDE>;
-  constexpr int PD = C::PD, R = C::R, NG = C::NG;
+  constexpr int PD = C::PD, R = C::R;
   extern __shared__ float rows[];
   __shared__ int sh_e[R], sh_r[R];
   const int tid = threadIdx.x, lane = tid % kWave;
@@ -327,18 +362,10 @@ __global__ __launch_bounds__(kBigThreads) void bfly_big_kernel(BflyParams p) {
     const int sr = __shfl(my_src, i, 64);
     xv[it] = *reinterpret_cast<const uint4*>(src + (size_t)sr * D + ch * 8);
   }
-  // Coefficients of every group for the expert of the thread's first row.
-  float2 coef[NG][3][4];
-  int ce[NG];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const int G = Gr::G(g), s_lo = Gr::s_lo(g), nb = Gr::NB(g);
-    const int base = block_base(tid % nb, s_lo, G);
-    ce[g] = __shfl(my_e, tid / nb, 64);
-    if (G == 3) big_coef<D, 3>(coef[g], p.cs, ce[g], s_lo, base);
-    else if (G == 2) big_coef<D, 2>(coef[g], p.cs, ce[g], s_lo, base);
-    else big_coef<D, 1>(coef[g], p.cs, ce[g], s_lo, base);
-  }
+  // Coefficients of group 0 for the expert of the thread's first row.
+  float2 coef[2][3][4];
+  int ce[2];
+  big_group_coef<D, IN_SIDE, 0>(coef[0], ce[0], p.cs, my_e, tid);
 #pragma unroll
   for (int it = 0; it < LPT; ++it) {
     const int c = tid + it * kBigThreads;
@@ -350,19 +377,7 @@ __global__ __launch_bounds__(kBigThreads) void bfly_big_kernel(BflyParams p) {
   }
   __syncthreads();
 
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const int G = Gr::G(g), s_lo = Gr::s_lo(g), nb = Gr::NB(g), tpb = Gr::TPB(g);
-    const int base = block_base(tid % nb, s_lo, G);
-    const int ph = tid / nb;
-    if (G == 3)
-      big_rows<D, 3, IN_SIDE>(rows, sh_e, R, p.cs, coef[g], ce[g], s_lo, base, ph, tpb);
-    else if (G == 2)
-      big_rows<D, 2, IN_SIDE>(rows, sh_e, R, p.cs, coef[g], ce[g], s_lo, base, ph, tpb);
-    else
-      big_rows<D, 1, IN_SIDE>(rows, sh_e, R, p.cs, coef[g], ce[g], s_lo, base, ph, tpb);
-    __syncthreads();
-  }
+  big_groups<D, IN_SIDE, 0>(rows, sh_e, p.cs, coef, ce, my_e, tid);
 
   uint16_t* dst = static_cast<uint16_t*>(p.dst);
 #pragma unroll
