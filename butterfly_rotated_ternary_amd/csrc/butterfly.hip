@@ -192,16 +192,17 @@ __global__ __launch_bounds__(kThreads) void bfly_kernel(BflyParams p) {
 // trip up front; rows are rotated four at a time while they share an expert.
 constexpr int kBigThreads = 512;
 
-// Two workgroups per CU: R fp32 rows each (74 KiB of LDS) and at most 128
+// Two workgroups per CU: R fp32 rows each (at most 74 KiB of LDS; 16 or 32
+// rows at d = 256 and 512 keep two or more tiles per CU) and at most 128
 // registers per lane (four waves per SIMD), so one workgroup's row loads and
 // stores overlap the other's rotations. A thread holds the coefficients of
 // the group it rotates and of the next one (fetched during the current one).
 template <int D>
 struct BigCfg {
-  static_assert(D == 1024 || D == 2048 || D == 4096, "large-d kernel sizes");
-  static constexpr int L = D == 1024 ? 10 : D == 2048 ? 11 : 12;
+  static_assert(D >= 256 && D <= 4096, "large-d kernel sizes");
+  static constexpr int L = D == 256 ? 8 : D == 512 ? 9 : D == 1024 ? 10 : D == 2048 ? 11 : 12;
   static constexpr int PD = D + D / 8;
-  static constexpr int R = D == 1024 ? 16 : D == 2048 ? 8 : 4;
+  static constexpr int R = D == 256 ? 32 : D == 512 ? 16 : D == 1024 ? 16 : D == 2048 ? 8 : 4;
   static constexpr int NG = (L + 2) / 3;
   static_assert(R * PD * 4 <= 80 * 1024, "two workgroups per CU");
 };
@@ -413,6 +414,8 @@ hipError_t launch_big(const BflyParams& p, hipStream_t s, const KernelTiming& t)
 template <bool IN_SIDE>
 hipError_t launch_big_d(const BflyParams& p, hipStream_t s, const KernelTiming& t) {
   switch (p.d) {
+    case 256: return launch_big<256, IN_SIDE>(p, s, t);
+    case 512: return launch_big<512, IN_SIDE>(p, s, t);
     case 1024: return launch_big<1024, IN_SIDE>(p, s, t);
     case 2048: return launch_big<2048, IN_SIDE>(p, s, t);
     case 4096: return launch_big<4096, IN_SIDE>(p, s, t);
@@ -459,7 +462,7 @@ hipError_t launch_bfly_in(bmoe_dtype dt, int M, int d, int k, const void* x,
                           const KernelTiming& t, bool routed_out) {
   BflyParams p = make_params(M, d, k, rt, cs_in, x, z, nullptr);
   p.routed_out = routed_out ? 1 : 0;
-  if (dt == BMOE_BF16 && d >= 1024 && d <= 4096) return launch_big_d<true>(p, s, t);
+  if (dt == BMOE_BF16 && d >= 256 && d <= 4096) return launch_big_d<true>(p, s, t);
   if (dt == BMOE_BF16) return launch_rows(bfly_kernel<true, uint16_t, uint16_t>, p, s, t);
   return launch_rows(bfly_kernel<true, float, float>, p, s, t);
 }
@@ -468,7 +471,7 @@ hipError_t launch_bfly_out(bmoe_dtype dt, int M, int d, const void* h, const flo
                            const RouteTables& rt, const float2* cs_out, void* u,
                            hipStream_t s, const KernelTiming& t) {
   const BflyParams p = make_params(M, d, 1, rt, cs_out, h, u, gates);
-  if (dt == BMOE_BF16 && d >= 1024 && d <= 4096) return launch_big_d<false>(p, s, t);
+  if (dt == BMOE_BF16 && d >= 256 && d <= 4096) return launch_big_d<false>(p, s, t);
   if (dt == BMOE_BF16) return launch_rows(bfly_kernel<false, uint16_t, uint16_t>, p, s, t);
   return launch_rows(bfly_kernel<false, float, float>, p, s, t);
 }

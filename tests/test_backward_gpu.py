@@ -77,7 +77,7 @@ def test_backward_matches_oracle(name, T):
 
 @pytest.mark.parametrize("d,N,k,T,dtype", [(16, 3, 2, 9, "f32"), (32, 5, 5, 4, "bf16"),
                                            (128, 70, 1, 150, "bf16"), (256, 2, 2, 129, "f32"),
-                                           (1024, 3, 2, 40, "bf16")])
+                                           (256, 9, 3, 203, "bf16"), (1024, 3, 2, 40, "bf16")])
 def test_backward_edge_shapes(d, N, k, T, dtype):
     # more than 64 rows per expert (several tiles), single-row experts, k = N
     _run("tiny_d64_e8_top2_f32", T, d=d, N=N, k=k, dtype=dtype, seed=900 + d)

@@ -31,7 +31,8 @@ def test_rotate_in_matches_oracle(name, T):
 
 
 @pytest.mark.parametrize("d,N,k,T,dtype", [(16, 3, 2, 9, "f32"), (1024, 5, 3, 50, "bf16"),
-                                           (8192, 2, 1, 5, "bf16"), (256, 70, 1, 130, "f32")])
+                                           (8192, 2, 1, 5, "bf16"), (256, 70, 1, 130, "f32"),
+                                           (256, 70, 1, 130, "bf16"), (512, 33, 2, 77, "bf16")])
 def test_rotate_in_edge_shapes(d, N, k, T, dtype):
     inp = W.make_inputs("tiny_d64_e8_top2_f32", T=T, d=d, N=N, k=k, dtype=dtype, seed=d + N)
     dev = to_device(inp)
