@@ -828,11 +828,16 @@ hipError_t launch_gemm(bmoe_dtype dt, int M, int d, const void* z, const uint32_
   uint16_t* hb = static_cast<uint16_t*>(h);
   const uint16_t* zb = static_cast<const uint16_t*>(z);
   // Large problems: 128x512 tiles (4 waves of 128x128, tile-major substrate
-  // copy). Smaller ones: 128x128 tiles so that the grid still covers the CUs.
+  // copy). Smaller ones: 128x128 or 64x128 tiles so that the grid still
+  // covers the CUs.
   if (gemm_tiled_w_block(dt, M, d)) {
     if (!wt) return hipErrorInvalidValue;
     return launch_rb<LargeCfg>(zb, wt, hb, M, d, alpha, s, t);
   }
+  // Fewer than two 128x128 tiles per CU: 64x128 tiles (same per-element
+  // accumulation order, so the same bits).
+  if (d >= 128 && (long long)((M + 127) / 128) * (d / 128) < 512)
+    return launch_dl<DCfg<64, 128, 2, 2>>(zb, w_packed, hb, M, d, alpha, s, t);
   if (d >= 128) return launch_dl<DCfg<128, 128, 2, 2>>(zb, w_packed, hb, M, d, alpha, s, t);
   return launch_cfg<Cfg<64, 64, 2, 2, false>, uint16_t>(z, w_packed, hb, M, d, alpha, s, t);
 }
