@@ -91,10 +91,13 @@ struct BwdLayout {
   int max_tiles, wt_block;
 };
 
-// The substrate gradient's reduction over M routed rows is split into
-// dw_splits() equal row ranges (plus one for the remainder) when d is small,
-// so the library GEMM has enough output tiles to fill the chip; the fp32
-// partial products are then summed in a fixed order.
+// bf16 with 128 <= d <= 1024: the library's own MFMA kernel (launch_dw), whose
+// row splits need dw_kernel_splits() partial slices. Otherwise (fp32, small d) the
+// library GEMM, with the reduction over M routed rows split into dw_splits()
+// equal row ranges (plus one for the remainder) when d is small, so it has
+// enough output tiles to fill the chip. Either way the fp32 partial products
+// are summed in a fixed order.
+bool dw_own_kernel(bmoe_dtype dt, int d) { return dt == BMOE_BF16 && d >= 128 && d <= 1024; }
 int dw_splits(int M, int d) {
   if (d >= 2048) return 1;
   const int tiles = d >= 128 ? (d / 128) * (d / 128) : 1;
@@ -102,7 +105,11 @@ int dw_splits(int M, int d) {
   if (S > M / 256) S = M / 256;
   return S < 1 ? 1 : S;
 }
-int dw_slots(int M, int d) {
+int dw_slots(bmoe_dtype dt, int M, int d) {
+  if (dw_own_kernel(dt, d)) {
+    const int S = dw_kernel_splits(M, d);
+    return S > 1 ? S : 0;
+  }
   const int S = dw_splits(M, d);
   return S == 1 ? 0 : S + (M % S != 0 ? 1 : 0);
 }
@@ -134,7 +141,7 @@ BwdLayout bwd_layout(bmoe_dtype dt, int T, int d, int N, int k) {
   l.tile_base = off; off = align_up(off + sizeof(int32_t) * (N + 1));
   l.part_in = off;   off = align_up(off + sizeof(float) * l.max_tiles * L * (d / 2));
   l.part_out = off;  off = align_up(off + sizeof(float) * l.max_tiles * L * (d / 2));
-  l.dw_part = off;   off = align_up(off + sizeof(float) * dw_slots((int)M, d) * d * d);
+  l.dw_part = off;   off = align_up(off + sizeof(float) * dw_slots(dt, (int)M, d) * d * d);
   l.total = off;
   return l;
 }
@@ -148,12 +155,18 @@ bool bwd_shape_ok(bmoe_dtype dt, int T, int d, int N, int k) {
   return shape_ok(dt, T, d, N, k) && d <= 4096;
 }
 
-// dW = alpha * dH^T Z (row-major [d][d], fp32): the column-major product
-// Z_cm * dH_cm^T of the row-major [M][d] matrices viewed column-major. With
+// dW = alpha * dH^T Z (row-major [d][d], fp32). bf16 with d = 128 .. 1024:
+// the library's kernel. Otherwise the library GEMM: the column-major product
+// Z_cm * dH_cm^T of the row-major [M][d] matrices viewed column-major; with
 // S > 1 splits, batch b takes rows b*Kb .. (b+1)*Kb - 1 into part[b], the
 // remainder rows go to part[S], and a kernel sums the slices in order.
 bmoe_status substrate_grad(bmoe_dtype dt, int M, int d, const void* dh, const void* z,
                            float alpha, float* dw, float* part, hipStream_t s) {
+  if (dw_own_kernel(dt, d))
+    return launch_dw(M, d, static_cast<const uint16_t*>(dh), static_cast<const uint16_t*>(z),
+                     alpha, dw, part, s) == hipSuccess
+               ? BMOE_OK
+               : BMOE_E_HIP;
   static std::once_flag once;
   static rocblas_handle handle = nullptr;
   static rocblas_status created = rocblas_status_internal_error;

@@ -1,0 +1,293 @@
+// Substrate gradient dW = alpha * dH^T Z (ButterflyMoE gist.science summary,
+// §2.1 and §2.4: the shared ternary W_base is trained through its latent
+// full-precision copy, whose gradient is the sum over every routed row of
+// the outer product of the product's output gradient dH and its input Z).
+//
+// dH and Z are [M][d] bf16, rows in sorted order; dW is [d][d] fp32, row o
+// (output), column c (input): dW[o][c] = alpha * sum_q dH[q][o] Z[q][c].
+// The reduction index q is the row index of both operands, so both MFMA
+// operands need 8 consecutive q per lane: each K-step's 32 rows of dH and Z
+// go to LDS by DMA with their 16-byte chunks XOR-swizzled by row, and gfx950's
+// transposing LDS read (ds_read_b64_tr_b16) gathers a lane's 4 q values of
+// one column in one instruction.
+//
+// Tiles of 128 x 128 outputs, 4 waves of 64 x 64, v_mfma_f32_32x32x16_bf16
+// fragments, for d = 128 .. 1024 (at d = 2048 and 4096 the library GEMM
+// measured as fast or faster). The rows are split into S equal ranges
+// (multiples of 32) so the grid fills the CUs; split s writes its fp32
+// partial product to part[s] and a second kernel adds the S slices in order,
+// so the result does not depend on scheduling.
+#include "common.h"
+#include "kernels.h"
+
+namespace bmoe {
+namespace {
+
+
+constexpr int kDwRows = 32;  // rows of dH and Z per K-step
+
+template <int BM_, int BN_>
+struct DwCfg {
+  static constexpr int BM = BM_, BN = BN_, THREADS = 256;
+  static constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
+  static constexpr int A_BYTES = kDwRows * BM * 2, B_BYTES = kDwRows * BN * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES, NSTAGE = 4;
+  static constexpr int A_LOADS = A_BYTES / 1024 / 4, B_LOADS = B_BYTES / 1024 / 4;
+  static constexpr int V = A_LOADS + B_LOADS;  // DMA instructions per wave and K-step
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1 && 2 * V <= 63, "DMA counts");
+  static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS budget");
+};
+
+// 16-byte chunk position of chunk ch in LDS row r: rows r..r+3 of a
+// transposing read land on four different 64-byte bank ranges.
+__device__ __forceinline__ int dw_swz(int r, int ch) { return ch ^ ((r & 3) << 2); }
+
+// Sixteen zero bytes: the DMA source of rows past the end of a range.
+__device__ const uint4 kZero16 = {0u, 0u, 0u, 0u};
+
+// Issue K-step rows [q, q + 32) of dH (columns o0 .. o0 + BM) and Z (columns
+// c0 .. c0 + BN) into stage `stg`; rows at or past q_end read zeros.
+template <class C>
+__device__ __forceinline__ void dw_load(char* stg, const uint16_t* dH, const uint16_t* Z, int d,
+                                        int q, int q_end, int o0, int c0, int lane, int wave) {
+  constexpr int ACH = C::BM / 8, BCH = C::BN / 8;  // 16-byte chunks per LDS row
+#pragma unroll
+  for (int j = 0; j < C::A_LOADS; ++j) {
+    const int blk = wave * C::A_LOADS + j;  // 1 KiB of the A region
+    const int e = blk * 64 + lane;          // 16-byte slot
+    const int r = e / ACH, slot = e % ACH;
+    const int ch = dw_swz(r, slot);
+    const void* g = q + r < q_end ? (const void*)(dH + (size_t)(q + r) * d + o0 + ch * 8)
+                                  : (const void*)&kZero16;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)(stg + blk * 1024),
+                                     16, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < C::B_LOADS; ++j) {
+    const int blk = wave * C::B_LOADS + j;
+    const int e = blk * 64 + lane;
+    const int r = e / BCH, slot = e % BCH;
+    const int ch = dw_swz(r, slot);
+    const void* g = q + r < q_end ? (const void*)(Z + (size_t)(q + r) * d + c0 + ch * 8)
+                                  : (const void*)&kZero16;
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)g,
+        (__attribute__((address_space(3))) void*)(stg + C::A_BYTES + blk * 1024), 16, 0, 0);
+  }
+}
+
+// LDS byte offset (within a region of WIDTH columns) of this lane's first
+// transposing read for the 32 columns from col, K-slice 0. In each 16-lane
+// group, lane 4j + q points at row kb + j, columns 4q .. 4q + 3 of the
+// group's 16 (kb = 8 for lanes 32..63); the read hands lane i the group's
+// column i of those 4 rows. Rows kb + 4 .. kb + 7 and K-slice kk (rows
+// + 16 kk) keep the row's swizzle, so they sit 4 and 16 kk rows further on.
+template <int WIDTH>
+__device__ __forceinline__ uint32_t dw_frag_offset(int col, int lane) {
+  const int gr = lane >> 4, L = lane & 15;
+  const int c = col + 16 * (gr & 1) + 4 * (L & 3);
+  const int r0 = 8 * (gr >> 1) + (L >> 2);
+  return (uint32_t)(r0 * (WIDTH * 2) + dw_swz(r0, c >> 3) * 16 + (c & 7) * 2);
+}
+
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+
+// The FM + FN MFMA operands of K-slice KK from LDS addresses aA[i] / aB[j]
+// (first reads): lane l gets column l % 32 of each, rows 16 KK + 8 (l / 32)
+// + 0..7. Inline asm, waiting for its own reads, so the compiler does not add
+// a wait for the DMA filling other stages (it cannot tell them apart).
+template <class C, int KK>
+__device__ __forceinline__ void dw_read(bf16x8 (&fa)[C::FM], bf16x8 (&fb)[C::FN],
+                                        const uint32_t (&aA)[C::FM],
+                                        const uint32_t (&aB)[C::FN]) {
+  constexpr int LO_A = KK * 16 * C::BM * 2, HI_A = LO_A + 4 * C::BM * 2;
+  constexpr int LO_B = KK * 16 * C::BN * 2, HI_B = LO_B + 4 * C::BN * 2;
+  static_assert(C::FM == 2 && C::FN == 2, "operand counts");
+  uint64_t v[2 * (C::FM + C::FN)];
+  {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %4, %10 offset:%14\n\t"
+        "ds_read_b64_tr_b16 %5, %10 offset:%15\n\t"
+        "ds_read_b64_tr_b16 %6, %11 offset:%14\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:%15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+          "=&v"(v[6]), "=&v"(v[7])
+        : "v"(aA[0]), "v"(aA[1]), "v"(aB[0]), "v"(aB[1]), "n"(LO_A), "n"(HI_A), "n"(LO_B),
+          "n"(HI_B));
+  }
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    const u64x2 x = {v[2 * i], v[2 * i + 1]};
+    fa[i] = __builtin_bit_cast(bf16x8, x);
+  }
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) {
+    const u64x2 x = {v[2 * C::FM + 2 * j], v[2 * C::FM + 2 * j + 1]};
+    fb[j] = __builtin_bit_cast(bf16x8, x);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void dw_wait() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
+// K-step kt in ring stage S. The stage is a compile-time constant and every
+// step issues its DMA unconditionally (steps past the range load zeros), so
+// the compiler can tell the stage read here from the stages the DMA is
+// filling and adds no wait of its own for them.
+template <class C, int S>
+__device__ __forceinline__ void dw_step(f32x16 (&acc)[C::FM][C::FN], char* const (&ring)[4],
+                                        const uint32_t (&lds)[4], const uint32_t (&offA)[C::FM],
+                                        const uint32_t (&offB)[C::FN], const uint16_t* dH,
+                                        const uint16_t* Z, int d, int kt, int q_begin,
+                                        int q_end, int o0, int c0, int lane, int wave) {
+  // This wave's loads of step kt have landed once only those of the two
+  // later steps already issued are outstanding.
+  __asm__ volatile("" ::: "memory");
+  dw_wait<2 * C::V>();
+  // Every wave's part of step kt has landed, and every wave is done with
+  // step kt - 1, whose stage the next DMA overwrites.
+  lds_barrier();
+  dw_load<C>(ring[(S + 3) & 3], dH, Z, d, q_begin + (kt + 3) * kDwRows, q_end, o0, c0, lane, wave);
+  __asm__ volatile("" ::: "memory");
+  uint32_t aA[C::FM], aB[C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) aA[i] = lds[S] + offA[i];
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) aB[j] = lds[S] + C::A_BYTES + offB[j];
+  bf16x8 fa[C::FM], fb[C::FN];
+  dw_read<C, 0>(fa, fb, aA, aB);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  dw_read<C, 1>(fa, fb, aA, aB);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+}
+
+// One workgroup: one output tile and one row range of the S. Work item w
+// = split * tiles + t; when the grid is a multiple of 8, XCD x (workgroups
+// dealt round-robin) takes the contiguous items [x * n/8, (x+1) * n/8), so
+// the workgroups sharing rows of dH and Z share that XCD's L2. Tiles run in
+// panels of four tile rows. out: dW (S == 1) or part + split * d * d.
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void dw_kernel(const uint16_t* dH, const uint16_t* Z,
+                                                         int M, int d, int rows_per_split,
+                                                         float alpha, float* out) {
+  __shared__ __attribute__((aligned(1024))) char st0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st3[C::STAGE];
+  char* const ring[4] = {st0, st1, st2, st3};
+  // LDS byte addresses of the stages, for the reads written in asm.
+  const uint32_t lds[4] = {(uint32_t)(size_t)(__attribute__((address_space(3))) char*)st0,
+                           (uint32_t)(size_t)(__attribute__((address_space(3))) char*)st1,
+                           (uint32_t)(size_t)(__attribute__((address_space(3))) char*)st2,
+                           (uint32_t)(size_t)(__attribute__((address_space(3))) char*)st3};
+
+  const int tn = d / C::BN, tm = d / C::BM, tiles = tm * tn;
+  const int n = gridDim.x;
+  const int w = n % 8 == 0 ? (blockIdx.x % 8) * (n / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int split = w / tiles, t = w % tiles;
+  const int P = tm < 4 ? tm : 4;  // tile rows per panel (tm is a power of two)
+  const int o0 = (P * (t / (P * tn)) + t % P) * C::BM;
+  const int c0 = ((t / P) % tn) * C::BN;
+  const int q_begin = split * rows_per_split;
+  const int q_end = min(M, q_begin + rows_per_split);
+  // K-steps rounded up to a multiple of 4 (the extra ones hold zero rows).
+  const int nsteps = q_end > q_begin ? (q_end - q_begin + 4 * kDwRows - 1) / (4 * kDwRows) * 4 : 0;
+  float* dst = out + (size_t)split * d * d;
+
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int wm = wave >> 1, wn = wave & 1;
+  uint32_t offA[C::FM], offB[C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) offA[i] = dw_frag_offset<C::BM>(wm * C::TM + 32 * i, lane);
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) offB[j] = dw_frag_offset<C::BN>(wn * C::TN + 32 * j, lane);
+
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // Steps 0..2 in flight before the loop.
+  dw_load<C>(st0, dH, Z, d, q_begin, q_end, o0, c0, lane, wave);
+  __asm__ volatile("" ::: "memory");
+  dw_load<C>(st1, dH, Z, d, q_begin + kDwRows, q_end, o0, c0, lane, wave);
+  __asm__ volatile("" ::: "memory");
+  dw_load<C>(st2, dH, Z, d, q_begin + 2 * kDwRows, q_end, o0, c0, lane, wave);
+  __asm__ volatile("" ::: "memory");
+  for (int kt = 0; kt < nsteps; kt += 4) {
+    dw_step<C, 0>(acc, ring, lds, offA, offB, dH, Z, d, kt, q_begin, q_end, o0, c0,
+                  lane, wave);
+    dw_step<C, 1>(acc, ring, lds, offA, offB, dH, Z, d, kt + 1, q_begin, q_end, o0, c0,
+                  lane, wave);
+    dw_step<C, 2>(acc, ring, lds, offA, offB, dH, Z, d, kt + 2, q_begin, q_end, o0, c0,
+                  lane, wave);
+    dw_step<C, 3>(acc, ring, lds, offA, offB, dH, Z, d, kt + 3, q_begin, q_end, o0, c0,
+                  lane, wave);
+  }
+  dw_wait<0>();  // no DMA may land in LDS after the workgroup ends
+
+  // 32x32 block layout: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4,
+  // column l%32.
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int col = c0 + wn * C::TN + 32 * j + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = o0 + wm * C::TM + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        dst[(size_t)row * d + col] = alpha * acc[i][j][r];
+      }
+    }
+}
+
+template <class C>
+hipError_t launch_dw_cfg(int M, int d, const uint16_t* dh, const uint16_t* z, float alpha,
+                         float* dw, float* part, int S, hipStream_t s, const KernelTiming& t) {
+  const int tiles = (d / C::BM) * (d / C::BN);
+  const int rows = ((M + S - 1) / S + kDwRows - 1) / kDwRows * kDwRows;
+  float* out = S == 1 ? dw : part;
+  hipError_t e = launch_kernel(dw_kernel<C>, dim3(tiles * S), dim3(C::THREADS), 0, s, t, dh, z, M,
+                               d, rows, alpha, out);
+  if (e != hipSuccess || S == 1) return e;
+  return launch_sum_slices(part, S, (size_t)d * d, dw, s);
+}
+
+}  // namespace
+
+int dw_kernel_splits(int M, int d) {
+  if (d < 128 || d > 1024) return 0;
+  const int tiles = (d / 128) * (d / 128);
+  int S = (256 + tiles - 1) / tiles;
+  const int max_s = M / (16 * kDwRows);  // at least 16 K-steps per split
+  if (S > max_s) S = max_s;
+  return S < 1 ? 1 : S;
+}
+
+hipError_t launch_dw(int M, int d, const uint16_t* dh, const uint16_t* z, float alpha, float* dw,
+                     float* part, hipStream_t s, const KernelTiming& t) {
+  const int S = dw_kernel_splits(M, d);
+  if (S == 0) return hipErrorInvalidValue;
+  return launch_dw_cfg<DwCfg<128, 128>>(M, d, dh, z, alpha, dw, part, S, s, t);
+}
+
+}  // namespace bmoe

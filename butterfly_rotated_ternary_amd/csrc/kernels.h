@@ -108,6 +108,13 @@ hipError_t launch_bfly_bwd(bool in_side, bmoe_dtype dt, int M, int d, int k, con
                            int max_tiles, const int32_t* perm, const float2* cs,
                            const float* gates, const void* src, const void* grad, void* dst,
                            float* dgates, float* partial, hipStream_t s, const KernelTiming& t = {});
+// dW [d][d] fp32 = alpha * dH^T Z for bf16 dH, Z [M][d] (128 <= d <= 1024):
+// MFMA tiles over row ranges; with dw_kernel_splits(M, d) = S > 1 the ranges'
+// partial products go to part [S][d][d] and are summed in order. 0 splits:
+// d outside that range.
+int dw_kernel_splits(int M, int d);
+hipError_t launch_dw(int M, int d, const uint16_t* dh, const uint16_t* z, float alpha, float* dw,
+                     float* part, hipStream_t s, const KernelTiming& t = {});
 // out[i] = sum over b < S of part[b * n + i], in order of b (n % 4 == 0).
 hipError_t launch_sum_slices(const float* part, int S, size_t n, float* out, hipStream_t s);
 // dphi / dtheta [N][L][d/2] = sums over each expert's tiles of the output /

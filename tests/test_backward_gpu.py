@@ -66,7 +66,8 @@ def _check_case(inp, seed):
 @pytest.mark.parametrize("name,T", [
     ("tiny_d64_e8_top2_f32", 256),
     ("d512_e64_top2_bf16", 301),
-    ("d512_e64_top2_bf16", 401),   # substrate gradient split 3 x 267 rows + 1
+    ("d512_e64_top2_bf16", 401),
+    ("d512_e64_top2_bf16", 4103),  # substrate gradient: 16 row ranges, 15 x 544 rows + 46
     ("d512_e256_top2_zipf_bf16", 700),
     ("d2048_e64_top2_outliers_bf16", 97),
     ("d4096_e256_top4_bf16", 23),
