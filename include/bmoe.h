@@ -26,9 +26,10 @@
  *   - All array pointers are DEVICE pointers owned by the caller, 16-byte
  *     aligned. The library allocates nothing on the call path and keeps no
  *     state between calls besides the loaded code object, with one
- *     exception: bmoe_backward with dw != NULL creates, on its first such
- *     call, a rocBLAS handle (which holds device memory of its own) that
- *     lives until the process ends.
+ *     exception: bmoe_backward with dw != NULL, when rocBLAS computes dw
+ *     (fp32, or d outside 128..1024), creates on its first such call a
+ *     rocBLAS handle (which holds device memory of its own) that lives until
+ *     the process ends.
  *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *     asynchronously; a call returns before the GPU finishes.
  *   - A non-BMOE_OK return comes from host-side validation, before anything
@@ -200,9 +201,11 @@ size_t bmoe_backward_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts,
  * The other arguments are bmoe_forward's (same routing and rounding points;
  * the forward is recomputed inside). All outputs are overwritten; dtheta and
  * dphi are summed per expert in a fixed order (run-to-run bit-identical). The
- * dw product is a plain library GEMM (rocBLAS; for d < 2048 split into row
- * ranges whose fp32 products are summed in a fixed order): the first call
- * with dw != NULL creates a rocBLAS handle kept for the life of the process.
+ * dw product is a plain GEMM over the routed rows: the library's own MFMA
+ * kernel for bf16 with 128 <= d <= 1024, else rocBLAS; for d < 2048 it is
+ * split into row ranges whose fp32 products are summed in a fixed order. The
+ * first call that runs it on rocBLAS creates a rocBLAS handle kept for the
+ * life of the process.
  * ws: at least bmoe_backward_workspace_bytes(), 16-byte aligned. Errors as
  * bmoe_forward.
  */
