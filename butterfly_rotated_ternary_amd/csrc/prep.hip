@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
   // ---- routing ----------------------------------------------------------
   extern __shared__ int sh[];
   const int N = p.N, M = p.M;
-  int* cnt = sh;                 // [N] counts, then offsets
+  int* cnt = sh;                 // [N] counts from this chunk on, then totals, then offsets
   int* before = sh + N;          // [N] counts of rows before this chunk, then bases
   int* wcur = sh + 2 * N;        // [kWaves][N] per-wave counts, then cursors
   int* cid = sh + (2 + kWaves) * N;  // [chunk] this chunk's expert ids (clamped)
@@ -128,8 +128,9 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
 
   // Histogram of every id (all blocks need the global offsets), 4 ids per
   // load, a whole batch of loads in flight per thread (one round trip for
-  // M <= 4 * kBatch * kThreads). The ids of this block's chunk go to LDS
-  // from the same loads.
+  // M <= 4 * kBatch * kThreads): rows before this block's chunk count into
+  // `before`, the others into `cnt` (one LDS atomic per id). The ids of this
+  // block's chunk go to LDS from the same loads.
   bool bad = false;
   const int M4 = M / 4;
   const int4* ids4 = reinterpret_cast<const int4*>(p.ids);
@@ -148,22 +149,21 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
       const int r = 4 * i;
       const int e0 = clamp_expert(v[j].x, N, bad), e1 = clamp_expert(v[j].y, N, bad);
       const int e2 = clamp_expert(v[j].z, N, bad), e3 = clamp_expert(v[j].w, N, bad);
-      atomicAdd(&cnt[e0], 1); atomicAdd(&cnt[e1], 1);
-      atomicAdd(&cnt[e2], 1); atomicAdd(&cnt[e3], 1);
-      if (r < r0) {  // chunks start at multiples of 4
-        atomicAdd(&before[e0], 1); atomicAdd(&before[e1], 1);
-        atomicAdd(&before[e2], 1); atomicAdd(&before[e3], 1);
-      } else if (r < r1) {  // r1 - r0 is a multiple of 4 except at M
+      int* h = r < r0 ? before : cnt;  // chunks start at multiples of 4
+      atomicAdd(&h[e0], 1); atomicAdd(&h[e1], 1);
+      atomicAdd(&h[e2], 1); atomicAdd(&h[e3], 1);
+      if (r >= r0 && r < r1) {  // r1 - r0 is a multiple of 4 except at M
         cid[r - r0] = e0; cid[r - r0 + 1] = e1; cid[r - r0 + 2] = e2; cid[r - r0 + 3] = e3;
       }
     }
   }
   for (int r = 4 * M4 + tid; r < M; r += kThreads) {  // the last M % 4 ids
     const int e = clamp_expert(p.ids[r], N, bad);
-    atomicAdd(&cnt[e], 1);
-    if (r < r0) atomicAdd(&before[e], 1);
-    else if (r < r1) cid[r - r0] = e;
+    atomicAdd(r < r0 ? &before[e] : &cnt[e], 1);
+    if (r >= r0 && r < r1) cid[r - r0] = e;
   }
+  __syncthreads();
+  for (int e = tid; e < N; e += kThreads) cnt[e] += before[e];  // totals
   __syncthreads();
 
   // Exclusive scan of the counts: each thread owns a contiguous segment.
