@@ -23,7 +23,6 @@
 namespace bmoe {
 namespace {
 
-
 constexpr int kDwRows = 32;  // rows of dH and Z per K-step
 
 template <int BM_, int BN_>
@@ -105,22 +104,20 @@ __device__ __forceinline__ void dw_read(bf16x8 (&fa)[C::FM], bf16x8 (&fb)[C::FN]
   constexpr int LO_B = KK * 16 * C::BN * 2, HI_B = LO_B + 4 * C::BN * 2;
   static_assert(C::FM == 2 && C::FN == 2, "operand counts");
   uint64_t v[2 * (C::FM + C::FN)];
-  {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
-        "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
-        "ds_read_b64_tr_b16 %4, %10 offset:%14\n\t"
-        "ds_read_b64_tr_b16 %5, %10 offset:%15\n\t"
-        "ds_read_b64_tr_b16 %6, %11 offset:%14\n\t"
-        "ds_read_b64_tr_b16 %7, %11 offset:%15\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
-          "=&v"(v[6]), "=&v"(v[7])
-        : "v"(aA[0]), "v"(aA[1]), "v"(aB[0]), "v"(aB[1]), "n"(LO_A), "n"(HI_A), "n"(LO_B),
-          "n"(HI_B));
-  }
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %4, %10 offset:%14\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:%15\n\t"
+      "ds_read_b64_tr_b16 %6, %11 offset:%14\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:%15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+        "=&v"(v[6]), "=&v"(v[7])
+      : "v"(aA[0]), "v"(aA[1]), "v"(aB[0]), "v"(aB[1]), "n"(LO_A), "n"(HI_A), "n"(LO_B),
+        "n"(HI_B));
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
     const u64x2 x = {v[2 * i], v[2 * i + 1]};
@@ -138,10 +135,10 @@ __device__ __forceinline__ void dw_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
 }
 
-// K-step kt in ring stage S. The stage is a compile-time constant and every
-// step issues its DMA unconditionally (steps past the range load zeros), so
-// the compiler can tell the stage read here from the stages the DMA is
-// filling and adds no wait of its own for them.
+// K-step kt in ring stage S (compile-time). Every step issues its DMA
+// unconditionally (steps past the range load zeros), so each wave has the
+// same count of DMA instructions in flight per step and the wait counts
+// below are exact.
 template <class C, int S>
 __device__ __forceinline__ void dw_step(f32x16 (&acc)[C::FM][C::FN], char* const (&ring)[4],
                                         const uint32_t (&lds)[4], const uint32_t (&offA)[C::FM],
