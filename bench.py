@@ -562,6 +562,27 @@ QUANTISERS = [("int8_absmax", 127, 0), ("int4_absmax", 7, 0), ("ternary_absmax",
               ("ternary_absmean", 1, 1)]
 
 
+def workloads_section(steps, skip):
+    """Forward step time and per-kernel times of the other workloads (the
+    headline and the d = 4096 workload have sections of their own)."""
+    import torch
+    from butterfly_rotated_ternary_amd import workloads as W
+    res = {}
+    for wname in W.WORKLOADS:
+        if wname in skip:
+            continue
+        P = Problem(wname)
+        ms = P.time_steps(steps, 5)
+        per = P.time_kernels(min(steps, 50))
+        res[wname] = {"tokens": P.T, "ms_per_step": ms, "tokens_per_s": P.T / (ms * 1e-3),
+                      "kernels_us": {n: v * 1e3 for n, v in per.items()}}
+        log(f"[bench] {wname}: {ms * 1e3:.1f} us/step, {P.T / (ms * 1e-3):.4g} tokens/s; "
+            + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in per.items()))
+        del P
+        torch.cuda.empty_cache()
+    return res
+
+
 def outliers_section():
     """Outlier spreading on the workload with outlier channels: per-token
     quantisation error and crest factor of x and of z = B(theta_e)^T x (the
@@ -631,6 +652,8 @@ def main():
                     help="backward passes timed on the same workload (0: skip)")
     ap.add_argument("--router-steps", type=int, default=200,
                     help="router passes timed on the same workload (0: skip)")
+    ap.add_argument("--workload-steps", type=int, default=50,
+                    help="forward steps timed for each other workload (0: skip)")
     ap.add_argument("--no-outliers", action="store_true",
                     help="skip the outlier-spreading measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -737,6 +760,9 @@ def main():
             + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in s_per.items()))
         del S
         torch.cuda.empty_cache()
+
+    if args.workload_steps > 0:
+        out["workloads"] = workloads_section(args.workload_steps, skip=(name, GEMM_WORKLOAD))
 
     if not args.no_outliers:
         out["outliers"] = outliers_section()
