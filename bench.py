@@ -127,9 +127,23 @@ def backward_work(name, act_bytes, T, d, N, k):
         if name == "bfly_bwd_out_kernel":
             b += 2 * M * 4                   # gates in, dgates out
         return {"bytes": b, "mfma_flops": 0, "valu_flops": M * L * (d // 2) * 22}
-    if name == "angle_reduce_kernel":       # both sides
-        return {"bytes": 2 * (partial + A * 4), "mfma_flops": 0, "valu_flops": 0}
+    if name == "finish_kernel":             # dx combine, both angle sums, dW slices
+        slices = dw_slices(M, d)
+        b = (M + T) * d * act_bytes + 2 * (partial + A * 4)
+        if slices > 1:
+            b += (slices + 1) * d * d * 4
+        return {"bytes": b, "mfma_flops": 0, "valu_flops": 0}
     raise KeyError(name)
+
+
+def dw_slices(M, d):
+    """Row-range slices of the bf16 substrate gradient the closing kernel sums
+    (the library's split rule for d = 128 .. 1024; 0 or 1: no sum)."""
+    if d < 128 or d > 1024:
+        return 0
+    tiles = (d // 128) ** 2
+    S = min(-(-256 // tiles), M // 512)
+    return max(S, 1)
 
 
 def router_work(name, act_bytes, T, d, N, k):

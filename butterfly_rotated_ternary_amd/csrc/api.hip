@@ -158,10 +158,14 @@ bool bwd_shape_ok(bmoe_dtype dt, int T, int d, int N, int k) {
 // dW = alpha * dH^T Z (row-major [d][d], fp32). bf16 with d = 128 .. 1024:
 // the library's kernel. Otherwise the library GEMM: the column-major product
 // Z_cm * dH_cm^T of the row-major [M][d] matrices viewed column-major; with
-// S > 1 splits, batch b takes rows b*Kb .. (b+1)*Kb - 1 into part[b], the
-// remainder rows go to part[S], and a kernel sums the slices in order.
+// S > 1 splits, batch b takes rows b*Kb .. (b+1)*Kb - 1 into part[b] and the
+// remainder rows go to part[S]; the backward's closing kernel sums the slices
+// in order.
+// *slices: the number of fp32 partial products left in part for the
+// backward's closing kernel to sum (0: dw written directly).
 bmoe_status substrate_grad(bmoe_dtype dt, int M, int d, const void* dh, const void* z,
-                           float alpha, float* dw, float* part, hipStream_t s) {
+                           float alpha, float* dw, float* part, int* slices, hipStream_t s) {
+  *slices = dw_slots(dt, M, d);
   if (dw_own_kernel(dt, d))
     return launch_dw(M, d, static_cast<const uint16_t*>(dh), static_cast<const uint16_t*>(z),
                      alpha, dw, part, s) == hipSuccess
@@ -205,9 +209,7 @@ bmoe_status substrate_grad(bmoe_dtype dt, int M, int d, const void* dh, const vo
                          rocblas_gemm_algo_standard, 0, 0);
     if (st != rocblas_status_success) return BMOE_E_HIP;
   }
-  return launch_sum_slices(part, S + (rest > 0 ? 1 : 0), (size_t)d * d, dw, s) == hipSuccess
-             ? BMOE_OK
-             : BMOE_E_HIP;
+  return BMOE_OK;
 }
 
 }  // namespace
@@ -515,23 +517,25 @@ bmoe_status backward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, con
   if (launch_bfly_bwd(false, dt, M, d, k, tiles, l.max_tiles, rt.perm, cs_out, gates, h, dy, dh,
                       dgates, part_out, s, timing()) != hipSuccess)
     return BMOE_E_HIP;
+  float* dw_part = reinterpret_cast<float*>(base + l.dw_part);
+  int dw_slices = 0;
   {
     const KernelTiming t = timing();
     if (t.start && hipEventRecord(t.start, s) != hipSuccess) return BMOE_E_HIP;
-    if (dw && substrate_grad(dt, M, d, dh, z, alpha, dw,
-                             reinterpret_cast<float*>(base + l.dw_part), s) != BMOE_OK)
+    if (dw && substrate_grad(dt, M, d, dh, z, alpha, dw, dw_part, &dw_slices, s) != BMOE_OK)
       return BMOE_E_HIP;
     if (t.stop && hipEventRecord(t.stop, s) != hipSuccess) return BMOE_E_HIP;
   }
   // dZ = alpha dH W (the product with the transposed substrate).
   if (launch_gemm(dt, M, d, dh, wpt, wtt, alpha, dz, s, timing()) != hipSuccess) return BMOE_E_HIP;
-  // Input side: dX per routed row, dtheta partials; dx_t = sum_j dX[t k + j].
+  // Input side: dX per routed row, dtheta partials.
   if (launch_bfly_bwd(true, dt, M, d, k, tiles, l.max_tiles, rt.perm, cs_in, gates, x, dz, dxr,
                       nullptr, part_in, s, timing()) != hipSuccess)
     return BMOE_E_HIP;
-  if (launch_combine(dt, T, d, k, dxr, dx, s, timing()) != hipSuccess) return BMOE_E_HIP;
-  if (launch_angle_reduce(part_out, part_in, tile_base, n_experts, d, dphi, dtheta, s,
-                          timing()) != hipSuccess)
+  // dx_t = sum_j dX[t k + j], dphi / dtheta from the tile partials, and dW
+  // from its row-range slices, in one launch.
+  if (launch_bwd_finish(dt, T, d, k, dxr, dx, part_out, part_in, tile_base, n_experts, dphi,
+                        dtheta, dw_part, dw_slices, dw, s, timing()) != hipSuccess)
     return BMOE_E_HIP;
   return BMOE_OK;
 }
@@ -582,7 +586,7 @@ namespace {
 const char* const kBackwardNames[] = {
     "prep_kernel",         "bwd_setup_kernel",    "bfly_in_kernel",     "gemm_kernel",
     "bfly_bwd_out_kernel", "substrate_grad_gemm", "gemm_t_kernel",      "bfly_bwd_in_kernel",
-    "combine_kernel",      "angle_reduce_kernel"};
+    "finish_kernel"};
 constexpr int kBackwardLaunches = sizeof(kBackwardNames) / sizeof(kBackwardNames[0]);
 }  // namespace
 

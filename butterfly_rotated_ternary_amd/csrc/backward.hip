@@ -464,39 +464,81 @@ __global__ __launch_bounds__(BwdCfg<D>::NTHR) void bfly_bwd_kernel(BwdParams p) 
   write_partials<D>(V, p.partial + (size_t)blockIdx.x * L * (D / 2), tid, acc);
 }
 
-// dA[e][s][p] = sum of expert e's tile partials, in tile order (0 if no rows),
-// for both sides in one launch: indices below N * per_expert reduce the
-// output side into out0, the rest the input side into out1.
-__global__ __launch_bounds__(256) void angle_reduce_kernel(const float* partial0,
-                                                           const float* partial1,
-                                                           const int32_t* tile_base, int N,
-                                                           int per_expert, float* out0,
-                                                           float* out1) {
-  const size_t n = (size_t)N * per_expert;
-  for (size_t v = (size_t)blockIdx.x * 256 + threadIdx.x; v < 2 * n;
-       v += (size_t)gridDim.x * 256) {
-    const bool second = v >= n;
-    const size_t u = second ? v - n : v;
-    const float* partial = second ? partial1 : partial0;
-    const int e = (int)(u / per_expert), off = (int)(u % per_expert);
-    float s = 0.f;
-    for (int t = tile_base[e]; t < tile_base[e + 1]; ++t) s += partial[(size_t)t * per_expert + off];
-    (second ? out1 : out0)[u] = s;
-  }
-}
+// The backward's closing sums, one launch with three block roles (each a
+// grid-stride loop over its own blocks):
+//   * dx[t] = sum_j dX[t k + j], ascending j, fp32 (like the forward's combine);
+//   * dA[e][s][p] = sum of expert e's tile partials in tile order (0 if no
+//     rows), for both sides: indices below N * per_expert reduce the output
+//     side into dphi, the rest the input side into dtheta;
+//   * dW = sum over the row ranges' fp32 partial products, in range order
+//     (when the substrate gradient was split, else no blocks).
+struct FinishParams {
+  const void* dxr;
+  void* dx;
+  int T, d, k;
+  const float* part_out;
+  const float* part_in;
+  const int32_t* tile_base;
+  int N, per_expert;
+  float* dphi;
+  float* dtheta;
+  const float4* dw_part;
+  int slices;
+  size_t dw4;  // d * d / 4
+  float4* dw;
+  int nb_combine, nb_angle;
+};
 
-__global__ __launch_bounds__(256) void sum_slices_kernel(const float4* part, int S, size_t n4,
-                                                         float4* out) {
-  for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < n4; u += (size_t)gridDim.x * 256) {
-    float4 a = part[u];
-    for (int b = 1; b < S; ++b) {
-      const float4 v = part[(size_t)b * n4 + u];
+template <typename T>
+__global__ __launch_bounds__(256) void finish_kernel(FinishParams p) {
+  const int b = blockIdx.x;
+  if (b < p.nb_combine) {
+    const T* U = static_cast<const T*>(p.dxr);
+    T* y = static_cast<T*>(p.dx);
+    const int d8 = p.d / 8;
+    const size_t n = (size_t)p.T * d8;
+    for (size_t idx = (size_t)b * 256 + threadIdx.x; idx < n; idx += (size_t)p.nb_combine * 256) {
+      const size_t t = idx / d8, c = (idx % d8) * 8;
+      float acc[8];
+      for (int j = 0; j < p.k; ++j) {
+        float v[8];
+        load16<T>(U + (t * p.k + j) * p.d + c, v);
+        if constexpr (sizeof(T) == 4) load16<T>(U + (t * p.k + j) * p.d + c + 4, v + 4);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) acc[m] = j == 0 ? v[m] : acc[m] + v[m];
+      }
+      store16<T>(acc, y + t * p.d + c, 1.0f);
+      if constexpr (sizeof(T) == 4) store16<T>(acc + 4, y + t * p.d + c + 4, 1.0f);
+    }
+    return;
+  }
+  if (b < p.nb_combine + p.nb_angle) {
+    const size_t n = (size_t)p.N * p.per_expert;
+    for (size_t v = (size_t)(b - p.nb_combine) * 256 + threadIdx.x; v < 2 * n;
+         v += (size_t)p.nb_angle * 256) {
+      const bool second = v >= n;
+      const size_t u = second ? v - n : v;
+      const float* partial = second ? p.part_in : p.part_out;
+      const int e = (int)(u / p.per_expert), off = (int)(u % p.per_expert);
+      float sum = 0.f;
+      for (int t = p.tile_base[e]; t < p.tile_base[e + 1]; ++t)
+        sum += partial[(size_t)t * p.per_expert + off];
+      (second ? p.dtheta : p.dphi)[u] = sum;
+    }
+    return;
+  }
+  const int nb = gridDim.x - p.nb_combine - p.nb_angle;
+  for (size_t u = (size_t)(b - p.nb_combine - p.nb_angle) * 256 + threadIdx.x; u < p.dw4;
+       u += (size_t)nb * 256) {
+    float4 a = p.dw_part[u];
+    for (int s = 1; s < p.slices; ++s) {
+      const float4 v = p.dw_part[(size_t)s * p.dw4 + u];
       a.x += v.x;
       a.y += v.y;
       a.z += v.z;
       a.w += v.w;
     }
-    out[u] = a;
+    p.dw[u] = a;
   }
 }
 
@@ -572,20 +614,36 @@ hipError_t launch_bfly_bwd(bool in_side, bmoe_dtype dt, int M, int d, int k, con
                  : launch_bwd<false>(dt, d, max_tiles, p, s, t);
 }
 
-hipError_t launch_sum_slices(const float* part, int S, size_t n, float* out, hipStream_t s) {
-  return launch_kernel(sum_slices_kernel, dim3(grid_for(n / 4)), dim3(256), 0, s, KernelTiming{},
-                       reinterpret_cast<const float4*>(part), S, n / 4,
-                       reinterpret_cast<float4*>(out));
-}
-
-hipError_t launch_angle_reduce(const float* partial_out, const float* partial_in,
-                               const int32_t* tile_base, int N, int d, float* dphi, float* dtheta,
-                               hipStream_t s, const KernelTiming& t) {
+hipError_t launch_bwd_finish(bmoe_dtype dt, int T, int d, int k, const void* dxr, void* dx,
+                             const float* part_out, const float* part_in,
+                             const int32_t* tile_base, int N, float* dphi, float* dtheta,
+                             const float* dw_part, int slices, float* dw, hipStream_t s,
+                             const KernelTiming& t) {
   int L = 0;
   while ((1 << L) < d) ++L;
-  const int per = L * (d / 2);
-  return launch_kernel(angle_reduce_kernel, dim3(grid_for(2 * (size_t)N * per)), dim3(256), 0, s,
-                       t, partial_out, partial_in, tile_base, N, per, dphi, dtheta);
+  FinishParams p;
+  p.dxr = dxr;
+  p.dx = dx;
+  p.T = T;
+  p.d = d;
+  p.k = k;
+  p.part_out = part_out;
+  p.part_in = part_in;
+  p.tile_base = tile_base;
+  p.N = N;
+  p.per_expert = L * (d / 2);
+  p.dphi = dphi;
+  p.dtheta = dtheta;
+  p.dw_part = reinterpret_cast<const float4*>(dw_part);
+  p.slices = slices;
+  p.dw4 = (size_t)d * d / 4;
+  p.dw = reinterpret_cast<float4*>(dw);
+  p.nb_combine = grid_for((size_t)T * (d / 8));
+  p.nb_angle = grid_for(2 * (size_t)N * p.per_expert);
+  const int nb_dw = slices > 1 && dw ? grid_for(p.dw4) : 0;
+  const dim3 grid(p.nb_combine + p.nb_angle + nb_dw);
+  if (dt == BMOE_BF16) return launch_kernel(finish_kernel<uint16_t>, grid, dim3(256), 0, s, t, p);
+  return launch_kernel(finish_kernel<float>, grid, dim3(256), 0, s, t, p);
 }
 
 }  // namespace bmoe

@@ -15,8 +15,8 @@
 // fragments, for d = 128 .. 1024 (at d = 2048 and 4096 the library GEMM
 // measured as fast or faster). The rows are split into S equal ranges
 // (multiples of 32) so the grid fills the CUs; split s writes its fp32
-// partial product to part[s] and a second kernel adds the S slices in order,
-// so the result does not depend on scheduling.
+// partial product to part[s], and the backward's closing kernel adds the S
+// slices in order, so the result does not depend on scheduling.
 #include "common.h"
 #include "kernels.h"
 
@@ -263,10 +263,8 @@ hipError_t launch_dw_cfg(int M, int d, const uint16_t* dh, const uint16_t* z, fl
   const int tiles = (d / C::BM) * (d / C::BN);
   const int rows = ((M + S - 1) / S + kDwRows - 1) / kDwRows * kDwRows;
   float* out = S == 1 ? dw : part;
-  hipError_t e = launch_kernel(dw_kernel<C>, dim3(tiles * S), dim3(C::THREADS), 0, s, t, dh, z, M,
-                               d, rows, alpha, out);
-  if (e != hipSuccess || S == 1) return e;
-  return launch_sum_slices(part, S, (size_t)d * d, dw, s);
+  return launch_kernel(dw_kernel<C>, dim3(tiles * S), dim3(C::THREADS), 0, s, t, dh, z, M, d, rows,
+                       alpha, out);
 }
 
 }  // namespace

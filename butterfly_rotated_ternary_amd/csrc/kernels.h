@@ -109,19 +109,22 @@ hipError_t launch_bfly_bwd(bool in_side, bmoe_dtype dt, int M, int d, int k, con
                            const float* gates, const void* src, const void* grad, void* dst,
                            float* dgates, float* partial, hipStream_t s, const KernelTiming& t = {});
 // dW [d][d] fp32 = alpha * dH^T Z for bf16 dH, Z [M][d] (128 <= d <= 1024):
-// MFMA tiles over row ranges; with dw_kernel_splits(M, d) = S > 1 the ranges'
-// partial products go to part [S][d][d] and are summed in order. 0 splits:
-// d outside that range.
+// MFMA tiles over row ranges. With dw_kernel_splits(M, d) = S > 1 the ranges'
+// partial products go to part [S][d][d] (launch_bwd_finish sums them), else
+// straight to dw. 0 splits: d outside that range.
 int dw_kernel_splits(int M, int d);
 hipError_t launch_dw(int M, int d, const uint16_t* dh, const uint16_t* z, float alpha, float* dw,
                      float* part, hipStream_t s, const KernelTiming& t = {});
-// out[i] = sum over b < S of part[b * n + i], in order of b (n % 4 == 0).
-hipError_t launch_sum_slices(const float* part, int S, size_t n, float* out, hipStream_t s);
-// dphi / dtheta [N][L][d/2] = sums over each expert's tiles of the output /
-// input side partials [tiles][L][d/2], in tile order (one launch).
-hipError_t launch_angle_reduce(const float* partial_out, const float* partial_in,
-                               const int32_t* tile_base, int N, int d, float* dphi, float* dtheta,
-                               hipStream_t s, const KernelTiming& t = {});
+// The backward's closing sums in one launch: dx[t] = sum_j dxr[t k + j]
+// (ascending j, fp32; dtype dt); dphi / dtheta [N][L][d/2] = sums over each
+// expert's tiles of the output / input side partials [tiles][L][d/2], in tile
+// order; and, when slices > 1 and dw is set, dw [d][d] = sum over the slices
+// of dw_part [slices][d][d], in order.
+hipError_t launch_bwd_finish(bmoe_dtype dt, int T, int d, int k, const void* dxr, void* dx,
+                             const float* part_out, const float* part_in,
+                             const int32_t* tile_base, int N, float* dphi, float* dtheta,
+                             const float* dw_part, int slices, float* dw, hipStream_t s,
+                             const KernelTiming& t = {});
 
 // ---- outlier measurement ---------------------------------------------------------
 // Per row of src [rows][d] (dtype dt): err = ||v - q|| / ||v|| with
