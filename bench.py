@@ -112,11 +112,12 @@ def backward_work(name, act_bytes, T, d, N, k):
     tiles = -(-M // 64) + N                  # upper bound on expert-aligned row tiles
     partial = tiles * L * (d // 2) * 4
     routing = M * 4
-    if name in ("prep_kernel", "bfly_in_kernel", "gemm_kernel", "combine_kernel"):
+    if name == "prep_kernel":               # the forward's prep + tile list and packed W_base^T
+        w = kernel_work(name, act_bytes, T, d, N, k)
+        w["bytes"] += d * d // 4 * (3 if d % 512 == 0 else 2) + (N + 1) * 4 * 2 + tiles * 16
+        return w
+    if name in ("bfly_in_kernel", "gemm_kernel", "combine_kernel"):
         return kernel_work(name, act_bytes, T, d, N, k)
-    if name == "bwd_setup_kernel":          # tile list + packed W_base^T (1 or 2 copies)
-        return {"bytes": d * d // 4 * (3 if d % 512 == 0 else 2) + (N + 1) * 4 * 2 + tiles * 16,
-                "mfma_flops": 0, "valu_flops": 0}
     if name == "gemm_t_kernel":
         return kernel_work("gemm_kernel", act_bytes, T, d, N, k)
     if name == "substrate_grad_gemm":

@@ -26,7 +26,9 @@ int log2i(int d) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct FwdLayout {
-  size_t status, offsets, perm, inv, slot_e, cs_in, cs_out, z, h, u, w16, wt, total;
+  size_t status, offsets, perm, inv, slot_e, cs_in, cs_out, z, h, u, w16, wt, tiles, tile_base,
+      wpt, wtt, total;
+  int max_tiles;
 };
 
 bool shape_ok(bmoe_dtype dt, int T, int d, int N, int k) {
@@ -37,7 +39,8 @@ bool shape_ok(bmoe_dtype dt, int T, int d, int N, int k) {
 }
 
 // keep: the unfused path, with Z and H left in the workspace (with the
-// routing and cos/sin tables) for a later bmoe_backward_kept.
+// routing and cos/sin tables, and the backward's row tiles and packed
+// W_base^T) for a later bmoe_backward_kept.
 FwdLayout fwd_layout(bmoe_dtype dt, int T, int d, int N, int k, bool keep = false) {
   FwdLayout l{};
   const size_t M = (size_t)T * k;
@@ -61,7 +64,13 @@ FwdLayout fwd_layout(bmoe_dtype dt, int T, int d, int N, int k, bool keep = fals
   if (fused) off = align_up(off + sizeof(uint16_t) * (size_t)d * d);
   // Tile-major copy of the packed substrate for the large-tile product.
   l.wt = off;
-  if (gemm_tiled_w_block(dt, (int)M, d)) off = align_up(off + sizeof(uint32_t) * (size_t)d * (d / 16));
+  const bool wt_copy = gemm_tiled_w_block(dt, (int)M, d) != 0;
+  if (wt_copy) off = align_up(off + sizeof(uint32_t) * (size_t)d * (d / 16));
+  l.max_tiles = keep ? bwd_max_tiles((int)M, N, d) : 0;
+  l.tiles = off;     if (keep) off = align_up(off + sizeof(int4) * l.max_tiles);
+  l.tile_base = off; if (keep) off = align_up(off + sizeof(int32_t) * (N + 1));
+  l.wpt = off;       if (keep) off = align_up(off + sizeof(uint32_t) * (size_t)d * (d / 16));
+  l.wtt = off;       if (keep && wt_copy) off = align_up(off + sizeof(uint32_t) * (size_t)d * (d / 16));
   l.total = off;
   return l;
 }
@@ -340,8 +349,18 @@ bmoe_status forward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, cons
   uint16_t* w16 = fused ? reinterpret_cast<uint16_t*>(base + l.w16) : nullptr;
   const int wt_block = gemm_tiled_w_block(dt, M, d);
   uint32_t* wt = wt_block ? reinterpret_cast<uint32_t*>(base + l.wt) : nullptr;
+  BwdSetup bs;  // keep: the backward's tiles and W_base^T, for bmoe_backward_kept
+  if (keep) {
+    bs.tiles = reinterpret_cast<int4*>(base + l.tiles);
+    bs.tile_base = reinterpret_cast<int32_t*>(base + l.tile_base);
+    bs.max_tiles = l.max_tiles;
+    bs.tile_rows = bwd_tile_rows_for(d);
+    bs.wpt = reinterpret_cast<uint32_t*>(base + l.wpt);
+    bs.wtt = wt_block ? reinterpret_cast<uint32_t*>(base + l.wtt) : nullptr;
+    bs.wtt_block = wt_block;
+  }
   if (launch_prep(ids, M, n_experts, theta, phi, d, rt, cs_in, cs_out, status, w_packed, w16, wt,
-                  wt_block, s, timing()) != hipSuccess)
+                  wt_block, s, timing(), bs) != hipSuccess)
     return BMOE_E_HIP;
   if (fused) {
     if (launch_fused(M, d, k, x, gates, rt, cs_in, cs_out, w16, w_packed, alpha, u, s,
@@ -469,10 +488,12 @@ bmoe_status backward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, con
   void* dh = base + l.dh;
   void* dxr = base + l.dx;
   uint32_t* wt = l.wt_block ? reinterpret_cast<uint32_t*>(base + l.wt) : nullptr;
-  uint32_t* wpt = reinterpret_cast<uint32_t*>(base + l.wpt);
-  uint32_t* wtt = l.wt_block ? reinterpret_cast<uint32_t*>(base + l.wtt) : nullptr;
-  int4* tiles = reinterpret_cast<int4*>(base + l.tiles);
-  int32_t* tile_base = reinterpret_cast<int32_t*>(base + l.tile_base);
+  // Row tiles and W_base^T: written by this call's prep, or the kept forward's.
+  uint32_t* wpt = reinterpret_cast<uint32_t*>(src + (kept ? fl.wpt : l.wpt));
+  uint32_t* wtt =
+      l.wt_block ? reinterpret_cast<uint32_t*>(src + (kept ? fl.wtt : l.wtt)) : nullptr;
+  int4* tiles = reinterpret_cast<int4*>(src + (kept ? fl.tiles : l.tiles));
+  int32_t* tile_base = reinterpret_cast<int32_t*>(src + (kept ? fl.tile_base : l.tile_base));
   float* part_in = reinterpret_cast<float*>(base + l.part_in);
   float* part_out = reinterpret_cast<float*>(base + l.part_out);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -494,18 +515,25 @@ bmoe_status backward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, con
     return (!t.start || hipEventRecord(t.start, s) == hipSuccess) &&
            (!t.stop || hipEventRecord(t.stop, s) == hipSuccess);
   };
-  // Forward recompute: routing, cos/sin, Z = B^T x, H = alpha Z W^T.
+  // Forward recompute: routing, cos/sin (with the row tiles and W_base^T),
+  // Z = B^T x, H = alpha Z W^T.
   if (kept) {
-    // Bad ids were the forward's to report; the setup kernel below clears
-    // this workspace's status word.
+    // Bad ids were the forward's to report; the closing kernel clears this
+    // workspace's status word.
     if (!skip()) return BMOE_E_HIP;
-  } else if (launch_prep(ids, M, n_experts, theta, phi, d, rt, cs_in, cs_out, status, w_packed,
-                         nullptr, wt, l.wt_block, s, timing()) != hipSuccess) {
-    return BMOE_E_HIP;
+  } else {
+    BwdSetup bs;
+    bs.tiles = tiles;
+    bs.tile_base = tile_base;
+    bs.max_tiles = l.max_tiles;
+    bs.tile_rows = bwd_tile_rows_for(d);
+    bs.wpt = wpt;
+    bs.wtt = wtt;
+    bs.wtt_block = l.wt_block;
+    if (launch_prep(ids, M, n_experts, theta, phi, d, rt, cs_in, cs_out, status, w_packed, nullptr,
+                    wt, l.wt_block, s, timing(), bs) != hipSuccess)
+      return BMOE_E_HIP;
   }
-  if (launch_bwd_setup(rt.offsets, n_experts, d, tiles, tile_base, l.max_tiles, w_packed, wpt, wtt,
-                       l.wt_block, kept ? status : nullptr, s, timing()) != hipSuccess)
-    return BMOE_E_HIP;
   if (kept) {
     if (!skip() || !skip()) return BMOE_E_HIP;
   } else {
@@ -535,7 +563,8 @@ bmoe_status backward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, con
   // dx_t = sum_j dX[t k + j], dphi / dtheta from the tile partials, and dW
   // from its row-range slices, in one launch.
   if (launch_bwd_finish(dt, T, d, k, dxr, dx, part_out, part_in, tile_base, n_experts, dphi,
-                        dtheta, dw_part, dw_slices, dw, s, timing()) != hipSuccess)
+                        dtheta, dw_part, dw_slices, dw, kept ? status : nullptr, s,
+                        timing()) != hipSuccess)
     return BMOE_E_HIP;
   return BMOE_OK;
 }
@@ -584,9 +613,8 @@ bmoe_status bmoe_backward(bmoe_dtype dt, int T, int d, int n_experts, int k, con
 
 namespace {
 const char* const kBackwardNames[] = {
-    "prep_kernel",         "bwd_setup_kernel",    "bfly_in_kernel",     "gemm_kernel",
-    "bfly_bwd_out_kernel", "substrate_grad_gemm", "gemm_t_kernel",      "bfly_bwd_in_kernel",
-    "finish_kernel"};
+    "prep_kernel",         "bfly_in_kernel",      "gemm_kernel",        "bfly_bwd_out_kernel",
+    "substrate_grad_gemm", "gemm_t_kernel",       "bfly_bwd_in_kernel", "finish_kernel"};
 constexpr int kBackwardLaunches = sizeof(kBackwardNames) / sizeof(kBackwardNames[0]);
 }  // namespace
 

@@ -27,81 +27,6 @@ namespace {
 
 __device__ __forceinline__ int pad(int i) { return i + (i >> 3); }
 
-// ---- backward setup: expert-aligned row tiles + packed W_base^T -------------
-// Block 0: tiles[i] = (expert, first sorted row, end row, 0), at most tr rows
-// each; tile_base[e] = first tile of expert e, tile_base[N] = number of
-// tiles; unused entries get expert -1.
-// Blocks 1..: one thread per word of W^T: row c, columns o = 16 g .. 16 g + 15
-// (the codes W[o][c]), written row-major (wpt) and, when cb > 0, into the
-// tile-major copy the large-tile GEMM reads (wtt: 4-word K-steps of 64
-// columns, cb rows each).
-__device__ __forceinline__ int code_pos(int v) { return (v & 1) ? 16 + 2 * (v >> 1) : 2 * (v >> 1); }
-
-constexpr int kSetupThreads = 256;
-
-__device__ void tiles_role(const int32_t* offsets, int N, int tr, int4* tiles, int32_t* tile_base,
-                           int max_tiles) {
-  __shared__ int scan[kSetupThreads];
-  __shared__ int carry;
-  const int tid = threadIdx.x;
-  if (tid == 0) carry = 0;
-  __syncthreads();
-  for (int e0 = 0; e0 < N; e0 += kSetupThreads) {
-    const int e = e0 + tid;
-    const int cnt = e < N ? offsets[e + 1] - offsets[e] : 0;
-    const int nt = (cnt + tr - 1) / tr;
-    scan[tid] = nt;
-    __syncthreads();
-    for (int off = 1; off < kSetupThreads; off <<= 1) {
-      const int v = tid >= off ? scan[tid - off] : 0;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
-    }
-    const int base = carry + scan[tid] - nt;
-    if (e < N) {
-      tile_base[e] = base;
-      const int q0 = offsets[e];
-      for (int i = 0; i < nt; ++i)
-        tiles[base + i] = make_int4(e, q0 + i * tr, min(q0 + (i + 1) * tr, q0 + cnt), 0);
-    }
-    __syncthreads();
-    if (tid == kSetupThreads - 1) carry += scan[kSetupThreads - 1];
-    __syncthreads();
-  }
-  const int total = carry;
-  if (tid == 0) tile_base[N] = total;
-  for (int i = total + tid; i < max_tiles; i += kSetupThreads) tiles[i] = make_int4(-1, 0, 0, 0);
-}
-
-__global__ __launch_bounds__(kSetupThreads) void bwd_setup_kernel(
-    const int32_t* offsets, int N, int tr, int4* tiles, int32_t* tile_base, int max_tiles,
-    const uint32_t* wp, int d, uint32_t* wpt, uint32_t* wtt, int cb, int32_t* status) {
-  if (blockIdx.x == 0) {
-    if (status && threadIdx.x == 0) *status = BMOE_OK;
-    tiles_role(offsets, N, tr, tiles, tile_base, max_tiles);
-    return;
-  }
-  const int G = d / 16;
-  const size_t n = (size_t)d * G;
-  for (size_t u = (size_t)(blockIdx.x - 1) * kSetupThreads + threadIdx.x; u < n;
-       u += (size_t)(gridDim.x - 1) * kSetupThreads) {
-    const int c = (int)(u / G), g = (int)(u % G);
-    const int cw = c / 16, cpos = code_pos(c % 16);
-    uint32_t out = 0u;
-#pragma unroll
-    for (int o16 = 0; o16 < 16; ++o16) {
-      const uint32_t code = (wp[(size_t)(g * 16 + o16) * G + cw] >> cpos) & 3u;
-      out |= code << code_pos(o16);
-    }
-    wpt[(size_t)c * G + g] = out;
-    if (cb > 0) {
-      const int nk = d / 64;
-      wtt[(((size_t)(c / cb) * nk + g / 4) * cb + c % cb) * 4 + g % 4] = out;
-    }
-  }
-}
-
 // ---- butterfly backward --------------------------------------------------------
 // Stages are grouped three at a time as in the forward kernels: group g holds
 // stages 3g .. min(3g + 3, L) - 1. A thread owns register blocks of a group
@@ -486,12 +411,14 @@ struct FinishParams {
   int slices;
   size_t dw4;  // d * d / 4
   float4* dw;
+  int32_t* status;
   int nb_combine, nb_angle;
 };
 
 template <typename T>
 __global__ __launch_bounds__(256) void finish_kernel(FinishParams p) {
   const int b = blockIdx.x;
+  if (b == 0 && threadIdx.x == 0 && p.status) *p.status = BMOE_OK;
   if (b < p.nb_combine) {
     const T* U = static_cast<const T*>(p.dxr);
     T* y = static_cast<T*>(p.dx);
@@ -584,14 +511,7 @@ int bwd_max_tiles(int M, int N, int d) {
   return (M + tr - 1) / tr + N;
 }
 
-hipError_t launch_bwd_setup(const int32_t* offsets, int N, int d, int4* tiles,
-                           int32_t* tile_base, int max_tiles, const uint32_t* wp, uint32_t* wpt,
-                           uint32_t* wtt, int cb, int32_t* status, hipStream_t s,
-                           const KernelTiming& t) {
-  return launch_kernel(bwd_setup_kernel, dim3(1 + grid_for((size_t)d * (d / 16))),
-                       dim3(kSetupThreads), 0, s, t, offsets, N, bwd_tile_rows(d), tiles,
-                       tile_base, max_tiles, wp, d, wpt, wtt, cb, status);
-}
+int bwd_tile_rows_for(int d) { return bwd_tile_rows(d); }
 
 hipError_t launch_bfly_bwd(bool in_side, bmoe_dtype dt, int M, int d, int k, const int4* tiles,
                            int max_tiles, const int32_t* perm, const float2* cs,
@@ -617,8 +537,8 @@ hipError_t launch_bfly_bwd(bool in_side, bmoe_dtype dt, int M, int d, int k, con
 hipError_t launch_bwd_finish(bmoe_dtype dt, int T, int d, int k, const void* dxr, void* dx,
                              const float* part_out, const float* part_in,
                              const int32_t* tile_base, int N, float* dphi, float* dtheta,
-                             const float* dw_part, int slices, float* dw, hipStream_t s,
-                             const KernelTiming& t) {
+                             const float* dw_part, int slices, float* dw, int32_t* status,
+                             hipStream_t s, const KernelTiming& t) {
   int L = 0;
   while ((1 << L) < d) ++L;
   FinishParams p;
@@ -638,6 +558,7 @@ hipError_t launch_bwd_finish(bmoe_dtype dt, int T, int d, int k, const void* dxr
   p.slices = slices;
   p.dw4 = (size_t)d * d / 4;
   p.dw = reinterpret_cast<float4*>(dw);
+  p.status = status;
   p.nb_combine = grid_for((size_t)T * (d / 8));
   p.nb_angle = grid_for(2 * (size_t)N * p.per_expert);
   const int nb_dw = slices > 1 && dw ? grid_for(p.dw4) : 0;

@@ -30,14 +30,30 @@ struct RouteTables {
   int32_t* slot_e;   // [M] sorted slot -> expert
 };
 
+// What the backward needs besides the forward's tables: expert-aligned row
+// tiles (tiles[i] = (expert, first sorted row, end row, 0), at most
+// tile_rows rows each; tile_base[e] = first tile of expert e, tile_base[N] =
+// number of tiles; entries up to max_tiles past the last get expert -1) and
+// the packed W_base^T, row-major (wpt) and, when wtt_block > 0, in the
+// large-tile GEMM's tile-major order (wtt). tiles == NULL: none.
+struct BwdSetup {
+  int4* tiles = nullptr;
+  int32_t* tile_base = nullptr;
+  int max_tiles = 0, tile_rows = 0;
+  uint32_t* wpt = nullptr;
+  uint32_t* wtt = nullptr;
+  int wtt_block = 0;
+};
+
 // Routing (histogram, scan, stable scatter), the per-call cos/sin tables of
-// both rotation sides and, optionally, a per-call copy of the packed
-// substrate for the product: w16 (bf16 expansion, d <= 512 fused path) or wt
-// (tile-major packed words for the large-tile GEMM), in one launch.
+// both rotation sides, optionally a per-call copy of the packed substrate for
+// the product (w16: bf16 expansion, d <= 512 fused path; wt: tile-major
+// packed words for the large-tile GEMM) and optionally the backward's setup,
+// in one launch.
 hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, const float* phi,
                        int d, RouteTables rt, float2* cs_in, float2* cs_out, int32_t* status,
                        const uint32_t* w_packed, uint16_t* w16, uint32_t* wt, int wt_block,
-                       hipStream_t s, const KernelTiming& t = {});
+                       hipStream_t s, const KernelTiming& t = {}, const BwdSetup& bs = {});
 
 // Column block CB of the tile-major substrate copy `wt` the large-tile GEMM
 // reads, or 0 when launch_gemm does not use that kernel. For output-column
@@ -88,18 +104,10 @@ hipError_t launch_pack(const int8_t* w, int d, uint32_t* packed, int32_t* status
                        hipStream_t s);
 
 // ---- backward ----------------------------------------------------------------
-// Upper bound on the expert-aligned row tiles of the backward kernels.
+// Upper bound on the expert-aligned row tiles of the backward kernels, and
+// the rows per tile (BwdSetup::tile_rows).
 int bwd_max_tiles(int M, int N, int d);
-// One launch: the tile list from the routing offsets (tiles[i] = (expert, q0,
-// q1, 0) with at most a d-dependent number of sorted rows each; tile_base[e] =
-// first tile of expert e, tile_base[N] = count; unused entries have expert
-// -1), and packed W_base^T (row c holds the codes of column c) row-major into
-// wpt and, when cb > 0, in the large-tile GEMM's tile-major order into wtt.
-// status (may be NULL): set to BMOE_OK.
-hipError_t launch_bwd_setup(const int32_t* offsets, int N, int d, int4* tiles,
-                           int32_t* tile_base, int max_tiles, const uint32_t* wp, uint32_t* wpt,
-                           uint32_t* wtt, int cb, int32_t* status, hipStream_t s,
-                           const KernelTiming& t = {});
+int bwd_tile_rows_for(int d);
 // Butterfly backward over the tiles. Output side (in_side = false): src = H
 // (sorted), grad = dy (token rows) -> dst = dH (sorted), dgates, partials of
 // dphi. Input side: src = x (token rows), grad = dZ (sorted) -> dst = dX
@@ -119,12 +127,12 @@ hipError_t launch_dw(int M, int d, const uint16_t* dh, const uint16_t* z, float 
 // (ascending j, fp32; dtype dt); dphi / dtheta [N][L][d/2] = sums over each
 // expert's tiles of the output / input side partials [tiles][L][d/2], in tile
 // order; and, when slices > 1 and dw is set, dw [d][d] = sum over the slices
-// of dw_part [slices][d][d], in order.
+// of dw_part [slices][d][d], in order. status (may be NULL): set to BMOE_OK.
 hipError_t launch_bwd_finish(bmoe_dtype dt, int T, int d, int k, const void* dxr, void* dx,
                              const float* part_out, const float* part_in,
                              const int32_t* tile_base, int N, float* dphi, float* dtheta,
-                             const float* dw_part, int slices, float* dw, hipStream_t s,
-                             const KernelTiming& t = {});
+                             const float* dw_part, int slices, float* dw, int32_t* status,
+                             hipStream_t s, const KernelTiming& t = {});
 
 // ---- outlier measurement ---------------------------------------------------------
 // Per row of src [rows][d] (dtype dt): err = ||v - q|| / ||v|| with

@@ -1,5 +1,7 @@
 // Per-call preparation, one launch:
-//  * (fused path) the packed substrate expanded to bf16 rows once per call;
+//  * (fused path) the packed substrate expanded to bf16 rows once per call,
+//    or (large-tile product) copied into tile-major order;
+//  * (backward) the expert-aligned row tiles and the packed W_base^T;
 //  * routing: per-expert histogram, exclusive scan and a stable scatter of
 //    routed rows r = t*k + j grouped by expert (ascending r inside a group);
 //  * the cos/sin tables of both rotation sides, computed once per call so no
@@ -33,8 +35,49 @@ struct PrepParams {
   uint16_t* w16;
   uint32_t* wt;
   int wt_block;
-  int d, n_trig_blocks;
+  int d, n_trig_blocks, n_w_blocks, n_wt_blocks;
+  BwdSetup bs;
 };
+
+// 2-bit code position of column v within a packed word (column 2j at bit
+// 2j, column 2j+1 at bit 16 + 2j).
+__device__ __forceinline__ int code_pos(int v) { return (v & 1) ? 16 + 2 * (v >> 1) : 2 * (v >> 1); }
+
+// Backward tile list from the routing offsets (one 256-thread block).
+__device__ void tiles_role(const int32_t* offsets, int N, int tr, int4* tiles, int32_t* tile_base,
+                           int max_tiles) {
+  __shared__ int scan[kThreads];
+  __shared__ int carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int e0 = 0; e0 < N; e0 += kThreads) {
+    const int e = e0 + tid;
+    const int cnt = e < N ? offsets[e + 1] - offsets[e] : 0;
+    const int nt = (cnt + tr - 1) / tr;
+    scan[tid] = nt;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      const int v = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const int base = carry + scan[tid] - nt;
+    if (e < N) {
+      tile_base[e] = base;
+      const int q0 = offsets[e];
+      for (int i = 0; i < nt; ++i)
+        tiles[base + i] = make_int4(e, q0 + i * tr, min(q0 + (i + 1) * tr, q0 + cnt), 0);
+    }
+    __syncthreads();
+    if (tid == kThreads - 1) carry += scan[kThreads - 1];
+    __syncthreads();
+  }
+  const int total = carry;
+  if (tid == 0) tile_base[N] = total;
+  for (int i = total + tid; i < max_tiles; i += kThreads) tiles[i] = make_int4(-1, 0, 0, 0);
+}
 
 __device__ __forceinline__ int clamp_expert(int e, int N, bool& bad) {
   if ((unsigned)e >= (unsigned)N) {
@@ -62,15 +105,38 @@ __device__ int block_exclusive_scan(int v, int* scratch) {
 }
 
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
-  if ((int)blockIdx.x >= p.n_route_blocks + p.n_trig_blocks && p.wt) {
+  const int b_w = p.n_route_blocks + p.n_trig_blocks, b_wt = b_w + p.n_w_blocks;
+  if ((int)blockIdx.x >= b_wt) {
+    // ---- packed W_base^T: one thread per word (row c of W^T holds the codes
+    // of column c of W, 16 per word; word g covers rows o = 16g .. 16g+15) --
+    const int G = p.d / 16;
+    const size_t n = (size_t)p.d * G;
+    for (size_t u = (size_t)(blockIdx.x - b_wt) * kThreads + threadIdx.x; u < n;
+         u += (size_t)p.n_wt_blocks * kThreads) {
+      const int c = (int)(u / G), g = (int)(u % G);
+      const int cw = c / 16, cpos = code_pos(c % 16);
+      uint32_t out = 0u;
+#pragma unroll
+      for (int o16 = 0; o16 < 16; ++o16) {
+        const uint32_t code = (p.w_packed[(size_t)(g * 16 + o16) * G + cw] >> cpos) & 3u;
+        out |= code << code_pos(o16);
+      }
+      p.bs.wpt[(size_t)c * G + g] = out;
+      if (p.bs.wtt_block > 0) {
+        const int cb = p.bs.wtt_block, nk = p.d / 64;
+        p.bs.wtt[(((size_t)(c / cb) * nk + g / 4) * cb + c % cb) * 4 + g % 4] = out;
+      }
+    }
+    return;
+  }
+  if ((int)blockIdx.x >= b_w && p.wt) {
     // ---- packed substrate -> tile-major order ---------------------------
     // Destination-ordered: uint4 u = (ob * nk + kt) * CB + oo holds the 16
     // bytes of row ob * CB + oo for K-step kt.
     const int nk = p.d / 64;
     const size_t cb = (size_t)p.wt_block;
     const size_t n = (size_t)p.d * nk;
-    const int b = blockIdx.x - p.n_route_blocks - p.n_trig_blocks;
-    const int nb = gridDim.x - p.n_route_blocks - p.n_trig_blocks;
+    const int b = blockIdx.x - b_w, nb = p.n_w_blocks;
     for (size_t u = (size_t)b * kThreads + threadIdx.x; u < n; u += (size_t)nb * kThreads) {
       const size_t oo = u % cb, rest = u / cb;
       const size_t kt = rest % nk, ob = rest / nk;
@@ -80,12 +146,11 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
     }
     return;
   }
-  if ((int)blockIdx.x >= p.n_route_blocks + p.n_trig_blocks) {
+  if ((int)blockIdx.x >= b_w) {
     // ---- packed substrate -> bf16 rows ----------------------------------
     const int G = p.d / 16;
     const size_t nwords = (size_t)p.d * G;
-    const int b = blockIdx.x - p.n_route_blocks - p.n_trig_blocks;
-    const int nb = gridDim.x - p.n_route_blocks - p.n_trig_blocks;
+    const int b = blockIdx.x - b_w, nb = p.n_w_blocks;
     for (size_t i = (size_t)b * kThreads + threadIdx.x; i < nwords; i += (size_t)nb * kThreads) {
       const uint32_t w = p.w_packed[i];
       uint4* dst = reinterpret_cast<uint4*>(p.w16 + i * 16);
@@ -232,6 +297,11 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
     }
     __builtin_amdgcn_wave_barrier();
   }
+
+  if (blockIdx.x == 0 && p.bs.tiles) {
+    __syncthreads();  // this block wrote the offsets above
+    tiles_role(p.rt.offsets, N, p.bs.tile_rows, p.bs.tiles, p.bs.tile_base, p.bs.max_tiles);
+  }
 }
 
 }  // namespace
@@ -239,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
 hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, const float* phi,
                        int d, RouteTables rt, float2* cs_in, float2* cs_out, int32_t* status,
                        const uint32_t* w_packed, uint16_t* w16, uint32_t* wt, int wt_block,
-                       hipStream_t s, const KernelTiming& t) {
+                       hipStream_t s, const KernelTiming& t, const BwdSetup& bs) {
   int L = 0;
   while ((1 << L) < d) ++L;
   PrepParams p;
@@ -274,13 +344,21 @@ hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, con
     const long long quads = (long long)d * (d / 64);
     w_blocks = (int)((quads + kThreads * 4 - 1) / (kThreads * 4));
   }
+  p.n_w_blocks = w_blocks;
+  p.bs = bs;
+  p.n_wt_blocks = 0;
+  if (bs.tiles) {
+    const long long words = (long long)d * (d / 16);
+    p.n_wt_blocks = (int)((words + kThreads * 4 - 1) / (kThreads * 4));
+  }
   const size_t shmem = sizeof(int) * ((size_t)(2 + kWaves) * N + p.chunk);
   if (shmem > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
   }
-  return launch_kernel(prep_kernel, dim3(p.n_route_blocks + p.n_trig_blocks + w_blocks),
+  return launch_kernel(prep_kernel,
+                       dim3(p.n_route_blocks + p.n_trig_blocks + w_blocks + p.n_wt_blocks),
                        dim3(kThreads), (uint32_t)shmem, s, t, p);
 }
 

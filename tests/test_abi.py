@@ -93,12 +93,12 @@ def test_backward_launch_table_and_validation():
     bf = bmoe.BMOE_BF16
     names = [bmoe.bmoe_backward_kernel_name(bf, 64, 512, 8, 2, i)
              for i in range(bmoe.bmoe_backward_kernel_count(bf, 64, 512, 8, 2))]
-    assert len(names) == 9 and len(set(names)) == 9
+    assert len(names) == 8 and len(set(names)) == 8
     assert "bfly_bwd_out_kernel" in names and "gemm_t_kernel" in names
-    assert "bwd_setup_kernel" in names and names[-1] == "finish_kernel"
+    assert names[0] == "prep_kernel" and names[-1] == "finish_kernel"
     assert bmoe.bmoe_backward_kernel_count(bf, 64, 8192, 8, 2) == 0   # d > 4096
     assert bmoe.bmoe_backward_kernel_count(bf, 0, 512, 8, 2) == 0
-    assert bmoe.bmoe_backward_kernel_name(bf, 64, 512, 8, 2, 9) == ""
+    assert bmoe.bmoe_backward_kernel_name(bf, 64, 512, 8, 2, 8) == ""
     assert bmoe.bmoe_backward_workspace_bytes(bf, 64, 8192, 8, 2) == 0
     assert bmoe.bmoe_backward_workspace_bytes(bf, 64, 4096, 8, 2) > 0
     lib = bmoe.lib()
