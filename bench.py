@@ -67,12 +67,14 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
-def kernel_work(name, act_bytes, T, d, N, k):
+def kernel_work(name, act_bytes, T, d, N, k, routed=False):
     """Algorithmic work of one launch of a forward kernel: the bytes it must
     move to or from HBM (each input read once, each output written once), the
     flops of its dense contraction (MFMA) and the flops of its rotations
     (fp32 VALU: 2 multiplies and 2 fused multiply-adds, 6 flops, per pair and
-    stage). act_bytes is the size of one activation element (x, Z, H, U, y)."""
+    stage). act_bytes is the size of one activation element (x, Z, H, U, y).
+    routed: the fused kernel routes itself (no prep launch): it reads the ids,
+    both angle sets and the packed substrate, and writes the routing tables."""
     M = T * k
     L = d.bit_length() - 1
     A = N * L * (d // 2)                     # angles (pairs) per side
@@ -83,6 +85,10 @@ def kernel_work(name, act_bytes, T, d, N, k):
         if act_bytes == 2 and d in (256, 512):
             b += d * d // 4 + d * d * 2      # bf16 expansion of the packed substrate
         return {"bytes": b, "mfma_flops": 0, "valu_flops": 0}
+    if name.startswith("fused") and routed:
+        b = (T * d * act_bytes + M * d * act_bytes + d * d // 4 + 2 * A * 4
+             + 5 * routing + (N + 1) * 4)     # ids and gates in; perm, inv, slot_e out
+        return {"bytes": b, "mfma_flops": 2 * M * d * d, "valu_flops": 2 * rot}
     if name.startswith("fused"):
         b = (T * d * act_bytes + M * d * act_bytes + d * d * 2 + 2 * A * 8
              + 2 * routing + M * 4)
@@ -699,13 +705,14 @@ def main():
     log("[bench] per-kernel us (dispatch events): "
         + ", ".join(f"{n}={v * 1e3:.2f}" for n, v in per_kernel.items()))
     dom = max(per_kernel, key=per_kernel.get)
-    work = kernel_work(dom, P.act_bytes, T, d, N, k)
+    routed = "prep_kernel" not in per_kernel
+    work = kernel_work(dom, P.act_bytes, T, d, N, k, routed)
     roof = roofline(work, per_kernel[dom] * 1e-3, P.mfma_peak())
     roof["traffic"] = stored_traffic(dom, name)
     roof["kernel"] = dom
     others = {}
     for n, v in per_kernel.items():
-        r = roofline(kernel_work(n, P.act_bytes, T, d, N, k), v * 1e-3, P.mfma_peak())
+        r = roofline(kernel_work(n, P.act_bytes, T, d, N, k, routed), v * 1e-3, P.mfma_peak())
         others[n] = {"us": v * 1e3, "bound": r["bound"], "frac": r["frac"]}
 
     M = T * k

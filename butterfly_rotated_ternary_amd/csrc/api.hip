@@ -52,16 +52,19 @@ FwdLayout fwd_layout(bmoe_dtype dt, int T, int d, int N, int k, bool keep = fals
   l.perm = off;    off = align_up(off + sizeof(int32_t) * M);
   l.inv = off;     off = align_up(off + sizeof(int32_t) * M);
   l.slot_e = off;  off = align_up(off + sizeof(int32_t) * M);
-  l.cs_in = off;   off = align_up(off + sizeof(float2) * N * L * (d / 2));
-  l.cs_out = off;  off = align_up(off + sizeof(float2) * N * L * (d / 2));
   const bool fused = !keep && fused_supported(dt, d);
+  // The routed fused kernel computes its own coefficient tables and streams
+  // no bf16 substrate.
+  const bool routed = fused && fused_routes(dt, (int)M, d, N);
+  l.cs_in = off;   if (!routed) off = align_up(off + sizeof(float2) * N * L * (d / 2));
+  l.cs_out = off;  if (!routed) off = align_up(off + sizeof(float2) * N * L * (d / 2));
   // The fused path keeps Z and H on chip; only U (and the bf16 substrate)
   // live in the workspace.
   l.z = off;       if (!fused) off = align_up(off + zel * M * d);
   l.h = off;       if (!fused) off = align_up(off + zel * M * d);
   l.u = off;       off = align_up(off + zel * M * d);
   l.w16 = off;
-  if (fused) off = align_up(off + sizeof(uint16_t) * (size_t)d * d);
+  if (fused && !routed) off = align_up(off + sizeof(uint16_t) * (size_t)d * d);
   // Tile-major copy of the packed substrate for the large-tile product.
   l.wt = off;
   const bool wt_copy = gemm_tiled_w_block(dt, (int)M, d) != 0;
@@ -346,7 +349,8 @@ bmoe_status forward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, cons
     return t;
   };
   const bool fused = !keep && fused_supported(dt, d);
-  uint16_t* w16 = fused ? reinterpret_cast<uint16_t*>(base + l.w16) : nullptr;
+  const bool routed = fused && fused_routes(dt, M, d, n_experts);
+  uint16_t* w16 = fused && !routed ? reinterpret_cast<uint16_t*>(base + l.w16) : nullptr;
   const int wt_block = gemm_tiled_w_block(dt, M, d);
   uint32_t* wt = wt_block ? reinterpret_cast<uint32_t*>(base + l.wt) : nullptr;
   BwdSetup bs;  // keep: the backward's tiles and W_base^T, for bmoe_backward_kept
@@ -358,6 +362,14 @@ bmoe_status forward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, cons
     bs.wpt = reinterpret_cast<uint32_t*>(base + l.wpt);
     bs.wtt = wt_block ? reinterpret_cast<uint32_t*>(base + l.wtt) : nullptr;
     bs.wtt_block = wt_block;
+  }
+  if (routed) {
+    // Routing and coefficient tables inside the fused kernel: no prep launch.
+    if (launch_fused_routed(M, d, k, n_experts, x, ids, gates, theta, phi, w_packed, alpha, u, rt,
+                            status, s, timing()) != hipSuccess)
+      return BMOE_E_HIP;
+    if (launch_combine(dt, T, d, k, u, y, s, timing()) != hipSuccess) return BMOE_E_HIP;
+    return BMOE_OK;
   }
   if (launch_prep(ids, M, n_experts, theta, phi, d, rt, cs_in, cs_out, status, w_packed, w16, wt,
                   wt_block, s, timing(), bs) != hipSuccess)
@@ -411,14 +423,17 @@ bmoe_status bmoe_forward(bmoe_dtype dt, int T, int d, int n_experts, int k, cons
 
 int bmoe_forward_kernel_count(bmoe_dtype dt, int T, int d, int n_experts, int k) {
   if (!shape_ok(dt, T, d, n_experts, k) || T == 0) return 0;
+  if (fused_routes(dt, T * k, d, n_experts)) return 2;
   return fused_supported(dt, d) ? 3 : 5;
 }
 
 const char* bmoe_forward_kernel_name(bmoe_dtype dt, int T, int d, int n_experts, int k, int i) {
+  static const char* routed_names[] = {"fused_kernel", "combine_kernel"};
   static const char* fused_names[] = {"prep_kernel", "fused_kernel", "combine_kernel"};
   static const char* split_names[] = {"prep_kernel", "bfly_in_kernel", "gemm_kernel",
                                       "bfly_out_kernel", "combine_kernel"};
   if (i < 0 || i >= bmoe_forward_kernel_count(dt, T, d, n_experts, k)) return "";
+  if (fused_routes(dt, T * k, d, n_experts)) return routed_names[i];
   return fused_supported(dt, d) ? fused_names[i] : split_names[i];
 }
 

@@ -61,8 +61,10 @@ hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, con
 // uint4 index (ob * (d/64) + kt) * CB + o % CB of `wt`.
 int gemm_tiled_w_block(bmoe_dtype dt, int M, int d);
 
-// Whether the fused d <= 512 path handles this shape.
+// Whether the fused d <= 512 path handles this shape, and whether its routed
+// variant (no prep launch) does: M <= 8192 routed rows and N <= 512 experts.
 bool fused_supported(bmoe_dtype dt, int d);
+bool fused_routes(bmoe_dtype dt, int M, int d, int N);
 
 // Fused per-tile forward for d <= 512 (bf16): U[r] = g_r * B(phi_e) *
 // alpha * W_base * B(theta_e)^T x[t] for every routed row, in routed order.
@@ -70,6 +72,17 @@ hipError_t launch_fused(int M, int d, int k, const void* x, const float* gates,
                         const RouteTables& rt, const float2* cs_in, const float2* cs_out,
                         const uint16_t* w16, const uint32_t* w_packed, float alpha, void* u,
                         hipStream_t s, const KernelTiming& t = {});
+
+// The same with the routing and the cos/sin tables computed inside: each
+// workgroup ranks its own 32 sorted rows from all M ids (stable, ascending
+// routed index within an expert) and writes their entries of rt (perm, inv,
+// slot_e; workgroup 0 also offsets[0..N] and *status, BMOE_E_EXPERT for an
+// id outside [0, N)). Requires fused_routes(BMOE_BF16, M, d, N).
+hipError_t launch_fused_routed(int M, int d, int k, int N, const void* x, const int32_t* ids,
+                               const float* gates, const float* theta, const float* phi,
+                               const uint32_t* w_packed, float alpha, void* u,
+                               const RouteTables& rt, int32_t* status, hipStream_t s,
+                               const KernelTiming& t = {});
 
 // Z[q] = B(theta_e)^T x[t]   (t = perm[q] / k, e = slot_e[q]).
 // routed_out: row perm[q] of z instead of row q (routed order).

@@ -79,7 +79,8 @@ size_t bmoe_param_count(int d, int n_experts);
 
 /* Workspace bytes bmoe_forward needs for this shape (0 if the shape is
  * invalid). The workspace holds the routing tables, the per-call rotation
- * coefficient tables and the intermediate activations. */
+ * coefficient tables (on the shapes that compute them in a separate launch)
+ * and the intermediate activations. */
 size_t bmoe_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts, int k);
 
 /* Workspace bytes bmoe_pack_ternary needs (a status word). */
@@ -149,6 +150,12 @@ bmoe_status bmoe_unpack_ternary_b3_timed(const uint8_t* packed3, int d, uint32_t
  * T = 0 is a no-op. Bad expert ids are clamped for addressing (so every
  * access stays in bounds) and reported by bmoe_sync_status(); y is then
  * unspecified.
+ * For bf16 with d = 256 or 512, T*k <= 8192 and N <= 512, one kernel does
+ * the whole per-row computation, routing included (then the combine); it
+ * evaluates the rotation coefficients on the hardware sine/cosine unit
+ * (about 1e-6 absolute error). Other shapes compute them with sincosf in a
+ * preparation launch. Both are far inside the bf16 tolerance, but the two
+ * are not bit-identical.
  */
 bmoe_status bmoe_forward(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
                          const int32_t* ids, const float* gates, const float* theta,

@@ -89,6 +89,25 @@ def test_host_validation_needs_no_gpu():
     assert lib.bmoe_pack_ternary(None, 16, None, None, 0, None) == 1
 
 
+def test_forward_launch_table():
+    bf, f32 = bmoe.BMOE_BF16, bmoe.BMOE_F32
+
+    def names(dt, T, d, N, k):
+        return [bmoe.bmoe_forward_kernel_name(dt, T, d, N, k, i)
+                for i in range(bmoe.bmoe_forward_kernel_count(dt, T, d, N, k))]
+    # fused d = 512 with routing inside: up to 8192 routed rows and 512 experts
+    assert names(bf, 4096, 512, 64, 2) == ["fused_kernel", "combine_kernel"]
+    assert names(bf, 4096, 512, 512, 2) == ["fused_kernel", "combine_kernel"]
+    # beyond either limit the prep kernel routes
+    assert names(bf, 4097, 512, 64, 2) == ["prep_kernel", "fused_kernel", "combine_kernel"]
+    assert names(bf, 64, 256, 513, 2) == ["prep_kernel", "fused_kernel", "combine_kernel"]
+    # split path
+    assert names(f32, 64, 512, 8, 2) == ["prep_kernel", "bfly_in_kernel", "gemm_kernel",
+                                         "bfly_out_kernel", "combine_kernel"]
+    assert names(bf, 64, 1024, 8, 2)[0] == "prep_kernel"
+    assert bmoe.bmoe_forward_kernel_name(bf, 4096, 512, 64, 2, 2) == ""
+
+
 def test_backward_launch_table_and_validation():
     bf = bmoe.BMOE_BF16
     names = [bmoe.bmoe_backward_kernel_name(bf, 64, 512, 8, 2, i)
