@@ -662,6 +662,10 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
     __asm__ volatile("" ::: "memory");
   }
   const int my_t = my_r / a.k;
+  // Routed: lane i holds row i's gate, requested now (it is long in by the
+  // stores).
+  float my_g = 0.f;
+  if constexpr (RT) my_g = a.gates[my_r];
 
   // Gather x rows (8 bf16 per 16-byte chunk) into registers and fetch the
   // butterfly-in coefficients. Token indices come from the lanes holding them
@@ -841,10 +845,10 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
       rows.row(row)[padi(col)] = a.alpha * acc[j][r];
     }
   }
-  // Routed: lane i holds row i's gate (it lands during the butterfly).
-  float my_g = 0.f;
-  if constexpr (RT) my_g = a.gates[my_r];
-  __syncthreads();
+  // The rows are complete (the routed variant has no global loads left to
+  // order here).
+  if constexpr (RT) lds_barrier();
+  else __syncthreads();
 
   cout.apply(rows, a.cs_out, sh_e, tab, e_tab);
 
