@@ -159,9 +159,10 @@ __device__ __forceinline__ void load_coef_lds(float2 (&c)[3][4], const float2* t
 
 // Routed variant: (cos x, sin x) on the transcendental unit, whose v_sin /
 // v_cos take revolutions. x is first reduced to [-pi, pi] by subtracting the
-// nearest multiple of 2pi in two parts (Cody and Waite's method: 2pi split
-// into its nearest float and the remainder, so k * 2pi_hi is exact for
-// |k| < 2^16), then scaled by 1/2pi. About 1e-6 absolute error.
+// nearest multiple of 2pi in two fused steps (Cody and Waite's method: 2pi
+// split into its nearest float and the remainder), then scaled by 1/2pi.
+// Measured against double precision: at most 4e-7 absolute error for
+// |x| <= 1000 (sincosf: 7e-8).
 __device__ __forceinline__ float2 tile_cos_sin(float x) {
   constexpr float kInv2Pi = 0.159154943091895336f;
   constexpr float k2PiHi = 6.28318548202514648f;   // float(2 pi)
