@@ -137,7 +137,10 @@ def test_identity_substrate_equal_angles(dtype):
 
 
 @pytest.mark.parametrize("d,N,k,T", [(16, 1, 1, 1), (32, 3, 3, 5), (64, 300, 1, 1000),
-                                     (1024, 2, 2, 33), (8192, 4, 2, 3)])
+                                     (1024, 2, 2, 33), (8192, 4, 2, 3),
+                                     # the routed fused kernel at its limits:
+                                     # 8192 routed rows, 512 experts
+                                     (256, 64, 2, 4096), (512, 512, 1, 8192)])
 def test_edge_shapes(d, N, k, T):
     inp = W.make_inputs("custom", d=d, N=N, k=k, T=T, seed=d + N, dtype="bf16")
     _announce(f"[edge] d={d} N={N} k={k} T={T}")
