@@ -44,6 +44,16 @@ constexpr int kRouteMaxN = 512;
 
 __device__ __forceinline__ int padi(int i) { return i + (i >> 3); }
 
+// Sorted slot q of a tile lives in LDS row row_of_slot(q). The butterfly
+// threads of phase p rotate rows p, p + 8, p + 16 and p + 24 (three-stage
+// groups at d = 512), which then hold the four consecutive slots 4p .. 4p+3:
+// the rows of one thread, and of one wave, stay inside one expert wherever
+// the tile's expert boundary allows. Any permutation is correct; this one
+// keeps each thread's slots ascending.
+static_assert(kBM == 32, "the slot permutation is written for 32-row tiles");
+__device__ __forceinline__ int row_of_slot(int q) { return 8 * (q % 4) + q / 4; }
+__device__ __forceinline__ int slot_of_row(int l) { return 4 * (l % 8) + l / 8; }
+
 template <int D>
 struct FCfg {
   static constexpr int L = D == 128 ? 7 : D == 256 ? 8 : 9;
@@ -488,9 +498,10 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int q0 = blockIdx.x * kBM;
   const int nr = min(kBM, a.M - q0);
-  // Lane l < 32 of every wave keeps row l's (expert, routed index) in
-  // registers (an LDS copy serves the butterflies). Rows past the end repeat
-  // the last row's expert (their values are zero).
+  // Lane l < 32 of every wave keeps the (expert, routed index) of LDS row l,
+  // that is of slot slot_of_row(l), in registers (an LDS copy serves the
+  // butterflies). Rows of slots past the end repeat the last slot (computed,
+  // never stored).
   int my_e, my_r, e_tab, e_first = -1, e_last = -1;
   float th[RT ? NTB : 1];
   if constexpr (RT) {
@@ -627,27 +638,32 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
       for (int j = 0; j < kRouteIds; ++j) {
         if (j < nv && id[j] == e) {
           if ((unsigned)q < (unsigned)nr) {
-            sh_e[q] = e;
-            sh_r[q] = i0 + j;
+            sh_e[row_of_slot(q)] = e;
+            sh_r[row_of_slot(q)] = i0 + j;
           }
           ++q;
         }
       }
     }
     lds_barrier();
-    const int li = min(lane & 31, nr - 1);
+    // Lane l < 32 holds LDS row l (slot sl); rows of slots past nr repeat
+    // the last slot.
+    const int sl = slot_of_row(lane & 31);
+    const int li = sl < nr ? (lane & 31) : row_of_slot(nr - 1);
     my_e = sh_e[li];
     my_r = sh_r[li];
-    if (tid < nr) {
-      a.rt.perm[q0 + tid] = my_r;
-      a.rt.inv[my_r] = q0 + tid;
-      a.rt.slot_e[q0 + tid] = my_e;
-    } else if (tid < kBM) {
-      sh_e[tid] = my_e;  // tail rows repeat the last row
-      sh_r[tid] = my_r;
+    if (tid < kBM) {
+      if (sl < nr) {
+        a.rt.perm[q0 + sl] = my_r;
+        a.rt.inv[my_r] = q0 + sl;
+        a.rt.slot_e[q0 + sl] = my_e;
+      } else {
+        sh_e[tid] = my_e;
+        sh_r[tid] = my_r;
+      }
     }
   } else {
-    const int q_meta = q0 + min(lane & 31, nr - 1);
+    const int q_meta = q0 + min(slot_of_row(lane & 31), nr - 1);
     my_e = a.slot_e[q_meta];
     my_r = a.perm[q_meta];
     if (tid < kBM) {
@@ -860,7 +876,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
     const int i = c / CPR, ch = c % CPR;
     float g = 0.f;
     if constexpr (RT) g = __shfl(my_g, i, 64);
-    if (i < nr) {
+    if (slot_of_row(i) < nr) {
       const int r = sh_r[i];
       if constexpr (!RT) g = a.gates[r];
       const float* s = rows.row(i) + padi(ch * 8);
