@@ -247,20 +247,8 @@ struct BflyCoef {
     }
   }
 
-  __device__ __forceinline__ void prefetch(const float2* cs, const int* sh_e) {
-#pragma unroll
-    for (int g = 0; g < Gr::N; ++g) {
-      const int G = Gr::G(g), s_lo = Gr::s_lo(g);
-      const int nb = D >> G;
-      const int base = block_base(threadIdx.x % nb, s_lo, G);
-      e[g] = sh_e[threadIdx.x / nb];
-      if (G == 3) load_coef<D, 3>(c[g], cs, e[g], s_lo, base);
-      else if (G == 2) load_coef<D, 2>(c[g], cs, e[g], s_lo, base);
-      else load_coef<D, 1>(c[g], cs, e[g], s_lo, base);
-    }
-  }
-
-  // As prefetch(), reading the expert of row i from lane i's `lane_e`.
+  // Coefficients of every group for the expert of the thread's first row,
+  // read from lane i's `lane_e` for row i.
   __device__ __forceinline__ void prefetch_from_lanes(const float2* cs, int lane_e) {
 #pragma unroll
     for (int g = 0; g < Gr::N; ++g) {
@@ -279,7 +267,6 @@ struct BflyCoef {
                                               const float2* cs, const float2* tab, int e_tab,
                                               int g, int s_lo, int base,
                                               const int (&off)[8], int ph, int tpb) {
-    constexpr int RPT_MAX = kBM;  // loop bound; actual rows per thread = kBM / tpb
     const int rpt = kBM / tpb;
     const int first = ph, last = ph + (rpt - 1) * tpb;
     if (sh_e[first] == e[g] && sh_e[last] == e[g]) {
@@ -306,7 +293,6 @@ struct BflyCoef {
           }
         }
       }
-      (void)RPT_MAX;
       return;
     }
     for (int j = 0; j < rpt; ++j) {
