@@ -140,7 +140,9 @@ def test_identity_substrate_equal_angles(dtype):
                                      (1024, 2, 2, 33), (8192, 4, 2, 3),
                                      # the routed fused kernel at its limits:
                                      # 8192 routed rows, 512 experts
-                                     (256, 64, 2, 4096), (512, 512, 1, 8192)])
+                                     (256, 64, 2, 4096), (512, 512, 1, 8192),
+                                     # routed: top-3 and top-4, one expert
+                                     (256, 8, 3, 111), (512, 16, 4, 300), (512, 1, 1, 100)])
 def test_edge_shapes(d, N, k, T):
     inp = W.make_inputs("custom", d=d, N=N, k=k, T=T, seed=d + N, dtype="bf16")
     _announce(f"[edge] d={d} N={N} k={k} T={T}")
@@ -246,12 +248,13 @@ def test_bitwise_deterministic():
         assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("d", [64, 512])
-def test_out_of_range_expert_is_reported(d):
-    """d = 512 routes inside the fused kernel, d = 64 in the prep kernel."""
+@pytest.mark.parametrize("d,bad", [(64, 4), (512, 4), (512, -1)])
+def test_out_of_range_expert_is_reported(d, bad):
+    """d = 512 routes inside the fused kernel, d = 64 in the prep kernel;
+    ids past either end are clamped for addressing and reported."""
     inp = W.make_inputs("custom", d=d, N=4, k=2, T=20, seed=6, dtype="bf16")
     dev = to_device(inp)
-    dev["ids"][3, 1] = 4
+    dev["ids"][3, 1] = bad
     ws = bmoe.Workspace(bmoe.BMOE_BF16, inp.T, inp.d, inp.N, inp.k)
     bmoe.forward(dev["x"], dev["ids"], dev["gates"], dev["theta"], dev["phi"], dev["w_packed"],
                  dev["alpha"], ws=ws)
