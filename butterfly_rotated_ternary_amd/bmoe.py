@@ -6,6 +6,7 @@ no CPU fallback: if the library is missing, loading it raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -119,6 +120,14 @@ def _ptr(t: Optional[torch.Tensor]):
 def _stream(stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _on(stream=None):
+    """Make `stream` torch's current stream while a wrapper allocates and
+    launches: the caching allocator then ties the temporary workspace and the
+    outputs to the stream the kernels run on, so memory freed when the wrapper
+    returns is not handed to other work before those kernels finish."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
 
 
 def _check(code: int, what: str):
@@ -358,17 +367,18 @@ class Workspace:
 def forward(x: torch.Tensor, ids: torch.Tensor, gates: torch.Tensor, theta: torch.Tensor,
             phi: torch.Tensor, w_packed: torch.Tensor, alpha: float, *, y=None, ws=None,
             route_out=None, stream=None) -> torch.Tensor:
-    T, d = x.shape
-    k = ids.shape[1]
-    N = theta.shape[0]
-    dt = dtype_code(x)
-    if y is None:
-        y = torch.empty_like(x)
-    if ws is None:
-        ws = Workspace(dt, T, d, N, k, device=x.device)
-    _check(bmoe_forward(dt, T, d, N, k, x, ids, gates, theta, phi, w_packed, alpha, y, ws.buf,
-                        route_out, stream), "bmoe_forward")
-    return y
+    with _on(stream):
+        T, d = x.shape
+        k = ids.shape[1]
+        N = theta.shape[0]
+        dt = dtype_code(x)
+        if y is None:
+            y = torch.empty_like(x)
+        if ws is None:
+            ws = Workspace(dt, T, d, N, k, device=x.device)
+        _check(bmoe_forward(dt, T, d, N, k, x, ids, gates, theta, phi, w_packed, alpha, y, ws.buf,
+                            route_out, stream), "bmoe_forward")
+        return y
 
 
 def backward(x: torch.Tensor, ids: torch.Tensor, gates: torch.Tensor, theta: torch.Tensor,
@@ -376,48 +386,50 @@ def backward(x: torch.Tensor, ids: torch.Tensor, gates: torch.Tensor, theta: tor
              want_dw: bool = True, stream=None) -> dict:
     """Gradients of sum(dy * y) for the layer bmoe_forward computes: dict of
     dx (dtype of x), dgates, dtheta, dphi and (want_dw) dw, all fp32 but dx."""
-    T, d = x.shape
-    k = ids.shape[1]
-    N = theta.shape[0]
-    dt = dtype_code(x)
-    n = bmoe_backward_workspace_bytes(dt, T, d, N, k)
-    if n == 0:
-        raise BmoeError(2, "bmoe_backward_workspace_bytes")
-    ws = torch.empty(n, dtype=torch.uint8, device=x.device)
-    out = {
-        "dx": torch.empty_like(x),
-        "dgates": torch.empty(T, k, dtype=torch.float32, device=x.device),
-        "dtheta": torch.empty_like(theta),
-        "dphi": torch.empty_like(phi),
-        "dw": torch.empty(d, d, dtype=torch.float32, device=x.device) if want_dw else None,
-    }
-    _check(bmoe_backward(dt, T, d, N, k, x, ids, gates, theta, phi, w_packed, alpha, dy,
-                         out["dx"], out["dgates"], out["dtheta"], out["dphi"], out["dw"], ws,
-                         stream), "bmoe_backward")
-    return out
+    with _on(stream):
+        T, d = x.shape
+        k = ids.shape[1]
+        N = theta.shape[0]
+        dt = dtype_code(x)
+        n = bmoe_backward_workspace_bytes(dt, T, d, N, k)
+        if n == 0:
+            raise BmoeError(2, "bmoe_backward_workspace_bytes")
+        ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+        out = {
+            "dx": torch.empty_like(x),
+            "dgates": torch.empty(T, k, dtype=torch.float32, device=x.device),
+            "dtheta": torch.empty_like(theta),
+            "dphi": torch.empty_like(phi),
+            "dw": torch.empty(d, d, dtype=torch.float32, device=x.device) if want_dw else None,
+        }
+        _check(bmoe_backward(dt, T, d, N, k, x, ids, gates, theta, phi, w_packed, alpha, dy,
+                             out["dx"], out["dgates"], out["dtheta"], out["dphi"], out["dw"], ws,
+                             stream), "bmoe_backward")
+        return out
 
 
 def route(x: torch.Tensor, w_router: torch.Tensor, k: int, *, want_logits: bool = False,
           stream=None):
     """Router: (ids int32 [T][k], gates fp32 [T][k]) for bmoe_forward, plus
     the fp32 [T][N] logits when want_logits."""
-    T, d = x.shape
-    N = w_router.shape[0]
-    dt = dtype_code(x)
-    if w_router.dtype != x.dtype or w_router.shape[1] != d:
-        raise ValueError("w_router must be [N][d] in x's dtype")
-    ids = torch.empty(T, k, dtype=torch.int32, device=x.device)
-    gates = torch.empty(T, k, dtype=torch.float32, device=x.device)
-    logits = torch.empty(T, N, dtype=torch.float32, device=x.device) if want_logits else None
-    ws = None
-    if logits is None:
-        n = bmoe_router_workspace_bytes(dt, T, d, N, k)
-        if n == 0:
-            raise BmoeError(2, "bmoe_router_workspace_bytes")
-        ws = torch.empty(n, dtype=torch.uint8, device=x.device)
-    _check(bmoe_router(dt, T, d, N, k, x, w_router, ids, gates, logits, ws, stream),
-           "bmoe_router")
-    return (ids, gates, logits) if want_logits else (ids, gates)
+    with _on(stream):
+        T, d = x.shape
+        N = w_router.shape[0]
+        dt = dtype_code(x)
+        if w_router.dtype != x.dtype or w_router.shape[1] != d:
+            raise ValueError("w_router must be [N][d] in x's dtype")
+        ids = torch.empty(T, k, dtype=torch.int32, device=x.device)
+        gates = torch.empty(T, k, dtype=torch.float32, device=x.device)
+        logits = torch.empty(T, N, dtype=torch.float32, device=x.device) if want_logits else None
+        ws = None
+        if logits is None:
+            n = bmoe_router_workspace_bytes(dt, T, d, N, k)
+            if n == 0:
+                raise BmoeError(2, "bmoe_router_workspace_bytes")
+            ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+        _check(bmoe_router(dt, T, d, N, k, x, w_router, ids, gates, logits, ws, stream),
+               "bmoe_router")
+        return (ids, gates, logits) if want_logits else (ids, gates)
 
 
 def pack_ternary_b3(w: torch.Tensor) -> torch.Tensor:
@@ -474,18 +486,19 @@ def forward_keep(x: torch.Tensor, ids: torch.Tensor, gates: torch.Tensor, theta:
     """(y, kept workspace): the forward on the unfused path, with its routing
     tables, cos/sin tables, Z and H left in the returned workspace for
     backward_kept."""
-    T, d = x.shape
-    k = ids.shape[1]
-    N = theta.shape[0]
-    dt = dtype_code(x)
-    n = bmoe_forward_keep_workspace_bytes(dt, T, d, N, k)
-    if n == 0:
-        raise BmoeError(2, "bmoe_forward_keep_workspace_bytes")
-    ws = torch.empty(n, dtype=torch.uint8, device=x.device)
-    y = torch.empty_like(x)
-    _check(bmoe_forward_keep(dt, T, d, N, k, x, ids, gates, theta, phi, w_packed, alpha, y, ws,
-                             stream), "bmoe_forward_keep")
-    return y, ws
+    with _on(stream):
+        T, d = x.shape
+        k = ids.shape[1]
+        N = theta.shape[0]
+        dt = dtype_code(x)
+        n = bmoe_forward_keep_workspace_bytes(dt, T, d, N, k)
+        if n == 0:
+            raise BmoeError(2, "bmoe_forward_keep_workspace_bytes")
+        ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+        y = torch.empty_like(x)
+        _check(bmoe_forward_keep(dt, T, d, N, k, x, ids, gates, theta, phi, w_packed, alpha, y, ws,
+                                 stream), "bmoe_forward_keep")
+        return y, ws
 
 
 def backward_kept(x: torch.Tensor, gates: torch.Tensor, n_experts: int, w_packed: torch.Tensor,
@@ -493,23 +506,24 @@ def backward_kept(x: torch.Tensor, gates: torch.Tensor, n_experts: int, w_packed
                   stream=None) -> dict:
     """As backward(), reading the forward's intermediates from forward_keep's
     workspace instead of recomputing them."""
-    T, d = x.shape
-    k = gates.shape[1]
-    N = n_experts
-    dt = dtype_code(x)
-    L = int(d).bit_length() - 1
-    n = bmoe_backward_workspace_bytes(dt, T, d, N, k)
-    if n == 0:
-        raise BmoeError(2, "bmoe_backward_workspace_bytes")
-    ws = torch.empty(n, dtype=torch.uint8, device=x.device)
-    out = {
-        "dx": torch.empty_like(x),
-        "dgates": torch.empty(T, k, dtype=torch.float32, device=x.device),
-        "dtheta": torch.empty(N, L, d // 2, dtype=torch.float32, device=x.device),
-        "dphi": torch.empty(N, L, d // 2, dtype=torch.float32, device=x.device),
-        "dw": torch.empty(d, d, dtype=torch.float32, device=x.device) if want_dw else None,
-    }
-    _check(bmoe_backward_kept(dt, T, d, N, k, x, gates, w_packed, alpha, dy, out["dx"],
-                              out["dgates"], out["dtheta"], out["dphi"], out["dw"], kept, ws,
-                              stream), "bmoe_backward_kept")
-    return out
+    with _on(stream):
+        T, d = x.shape
+        k = gates.shape[1]
+        N = n_experts
+        dt = dtype_code(x)
+        L = int(d).bit_length() - 1
+        n = bmoe_backward_workspace_bytes(dt, T, d, N, k)
+        if n == 0:
+            raise BmoeError(2, "bmoe_backward_workspace_bytes")
+        ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+        out = {
+            "dx": torch.empty_like(x),
+            "dgates": torch.empty(T, k, dtype=torch.float32, device=x.device),
+            "dtheta": torch.empty(N, L, d // 2, dtype=torch.float32, device=x.device),
+            "dphi": torch.empty(N, L, d // 2, dtype=torch.float32, device=x.device),
+            "dw": torch.empty(d, d, dtype=torch.float32, device=x.device) if want_dw else None,
+        }
+        _check(bmoe_backward_kept(dt, T, d, N, k, x, gates, w_packed, alpha, dy, out["dx"],
+                                  out["dgates"], out["dtheta"], out["dphi"], out["dw"], kept, ws,
+                                  stream), "bmoe_backward_kept")
+        return out

@@ -15,7 +15,13 @@ namespace {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-bool valid_d(int d) { return d >= 16 && d <= 8192 && (d & (d - 1)) == 0; }
+// The forward and the pack step take d = 2 .. 8192; everything else (the
+// backward, the router, the input-side rotation, the quantisation error and
+// the base-3 storage) needs whole 16-column words per row: d >= 16.
+bool valid_d(int d) { return d >= 2 && d <= 8192 && (d & (d - 1)) == 0; }
+bool valid_d16(int d) { return d >= 16 && valid_d(d); }
+// d in {2, 4, 8}: the one-thread-per-token forward.
+bool small_d(int d) { return d < 16; }
 
 int log2i(int d) {
   int L = 0;
@@ -60,9 +66,10 @@ FwdLayout fwd_layout(bmoe_dtype dt, int T, int d, int N, int k, bool keep = fals
   l.cs_out = off;  if (!routed) off = align_up(off + sizeof(float2) * N * L * (d / 2));
   // The fused path keeps Z and H on chip; only U (and the bf16 substrate)
   // live in the workspace.
-  l.z = off;       if (!fused) off = align_up(off + zel * M * d);
-  l.h = off;       if (!fused) off = align_up(off + zel * M * d);
-  l.u = off;       off = align_up(off + zel * M * d);
+  const bool small = small_d(d);
+  l.z = off;       if (!fused && !small) off = align_up(off + zel * M * d);
+  l.h = off;       if (!fused && !small) off = align_up(off + zel * M * d);
+  l.u = off;       if (!small) off = align_up(off + zel * M * d);
   l.w16 = off;
   if (fused && !routed) off = align_up(off + sizeof(uint16_t) * (size_t)d * d);
   // Tile-major copy of the packed substrate for the large-tile product.
@@ -160,11 +167,11 @@ BwdLayout bwd_layout(bmoe_dtype dt, int T, int d, int N, int k) {
 
 constexpr int kRouterMaxK = 64;
 bool router_shape_ok(bmoe_dtype dt, int T, int d, int N, int k) {
-  return shape_ok(dt, T, d, N, k) && k <= kRouterMaxK;
+  return shape_ok(dt, T, d, N, k) && valid_d16(d) && k <= kRouterMaxK;
 }
 
 bool bwd_shape_ok(bmoe_dtype dt, int T, int d, int N, int k) {
-  return shape_ok(dt, T, d, N, k) && d <= 4096;
+  return shape_ok(dt, T, d, N, k) && valid_d16(d) && d <= 4096;
 }
 
 // dW = alpha * dH^T Z (row-major [d][d], fp32). bf16 with d = 128 .. 1024:
@@ -260,14 +267,14 @@ bmoe_status bmoe_pack_ternary(const int8_t* w, int d, uint32_t* packed, void* ws
 }
 
 size_t bmoe_packed3_bytes(int d) {
-  if (!valid_d(d)) return 0;
+  if (!valid_d16(d)) return 0;
   return ((size_t)d * d + 4) / 5;
 }
 
 bmoe_status bmoe_pack_ternary_b3(const int8_t* w, int d, uint8_t* packed3, void* ws,
                                  size_t ws_bytes, void* stream) {
   if (!w || !packed3) return BMOE_E_NULL;
-  if (!valid_d(d)) return BMOE_E_SHAPE;
+  if (!valid_d16(d)) return BMOE_E_SHAPE;
   if (!ws || ws_bytes < bmoe_pack_workspace_bytes()) return BMOE_E_WORKSPACE;
   if (!aligned16(w) || !aligned16(packed3) || !aligned16(ws)) return BMOE_E_ALIGN;
   if (launch_pack_b3(w, d, packed3, static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream)) !=
@@ -280,7 +287,7 @@ bmoe_status bmoe_unpack_ternary_b3_timed(const uint8_t* packed3, int d, uint32_t
                                          void* ws, size_t ws_bytes, void* stream,
                                          void* const* events) {
   if (!packed3 || !packed) return BMOE_E_NULL;
-  if (!valid_d(d)) return BMOE_E_SHAPE;
+  if (!valid_d16(d)) return BMOE_E_SHAPE;
   if (!ws || ws_bytes < bmoe_pack_workspace_bytes()) return BMOE_E_WORKSPACE;
   if (!aligned16(packed3) || !aligned16(packed) || !aligned16(ws)) return BMOE_E_ALIGN;
   KernelTiming t;
@@ -306,7 +313,7 @@ bmoe_status forward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, cons
                          void* ws, size_t ws_bytes, int32_t* route_out, void* stream,
                          void* const* events, bool keep) {
   if (dt != BMOE_F32 && dt != BMOE_BF16) return BMOE_E_DTYPE;
-  if (!shape_ok(dt, T, d, n_experts, k)) return BMOE_E_SHAPE;
+  if (!shape_ok(dt, T, d, n_experts, k) || (keep && small_d(d))) return BMOE_E_SHAPE;
   if (T == 0) return BMOE_OK;
   if (!x || !ids || !gates || !theta || !phi || !w_packed || !y) return BMOE_E_NULL;
   const FwdLayout l = fwd_layout(dt, T, d, n_experts, k, keep);
@@ -374,6 +381,13 @@ bmoe_status forward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, cons
   if (launch_prep(ids, M, n_experts, theta, phi, d, rt, cs_in, cs_out, status, w_packed, w16, wt,
                   wt_block, s, timing(), bs) != hipSuccess)
     return BMOE_E_HIP;
+  if (small_d(d)) {
+    // Rotations, product, gates and the sum over j in one launch.
+    return launch_small(dt, T, d, k, n_experts, x, ids, gates, cs_in, cs_out, w_packed, alpha, y,
+                        s, timing()) == hipSuccess
+               ? BMOE_OK
+               : BMOE_E_HIP;
+  }
   if (fused) {
     if (launch_fused(M, d, k, x, gates, rt, cs_in, cs_out, w16, w_packed, alpha, u, s,
                      timing()) != hipSuccess)
@@ -401,7 +415,7 @@ bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k
 }
 
 size_t bmoe_forward_keep_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts, int k) {
-  if (!shape_ok(dt, T, d, n_experts, k)) return 0;
+  if (!shape_ok(dt, T, d, n_experts, k) || !valid_d16(d)) return 0;
   return fwd_layout(dt, T, d, n_experts, k, true).total;
 }
 
@@ -423,16 +437,19 @@ bmoe_status bmoe_forward(bmoe_dtype dt, int T, int d, int n_experts, int k, cons
 
 int bmoe_forward_kernel_count(bmoe_dtype dt, int T, int d, int n_experts, int k) {
   if (!shape_ok(dt, T, d, n_experts, k) || T == 0) return 0;
+  if (small_d(d)) return 2;
   if (fused_routes(dt, T * k, d, n_experts)) return 2;
   return fused_supported(dt, d) ? 3 : 5;
 }
 
 const char* bmoe_forward_kernel_name(bmoe_dtype dt, int T, int d, int n_experts, int k, int i) {
   static const char* routed_names[] = {"fused_kernel", "combine_kernel"};
+  static const char* small_names[] = {"prep_kernel", "small_kernel"};
   static const char* fused_names[] = {"prep_kernel", "fused_kernel", "combine_kernel"};
   static const char* split_names[] = {"prep_kernel", "bfly_in_kernel", "gemm_kernel",
                                       "bfly_out_kernel", "combine_kernel"};
   if (i < 0 || i >= bmoe_forward_kernel_count(dt, T, d, n_experts, k)) return "";
+  if (small_d(d)) return small_names[i];
   if (fused_routes(dt, T * k, d, n_experts)) return routed_names[i];
   return fused_supported(dt, d) ? fused_names[i] : split_names[i];
 }
@@ -634,7 +651,7 @@ constexpr int kBackwardLaunches = sizeof(kBackwardNames) / sizeof(kBackwardNames
 }  // namespace
 
 size_t bmoe_rotate_in_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts, int k) {
-  if (!shape_ok(dt, T, d, n_experts, k)) return 0;
+  if (!shape_ok(dt, T, d, n_experts, k) || !valid_d16(d)) return 0;
   return rot_layout(T, d, n_experts, k).total;
 }
 
@@ -642,7 +659,7 @@ bmoe_status bmoe_rotate_in(bmoe_dtype dt, int T, int d, int n_experts, int k, co
                            const int32_t* ids, const float* theta, void* z, void* ws,
                            size_t ws_bytes, void* stream) {
   if (dt != BMOE_F32 && dt != BMOE_BF16) return BMOE_E_DTYPE;
-  if (!shape_ok(dt, T, d, n_experts, k)) return BMOE_E_SHAPE;
+  if (!shape_ok(dt, T, d, n_experts, k) || !valid_d16(d)) return BMOE_E_SHAPE;
   if (T == 0) return BMOE_OK;
   if (!x || !ids || !theta || !z) return BMOE_E_NULL;
   const RotLayout l = rot_layout(T, d, n_experts, k);
@@ -671,7 +688,7 @@ bmoe_status bmoe_rotate_in(bmoe_dtype dt, int T, int d, int n_experts, int k, co
 bmoe_status bmoe_quant_error(bmoe_dtype dt, int rows, int d, const void* src, int m, int mode,
                              float* err, float* crest, void* stream) {
   if (dt != BMOE_F32 && dt != BMOE_BF16) return BMOE_E_DTYPE;
-  if (rows < 0 || !valid_d(d) || m < 1 || (mode != 0 && mode != 1)) return BMOE_E_SHAPE;
+  if (rows < 0 || !valid_d16(d) || m < 1 || (mode != 0 && mode != 1)) return BMOE_E_SHAPE;
   if (rows == 0) return BMOE_OK;
   if (!src || !err) return BMOE_E_NULL;
   if (!aligned16(src) || !aligned16(err) || (crest && !aligned16(crest))) return BMOE_E_ALIGN;
@@ -737,7 +754,9 @@ const char* bmoe_status_str(bmoe_status s) {
   switch (s) {
     case BMOE_OK: return "ok";
     case BMOE_E_NULL: return "required pointer is NULL";
-    case BMOE_E_SHAPE: return "unsupported shape (d power of two in [16,8192], 1<=N<=4096, 1<=k<=N, T>=0)";
+    case BMOE_E_SHAPE:
+      return "unsupported shape (d power of two in [2,8192] for the forward and pack, [16,8192] "
+             "otherwise (backward: [16,4096]); 1<=N<=4096, 1<=k<=N, T>=0)";
     case BMOE_E_DTYPE: return "unknown dtype";
     case BMOE_E_TERNARY: return "W_base entry outside {-1,0,+1}";
     case BMOE_E_EXPERT: return "expert id outside [0,N)";

@@ -61,6 +61,14 @@ hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, con
 // uint4 index (ob * (d/64) + kt) * CB + o % CB of `wt`.
 int gemm_tiled_w_block(bmoe_dtype dt, int M, int d);
 
+// Whole forward for d in {2, 4, 8}: one thread per token, its k routed rows
+// in ascending j (rotations with the prep kernel's cos/sin tables, the
+// ternary product, the gate and the fp32 sum), written straight to y.
+hipError_t launch_small(bmoe_dtype dt, int T, int d, int k, int N, const void* x,
+                        const int32_t* ids, const float* gates, const float2* cs_in,
+                        const float2* cs_out, const uint32_t* w_packed, float alpha, void* y,
+                        hipStream_t s, const KernelTiming& t = {});
+
 // Whether the fused d <= 512 path handles this shape, and whether its routed
 // variant (no prep launch) does: M <= 8192 routed rows and N <= 512 experts.
 bool fused_supported(bmoe_dtype dt, int d);

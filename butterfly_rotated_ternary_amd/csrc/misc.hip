@@ -48,16 +48,23 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const UT* U, YT* y, i
 
 __global__ void set_status_kernel(int32_t* status, int32_t v) { *status = v; }
 
-// One thread per packed word: 16 consecutive int8 entries of one row.
+// One thread per packed word: 16 consecutive int8 entries of one row (d < 16:
+// the row's d entries, the rest of the word zero codes).
 __global__ __launch_bounds__(kThreads) void pack_kernel(const int8_t* w, int d, uint32_t* packed,
                                                         int32_t* status) {
-  const int G = d / 16;
+  const int G = (d + 15) / 16;
   const size_t n = (size_t)d * G;
   for (size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x; idx < n;
        idx += (size_t)gridDim.x * kThreads) {
     const size_t o = idx / G, g = idx % G;
-    const uint4 raw = *reinterpret_cast<const uint4*>(w + o * d + g * 16);
-    const uint32_t parts[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t parts[4] = {0u, 0u, 0u, 0u};
+    if (d >= 16) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(w + o * d + g * 16);
+      parts[0] = raw.x; parts[1] = raw.y; parts[2] = raw.z; parts[3] = raw.w;
+    } else {
+      for (int v = 0; v < d; ++v)
+        parts[v >> 2] |= (uint32_t)(uint8_t)w[o * d + v] << (8 * (v & 3));
+    }
     uint32_t word = 0;
     bool bad = false;
 #pragma unroll
@@ -172,8 +179,8 @@ hipError_t launch_combine(bmoe_dtype dt, int T, int d, int k, const void* u, voi
 hipError_t launch_pack(const int8_t* w, int d, uint32_t* packed, int32_t* status,
                        hipStream_t s) {
   hipLaunchKernelGGL(set_status_kernel, dim3(1), dim3(1), 0, s, status, (int32_t)BMOE_OK);
-  hipLaunchKernelGGL(pack_kernel, dim3(grid_for((size_t)d * (d / 16))), dim3(kThreads), 0, s, w, d,
-                     packed, status);
+  hipLaunchKernelGGL(pack_kernel, dim3(grid_for((size_t)d * ((d + 15) / 16))), dim3(kThreads), 0,
+                     s, w, d, packed, status);
   return hipGetLastError();
 }
 

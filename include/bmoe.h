@@ -52,8 +52,11 @@ extern "C" {
 typedef enum {
   BMOE_OK = 0,
   BMOE_E_NULL = 1,       /* a required pointer is NULL */
-  BMOE_E_SHAPE = 2,      /* d not a power of two in [16, 8192], N < 1 or N > 4096,
-                            k < 1 or k > N, T < 0, or T*k beyond 2^31 - 1 */
+  BMOE_E_SHAPE = 2,      /* d not a power of two in [2, 8192] (bmoe_forward,
+                            bmoe_pack_ternary and the size helpers) or in
+                            [16, 8192] (every other entry point; the backward
+                            also needs d <= 4096), N < 1 or N > 4096, k < 1 or
+                            k > N, T < 0, or T*k beyond 2^31 - 1 */
   BMOE_E_DTYPE = 3,      /* unknown bmoe_dtype */
   BMOE_E_TERNARY = 4,    /* device: a W_base entry outside {-1, 0, +1} */
   BMOE_E_EXPERT = 5,     /* device: an expert id outside [0, N) */
@@ -150,6 +153,10 @@ bmoe_status bmoe_unpack_ternary_b3_timed(const uint8_t* packed3, int d, uint32_t
  * T = 0 is a no-op. Bad expert ids are clamped for addressing (so every
  * access stays in bounds) and reported by bmoe_sync_status(); y is then
  * unspecified.
+ * d is a power of two from 2 to 8192. For d = 2, 4 or 8 one thread per token
+ * runs its k rows after the preparation launch: Z is rounded to the
+ * activation type before the product, H stays fp32, and each gate-weighted
+ * row is rounded to the activation type before the fp32 sum over j.
  * For bf16 with d = 256 or 512, T*k <= 8192 and N <= 512, one kernel does
  * the whole per-row computation, routing included (then the combine); it
  * evaluates the rotation coefficients on the hardware sine/cosine unit
@@ -189,7 +196,7 @@ bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k
 bmoe_status bmoe_sync_status(const void* ws, void* stream);
 
 /* Workspace bytes bmoe_backward needs for this shape (0 if the shape is not
- * supported: as bmoe_forward, and d <= 4096). */
+ * supported: as bmoe_forward, and 16 <= d <= 4096). */
 size_t bmoe_backward_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts, int k);
 
 /*

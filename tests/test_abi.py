@@ -47,8 +47,34 @@ def test_packed_words():
     assert bmoe.bmoe_packed_words(16) == 16
     assert bmoe.bmoe_packed_words(512) == 512 * 32
     assert bmoe.bmoe_packed_words(4096) == 4096 * 256
-    for bad in (0, 8, 24, 16384, -16):
+    # d = 2, 4, 8: one zero-padded word per row
+    for d in (2, 4, 8):
+        assert bmoe.bmoe_packed_words(d) == d
+    for bad in (0, 1, 6, 24, 16384, -16):
         assert bmoe.bmoe_packed_words(bad) == 0
+
+
+def test_small_d_contract():
+    """d = 2, 4, 8: the forward and the pack step take them; the entry points
+    that need whole 16-column words per row reject them."""
+    bf, f32 = bmoe.BMOE_BF16, bmoe.BMOE_F32
+    for d in (2, 4, 8):
+        for dt in (bf, f32):
+            assert bmoe.bmoe_workspace_bytes(dt, 100, d, 3, 2) > 0
+            assert bmoe.bmoe_forward_kernel_count(dt, 100, d, 3, 2) == 2
+            assert [bmoe.bmoe_forward_kernel_name(dt, 100, d, 3, 2, i) for i in range(2)] == \
+                ["prep_kernel", "small_kernel"]
+            assert bmoe.bmoe_backward_workspace_bytes(dt, 100, d, 3, 2) == 0
+            assert bmoe.bmoe_forward_keep_workspace_bytes(dt, 100, d, 3, 2) == 0
+            assert bmoe.bmoe_rotate_in_workspace_bytes(dt, 100, d, 3, 2) == 0
+            assert bmoe.bmoe_router_workspace_bytes(dt, 100, d, 3, 2) == 0
+        assert bmoe.bmoe_packed3_bytes(d) == 0
+        assert bmoe.bmoe_param_count(d, 5) == d * d + 2 * 5 * (d.bit_length() - 1) * (d // 2)
+    lib = bmoe.lib()
+    a = [None] * 10
+    assert lib.bmoe_backward(1, 4, 8, 8, 2, *a[:6], 1.0, *a[:7], 0, None) == 2
+    assert lib.bmoe_forward(1, 4, 8, 8, 2, None, None, None, None, None, None, 1.0, None, None,
+                            0, None, None) == 1     # shape accepted, pointers checked next
 
 
 def test_workspace_bytes_validates_shape():
