@@ -64,6 +64,9 @@ def lib():
         L.bmoe_forward.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp, c_f,
                                    vp, vp, c_sz, vp, vp]
         L.bmoe_forward.restype = c_int
+        L.bmoe_forward_noalloc.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp,
+                                           vp, c_f, vp, vp, vp, vp]
+        L.bmoe_forward_noalloc.restype = c_int
         L.bmoe_forward_timed.argtypes = L.bmoe_forward.argtypes + [vp]
         L.bmoe_forward_timed.restype = c_int
         L.bmoe_forward_kernel_count.argtypes = [c_int, c_int, c_int, c_int, c_int]
@@ -203,6 +206,17 @@ def bmoe_forward_timed(dt: int, T: int, d: int, n_experts: int, k: int, x, ids, 
                                     _ptr(theta), _ptr(phi), _ptr(w_packed), float(alpha), _ptr(y),
                                     _ptr(ws), ws.numel() * ws.element_size(), _ptr(route_out),
                                     _stream(stream), ev)
+
+
+def bmoe_forward_noalloc(dt: int, T: int, d: int, n_experts: int, k: int, x, ids, gates, theta,
+                         phi, w_packed, alpha: float, y, route_out=None, status=None,
+                         stream=None) -> int:
+    return lib().bmoe_forward_noalloc(dt, T, d, n_experts, k, _ptr(x), _ptr(ids), _ptr(gates),
+                                      _ptr(theta), _ptr(phi), _ptr(w_packed), alpha, _ptr(y),
+                                      _ptr(route_out), _ptr(status), _stream(stream))
+
+
+BMOE_NOALLOC_MAX_WORKSPACE = 64 << 20
 
 
 def bmoe_forward_kernel_count(dt: int, T: int, d: int, n_experts: int, k: int) -> int:

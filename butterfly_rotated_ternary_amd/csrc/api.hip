@@ -307,11 +307,13 @@ bmoe_status bmoe_unpack_ternary_b3(const uint8_t* packed3, int d, uint32_t* pack
 }
 
 namespace {
+// status_at: where the kernels write the status word (NULL: the workspace's
+// own word).
 bmoe_status forward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
                          const int32_t* ids, const float* gates, const float* theta,
                          const float* phi, const uint32_t* w_packed, float alpha, void* y,
                          void* ws, size_t ws_bytes, int32_t* route_out, void* stream,
-                         void* const* events, bool keep) {
+                         void* const* events, bool keep, int32_t* status_at = nullptr) {
   if (dt != BMOE_F32 && dt != BMOE_BF16) return BMOE_E_DTYPE;
   if (!shape_ok(dt, T, d, n_experts, k) || (keep && small_d(d))) return BMOE_E_SHAPE;
   if (T == 0) return BMOE_OK;
@@ -336,7 +338,7 @@ bmoe_status forward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, cons
     rt.inv = reinterpret_cast<int32_t*>(base + l.inv);
   }
   rt.slot_e = reinterpret_cast<int32_t*>(base + l.slot_e);
-  int32_t* status = reinterpret_cast<int32_t*>(base + l.status);
+  int32_t* status = status_at ? status_at : reinterpret_cast<int32_t*>(base + l.status);
   float2* cs_in = reinterpret_cast<float2*>(base + l.cs_in);
   float2* cs_out = reinterpret_cast<float2*>(base + l.cs_out);
   void* z = base + l.z;
@@ -412,6 +414,64 @@ bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k
                                void* const* events) {
   return forward_impl(dt, T, d, n_experts, k, x, ids, gates, theta, phi, w_packed, alpha, y, ws,
                       ws_bytes, route_out, stream, events, false);
+}
+
+}  // extern "C"
+
+// ---- allocation-free forward -------------------------------------------
+// The workspace of bmoe_forward_noalloc: one array per GPU, in the code
+// object's device memory, held until the process ends. In host code `scratch`
+// names a host-side stand-in, not device memory: kernels get the address
+// hipGetSymbolAddress returns for the device, never the name itself.
+static __device__ __align__(256) uint8_t scratch[BMOE_NOALLOC_MAX_WORKSPACE];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device `stream` belongs to (the
+// current device for the NULL stream), looked up once per device with that
+// device current.
+bmoe_status scratch_for(hipStream_t stream, void** out) {
+  int cur = 0, dev = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return BMOE_E_HIP;
+  dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return BMOE_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return BMOE_E_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_addr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return BMOE_E_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return BMOE_E_HIP;
+    if (e != hipSuccess || !p) return BMOE_E_HIP;
+    scratch_addr[dev] = p;
+  }
+  *out = scratch_addr[dev];
+  return BMOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+bmoe_status bmoe_forward_noalloc(bmoe_dtype dt, int T, int d, int n_experts, int k,
+                                 const void* x, const int32_t* ids, const float* gates,
+                                 const float* theta, const float* phi, const uint32_t* w_packed,
+                                 float alpha, void* y, int32_t* route_out, int32_t* status,
+                                 void* stream) {
+  if (dt != BMOE_F32 && dt != BMOE_BF16) return BMOE_E_DTYPE;
+  if (!shape_ok(dt, T, d, n_experts, k)) return BMOE_E_SHAPE;
+  if (T == 0) return BMOE_OK;
+  if (fwd_layout(dt, T, d, n_experts, k).total > BMOE_NOALLOC_MAX_WORKSPACE)
+    return BMOE_E_WORKSPACE;
+  if (status && (reinterpret_cast<uintptr_t>(status) & 3u)) return BMOE_E_ALIGN;
+  void* ws = nullptr;
+  const bmoe_status st = scratch_for(static_cast<hipStream_t>(stream), &ws);
+  if (st != BMOE_OK) return st;
+  return forward_impl(dt, T, d, n_experts, k, x, ids, gates, theta, phi, w_packed, alpha, y, ws,
+                      BMOE_NOALLOC_MAX_WORKSPACE, route_out, stream, nullptr, false,
+                      status ? status : nullptr);
 }
 
 size_t bmoe_forward_keep_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts, int k) {

@@ -189,6 +189,34 @@ bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k
                                void* ws, size_t ws_bytes, int32_t* route_out, void* stream,
                                void* const* events);
 
+/*
+ * bmoe_forward without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). The workspace is a fixed array in the library's
+ * device memory, BMOE_NOALLOC_MAX_WORKSPACE bytes on each GPU the library
+ * runs on, held until the process ends. Nothing is allocated on any call:
+ * no hipMalloc, hipFree or allocating library routine.
+ *   Arguments as bmoe_forward, without ws / ws_bytes, plus
+ *   status  nullable device int32: receives BMOE_OK, or BMOE_E_EXPERT for an
+ *           expert id outside [0, N) (read it with bmoe_sync_status(status,
+ *           stream)); NULL: such errors are not reported. 4-byte aligned.
+ * Returns BMOE_E_WORKSPACE when the shape needs more than
+ * BMOE_NOALLOC_MAX_WORKSPACE bytes of workspace (compare
+ * bmoe_workspace_bytes(dt, T, d, N, k) with it), before anything is
+ * enqueued. Results are identical to bmoe_forward's.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, or other threads
+ * without ordering) race and give undefined results; order them on one
+ * stream. The array's address is looked up once per GPU, on the first call
+ * that runs there (the GPU of `stream`, or the current one for NULL).
+ */
+#define BMOE_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+bmoe_status bmoe_forward_noalloc(bmoe_dtype dt, int T, int d, int n_experts, int k,
+                                 const void* x, const int32_t* ids, const float* gates,
+                                 const float* theta, const float* phi, const uint32_t* w_packed,
+                                 float alpha, void* y, int32_t* route_out, int32_t* status,
+                                 void* stream);
+
 /* Wait for `stream`, then return the device-side status of the last call
  * that used `ws` (bmoe_forward, bmoe_backward, bmoe_rotate_in, or a pack or
  * base-3 unpack): BMOE_OK, BMOE_E_EXPERT or BMOE_E_TERNARY, or BMOE_E_HIP if
