@@ -27,12 +27,11 @@ METRIC = "routed tokens/sec of ButterflyMoE layer fwd (d=512,N=64,top-2); % MFMA
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0        # dense bf16 MFMA
 PEAK_FP32_MFMA_TFLOPS = 157.3    # dense fp32 MFMA
-PEAK_VALU_F32_TFLOPS = 157.3     # fp32 vector, published (256 CU x 2.4 GHz x 256 flop/clk,
-                                 # which counts packed two-wide FMAs)
-# fp32 vector without packed ops: 256 CU x 4 SIMD x 16 lanes x 2 flop (FMA) x
-# 2.4 GHz. Every kernel here is built with packed fp32 disabled, so this is
-# the ALU ceiling its rotations can reach.
-PEAK_VALU_F32_SCALAR_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+# fp32 vector: 256 CU x 4 SIMD x 32 lanes x 2 flop (FMA) x 2.4 GHz. A plain
+# stream of non-packed v_fma_f32 (bench.py ceilings) reaches about 119
+# TFLOP/s on the box, above the 78.6 a 16-lane SIMD would allow, so the
+# published figure is the ceiling for the non-packed code built here too.
+PEAK_VALU_F32_TFLOPS = 256 * 4 * 32 * 2 * 2.4e9 / 1e12
 
 GEMM_WORKLOAD = "d4096_e256_top4_bf16"
 SHARD_TOKENS = 4096
@@ -175,33 +174,26 @@ def router_work(name, act_bytes, T, d, N, k):
 
 def roofline(work, dur_s, mfma_peak_tflops):
     """The roofline of one kernel: the resource whose ideal time (work over
-    its peak) is largest bounds it; achieved = that work / measured
-    duration. The ALU peak is the non-packed fp32 rate (the kernels are
-    built without packed fp32 ops); the published figure, which counts packed
-    FMAs, is reported beside it."""
+    published peak) is largest bounds it; achieved = that work / measured
+    duration. frac_by_resource gives each resource's ideal time over the
+    measured duration."""
     t_hbm = work["bytes"] / (PEAK_HBM_GBS * 1e9)
     t_mfma = work["mfma_flops"] / (mfma_peak_tflops * 1e12)
-    t_alu = work["valu_flops"] / (PEAK_VALU_F32_SCALAR_TFLOPS * 1e12)
+    t_alu = work["valu_flops"] / (PEAK_VALU_F32_TFLOPS * 1e12)
     bound = max((t_hbm, "hbm"), (t_mfma, "mfma"), (t_alu, "alu"))[1]
-    extra = {}
     if bound == "hbm":
         ach, peak, unit, amount = work["bytes"] / dur_s / 1e9, PEAK_HBM_GBS, "GB/s", work["bytes"]
     elif bound == "mfma":
         ach, peak, unit = work["mfma_flops"] / dur_s / 1e12, mfma_peak_tflops, "TFLOP/s"
         amount = work["mfma_flops"]
     else:
-        ach, peak, unit = (work["valu_flops"] / dur_s / 1e12, PEAK_VALU_F32_SCALAR_TFLOPS,
-                           "TFLOP/s")
+        ach, peak, unit = work["valu_flops"] / dur_s / 1e12, PEAK_VALU_F32_TFLOPS, "TFLOP/s"
         amount = work["valu_flops"]
-        extra = {"published_peak": PEAK_VALU_F32_TFLOPS,
-                 "frac_of_published": ach / PEAK_VALU_F32_TFLOPS}
-    out = {"bound": bound, "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak,
-           "work_per_launch": amount, "duration_us": dur_s * 1e6,
-           "ideal_us": {"hbm": t_hbm * 1e6, "mfma": t_mfma * 1e6, "alu": t_alu * 1e6},
-           "frac_by_resource": {"hbm": t_hbm / dur_s, "mfma": t_mfma / dur_s,
-                                "alu": t_alu / dur_s}}
-    out.update(extra)
-    return out
+    return {"bound": bound, "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak,
+            "work_per_launch": amount, "duration_us": dur_s * 1e6,
+            "ideal_us": {"hbm": t_hbm * 1e6, "mfma": t_mfma * 1e6, "alu": t_alu * 1e6},
+            "frac_by_resource": {"hbm": t_hbm / dur_s, "mfma": t_mfma / dur_s,
+                                 "alu": t_alu / dur_s}}
 
 
 def min_hbm_bytes(act_bytes, T, d, N, k):
@@ -661,6 +653,91 @@ def outliers_section():
     return out
 
 
+def ceilings_section(reps=10):
+    """Measured ceilings of the three resources, beside the published peaks:
+    dense bf16 MFMA, fp32 vector FMA without packed ops, and a plain device
+    copy (bytes read + written over time). Median of `reps` timed launches
+    after two untimed ones, from each launch's own dispatch events."""
+    import torch
+    from butterfly_rotated_ternary_amd import bmoe
+    hip = HipEvents()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sink = torch.empty(bmoe.BMOE_CEILING_SINK_FLOATS, device=dev)
+
+    def median_ms(launch):
+        evsets = [hip.create(2) for _ in range(reps + 2)]
+        for evs in evsets:
+            rc = launch(evs)
+            if rc != 0:
+                raise bmoe.BmoeError(rc, "ceiling launch")
+        torch.cuda.synchronize()
+        ms = sorted(hip.elapsed_ms(e[0], e[1]) for e in evsets[2:])
+        for evs in evsets:
+            hip.destroy(evs)
+        return ms[len(ms) // 2]
+
+    out = {}
+    flops = {}
+
+    def mfma(evs):
+        rc, flops["mfma"] = bmoe.bmoe_ceiling_mfma_bf16(8000, sink, stream, evs)
+        return rc
+
+    def valu(evs):
+        rc, flops["valu"] = bmoe.bmoe_ceiling_valu_f32(2000, sink, stream, evs)
+        return rc
+
+    t = median_ms(mfma)
+    out["mfma_bf16"] = {"measured": flops["mfma"] / (t * 1e-3) / 1e12, "unit": "TFLOP/s",
+                        "published": PEAK_BF16_TFLOPS}
+    t = median_ms(valu)
+    out["valu_f32"] = {"measured": flops["valu"] / (t * 1e-3) / 1e12, "unit": "TFLOP/s",
+                       "published": PEAK_VALU_F32_TFLOPS}
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    t = median_ms(lambda evs: bmoe.bmoe_ceiling_copy(src, dst, nbytes, stream, evs))
+    out["hbm_copy"] = {"measured": 2 * nbytes / (t * 1e-3) / 1e9, "unit": "GB/s",
+                       "published": PEAK_HBM_GBS, "bytes_each_way": nbytes}
+    for v in out.values():
+        v["frac_of_published"] = v["measured"] / v["published"]
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    log("[bench] ceilings: " + "; ".join(f"{k} {v['measured']:.0f} {v['unit']} "
+                                         f"({100 * v['frac_of_published']:.0f}% of published)"
+                                         for k, v in out.items()))
+    return out
+
+
+def measured_ceiling(ceilings, roof):
+    """The measured ceiling of a roofline's bound resource, or None."""
+    key = {"hbm": "hbm_copy", "mfma": "mfma_bf16", "alu": "valu_f32"}[roof["bound"]]
+    if roof["bound"] == "mfma" and roof["peak"] != PEAK_BF16_TFLOPS:
+        return None
+    return ceilings[key]["measured"] if ceilings and key in ceilings else None
+
+
+def profile_run(names, steps, backward):
+    """Only `steps` forwards (and backwards) of each workload, for counter
+    collection under rocprofv3 --pmc: no timing, no JSON."""
+    import torch
+    for name in names:
+        P = Problem(name)
+        for _ in range(steps):
+            P.step()
+        if backward:
+            P.backward_setup()
+            for _ in range(steps):
+                rc = P.bmoe.bmoe_backward(*P.backward_args())
+                if rc != 0:
+                    raise P.bmoe.BmoeError(rc, "bmoe_backward")
+        torch.cuda.synchronize()
+        log(f"[bench] profiled {name}: {steps} forward(s)" + (" and backward(s)" if backward else ""))
+        del P
+        torch.cuda.empty_cache()
+
+
 def copy_calibration(mib, reps):
     """Plain device-to-device copies of a known size, for scaling the HBM
     byte counters (run under rocprofv3 --pmc)."""
@@ -695,6 +772,14 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain copies of MIB MiB (counter calibration) and exit")
     ap.add_argument("--print-source-digest", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured MFMA / VALU / copy ceilings")
+    ap.add_argument("--profile", default=None, metavar="WORKLOADS",
+                    help="only run --profile-steps forwards of these comma-separated workloads "
+                         "(counter collection) and exit")
+    ap.add_argument("--profile-steps", type=int, default=20)
+    ap.add_argument("--profile-backward", action="store_true",
+                    help="with --profile: also run that many backwards")
     args = ap.parse_args()
     if args.print_source_digest:
         print(source_digest())
@@ -706,10 +791,14 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 10)
         return
+    if args.profile:
+        profile_run(args.profile.split(","), args.profile_steps, args.profile_backward)
+        return
 
     from butterfly_rotated_ternary_amd import workloads as W
 
     name = args.workload or W.HEADLINE
+    ceilings = None if args.no_ceilings else ceilings_section()
     P = Problem(name)
     T, d, N, k = P.T, P.d, P.N, P.k
     ms = P.time_steps(args.steps, args.warmup)
@@ -725,6 +814,8 @@ def main():
     roof = roofline(work, per_kernel[dom] * 1e-3, P.mfma_peak())
     roof["traffic"] = stored_traffic(dom, name)
     roof["kernel"] = dom
+    mc = measured_ceiling(ceilings, roof)
+    roof["frac_of_measured_ceiling"] = roof["achieved"] / mc if mc else None
     others = {}
     for n, v in per_kernel.items():
         r = roofline(kernel_work(n, P.act_bytes, T, d, N, k, routed), v * 1e-3, P.mfma_peak())
@@ -752,6 +843,7 @@ def main():
                      "hbm": min_hbm_bytes(P.act_bytes, T, d, N, k) / (ms * 1e-3)
                      / (PEAK_HBM_GBS * 1e9)},
         "kernels": others,
+        "ceilings": ceilings,
     }
     if args.router_steps > 0:
         out["router"] = router_section(P, args.router_steps)
@@ -769,6 +861,8 @@ def main():
         g_work = kernel_work("gemm_kernel", G.act_bytes, G.T, G.d, G.N, G.k)
         g_roof = roofline(g_work, g_per["gemm_kernel"] * 1e-3, G.mfma_peak())
         g_roof["traffic"] = stored_traffic("gemm_kernel", GEMM_WORKLOAD)
+        mc = measured_ceiling(ceilings, g_roof)
+        g_roof["frac_of_measured_ceiling"] = g_roof["achieved"] / mc if mc else None
         out["gemm_d4096"] = {
             "workload": GEMM_WORKLOAD, "kernel": "gemm_kernel", "ms_per_step": g_ms,
             "tokens_per_s": G.T / (g_ms * 1e-3), "roofline": g_roof,

@@ -67,6 +67,12 @@ def lib():
         L.bmoe_forward_noalloc.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp,
                                            vp, c_f, vp, vp, vp, vp]
         L.bmoe_forward_noalloc.restype = c_int
+        c_dp = ctypes.POINTER(ctypes.c_double)
+        for name in ("bmoe_ceiling_mfma_bf16", "bmoe_ceiling_valu_f32"):
+            getattr(L, name).argtypes = [c_int, vp, vp, vp, c_dp]
+            getattr(L, name).restype = c_int
+        L.bmoe_ceiling_copy.argtypes = [vp, vp, c_sz, vp, vp]
+        L.bmoe_ceiling_copy.restype = c_int
         L.bmoe_forward_timed.argtypes = L.bmoe_forward.argtypes + [vp]
         L.bmoe_forward_timed.restype = c_int
         L.bmoe_forward_kernel_count.argtypes = [c_int, c_int, c_int, c_int, c_int]
@@ -217,6 +223,34 @@ def bmoe_forward_noalloc(dt: int, T: int, d: int, n_experts: int, k: int, x, ids
 
 
 BMOE_NOALLOC_MAX_WORKSPACE = 64 << 20
+
+
+BMOE_CEILING_SINK_FLOATS = 256 * 8 * 256
+
+
+def _events_arg(events):
+    return None if events is None else (ctypes.c_void_p * len(events))(*events)
+
+
+def bmoe_ceiling_mfma_bf16(iters: int, sink, stream=None, events=None):
+    """(status, flops executed)."""
+    f = ctypes.c_double()
+    rc = lib().bmoe_ceiling_mfma_bf16(iters, _ptr(sink), _stream(stream), _events_arg(events),
+                                      ctypes.byref(f))
+    return rc, f.value
+
+
+def bmoe_ceiling_valu_f32(iters: int, sink, stream=None, events=None):
+    """(status, flops executed)."""
+    f = ctypes.c_double()
+    rc = lib().bmoe_ceiling_valu_f32(iters, _ptr(sink), _stream(stream), _events_arg(events),
+                                     ctypes.byref(f))
+    return rc, f.value
+
+
+def bmoe_ceiling_copy(src, dst, nbytes: int, stream=None, events=None) -> int:
+    return lib().bmoe_ceiling_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream),
+                                   _events_arg(events))
 
 
 def bmoe_forward_kernel_count(dt: int, T: int, d: int, n_experts: int, k: int) -> int:

@@ -44,6 +44,7 @@ constexpr int kRouteMaxN = 512;
 
 __device__ __forceinline__ int padi(int i) { return i + (i >> 3); }
 
+
 // Sorted slot q of a tile lives in LDS row row_of_slot(q). The butterfly
 // threads of phase p rotate rows p, p + 8, p + 16 and p + 24 (three-stage
 // groups at d = 512), which then hold the four consecutive slots 4p .. 4p+3:

@@ -380,6 +380,28 @@ bmoe_status bmoe_router_timed(bmoe_dtype dt, int T, int d, int n_experts, int k,
 /* Static description of a status code. */
 const char* bmoe_status_str(bmoe_status s);
 
+/*
+ * Measured ceilings, reported by the benchmark beside the published peaks
+ * (they are not part of the layer). Each launches one kernel on `stream`,
+ * with events[0] / events[1] (may be NULL) as the start and stop events of
+ * its own dispatch.
+ *   bmoe_ceiling_mfma_bf16: chains of v_mfma_f32_32x32x16_bf16 on register
+ *     operands, eight waves per SIMD on every CU; *flops (may be NULL)
+ *     receives the multiply-add flops it executes (iters scales them).
+ *   bmoe_ceiling_valu_f32: chains of fp32 fused multiply-adds (no packed
+ *     ops), eight waves per SIMD; *flops as above.
+ *   sink: device fp32 [BMOE_CEILING_SINK_FLOATS], overwritten.
+ *   bmoe_ceiling_copy: a plain copy of `bytes` (a multiple of 16) from src to
+ *     dst, both 16-byte aligned device buffers; reads and writes `bytes`.
+ */
+#define BMOE_CEILING_SINK_FLOATS (256 * 8 * 256)
+bmoe_status bmoe_ceiling_mfma_bf16(int iters, float* sink, void* stream, void* const* events,
+                                   double* flops);
+bmoe_status bmoe_ceiling_valu_f32(int iters, float* sink, void* stream, void* const* events,
+                                  double* flops);
+bmoe_status bmoe_ceiling_copy(const void* src, void* dst, size_t bytes, void* stream,
+                              void* const* events);
+
 #ifdef __cplusplus
 }
 #endif

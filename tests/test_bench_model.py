@@ -46,17 +46,18 @@ def test_roofline_takes_the_resource_with_the_largest_ideal_time():
     assert r["bound"] == "mfma" and r["frac"] == pytest.approx(0.5)
 
 
-def test_alu_bound_uses_the_non_packed_rate():
-    # the routed d = 512 fused kernel: its rotations (226 MFLOP) take longer
-    # at the non-packed fp32 rate (78.6 TFLOP/s) than its bytes at 8 TB/s or
-    # its product at 2.5 PFLOP/s, so the ALU bounds it
-    assert bench.PEAK_VALU_F32_SCALAR_TFLOPS == pytest.approx(78.6432)
+def test_alu_peak_and_per_resource_fractions():
+    # 256 CU x 4 SIMD x 32 lanes x 2 flop x 2.4 GHz
+    assert bench.PEAK_VALU_F32_TFLOPS == pytest.approx(157.2864)
+    # the routed d = 512 fused kernel: its bytes at 8 TB/s (1.75 us) take
+    # longer than its product at 2.5 PFLOP/s (1.72 us) or its rotations at
+    # 157 TFLOP/s (1.44 us)
     w = bench.kernel_work("fused_kernel", 2, T, D, N, K, routed=True)
     r = bench.roofline(w, 26e-6, bench.PEAK_BF16_TFLOPS)
-    assert r["bound"] == "alu" and r["peak"] == pytest.approx(78.6432)
-    assert r["published_peak"] == 157.3
-    assert r["frac"] == pytest.approx(w["valu_flops"] / 26e-6 / 78.6432e12)
+    assert r["bound"] == "hbm"
     assert r["frac_by_resource"]["mfma"] == pytest.approx(2 * M * D * D / 2.5e15 / 26e-6)
+    assert r["frac_by_resource"]["alu"] == pytest.approx(w["valu_flops"] / 157.2864e12 / 26e-6)
+    assert r["frac"] == pytest.approx(r["frac_by_resource"]["hbm"])
 
 
 def test_stored_traffic_requires_the_current_sources(tmp_path, monkeypatch):
