@@ -374,8 +374,8 @@ bmoe_status forward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, cons
   }
   if (routed) {
     // Routing and coefficient tables inside the fused kernel: no prep launch.
-    if (launch_fused_routed(M, d, k, n_experts, x, ids, gates, theta, phi, w_packed, alpha, u, rt,
-                            status, s, timing()) != hipSuccess)
+    if (launch_fused_wave(M, d, k, n_experts, x, ids, gates, theta, phi, w_packed, alpha, u, rt,
+                          status, s, timing()) != hipSuccess)
       return BMOE_E_HIP;
     if (launch_combine(dt, T, d, k, u, y, s, timing()) != hipSuccess) return BMOE_E_HIP;
     return BMOE_OK;
@@ -503,7 +503,7 @@ int bmoe_forward_kernel_count(bmoe_dtype dt, int T, int d, int n_experts, int k)
 }
 
 const char* bmoe_forward_kernel_name(bmoe_dtype dt, int T, int d, int n_experts, int k, int i) {
-  static const char* routed_names[] = {"fused_kernel", "combine_kernel"};
+  static const char* routed_names[] = {"fused_wave_kernel", "combine_kernel"};
   static const char* small_names[] = {"prep_kernel", "small_kernel"};
   static const char* fused_names[] = {"prep_kernel", "fused_kernel", "combine_kernel"};
   static const char* split_names[] = {"prep_kernel", "bfly_in_kernel", "gemm_kernel",

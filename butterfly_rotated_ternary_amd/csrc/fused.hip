@@ -168,21 +168,6 @@ __device__ __forceinline__ void load_coef_lds(float2 (&c)[3][4], const float2* t
   }
 }
 
-// Routed variant: (cos x, sin x) on the transcendental unit, whose v_sin /
-// v_cos take revolutions. x is first reduced to [-pi, pi] by subtracting the
-// nearest multiple of 2pi in two fused steps (Cody and Waite's method: 2pi
-// split into its nearest float and the remainder), then scaled by 1/2pi.
-// Measured against double precision: at most 4e-7 absolute error for
-// |x| <= 1000 (sincosf: 7e-8).
-__device__ __forceinline__ float2 tile_cos_sin(float x) {
-  constexpr float kInv2Pi = 0.159154943091895336f;
-  constexpr float k2PiHi = 6.28318548202514648f;   // float(2 pi)
-  constexpr float k2PiLo = -1.74845553146951449e-7f;  // 2 pi - float(2 pi)
-  const float k = rintf(x * kInv2Pi);
-  const float r = fmaf(-k, k2PiLo, fmaf(-k, k2PiHi, x)) * kInv2Pi;
-  return make_float2(__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r));
-}
-
 // Expert e's table of one side (contiguous) -> LDS at dst, 1 KiB per wave
 // instruction (global->LDS DMA; completion is tracked by vmcnt).
 template <int D>
@@ -396,14 +381,6 @@ __device__ __forceinline__ void ring_load(char* stage, const uint16_t* w16, int 
                                      (__attribute__((address_space(3))) void*)(stage + blk * 1024),
                                      16, 0, 0);
   }
-}
-
-// Eight bf16 {-2,0,+2} of one packed word: values 8h .. 8h+7 (h = 0, 1).
-__device__ __forceinline__ bf16x8 unpack_frag(uint32_t w, int h) {
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = unpack_pair(w, 4 * h + i);
-  return __builtin_bit_cast(bf16x8, r);
 }
 
 template <int N>

@@ -1,0 +1,772 @@
+// Fused ButterflyMoE expert forward with register-resident butterflies, for
+// bf16 d = 256 and 512 when the kernel routes its own rows (M <= 8192 routed
+// rows, N <= 512 experts). ButterflyMoE gist.science summary, §2.3: rotate
+// each routed token by B(theta_e)^T, multiply by the one ternary W_base,
+// rotate by B(phi_e); §2.1 for the butterfly structure.
+//
+// One workgroup (8 waves) per 32 consecutive sorted slots. Each wave owns four
+// of those rows outright: a row of d values lives in one wave, d/64 values per
+// lane (lane l holds elements VPL*l .. VPL*l + VPL-1), so every butterfly
+// stage is a wave-local operation and no barrier separates stages:
+//   * stages whose partner is in the same lane (the low log2(VPL) bits) run
+//     in registers;
+//   * partners 1, 2 and 8 lanes away come through DPP (quad_perm, row_ror)
+//     and 4 lanes away through two masked row shifts; each lane computes its
+//     own element of the pair, c * mine +- s * partner;
+//   * partners 16 and 32 lanes away: v_permlane16_swap / v_permlane32_swap
+//     exchange half of one register with half of another, so that each lane
+//     holds a whole pair, the pair is rotated in registers, and a second swap
+//     restores the layout.
+// LDS carries only what must cross waves: the bf16 A tile of the product, the
+// fp32 H rows coming back from the product (each wave's MFMA output is a
+// column slice of all 32 rows), the routing scratch and the cos/sin tables of
+// the tile's first and last expert. Rows of any expert strictly between those
+// two take their coefficients straight from the angles.
+//
+// Routing (as in the first fused kernel): every workgroup reads all ids,
+// counts them per wave in LDS, derives the per-expert offsets and ranks only
+// its own slots (stable: ascending routed index within an expert), and writes
+// the same routing tables as the preparation kernel.
+#include <utility>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace bmoe {
+namespace {
+
+constexpr int kThreadsW = 512;
+constexpr int kWavesW = kThreadsW / kWave;
+constexpr int kSlots = 32;                 // sorted slots per workgroup
+constexpr int kRowsW = kSlots / kWavesW;   // rows per wave
+constexpr int kIdsW = 16;                  // ids per thread: M <= 8192
+constexpr int kMaxMW = kIdsW * kThreadsW;
+constexpr int kMaxNW = 512;
+
+template <int D>
+struct WCfg {
+  static constexpr int VPL = D / kWave;                        // values per lane
+  static constexpr int RB = VPL == 8 ? 3 : VPL == 4 ? 2 : 1;   // stages inside a lane
+  static constexpr int L = RB + 6;
+  static constexpr int P = D / 2;                              // pairs per stage
+  static constexpr int TBL = L * P;                            // one expert's side table
+  static constexpr int TAB_BYTES = TBL * 8;
+  // fp32 H row stride: rows r and r + 4 (written by the two halves of a wave
+  // in the MFMA output layout) land on opposite halves of the 64 banks.
+  static constexpr int HS = D + 8;
+  static constexpr int H_BYTES = kSlots * HS * 4;
+  static constexpr int WN = D / kWavesW;                       // product columns per wave
+  static constexpr int FN = WN / 32;
+  static constexpr int KS = 32;
+  static constexpr int NSTEP = D / KS;
+  static constexpr int ROUTE_BYTES = (kWavesW * kMaxNW + kMaxNW + 16) * 4;
+  // The packed substrate rows of one wave's output columns, copied to LDS
+  // as they lie in memory (WN rows of D/4 bytes), 16-byte chunks permuted
+  // within each row (see pw_chunk).
+  static constexpr int ROWB = D / 4;
+  static constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
+  static constexpr int PW_WAVE = WN * ROWB;
+  static constexpr int PW_LOADS = PW_WAVE / 1024;     // 1 KiB per wave-wide copy
+  // LDS regions (bytes):
+  //   A: routing scratch and the input-side tables; once the A tile is
+  //      complete, the output-side tables (written during the product);
+  //   META: the tile's slot -> (expert, routed index);
+  //   P: the packed substrate, then (with Z, after the product) the H rows;
+  //   Z: the bf16 A tile.
+  static constexpr int OFF_ROUTE = 0;
+  static constexpr int OFF_TIN = (ROUTE_BYTES + 255) / 256 * 256;
+  static constexpr int OFF_TOUT = 0;
+  static constexpr int END_A = OFF_TIN + 2 * TAB_BYTES;
+  static constexpr int OFF_META = (END_A + 255) / 256 * 256;
+  static constexpr int OFF_P = (OFF_META + (3 * kSlots + 8) * 4 + 1023) / 1024 * 1024;
+  static constexpr int OFF_H = OFF_P;
+  static constexpr int OFF_Z = OFF_P + kWavesW * PW_WAVE;
+  static constexpr int END_Z = OFF_Z + kSlots * D * 2;
+  static constexpr int LDS_BYTES = END_Z > OFF_H + H_BYTES ? END_Z : OFF_H + H_BYTES;
+  static_assert(2 * TAB_BYTES <= END_A, "output-side tables must fit in region A");
+  static_assert(PW_WAVE % 1024 == 0, "whole 1 KiB copies per wave");
+  static_assert(FN >= 1 && VPL >= 2, "d too small for this tiling");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  // Row R's chunk g sits at chunk g ^ pw_swz(R): a column of lanes reading
+  // one word of 32 consecutive rows hits at most two lanes per bank.
+  static __device__ __forceinline__ int pw_swz(int R) {
+    return ((R & 7) ^ ((R >> 3) & 3)) & (CPR - 1);
+  }
+};
+
+struct WaveArgs {
+  int M, k, N;
+  const uint16_t* x;
+  const int32_t* ids;
+  const float* gates;
+  const float* theta;
+  const float* phi;
+  const uint32_t* wp;
+  float alpha;  // scale for the +-2 substrate values
+  uint16_t* u;
+  RouteTables rt;
+  int32_t* status;
+};
+
+// Which pairs a lane needs in stage s, and where a table keeps them.
+//   in-lane stage (s < RB): the VPL/2 pairs (VPL/2) lane + u;
+//   DPP stage (m = s - RB < 4): the VPL pairs p0(lane) + r of its elements,
+//     shared with the partner lane (lane ^ 2^m);
+//   swap stage (m = 4, 5): the VPL/2 pairs p0 + 2i, p0 the pair of element
+//     VPL * (lane without bit m) + bit m.
+// A table of one side of one expert stores, for each stage, exactly its D/2
+// pairs in the order the lanes read them: 16-byte chunk i (two consecutive
+// coefficients of one lane) of lane l at float4 s * D/4 + i * 64 + l, or, in a
+// DPP stage, of compressed lane (l without bit m) at s * D/4 + i * 32 + that.
+// Every wave-wide 16-byte read is then 64 (or 32, each read by two lanes)
+// consecutive chunks: no bank conflicts.
+template <int D>
+__host__ __device__ constexpr int first_pair(int s, int lane) {
+  using C = WCfg<D>;
+  constexpr int VPL = C::VPL, RB = C::RB;
+  if (s < RB) return (VPL / 2) * lane;
+  const int m = s - RB;
+  const int idx = m < 4 ? VPL * lane : VPL * (lane & ~(1 << m)) + ((lane >> m) & 1);
+  return ((idx >> (s + 1)) << s) | (idx & ((1 << s) - 1));
+}
+
+// Pair of coefficient k of `lane` in stage s.
+template <int D>
+__host__ __device__ constexpr int pair_of(int s, int lane, int k) {
+  const int m = s - WCfg<D>::RB;
+  return first_pair<D>(s, lane) + (m >= 4 ? 2 * k : k);
+}
+
+// The pair a table keeps at float2 position k of stage s (the order the
+// lanes read them in, above).
+template <int D>
+__host__ __device__ constexpr int table_pair(int s, int k) {
+  using C = WCfg<D>;
+  const int f = k / 2, h = k % 2;
+  const int m = s - C::RB;
+  if (s >= C::RB && m < 4) {
+    const int i = f / 32, lam = f % 32;
+    const int lane = ((lam >> m) << (m + 1)) | (lam & ((1 << m) - 1));
+    return pair_of<D>(s, lane, 2 * i + h);
+  }
+  return pair_of<D>(s, f % 64, 2 * (f / 64) + h);
+}
+
+// Coefficients of one side of one expert from its LDS table.
+template <int D>
+struct TabSrc {
+  static constexpr bool kPerRow = false;
+  const float4* tab;
+  template <int S, int N>
+  __device__ __forceinline__ void get(float2 (&c)[N], int lane, int /*row*/) const {
+    load<S, N>(tab, c, lane);
+  }
+  template <int S, int N>
+  __device__ static __forceinline__ void load(const float4* tab, float2 (&c)[N], int lane) {
+    using C = WCfg<D>;
+    constexpr int M = S - C::RB;
+    const float4* t = tab + S * (C::P / 2);
+    int off = lane, stride = 64;
+    if constexpr (S >= C::RB && M < 4) {
+      off = ((lane >> (M + 1)) << M) | (lane & ((1 << M) - 1));
+      stride = 32;
+    }
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const float4 q = t[i * stride + off];
+      c[2 * i] = make_float2(q.x, q.y);
+      c[2 * i + 1] = make_float2(q.z, q.w);
+    }
+  }
+};
+
+// Each row its own expert's LDS table (a wave whose rows straddle the
+// tile's expert boundary).
+template <int D>
+struct TabRowSrc {
+  static constexpr bool kPerRow = true;
+  const float4* tab[kRowsW];
+  template <int S, int N>
+  __device__ __forceinline__ void get(float2 (&c)[N], int lane, int row) const {
+    TabSrc<D>::template load<S, N>(tab[row], c, lane);
+  }
+};
+
+// The same coefficients evaluated from the expert's angles in global memory
+// (an expert without a table in this tile).
+template <int D>
+struct AngSrc {
+  static constexpr bool kPerRow = false;
+  const float* ang;
+  template <int S, int N>
+  __device__ __forceinline__ void get(float2 (&c)[N], int lane, int /*row*/) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) c[i] = tile_cos_sin(ang[S * WCfg<D>::P + pair_of<D>(S, lane, i)]);
+  }
+};
+
+__device__ __forceinline__ float fneg_if(float v, int neg) {
+  return __int_as_float(__float_as_int(v) ^ (neg << 31));
+}
+
+// Partner value m lanes' bit away (bit m of the lane index flipped), m = 0..3.
+template <int M>
+__device__ __forceinline__ float lane_partner(float v) {
+  const int iv = __float_as_int(v);
+  int r;
+  if constexpr (M == 0) {
+    r = __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+  } else if constexpr (M == 1) {
+    r = __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+  } else if constexpr (M == 2) {
+    // lanes 0-3 and 8-11 of each row read 4 lanes up (row_shl:4), lanes
+    // 4-7 and 12-15 read 4 lanes down (row_shr:4)
+    r = __builtin_amdgcn_update_dpp(0, iv, 0x104, 0xF, 0x5, false);
+    r = __builtin_amdgcn_update_dpp(r, iv, 0x114, 0xF, 0xA, false);
+  } else {
+    r = __builtin_amdgcn_mov_dpp(iv, 0x128, 0xF, 0xF, true);  // row_ror:8
+  }
+  return __int_as_float(r);
+}
+
+// Swap half of register a with half of register b across lane bit M (4 or
+// 5): afterwards lanes with that bit clear hold (a, partner of a), lanes with
+// it set hold (partner of b, b). Applying it twice restores both.
+template <int M>
+__device__ __forceinline__ void lane_swap(float& a, float& b) {
+  const unsigned ia = __float_as_uint(a), ib = __float_as_uint(b);
+  if constexpr (M == 4) {
+    const auto r = __builtin_amdgcn_permlane16_swap(ia, ib, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(ia, ib, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  }
+}
+
+// One butterfly stage s on NR rows held VPL values per lane (element
+// VPL*lane + r in v[.][r]). TR: the transposed side (angle negated).
+template <int D, bool TR, int NR, int S, class Src>
+__device__ __forceinline__ void stage(float (&v)[NR][D / 64], const Src& src, int lane) {
+  using C = WCfg<D>;
+  constexpr int VPL = C::VPL, RB = C::RB;
+  constexpr int NC = Src::kPerRow ? NR : 1;  // coefficient sets: one per row, or shared
+  if constexpr (S < RB) {
+    // Both elements of every pair in this lane: pairs VPL/2 * lane + u.
+    float2 cc[NC][VPL / 2];
+#pragma unroll
+    for (int q = 0; q < NC; ++q) src.template get<S, VPL / 2>(cc[q], lane, q);
+#pragma unroll
+    for (int u = 0; u < VPL / 2; ++u) {
+      const int m = ((u >> S) << (S + 1)) | (u & ((1 << S) - 1)), n = m + (1 << S);
+#pragma unroll
+      for (int q = 0; q < NR; ++q) {
+        const float2 c = cc[NC == 1 ? 0 : q][u];
+        const float a = v[q][m], b = v[q][n];
+        if (TR) {
+          v[q][m] = c.x * a + c.y * b;
+          v[q][n] = c.x * b - c.y * a;
+        } else {
+          v[q][m] = c.x * a - c.y * b;
+          v[q][n] = c.y * a + c.x * b;
+        }
+      }
+    }
+  } else if constexpr (S < RB + 4) {
+    // Partner in lane ^ 2^(S-RB): out = c * mine + sigma * s * partner, with
+    // sigma = +1 for the lower element on the transposed side and -1 on the
+    // forward side (and the opposite for the upper element).
+    constexpr int M = S - RB;
+    float2 cc[NC][VPL];
+#pragma unroll
+    for (int q = 0; q < NC; ++q) src.template get<S, VPL>(cc[q], lane, q);
+    const int upper = (lane >> M) & 1;
+    const int neg = TR ? upper : upper ^ 1;
+#pragma unroll
+    for (int r = 0; r < VPL; ++r) {
+#pragma unroll
+      for (int q = 0; q < NR; ++q) {
+        const float2 c = cc[NC == 1 ? 0 : q][r];
+        const float sn = fneg_if(c.y, neg);
+        // the partner's DPP move folds into the multiply
+        const float t = sn * lane_partner<M>(v[q][r]);
+        v[q][r] = fmaf(c.x, v[q][r], t);
+      }
+    }
+  } else {
+    // Partner in lane ^ 16 or ^ 32: swap register pairs (r, r+1) so each lane
+    // holds one whole pair (the lower lanes that of register r, the upper
+    // lanes that of register r + 1), rotate, swap back.
+    constexpr int M = S - RB;
+    float2 c2[NC][VPL / 2];
+#pragma unroll
+    for (int q = 0; q < NC; ++q) src.template get<S, VPL / 2>(c2[q], lane, q);
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+#pragma unroll
+      for (int r = 0; r < VPL; r += 2) {
+        float a = v[q][r], b = v[q][r + 1];
+        lane_swap<M>(a, b);
+        const float cc = c2[NC == 1 ? 0 : q][r / 2].x, ss = c2[NC == 1 ? 0 : q][r / 2].y;
+        float a2, b2;
+        if (TR) {
+          a2 = cc * a + ss * b;
+          b2 = cc * b - ss * a;
+        } else {
+          a2 = cc * a - ss * b;
+          b2 = ss * a + cc * b;
+        }
+        lane_swap<M>(a2, b2);
+        v[q][r] = a2;
+        v[q][r + 1] = b2;
+      }
+    }
+  }
+}
+
+template <int D, bool TR, int NR, class Src, int... Ss>
+__device__ __forceinline__ void stages(float (&v)[NR][D / 64], const Src& src, int lane,
+                                       std::integer_sequence<int, Ss...>) {
+  if constexpr (TR) {
+    // B^T: S_{L-1}^T first
+    (stage<D, TR, NR, WCfg<D>::L - 1 - Ss>(v, src, lane), ...);
+  } else {
+    (stage<D, TR, NR, Ss>(v, src, lane), ...);
+  }
+}
+
+template <int D, bool TR, int NR, class Src>
+__device__ __forceinline__ void butterfly(float (&v)[NR][D / 64], const Src& src, int lane) {
+  stages<D, TR, NR>(v, src, lane, std::make_integer_sequence<int, WCfg<D>::L>{});
+}
+
+// Rotate this wave's four rows, row q by expert e[q]'s butterfly: all four
+// in one pass when every row's expert has a table here (shared by the four in
+// the usual case, per row where the tile's expert boundary falls inside the
+// wave), else one row at a time. Each pass takes its coefficients from one
+// kind of source, so its stages hold no branches.
+template <int D, bool TR>
+__device__ __forceinline__ void butterfly_rows(float (&v)[kRowsW][D / 64], const int (&e)[kRowsW],
+                                               int e_first, int e_last, const float4* tab_first,
+                                               const float4* tab_last, const float* ang,
+                                               int lane) {
+  using C = WCfg<D>;
+  constexpr int VPL = C::VPL;
+  auto table = [&](int ex) -> const float4* {
+    return ex == e_first ? tab_first : ex == e_last ? tab_last : nullptr;
+  };
+  if (e[0] == e[1] && e[0] == e[2] && e[0] == e[3] && table(e[0])) {
+    butterfly<D, TR, kRowsW>(v, TabSrc<D>{table(e[0])}, lane);
+    return;
+  }
+  const TabRowSrc<D> rows{{table(e[0]), table(e[1]), table(e[2]), table(e[3])}};
+  if (rows.tab[0] && rows.tab[1] && rows.tab[2] && rows.tab[3]) {
+    // rows of the tile's first and last experts: one pass, per-row tables
+    butterfly<D, TR, kRowsW>(v, rows, lane);
+    return;
+  }
+#pragma unroll 1
+  for (int q = 0; q < kRowsW; ++q) {
+    // row q through selects (q is uniform; no dynamic register indexing)
+    float one[1][VPL];
+    const int ex = q == 0 ? e[0] : q == 1 ? e[1] : q == 2 ? e[2] : e[3];
+#pragma unroll
+    for (int r = 0; r < VPL; ++r)
+      one[0][r] = q == 0 ? v[0][r] : q == 1 ? v[1][r] : q == 2 ? v[2][r] : v[3][r];
+    const float4* tab = table(ex);
+    if (tab) butterfly<D, TR, 1>(one, TabSrc<D>{tab}, lane);
+    else butterfly<D, TR, 1>(one, AngSrc<D>{ang + (size_t)ex * C::TBL}, lane);
+#pragma unroll
+    for (int i = 0; i < kRowsW; ++i)
+#pragma unroll
+      for (int r = 0; r < VPL; ++r) v[i][r] = q == i ? one[0][r] : v[i][r];
+  }
+}
+
+// The tables of the tile's first and last experts hold 2 * L stage blocks of
+// D/2 float2 positions, cut into pieces of 64; wave w fills pieces w, w + 8,
+// .. (NTB of them), lane l position 64 * (piece within the block) + l, so the
+// stage of a piece is uniform over the wave and the LDS writes are
+// consecutive; the angles are gathered in the table's order.
+template <int D>
+struct TableJob {
+  static constexpr int PPB = WCfg<D>::P / kWave;          // pieces per block
+  static constexpr int NQ = 2 * WCfg<D>::L * PPB;         // pieces
+  static constexpr int NTB = NQ / kWavesW;                // entries per thread
+  static_assert(NQ % kWavesW == 0, "pieces must split over the waves");
+  static_assert(NTB <= WCfg<D>::NSTEP, "one output-side entry per K-step");
+  // entry i of this thread: expert (0 first, 1 last), stage, position k
+  __device__ static __forceinline__ void at(int i, int wave, int lane, int& ex, int& s, int& k) {
+    const int q = wave + kWavesW * i;
+    const int blk = q / PPB;
+    ex = blk / WCfg<D>::L;
+    s = blk % WCfg<D>::L;
+    k = kWave * (q % PPB) + lane;
+  }
+};
+
+// Entry i of this thread's share of one side's tables (see TableJob), from
+// its angle; the last expert's entries only when it differs from the first.
+template <int D>
+__device__ __forceinline__ void write_table_entry(int i, float ang, float2* tab, bool two,
+                                                  int wave, int lane) {
+  int ex, s, k;
+  TableJob<D>::at(i, wave, lane, ex, s, k);
+  if (ex == 0 || two) tab[ex * WCfg<D>::TBL + s * WCfg<D>::P + k] = tile_cos_sin(ang);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
+  using C = WCfg<D>;
+  constexpr int VPL = C::VPL;
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
+  int* const wcnt = reinterpret_cast<int*>(lds + C::OFF_ROUTE);  // [waves][N]
+  int* const cnt = wcnt + kWavesW * kMaxNW;                        // [N + 1]
+  int* const misc = cnt + kMaxNW + 4;                              // bad id; first, last expert
+  float2* const tin = reinterpret_cast<float2*>(lds + C::OFF_TIN);    // first, last
+  float2* const tout = reinterpret_cast<float2*>(lds + C::OFF_TOUT);  // first, last
+  const float4* const tin_first = reinterpret_cast<const float4*>(tin);
+  const float4* const tin_last = reinterpret_cast<const float4*>(tin + C::TBL);
+  const float4* const tout_first = reinterpret_cast<const float4*>(tout);
+  const float4* const tout_last = reinterpret_cast<const float4*>(tout + C::TBL);
+  float* const hrows = reinterpret_cast<float*>(lds + C::OFF_H);
+  char* const zt = lds + C::OFF_Z;
+  int* const sh_e = reinterpret_cast<int*>(lds + C::OFF_META);
+  int* const sh_r = sh_e + kSlots;
+
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  char* const pwl = lds + C::OFF_P + wave * C::PW_WAVE;  // this wave's substrate rows
+  const int tile = blockIdx.x;
+  const int q0 = tile * kSlots;
+  const int nr = min(kSlots, a.M - q0);
+  const int N = a.N;
+
+  // ---- routing of this tile's slots ---------------------------------------
+  const int i0 = kIdsW * tid;
+  const int nv = max(0, min(kIdsW, a.M - i0));
+  int id[kIdsW];
+  if (nv == kIdsW) {
+#pragma unroll
+    for (int j = 0; j < kIdsW / 4; ++j) {
+      const int4 v = reinterpret_cast<const int4*>(a.ids + i0)[j];
+      id[4 * j] = v.x; id[4 * j + 1] = v.y; id[4 * j + 2] = v.z; id[4 * j + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kIdsW; ++j) id[j] = j < nv ? a.ids[i0 + j] : 0;
+  }
+
+  for (int e = tid; e < kWavesW * N; e += kThreadsW) wcnt[e] = 0;
+  if (tid == 0) {
+    misc[0] = 0;
+    misc[1] = 0;
+    misc[2] = 0;
+  }
+  if (tid < kSlots) {  // every valid slot is ranked below
+    sh_e[tid] = 0;
+    sh_r[tid] = 0;
+  }
+  lds_barrier();
+  bool bad = false;
+  int* const mine = wcnt + wave * N;
+#pragma unroll
+  for (int j = 0; j < kIdsW; ++j) {
+    if (j < nv) {
+      int e = id[j];
+      if ((unsigned)e >= (unsigned)N) {
+        bad = true;
+        e = e < 0 ? 0 : N - 1;
+      }
+      id[j] = e;
+      atomicAdd(&mine[e], 1);
+    }
+  }
+  if (bad) misc[0] = 1;
+  lds_barrier();
+  // Wave 0: totals, each wave's exclusive prefix in place, the exclusive
+  // offsets over experts, and the experts of the tile's first and last slot.
+  if (wave == 0) {
+    const int q_last = q0 + nr - 1;
+    int carry = 0;
+    for (int e0 = 0; e0 < N; e0 += kWave) {
+      const int e = e0 + lane;
+      int tot = 0;
+      if (e < N) {
+#pragma unroll
+        for (int w = 0; w < kWavesW; ++w) {
+          const int c = wcnt[w * N + e];
+          wcnt[w * N + e] = tot;
+          tot += c;
+        }
+      }
+      int incl = tot;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int t = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += t;
+      }
+      const int run = carry + incl - tot;
+      if (e < N) {
+        cnt[e] = run;
+        if (tile == 0) a.rt.offsets[e] = run;
+        if (run <= q0 && q0 < run + tot) misc[1] = e;
+        if (run <= q_last && q_last < run + tot) misc[2] = e;
+      }
+      carry += __shfl(incl, kWave - 1, kWave);
+    }
+    if (lane == 0) {
+      cnt[N] = a.M;
+      if (tile == 0) {
+        a.rt.offsets[N] = a.M;
+        *a.status = misc[0] ? BMOE_E_EXPERT : BMOE_OK;
+      }
+    }
+  }
+  lds_barrier();
+  const int e_first = misc[1], e_last = misc[2];
+  // Both sides' angles of the two tables, in flight during the ranking.
+  constexpr int NTB = TableJob<D>::NTB;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // uniform: scalar table indexing
+  const bool two = e_last != e_first;                    // a second table is needed
+  float th[NTB], ph[NTB];
+#pragma unroll
+  for (int i = 0; i < NTB; ++i) {
+    int ex, s, k;
+    TableJob<D>::at(i, wv, lane, ex, s, k);
+    th[i] = ph[i] = 0.f;
+    if (ex == 0 || two) {
+      const size_t src = (size_t)(ex ? e_last : e_first) * C::TBL + s * C::P + table_pair<D>(s, k);
+      th[i] = a.theta[src];
+      ph[i] = a.phi[src];
+    }
+  }
+  // Stable ranks of the tile's experts: an id's slot is its expert's offset,
+  // plus that expert's ids in earlier waves, earlier lanes of this wave and
+  // earlier positions of this thread.
+  for (int e = e_first; e <= e_last; ++e) {
+    if (cnt[e + 1] == cnt[e]) continue;  // uniform: no ids of e
+    const int w_lo = wcnt[wave * N + e];
+    const int w_hi = wave + 1 < kWavesW ? wcnt[(wave + 1) * N + e] : cnt[e + 1] - cnt[e];
+    if (w_hi <= q0 - cnt[e] || w_lo >= q0 + nr - cnt[e]) continue;  // uniform per wave
+    int below = 0;
+#pragma unroll
+    for (int j = 0; j < kIdsW; ++j) {
+      const uint64_t m = __ballot(j < nv && id[j] == e);
+      below += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+    }
+    int q = cnt[e] + w_lo + below - q0;
+#pragma unroll
+    for (int j = 0; j < kIdsW; ++j) {
+      if (j < nv && id[j] == e) {
+        if ((unsigned)q < (unsigned)nr) {
+          sh_e[q] = e;
+          sh_r[q] = i0 + j;
+        }
+        ++q;
+      }
+    }
+  }
+  lds_barrier();  // ranks are in; the routing scratch is dead from here on
+  if (tid < nr) {
+    const int r = sh_r[tid];
+    a.rt.perm[q0 + tid] = r;
+    a.rt.inv[r] = q0 + tid;
+    a.rt.slot_e[q0 + tid] = sh_e[tid];
+  }
+
+  // ---- this wave's rows: x, gates -----------------------------------------
+  int ew[kRowsW], rw[kRowsW];
+  uint4 xraw[kRowsW];
+  float gw[kRowsW];
+#pragma unroll
+  for (int i = 0; i < kRowsW; ++i) {
+    const int q = wave * kRowsW + i;
+    const int qq = q < nr ? q : nr - 1;  // rows past the end repeat the last one
+    ew[i] = sh_e[qq];
+    rw[i] = sh_r[qq];
+    const uint16_t* xr = a.x + (size_t)(rw[i] / a.k) * D + VPL * lane;
+    if constexpr (VPL == 8) {
+      xraw[i] = *reinterpret_cast<const uint4*>(xr);
+    } else {
+      const uint2 t = *reinterpret_cast<const uint2*>(xr);
+      xraw[i] = make_uint4(t.x, t.y, 0u, 0u);
+    }
+    gw[i] = a.gates[rw[i]];
+  }
+  // This wave's packed substrate rows (o = wave * WN ..), copied to LDS by
+  // the global->LDS path in 1 KiB pieces: lane l of piece i fills LDS chunk
+  // c = 64 i + l, which holds row c / CPR's global chunk (c % CPR) ^ swz.
+  // They land while the butterfly runs.
+  {
+    const char* wrows = reinterpret_cast<const char*>(a.wp) + (size_t)wave * C::PW_WAVE;
+#pragma unroll
+    for (int i = 0; i < C::PW_LOADS; ++i) {
+      const int c = 64 * i + lane, R = c / C::CPR, g = (c % C::CPR) ^ C::pw_swz(R);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(wrows + R * C::ROWB + 16 * g),
+          (__attribute__((address_space(3))) void*)(pwl + 1024 * i), 16, 0, 0);
+    }
+  }
+  // Input-side tables of the tile's first and last experts (the output
+  // side's are computed during the product).
+#pragma unroll
+  for (int i = 0; i < NTB; ++i) write_table_entry<D>(i, th[i], tin, two, wv, lane);
+  lds_barrier();
+
+  // ---- butterfly-in, Z rows into the A tile --------------------------------
+  float v[kRowsW][VPL];
+#pragma unroll
+  for (int i = 0; i < kRowsW; ++i) {
+    const uint32_t w4[4] = {xraw[i].x, xraw[i].y, xraw[i].z, xraw[i].w};
+#pragma unroll
+    for (int r = 0; r < VPL; r += 2) {
+      v[i][r] = bf16_lo(w4[r / 2]);
+      v[i][r + 1] = bf16_hi(w4[r / 2]);
+    }
+  }
+  butterfly_rows<D, true>(v, ew, e_first, e_last, tin_first, tin_last, a.theta, lane);
+  // Row q's 16-byte chunk c sits at chunk c ^ (q & 15) (conflict-free A reads).
+#pragma unroll
+  for (int i = 0; i < kRowsW; ++i) {
+    const int q = wave * kRowsW + i;
+    const int e0 = VPL * lane;
+    char* dst = zt + q * (2 * D) + 16 * ((e0 / 8) ^ (q & 15)) + 2 * (e0 % 8);
+    if constexpr (VPL == 8) {
+      *reinterpret_cast<uint4*>(dst) =
+          make_uint4(pack_bf16x2(v[i][0], v[i][1]), pack_bf16x2(v[i][2], v[i][3]),
+                     pack_bf16x2(v[i][4], v[i][5]), pack_bf16x2(v[i][6], v[i][7]));
+    } else {
+      *reinterpret_cast<uint2*>(dst) =
+          make_uint2(pack_bf16x2(v[i][0], v[i][1]), pack_bf16x2(v[i][2], v[i][3]));
+    }
+  }
+  // This wave's substrate rows have landed (its own copies only: no other
+  // wave reads them), and every wave's A rows are in.
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier();
+
+  // ---- substrate product: wave w computes all 32 rows x columns
+  // [w * WN, (w + 1) * WN) on v_mfma_f32_32x32x16_bf16.
+  f32x16 acc[C::FN];
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+  const int ra = lane & 31;
+  // B operand: lane l takes, in K-step ks, word 2 ks + (l >> 5) of W row
+  // o = wave * WN + 32 j + (l & 31) (K values 32 ks + 16 (l >> 5) .. + 15);
+  // the step's two MFMAs take its low and high eight values, and their A
+  // fragments the same K values.
+#pragma unroll
+  for (int ks = 0; ks < C::NSTEP; ++ks) {
+    uint32_t pw[C::FN];
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int R = 32 * j + ra, w = 2 * ks + (lane >> 5);
+      pw[j] = *reinterpret_cast<const uint32_t*>(pwl + R * C::ROWB +
+                                                 16 * ((w / 4) ^ C::pw_swz(R)) + 4 * (w % 4));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // K values 32 ks + 16 (lane >> 5) + 8 h .. + 7: 16-byte chunk ca of row ra
+      const int ca = 4 * ks + 2 * (lane >> 5) + h;
+      const bf16x8 av =
+          *reinterpret_cast<const bf16x8*>(zt + ra * (2 * D) + 16 * (ca ^ (ra & 15)));
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        const bf16x8 b = unpack_frag(pw[j], h);
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b, acc[j], 0, 0, 0);
+      }
+    }
+    // One entry per K-step: VALU work beside the matrix cores (no one reads
+    // this region before the barrier that follows the H rows).
+    if (ks < NTB) write_table_entry<D>(ks, ph[ks], tout, two, wv, lane);
+  }
+  lds_barrier();  // every wave is done with Z and P, which the H rows reuse
+  // alpha * H -> fp32 rows (32x32 block layout: lane l, register r -> row
+  // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32).
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) {
+    const int col = wave * C::WN + j * 32 + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      hrows[row * C::HS + col] = a.alpha * acc[j][r];
+    }
+  }
+  lds_barrier();  // the H rows are complete
+
+  // ---- butterfly-out, gate, g * U rows in routed order ---------------------
+#pragma unroll
+  for (int i = 0; i < kRowsW; ++i) {
+    const int q = wave * kRowsW + i;
+    const float* hr = hrows + q * C::HS + VPL * lane;
+#pragma unroll
+    for (int r = 0; r < VPL; r += 4) {
+      const float4 t = *reinterpret_cast<const float4*>(hr + r);
+      v[i][r] = t.x;
+      v[i][r + 1] = t.y;
+      v[i][r + 2] = t.z;
+      v[i][r + 3] = t.w;
+    }
+  }
+  butterfly_rows<D, false>(v, ew, e_first, e_last, tout_first, tout_last, a.phi, lane);
+#pragma unroll
+  for (int i = 0; i < kRowsW; ++i) {
+    const int q = wave * kRowsW + i;
+    if (q >= nr) continue;
+    const float g = gw[i];
+    uint16_t* dst = a.u + (size_t)rw[i] * D + VPL * lane;
+    if constexpr (VPL == 8) {
+      *reinterpret_cast<uint4*>(dst) =
+          make_uint4(pack_bf16x2(g * v[i][0], g * v[i][1]), pack_bf16x2(g * v[i][2], g * v[i][3]),
+                     pack_bf16x2(g * v[i][4], g * v[i][5]), pack_bf16x2(g * v[i][6], g * v[i][7]));
+    } else {
+      *reinterpret_cast<uint2*>(dst) =
+          make_uint2(pack_bf16x2(g * v[i][0], g * v[i][1]), pack_bf16x2(g * v[i][2], g * v[i][3]));
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_w(const WaveArgs& a, hipStream_t s, const KernelTiming& t) {
+  return launch_kernel(fused_wave_kernel<D>, dim3((a.M + kSlots - 1) / kSlots), dim3(kThreadsW),
+                       0, s, t, a);
+}
+
+}  // namespace
+
+bool fused_wave_routes(bmoe_dtype dt, int M, int d, int N) {
+  return dt == BMOE_BF16 && (d == 256 || d == 512) && M <= kMaxMW && N <= kMaxNW;
+}
+
+hipError_t launch_fused_wave(int M, int d, int k, int N, const void* x, const int32_t* ids,
+                             const float* gates, const float* theta, const float* phi,
+                             const uint32_t* wp, float alpha, void* u, const RouteTables& rt,
+                             int32_t* status, hipStream_t s, const KernelTiming& t) {
+  if (!fused_wave_routes(BMOE_BF16, M, d, N)) return hipErrorInvalidValue;
+  WaveArgs a{};
+  a.M = M;
+  a.k = k;
+  a.N = N;
+  a.x = static_cast<const uint16_t*>(x);
+  a.ids = ids;
+  a.gates = gates;
+  a.theta = theta;
+  a.phi = phi;
+  a.wp = wp;
+  a.alpha = substrate_scale(alpha);
+  a.u = static_cast<uint16_t*>(u);
+  a.rt = rt;
+  a.status = status;
+  switch (d) {
+    case 256: return launch_w<256>(a, s, t);
+    case 512: return launch_w<512>(a, s, t);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace bmoe

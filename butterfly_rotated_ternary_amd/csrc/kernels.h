@@ -61,6 +61,15 @@ hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, con
 // uint4 index (ob * (d/64) + kt) * CB + o % CB of `wt`.
 int gemm_tiled_w_block(bmoe_dtype dt, int M, int d);
 
+// Routed fused forward with wave-resident rows (bf16, d = 256 or 512, M <=
+// 8192 routed rows, N <= 512 experts): the same results and routing tables as
+// launch_fused_routed, with every butterfly stage done by wave shuffles.
+bool fused_wave_routes(bmoe_dtype dt, int M, int d, int N);
+hipError_t launch_fused_wave(int M, int d, int k, int N, const void* x, const int32_t* ids,
+                             const float* gates, const float* theta, const float* phi,
+                             const uint32_t* wp, float alpha, void* u, const RouteTables& rt,
+                             int32_t* status, hipStream_t s, const KernelTiming& t = {});
+
 // Whole forward for d in {2, 4, 8}: one thread per token, its k routed rows
 // in ascending j (rotations with the prep kernel's cos/sin tables, the
 // ternary product, the gate and the fp32 sum), written straight to y.
