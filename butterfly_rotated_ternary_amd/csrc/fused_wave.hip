@@ -152,6 +152,28 @@ __host__ __device__ constexpr int table_pair(int s, int k) {
   return pair_of<D>(s, f % 64, 2 * (f / 64) + h);
 }
 
+// Angle index (stage * D/2 + pair) of every table position, fixed at
+// compile time; each thread reads its few entries at the start of the kernel.
+template <int D>
+struct TabIdx {
+  uint16_t v[WCfg<D>::TBL];
+};
+template <int D>
+constexpr TabIdx<D> make_tab_idx() {
+  TabIdx<D> t{};
+  for (int s = 0; s < WCfg<D>::L; ++s)
+    for (int k = 0; k < WCfg<D>::P; ++k)
+      t.v[s * WCfg<D>::P + k] = (uint16_t)(s * WCfg<D>::P + table_pair<D>(s, k));
+  return t;
+}
+__device__ constexpr TabIdx<256> kTabIdx256 = make_tab_idx<256>();
+__device__ constexpr TabIdx<512> kTabIdx512 = make_tab_idx<512>();
+template <int D>
+__device__ __forceinline__ const uint16_t* tab_idx() {
+  if constexpr (D == 256) return kTabIdx256.v;
+  else return kTabIdx512.v;
+}
+
 // Coefficients of one side of one expert from its LDS table.
 template <int D>
 struct TabSrc {
@@ -458,6 +480,17 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
     for (int j = 0; j < kIdsW; ++j) id[j] = j < nv ? a.ids[i0 + j] : 0;
   }
 
+  // Angle indices of this thread's table entries (they do not depend on
+  // the routing).
+  constexpr int NTB = TableJob<D>::NTB;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // uniform: scalar table indexing
+  int tix[NTB];
+#pragma unroll
+  for (int i = 0; i < NTB; ++i) {
+    int ex, s, k;
+    TableJob<D>::at(i, wv, lane, ex, s, k);
+    tix[i] = tab_idx<D>()[s * C::P + k];
+  }
   for (int e = tid; e < kWavesW * N; e += kThreadsW) wcnt[e] = 0;
   if (tid == 0) {
     misc[0] = 0;
@@ -527,8 +560,6 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
   lds_barrier();
   const int e_first = misc[1], e_last = misc[2];
   // Both sides' angles of the two tables, in flight during the ranking.
-  constexpr int NTB = TableJob<D>::NTB;
-  const int wv = __builtin_amdgcn_readfirstlane(wave);  // uniform: scalar table indexing
   const bool two = e_last != e_first;                    // a second table is needed
   float th[NTB], ph[NTB];
 #pragma unroll
@@ -537,7 +568,7 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
     TableJob<D>::at(i, wv, lane, ex, s, k);
     th[i] = ph[i] = 0.f;
     if (ex == 0 || two) {
-      const size_t src = (size_t)(ex ? e_last : e_first) * C::TBL + s * C::P + table_pair<D>(s, k);
+      const size_t src = (size_t)(ex ? e_last : e_first) * C::TBL + tix[i];
       th[i] = a.theta[src];
       ph[i] = a.phi[src];
     }
