@@ -438,19 +438,20 @@ hipError_t launch_dl(const uint16_t* z, const uint32_t* wp, uint16_t* h, int M, 
 }
 
 // ---------------------------------------------------------------------------
-// 256x256-tile kernel for d % 256 == 0 (the large product): 4 waves, one per
-// SIMD, each owning a 256x64 block of the tile (8x2 fragments of 32x32, the
-// 16 accumulator blocks in AGPRs).
+// Large-tile kernel (the large product, d a multiple of its BN): BM x BN
+// output tiles, WM x WN waves, each owning a TM x TN block of 32x32
+// fragments (FM x FN accumulator blocks). The configuration in use is below
+// (LargeCfg).
 //
 // Both operands stream global->LDS with global_load_lds_dwordx4 through a
-// 4-stage ring, three K-steps ahead: a stage holds the Z tile (256 rows x 64
-// bf16, XOR-swizzled) and the packed substrate words of the step (256 output
-// columns x 16 bytes = 4 KiB). The substrate stays packed in LDS. In the MFMA
-// B layout lane l holds output column l % 32 of a fragment and K half l / 32
-// of each 16-wide slice, so a lane reads the 16 bytes of its column once per
+// 4-stage ring, three K-steps ahead: a stage holds the Z tile (BM rows x 64
+// bf16, XOR-swizzled) and the packed substrate words of the step (BN output
+// columns x 16 bytes). The substrate stays packed in LDS. In the MFMA B
+// layout lane l holds output column l % 32 of a fragment and K half l / 32 of
+// each 16-wide slice, so a lane reads the 16 bytes of its column once per
 // step and expands the 8 bf16 of a slice in registers (unpack_pair: two VALU
-// ops per bf16 pair) right before the MFMAs that use them. With 256 rows per
-// wave each expanded fragment feeds 8 MFMAs.
+// ops per bf16 pair) right before the MFMAs that use them; each expanded
+// fragment feeds FM MFMAs.
 //
 // One barrier per step, before the last slice's MFMAs: all waves are done
 // reading the step's stage (the DMA issued next step may overwrite it) and the
@@ -460,20 +461,23 @@ hipError_t launch_dl(const uint16_t* z, const uint32_t* wp, uint16_t* h, int M, 
 // are spread between MFMAs.
 template <int BM_, int BN_, int WM_, int WN_>
 struct RbCfg {
-  static constexpr int BM = BM_, BN = BN_, THREADS = 256;
-  static constexpr int WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int WM = WM_, WN = WN_, WAVES = WM * WN, THREADS = 64 * WAVES;
   static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   static constexpr int NSTAGE = 4, AHEAD = NSTAGE - 1;
   static constexpr int A_BYTES = BM * kRowBytes;       // Z: BM rows x 64 bf16
   static constexpr int B_BYTES = BN * 16;              // packed words: BN columns x 16 B
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int A_LOADS = A_BYTES / 1024 / 4;   // 1 KiB DMA blocks per wave
-  static constexpr int B_LOADS = B_BYTES / 1024 / 4;
+  static constexpr int A_LOADS = A_BYTES / 1024 / WAVES;  // 1 KiB DMA blocks per wave
+  static constexpr int B_LOADS = B_BYTES / 1024 / WAVES;
   static constexpr int VM_PER_STEP = A_LOADS + B_LOADS;
   static constexpr int OUT_BYTES = 16 * TN * 2;        // per-wave epilogue staging: 16 rows
-  static_assert(WM * WN == 4 && FM * FN == 16, "4 waves, 256 accumulator registers each");
+  // Global stores of one tile's epilogue per wave (16-byte row segments).
+  static constexpr int STORES = FM * 2 * (16 * TN * 2 / 16 / 64);
+  static_assert(WAVES * FM * FN * 32 * 32 == BM * BN, "the waves cover the tile");
+  static_assert(FM * FN * 16 <= 256, "accumulators fit the AGPRs");
   static_assert(A_LOADS >= 1 && B_LOADS >= 1, "whole DMA blocks per wave");
-  static_assert(NSTAGE * STAGE + 4 * OUT_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(NSTAGE * STAGE + WAVES * OUT_BYTES <= 160 * 1024, "LDS budget");
 };
 
 template <int N>
@@ -690,7 +694,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_rb_kernel(const uint16_t* Z,
   __shared__ __attribute__((aligned(1024))) char st1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) char st2[C::STAGE];
   __shared__ __attribute__((aligned(1024))) char st3[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) char stage_out[4 * C::OUT_BYTES];
+  __shared__ __attribute__((aligned(1024))) char stage_out[C::WAVES * C::OUT_BYTES];
   static_assert(C::NSTAGE == 4, "four stage arrays");
   char* ring[4];
   ring[0] = st0;
@@ -731,7 +735,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_rb_kernel(const uint16_t* Z,
   // have the previous tile's epilogue stores (8 per 32 rows) in flight; the
   // first tile has none, so it waits strictly there.
   constexpr int W3 = 2 * C::VM_PER_STEP;
-  constexpr int WS = W3 + 8 * C::FM;
+  constexpr int WS = W3 + C::STORES;
   static_assert(WS <= 63, "vmcnt range");
   bool first = true;
   for (;;) {
@@ -810,7 +814,10 @@ hipError_t launch_rb(const uint16_t* z, const uint32_t* wt, uint16_t* h, int M, 
 
 }  // namespace
 
-using LargeCfg = RbCfg<128, 512, 1, 4>;
+// Eight waves, two per SIMD, each a 128 x 64 block (8 accumulator blocks):
+// one wave's LDS reads and expansion overlap the other's MFMAs (measured
+// against four waves of 128 x 128: 1556 against 1492-1529 TFLOP/s at d = 4096).
+using LargeCfg = RbCfg<128, 512, 1, 8>;
 
 int gemm_tiled_w_block(bmoe_dtype dt, int M, int d) {
   if (dt != BMOE_BF16 || d % LargeCfg::BN != 0) return 0;
@@ -827,7 +834,7 @@ hipError_t launch_gemm(bmoe_dtype dt, int M, int d, const void* z, const uint32_
                                                       alpha, s, t);
   uint16_t* hb = static_cast<uint16_t*>(h);
   const uint16_t* zb = static_cast<const uint16_t*>(z);
-  // Large problems: 128x512 tiles (4 waves of 128x128, tile-major substrate
+  // Large problems: 128x512 tiles (8 waves of 128x64, tile-major substrate
   // copy). Smaller ones: 128x128 or 64x128 tiles so that the grid still
   // covers the CUs.
   if (gemm_tiled_w_block(dt, M, d)) {
