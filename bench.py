@@ -585,6 +585,53 @@ def base3_section(P, steps, fwd_ms):
             "decode_gbs": nbytes / us / 1e3, "decode_frac_of_forward": us * 1e-3 / fwd_ms}
 
 
+def product_formats_section(steps=20):
+    """The shared-substrate product alone (bmoe_product) with the substrate
+    as 2-bit words and as the base-3 stream decoded inside the product's
+    substrate staging, same kernel otherwise: median kernel time of `steps`
+    launches from its own dispatch events, on random bf16 Z of the d = 512
+    (M = 8192) and d = 4096 (M = 131072) workloads' routed-row counts."""
+    import torch
+    from butterfly_rotated_ternary_amd import bmoe
+    from butterfly_rotated_ternary_amd import workloads as W
+    hip = HipEvents()
+    dev = torch.device("cuda:0")
+    out = []
+    for wname in (W.HEADLINE, GEMM_WORKLOAD):
+        inp = W.make_inputs(wname, T=1)
+        full = W.WORKLOADS[wname]
+        M, d = full["T"] * full["k"], inp.d
+        w8 = torch.from_numpy(inp.w).to(dev)
+        fmts = {"2bit": bmoe.pack_ternary(w8), "base3": bmoe.pack_ternary_b3(w8)}
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(11)
+        z = torch.randn(M, d, device=dev, generator=gen).to(torch.bfloat16)
+        h = torch.empty_like(z)
+        res = {"d": d, "M": M}
+        for name, w in fmts.items():
+            code = bmoe.BMOE_W_2BIT if name == "2bit" else bmoe.BMOE_W_BASE3
+            evsets = [hip.create(2) for _ in range(steps + 2)]
+            for evs in evsets:
+                rc = bmoe.bmoe_product(M, d, z, w, code, float(inp.alpha), h, events=evs)
+                if rc != 0:
+                    raise bmoe.BmoeError(rc, "bmoe_product")
+            torch.cuda.synchronize()
+            ms = sorted(hip.elapsed_ms(e[0], e[1]) for e in evsets[2:])
+            for evs in evsets:
+                hip.destroy(evs)
+            us = ms[len(ms) // 2] * 1e3
+            res[name] = {"us": us, "tflops": 2.0 * M * d * d / (us * 1e-6) / 1e12,
+                         "substrate_bytes": int(w.numel() * w.element_size())}
+        res["base3_over_2bit"] = res["base3"]["us"] / res["2bit"]["us"]
+        log(f"[bench] product d={d} M={M}: 2-bit {res['2bit']['us']:.1f} us "
+            f"({res['2bit']['tflops']:.0f} TFLOP/s), base-3 {res['base3']['us']:.1f} us "
+            f"({res['base3']['tflops']:.0f} TFLOP/s)")
+        out.append(res)
+        del z, h, fmts, w8
+        torch.cuda.empty_cache()
+    return out
+
+
 OUTLIER_WORKLOAD = "d2048_e64_top2_outliers_bf16"
 QUANTISERS = [("int8_absmax", 127, 0), ("int4_absmax", 7, 0), ("ternary_absmax", 1, 0),
               ("ternary_absmean", 1, 1)]
@@ -848,6 +895,7 @@ def main():
     if args.router_steps > 0:
         out["router"] = router_section(P, args.router_steps)
         out["base3"] = base3_section(P, 50, ms)
+        out["base3"]["product"] = product_formats_section()
     if args.bwd_steps > 0:
         out["backward"] = backward_section(P, args.bwd_steps)
     del P

@@ -73,6 +73,8 @@ def lib():
             getattr(L, name).restype = c_int
         L.bmoe_ceiling_copy.argtypes = [vp, vp, c_sz, vp, vp]
         L.bmoe_ceiling_copy.restype = c_int
+        L.bmoe_product.argtypes = [c_int, c_int, vp, vp, c_int, c_f, vp, vp, vp]
+        L.bmoe_product.restype = c_int
         L.bmoe_forward_timed.argtypes = L.bmoe_forward.argtypes + [vp]
         L.bmoe_forward_timed.restype = c_int
         L.bmoe_forward_kernel_count.argtypes = [c_int, c_int, c_int, c_int, c_int]
@@ -223,6 +225,16 @@ def bmoe_forward_noalloc(dt: int, T: int, d: int, n_experts: int, k: int, x, ids
 
 
 BMOE_NOALLOC_MAX_WORKSPACE = 64 << 20
+
+
+BMOE_W_2BIT = 0
+BMOE_W_BASE3 = 1
+
+
+def bmoe_product(M: int, d: int, z, w, fmt: int, alpha: float, h, stream=None,
+                 events=None) -> int:
+    return lib().bmoe_product(M, d, _ptr(z), _ptr(w), fmt, alpha, _ptr(h), _stream(stream),
+                              _events_arg(events))
 
 
 BMOE_CEILING_SINK_FLOATS = 256 * 8 * 256
@@ -487,7 +499,8 @@ def pack_ternary_b3(w: torch.Tensor) -> torch.Tensor:
     n = bmoe_packed3_bytes(d)
     if n == 0 or w.shape != (d, d) or w.dtype != torch.int8:
         raise ValueError("w must be int8 [d][d] with a supported d")
-    out = torch.empty((n + 15) // 16 * 16, dtype=torch.uint8, device=w.device)
+    # 8 bytes of slack past the stream, as bmoe_product reads whole dwords
+    out = torch.zeros((n + 8 + 15) // 16 * 16, dtype=torch.uint8, device=w.device)
     ws = torch.empty(bmoe_pack_workspace_bytes(), dtype=torch.uint8, device=w.device)
     _check(bmoe_pack_ternary_b3(w, d, out, ws), "bmoe_pack_ternary_b3")
     _check(bmoe_sync_status(ws), "bmoe_pack_ternary_b3 (device)")

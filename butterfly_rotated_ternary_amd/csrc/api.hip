@@ -266,6 +266,24 @@ bmoe_status bmoe_pack_ternary(const int8_t* w, int d, uint32_t* packed, void* ws
   return BMOE_OK;
 }
 
+bmoe_status bmoe_product(int M, int d, const void* z, const void* w, bmoe_wformat fmt,
+                         float alpha, void* h, void* stream, void* const* events) {
+  if (fmt != BMOE_W_2BIT && fmt != BMOE_W_BASE3) return BMOE_E_DTYPE;
+  if (M < 0 || !valid_d(d) || d < 128) return BMOE_E_SHAPE;
+  if (M == 0) return BMOE_OK;
+  if (!z || !w || !h) return BMOE_E_NULL;
+  if (!aligned16(z) || !aligned16(w) || !aligned16(h)) return BMOE_E_ALIGN;
+  KernelTiming t;
+  if (events) {
+    t.start = static_cast<hipEvent_t>(events[0]);
+    t.stop = static_cast<hipEvent_t>(events[1]);
+  }
+  if (launch_product(M, d, static_cast<const uint16_t*>(z), w, fmt, alpha,
+                     static_cast<uint16_t*>(h), static_cast<hipStream_t>(stream), t) != hipSuccess)
+    return BMOE_E_HIP;
+  return BMOE_OK;
+}
+
 size_t bmoe_packed3_bytes(int d) {
   if (!valid_d16(d)) return 0;
   return ((size_t)d * d + 4) / 5;

@@ -281,26 +281,80 @@ __device__ __forceinline__ void d_load_a(char* abuf, const uint16_t* Z, int M, i
   }
 }
 
-template <class C>
-__device__ __forceinline__ void d_load_b(uint32_t (&rb)[C::B_PER], const uint32_t* wp, int d,
-                                         int n0, int k0) {
-  const int G = d / 16;
+// Where the substrate of the dl kernel comes from: the packed 2-bit words
+// (one register per word), or the base-3 stream (five ternary digits per
+// byte, row-major entries), decoded into the same words as they are written
+// to LDS. Both give exactly the same bf16 B tiles.
+struct Packed2Src {
+  static constexpr int REGS = 1;  // registers per word in flight
+  const uint32_t* wp;
+  __device__ __forceinline__ void load(uint32_t* r, int o, int d, int k0, int g) const {
+    r[0] = wp[(size_t)o * (d / 16) + k0 / 16 + g];
+  }
+  __device__ __forceinline__ uint32_t word(const uint32_t* r, int, int, int, int,
+                                           const uint16_t*) const {
+    return r[0];
+  }
+};
+
+struct Base3Src {
+  static constexpr int REGS = 2;
+  const uint8_t* w3;
+  // The word's 16 entries e0 .. e0+15 (e0 = o d + k0 + 16 g) lie in bytes
+  // e0/5 .. e0/5 + 3: the two aligned dwords from (e0/5) & ~3 hold them. For
+  // the stream's last words the second dword reaches up to 7 bytes past its
+  // end (the caller's buffer extends 8 bytes beyond it; those bytes are never
+  // decoded), so every lane issues the same two loads.
+  __device__ __forceinline__ void load(uint32_t* r, int o, int d, int k0, int g) const {
+    const size_t e0 = (size_t)o * d + k0 + 16 * g, a = (e0 / 5) & ~(size_t)3;
+    r[0] = *reinterpret_cast<const uint32_t*>(w3 + a);
+    r[1] = *reinterpret_cast<const uint32_t*>(w3 + a + 4);
+  }
+  // lut[b]: the five digits of byte b as 2-bit codes in entry order (digit 0,
+  // 1, 2 -> code 3, 0, 1, i.e. -1, 0, +1).
+  __device__ __forceinline__ uint32_t word(const uint32_t* r, int o, int d, int k0, int g,
+                                           const uint16_t* lut) const {
+    const size_t e0 = (size_t)o * d + k0 + 16 * g, b0 = e0 / 5;
+    const int pos = (int)(e0 - 5 * b0), sh = 8 * (int)(b0 & 3);
+    const uint64_t pair = ((uint64_t)r[1] << 32) | r[0];
+    uint64_t seq = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      seq |= (uint64_t)(lut[(uint32_t)(pair >> (sh + 8 * i)) & 0xFFu] & 0x3FFu) << (10 * i);
+    const uint32_t x = (uint32_t)(seq >> (2 * pos));  // entry v's code at bits 2v, 2v+1
+    // even entries (columns 2j) to the low half, odd ones to the high half
+    uint32_t ev = x & 0x33333333u, od = (x >> 2) & 0x33333333u;
+    ev = (ev | (ev >> 2)) & 0x0F0F0F0Fu;
+    od = (od | (od >> 2)) & 0x0F0F0F0Fu;
+    ev = (ev | (ev >> 4)) & 0x00FF00FFu;
+    od = (od | (od >> 4)) & 0x00FF00FFu;
+    ev = (ev | (ev >> 8)) & 0x0000FFFFu;
+    od = (od | (od >> 8)) & 0x0000FFFFu;
+    return ev | (od << 16);
+  }
+};
+
+template <class C, class Src>
+__device__ __forceinline__ void d_load_b(uint32_t (&rb)[C::B_PER * Src::REGS], const Src& src,
+                                         int d, int n0, int k0) {
 #pragma unroll
   for (int i = 0; i < C::B_PER; ++i) {
     const int wi = threadIdx.x + i * C::THREADS;
-    rb[i] = wp[(size_t)(n0 + wi / (BK / 16)) * G + k0 / 16 + wi % (BK / 16)];
+    src.load(rb + i * Src::REGS, n0 + wi / (BK / 16), d, k0, wi % (BK / 16));
   }
 }
 
-// Expand slice `part` (of 4) of the packed words into bf16 LDS rows.
-template <class C>
-__device__ __forceinline__ void d_write_b(const uint32_t (&rb)[C::B_PER], char* bbuf, int part) {
+// Expand slice `part` (of 4) of the words into bf16 LDS rows.
+template <class C, class Src>
+__device__ __forceinline__ void d_write_b(const uint32_t (&rb)[C::B_PER * Src::REGS],
+                                          const Src& src, const uint16_t* lut, char* bbuf,
+                                          int d, int n0, int k0, int part) {
 #pragma unroll
   for (int i = 0; i < C::B_PER; ++i) {
     if ((i * 4) / C::B_PER != part) continue;
     const int wi = threadIdx.x + i * C::THREADS;
     const int o = wi / (BK / 16), g = wi % (BK / 16);
-    const uint32_t w = rb[i];
+    const uint32_t w = src.word(rb + i * Src::REGS, n0 + o, d, k0, g, lut);
     *reinterpret_cast<uint4*>(bbuf + swz(o, 2 * g)) =
         make_uint4(unpack_pair(w, 0), unpack_pair(w, 1), unpack_pair(w, 2), unpack_pair(w, 3));
     *reinterpret_cast<uint4*>(bbuf + swz(o, 2 * g + 1)) =
@@ -336,48 +390,66 @@ __device__ __forceinline__ void d_mfma(f32x16 (&acc)[C::FM][C::FN], const DFrags
 }
 
 // One K-step on (acur, bcur). LOAD: start step kt+1's Z tile into anxt and
-// step kt+2's packed words into rl. WRITE: expand rn (step kt+1's words) into
-// bnxt. Ends with every Z load of this step landed and a barrier.
-template <class C, bool LOAD, bool WRITE>
+// step kt+2's substrate words into rl. WRITE: expand rn (step kt+1's words)
+// into bnxt. Ends with every Z load of this step landed and a barrier.
+template <class C, class Src, bool LOAD, bool WRITE>
 __device__ __forceinline__ void d_step(f32x16 (&acc)[C::FM][C::FN], const char* acur,
                                        const char* bcur, char* anxt, char* bnxt,
-                                       uint32_t (&rn)[C::B_PER], uint32_t (&rl)[C::B_PER],
-                                       const uint16_t* Z, const uint32_t* wp, int M, int d,
+                                       uint32_t (&rn)[C::B_PER * Src::REGS],
+                                       uint32_t (&rl)[C::B_PER * Src::REGS], const Src& src,
+                                       const uint16_t* lut, const uint16_t* Z, int M, int d,
                                        int m0, int n0, int kt, int wm, int wn, int lane) {
   if constexpr (LOAD) {
     d_load_a<C>(anxt, Z, M, d, m0, (kt + 1) * BK);
-    // The step-end wait counts the packed-word loads as the newest B_PER
-    // vector memory ops: keep the compiler from issuing them before the DMA.
+    // The step-end wait counts the substrate loads as the newest vector
+    // memory ops: keep the compiler from issuing them before the DMA.
     __asm__ volatile("" ::: "memory");
-    d_load_b<C>(rl, wp, d, n0, (kt + 2) * BK);
+    d_load_b<C>(rl, src, d, n0, (kt + 2) * BK);
   }
+  const int kw = (kt + 1) * BK;  // K offset of the words being written
   DFrags<C> f0, f1;
   d_read<C>(f0, acur, bcur, wm, wn, lane, 0);
   d_read<C>(f1, acur, bcur, wm, wn, lane, 16);
   d_mfma<C>(acc, f0);
-  if constexpr (WRITE) d_write_b<C>(rn, bnxt, 0);
+  if constexpr (WRITE) d_write_b<C>(rn, src, lut, bnxt, d, n0, kw, 0);
   d_read<C>(f0, acur, bcur, wm, wn, lane, 32);
   d_mfma<C>(acc, f1);
-  if constexpr (WRITE) d_write_b<C>(rn, bnxt, 1);
+  if constexpr (WRITE) d_write_b<C>(rn, src, lut, bnxt, d, n0, kw, 1);
   d_read<C>(f1, acur, bcur, wm, wn, lane, 48);
   d_mfma<C>(acc, f0);
-  if constexpr (WRITE) d_write_b<C>(rn, bnxt, 2);
+  if constexpr (WRITE) d_write_b<C>(rn, src, lut, bnxt, d, n0, kw, 2);
   d_mfma<C>(acc, f1);
-  if constexpr (WRITE) d_write_b<C>(rn, bnxt, 3);
-  if constexpr (LOAD) wait_vmcnt<C::B_PER>();  // Z tile of kt+1 has landed
+  if constexpr (WRITE) d_write_b<C>(rn, src, lut, bnxt, d, n0, kw, 3);
+  if constexpr (LOAD) wait_vmcnt<C::B_PER * Src::REGS>();  // Z tile of kt+1 has landed
   else wait_vmcnt<0>();
   lds_barrier();
 }
 
-template <class C>
-__global__ __launch_bounds__(C::THREADS) void gemm_dl_kernel(const uint16_t* Z,
-                                                             const uint32_t* wp, uint16_t* H,
-                                                             int M, int d, float alpha,
-                                                             int tiles_m, int tiles_n) {
+template <class C, class Src>
+__global__ __launch_bounds__(C::THREADS) void gemm_dl_kernel(const uint16_t* Z, Src src,
+                                                             uint16_t* H, int M, int d,
+                                                             float alpha, int tiles_m,
+                                                             int tiles_n) {
   __shared__ __attribute__((aligned(1024))) char a0[C::A_BYTES];
   __shared__ __attribute__((aligned(1024))) char a1[C::A_BYTES];
   __shared__ __attribute__((aligned(1024))) char b0[C::B_BYTES];
   __shared__ __attribute__((aligned(1024))) char b1[C::B_BYTES];
+  constexpr bool kB3 = Src::REGS == 2;
+  __shared__ uint16_t lut[kB3 ? 256 : 1];
+  if constexpr (kB3) {
+    // byte value -> its five digits as 2-bit codes (values above 242 do not
+    // occur in a stream written by the pack step)
+    for (int v = threadIdx.x; v < 256; v += C::THREADS) {
+      uint32_t codes = 0, rest = (uint32_t)v;
+      for (int i = 0; i < 5; ++i) {
+        const uint32_t t = rest % 3u;
+        rest /= 3u;
+        codes |= (t == 0 ? 3u : t == 2 ? 1u : 0u) << (2 * i);
+      }
+      lut[v] = (uint16_t)codes;
+    }
+    __syncthreads();
+  }
 
   const int ntiles = tiles_m * tiles_n;
   const int bid = blockIdx.x;
@@ -396,25 +468,29 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dl_kernel(const uint16_t* Z,
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int nk = d / BK;  // even
-  uint32_t r0[C::B_PER], r1[C::B_PER];
+  uint32_t r0[C::B_PER * Src::REGS], r1[C::B_PER * Src::REGS];
   d_load_a<C>(a0, Z, M, d, m0, 0);
-  d_load_b<C>(r0, wp, d, n0, 0);
-  d_load_b<C>(r1, wp, d, n0, BK);
-#pragma unroll
-  for (int part = 0; part < 4; ++part) d_write_b<C>(r0, b0, part);
+  d_load_b<C>(r0, src, d, n0, 0);
+  d_load_b<C>(r1, src, d, n0, BK);
   wait_vmcnt<0>();
+#pragma unroll
+  for (int part = 0; part < 4; ++part) d_write_b<C>(r0, src, lut, b0, d, n0, 0, part);
   __syncthreads();
 
   int kt = 0;
   for (; kt + 2 < nk; kt += 2) {
-    d_step<C, true, true>(acc, a0, b0, a1, b1, r1, r0, Z, wp, M, d, m0, n0, kt, wm, wn, lane);
-    d_step<C, true, true>(acc, a1, b1, a0, b0, r0, r1, Z, wp, M, d, m0, n0, kt + 1, wm, wn, lane);
+    d_step<C, Src, true, true>(acc, a0, b0, a1, b1, r1, r0, src, lut, Z, M, d, m0, n0, kt, wm,
+                               wn, lane);
+    d_step<C, Src, true, true>(acc, a1, b1, a0, b0, r0, r1, src, lut, Z, M, d, m0, n0, kt + 1,
+                               wm, wn, lane);
   }
   // kt = nk - 2: its Z tile for nk-1 still has to be fetched.
   d_load_a<C>(a1, Z, M, d, m0, (kt + 1) * BK);
-  d_step<C, false, true>(acc, a0, b0, a1, b1, r1, r0, Z, wp, M, d, m0, n0, kt, wm, wn, lane);
+  d_step<C, Src, false, true>(acc, a0, b0, a1, b1, r1, r0, src, lut, Z, M, d, m0, n0, kt, wm,
+                              wn, lane);
   // (the barrier inside d_step<.., false, ..> needs the Z loads landed first)
-  d_step<C, false, false>(acc, a1, b1, a0, b0, r0, r1, Z, wp, M, d, m0, n0, kt + 1, wm, wn, lane);
+  d_step<C, Src, false, false>(acc, a1, b1, a0, b0, r0, r1, src, lut, Z, M, d, m0, n0, kt + 1,
+                               wm, wn, lane);
 
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
@@ -429,12 +505,22 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dl_kernel(const uint16_t* Z,
     }
 }
 
-template <class C>
-hipError_t launch_dl(const uint16_t* z, const uint32_t* wp, uint16_t* h, int M, int d,
-                     float alpha, hipStream_t s, const KernelTiming& t) {
+template <class C, class Src>
+hipError_t launch_dl(const uint16_t* z, const Src& src, uint16_t* h, int M, int d, float alpha,
+                     hipStream_t s, const KernelTiming& t) {
   const int tm = (M + C::BM - 1) / C::BM, tn = d / C::BN;
-  return launch_kernel(gemm_dl_kernel<C>, dim3(tm * tn), dim3(C::THREADS), 0, s, t, z, wp, h, M,
-                       d, alpha, tm, tn);
+  return launch_kernel(gemm_dl_kernel<C, Src>, dim3(tm * tn), dim3(C::THREADS), 0, s, t, z, src,
+                       h, M, d, alpha, tm, tn);
+}
+
+// The dl kernel's tile choice: 64x128 tiles when 128x128 gives fewer than
+// two tiles per CU (same per-element accumulation order, so the same bits).
+template <class Src>
+hipError_t launch_dl_auto(const uint16_t* z, const Src& src, uint16_t* h, int M, int d,
+                          float alpha, hipStream_t s, const KernelTiming& t) {
+  if ((long long)((M + 127) / 128) * (d / 128) < 512)
+    return launch_dl<DCfg<64, 128, 2, 2>>(z, src, h, M, d, alpha, s, t);
+  return launch_dl<DCfg<128, 128, 2, 2>>(z, src, h, M, d, alpha, s, t);
 }
 
 // ---------------------------------------------------------------------------
@@ -841,12 +927,16 @@ hipError_t launch_gemm(bmoe_dtype dt, int M, int d, const void* z, const uint32_
     if (!wt) return hipErrorInvalidValue;
     return launch_rb<LargeCfg>(zb, wt, hb, M, d, alpha, s, t);
   }
-  // Fewer than two 128x128 tiles per CU: 64x128 tiles (same per-element
-  // accumulation order, so the same bits).
-  if (d >= 128 && (long long)((M + 127) / 128) * (d / 128) < 512)
-    return launch_dl<DCfg<64, 128, 2, 2>>(zb, w_packed, hb, M, d, alpha, s, t);
-  if (d >= 128) return launch_dl<DCfg<128, 128, 2, 2>>(zb, w_packed, hb, M, d, alpha, s, t);
+  if (d >= 128) return launch_dl_auto(zb, Packed2Src{w_packed}, hb, M, d, alpha, s, t);
   return launch_cfg<Cfg<64, 64, 2, 2, false>, uint16_t>(z, w_packed, hb, M, d, alpha, s, t);
+}
+
+hipError_t launch_product(int M, int d, const uint16_t* z, const void* w, bmoe_wformat fmt,
+                          float alpha, uint16_t* h, hipStream_t s, const KernelTiming& t) {
+  alpha = substrate_scale(alpha);
+  if (fmt == BMOE_W_BASE3)
+    return launch_dl_auto(z, Base3Src{static_cast<const uint8_t*>(w)}, h, M, d, alpha, s, t);
+  return launch_dl_auto(z, Packed2Src{static_cast<const uint32_t*>(w)}, h, M, d, alpha, s, t);
 }
 
 }  // namespace bmoe

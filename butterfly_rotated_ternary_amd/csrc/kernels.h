@@ -70,6 +70,12 @@ hipError_t launch_fused_wave(int M, int d, int k, int N, const void* x, const in
                              const uint32_t* wp, float alpha, void* u, const RouteTables& rt,
                              int32_t* status, hipStream_t s, const KernelTiming& t = {});
 
+// H = alpha Z W^T (bf16) with the substrate in either storage format (the dl
+// product kernel; d a multiple of 128; a base-3 buffer extends 8 bytes past
+// the stream).
+hipError_t launch_product(int M, int d, const uint16_t* z, const void* w, bmoe_wformat fmt,
+                          float alpha, uint16_t* h, hipStream_t s, const KernelTiming& t = {});
+
 // Whole forward for d in {2, 4, 8}: one thread per token, its k routed rows
 // in ascending j (rotations with the prep kernel's cos/sin tables, the
 // ternary product, the gate and the fp32 sum), written straight to y.

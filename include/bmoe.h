@@ -65,6 +65,10 @@ typedef enum {
   BMOE_E_ALIGN = 8       /* a pointer is not 16-byte aligned */
 } bmoe_status;
 
+/* Storage of the shared substrate: 2-bit words (bmoe_pack_ternary) or the
+ * base-3 stream (bmoe_pack_ternary_b3). */
+typedef enum { BMOE_W_2BIT = 0, BMOE_W_BASE3 = 1 } bmoe_wformat;
+
 typedef enum {
   BMOE_F32 = 0,   /* x and y fp32; all arithmetic fp32 (substrate product exact
                      to fp32 via a three-way bf16 split of the activations) */
@@ -188,6 +192,26 @@ bmoe_status bmoe_forward_timed(bmoe_dtype dt, int T, int d, int n_experts, int k
                                const float* phi, const uint32_t* w_packed, float alpha, void* y,
                                void* ws, size_t ws_bytes, int32_t* route_out, void* stream,
                                void* const* events);
+
+/*
+ * The shared-substrate product alone (§2.3, the middle step): for bf16 Z
+ * [M][d] (row-major; rows are routed rows after the input-side rotation),
+ * H [M][d] = alpha * Z * W_base^T in bf16, with fp32 accumulation over K in
+ * ascending 16-wide slices on bf16 MFMA (exact ternary products).
+ *   w       the substrate in format fmt: BMOE_W_2BIT, uint32 [d][d/16] from
+ *           bmoe_pack_ternary; BMOE_W_BASE3, the stream of
+ *           bmoe_pack_ternary_b3 (bmoe_packed3_bytes(d) bytes) in a buffer of
+ *           at least bmoe_packed3_bytes(d) + 8 bytes (the kernel reads whole
+ *           aligned dwords; the bytes past the stream are never decoded), whose
+ *           digits the kernel decodes as it stages each K-step of the
+ *           substrate (a 256-entry LDS table).
+ *   d       a multiple of 128 in [128, 8192]; M >= 0 (0: no-op).
+ * Both formats run the same kernel and give bit-identical H. z, w, h: device
+ * pointers, 16-byte aligned; h must not alias z. events (may be NULL):
+ * events[0] / events[1] become the kernel's start and stop events.
+ */
+bmoe_status bmoe_product(int M, int d, const void* z, const void* w, bmoe_wformat fmt,
+                         float alpha, void* h, void* stream, void* const* events);
 
 /*
  * bmoe_forward without a caller workspace, for callers that cannot allocate

@@ -96,6 +96,15 @@ def test_workspace_bytes_validates_shape():
         assert bmoe.bmoe_workspace_bytes(*args) == 0
 
 
+def test_product_validation_needs_no_gpu():
+    lib = bmoe.lib()
+    assert lib.bmoe_product(4, 512, None, None, 9, 1.0, None, None, None) == 3
+    assert lib.bmoe_product(4, 96, None, None, 0, 1.0, None, None, None) == 2
+    assert lib.bmoe_product(-1, 512, None, None, 0, 1.0, None, None, None) == 2
+    assert lib.bmoe_product(4, 512, None, None, 1, 1.0, None, None, None) == 1
+    assert lib.bmoe_product(0, 512, None, None, 1, 1.0, None, None, None) == 0
+
+
 def test_status_strings():
     for code in range(9):
         assert bmoe.bmoe_status_str(code)
