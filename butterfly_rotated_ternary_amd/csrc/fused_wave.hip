@@ -51,10 +51,13 @@ struct WCfg {
   static constexpr int P = D / 2;                              // pairs per stage
   static constexpr int TBL = L * P;                            // one expert's side table
   static constexpr int TAB_BYTES = TBL * 8;
-  // fp32 H row stride: rows r and r + 4 (written by the two halves of a wave
-  // in the MFMA output layout) land on opposite halves of the 64 banks.
-  static constexpr int HS = D + 8;
-  static constexpr int H_BYTES = kSlots * HS * 4;
+  // fp32 H rows: 16 of them in the substrate staging array, 16 in the A
+  // tile's (both dead once the product is done), D floats each. Rows r and
+  // r + 4 (written by the two halves of a wave in the MFMA output layout)
+  // land on opposite halves of the 64 banks: column c of row r is stored at
+  // c ^ hswz(r).
+  static constexpr int H_HALF_BYTES = (kSlots / 2) * D * 4;
+  static __device__ __forceinline__ int hswz(int r) { return 32 * ((r >> 2) & 1); }
   static constexpr int WN = D / kWavesW;                       // product columns per wave
   static constexpr int FN = WN / 32;
   static constexpr int KS = 32;
@@ -67,25 +70,23 @@ struct WCfg {
   static constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
   static constexpr int PW_WAVE = WN * ROWB;
   static constexpr int PW_LOADS = PW_WAVE / 1024;     // 1 KiB per wave-wide copy
-  // LDS regions (bytes):
+  // LDS, four arrays (distinct arrays let the compiler see that the global->
+  // LDS copies into P cannot alias the other regions, so it does not wait for
+  // them before unrelated LDS accesses):
   //   A: routing scratch and the input-side tables; once the A tile is
   //      complete, the output-side tables (written during the product);
   //   META: the tile's slot -> (expert, routed index);
-  //   P: the packed substrate, then (with Z, after the product) the H rows;
-  //   Z: the bf16 A tile.
+  //   P: the packed substrate, then H rows 0..15;
+  //   Z: the bf16 A tile, then H rows 16..31.
   static constexpr int OFF_ROUTE = 0;
   static constexpr int OFF_TIN = (ROUTE_BYTES + 255) / 256 * 256;
   static constexpr int OFF_TOUT = 0;
-  static constexpr int END_A = OFF_TIN + 2 * TAB_BYTES;
-  static constexpr int OFF_META = (END_A + 255) / 256 * 256;
-  static constexpr int OFF_P = (OFF_META + (3 * kSlots + 8) * 4 + 1023) / 1024 * 1024;
-  static constexpr int OFF_H = OFF_P;
-  static constexpr int OFF_Z = OFF_P + kWavesW * PW_WAVE;
-  static constexpr int END_Z = OFF_Z + kSlots * D * 2;
-  static constexpr int LDS_BYTES = END_Z > OFF_H + H_BYTES ? END_Z : OFF_H + H_BYTES;
-  static_assert(2 * TAB_BYTES <= END_A, "output-side tables must fit in region A");
-  static_assert(PW_WAVE % 1024 == 0, "whole 1 KiB copies per wave");
-  static_assert(FN >= 1 && VPL >= 2, "d too small for this tiling");
+  static constexpr int A_BYTES = OFF_TIN + 2 * TAB_BYTES;
+  static constexpr int META_BYTES = (3 * kSlots + 8) * 4;
+  static constexpr int P_BYTES = kWavesW * PW_WAVE;
+  static constexpr int Z_BYTES = kSlots * D * 2;
+  static constexpr int LDS_BYTES = A_BYTES + META_BYTES + P_BYTES + Z_BYTES;
+  static_assert(P_BYTES >= H_HALF_BYTES && Z_BYTES >= H_HALF_BYTES, "H rows reuse P and Z");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   // Row R's chunk g sits at chunk g ^ pw_swz(R): a column of lanes reading
   // one word of 32 consecutive rows hits at most two lanes per bank.
@@ -443,7 +444,10 @@ template <int D>
 __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
   using C = WCfg<D>;
   constexpr int VPL = C::VPL;
-  __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[C::A_BYTES];
+  __shared__ __attribute__((aligned(16))) int meta[C::META_BYTES / 4];
+  __shared__ __attribute__((aligned(1024))) char pst[C::P_BYTES];
+  __shared__ __attribute__((aligned(1024))) char zt[C::Z_BYTES];
   int* const wcnt = reinterpret_cast<int*>(lds + C::OFF_ROUTE);  // [waves][N]
   int* const cnt = wcnt + kWavesW * kMaxNW;                        // [N + 1]
   int* const misc = cnt + kMaxNW + 4;                              // bad id; first, last expert
@@ -453,13 +457,14 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
   const float4* const tin_last = reinterpret_cast<const float4*>(tin + C::TBL);
   const float4* const tout_first = reinterpret_cast<const float4*>(tout);
   const float4* const tout_last = reinterpret_cast<const float4*>(tout + C::TBL);
-  float* const hrows = reinterpret_cast<float*>(lds + C::OFF_H);
-  char* const zt = lds + C::OFF_Z;
-  int* const sh_e = reinterpret_cast<int*>(lds + C::OFF_META);
+  int* const sh_e = meta;
   int* const sh_r = sh_e + kSlots;
-
+  // fp32 H row r (after the product): rows 0..15 in P, 16..31 in Z
+  auto hrow = [&](int r) -> float* {
+    return reinterpret_cast<float*>(r < kSlots / 2 ? pst : zt) + (r % (kSlots / 2)) * D;
+  };
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  char* const pwl = lds + C::OFF_P + wave * C::PW_WAVE;  // this wave's substrate rows
+  char* const pwl = pst + wave * C::PW_WAVE;  // this wave's substrate rows
   const int tile = blockIdx.x;
   const int q0 = tile * kSlots;
   const int nr = min(kSlots, a.M - q0);
@@ -490,6 +495,21 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
     int ex, s, k;
     TableJob<D>::at(i, wv, lane, ex, s, k);
     tix[i] = tab_idx<D>()[s * C::P + k];
+  }
+  // This wave's packed substrate rows (o = wave * WN ..), copied to LDS by
+  // the global->LDS path in 1 KiB pieces: lane l of piece i fills LDS chunk
+  // c = 64 i + l, which holds row c / CPR's global chunk (c % CPR) ^ swz.
+  // Issued at the start: the compiler makes the first LDS access after a
+  // global->LDS copy wait for it, so they land during the routing.
+  {
+    const char* wrows = reinterpret_cast<const char*>(a.wp) + (size_t)wave * C::PW_WAVE;
+#pragma unroll
+    for (int i = 0; i < C::PW_LOADS; ++i) {
+      const int c = 64 * i + lane, R = c / C::CPR, g = (c % C::CPR) ^ C::pw_swz(R);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(wrows + R * C::ROWB + 16 * g),
+          (__attribute__((address_space(3))) void*)(pwl + 1024 * i), 16, 0, 0);
+    }
   }
   for (int e = tid; e < kWavesW * N; e += kThreadsW) wcnt[e] = 0;
   if (tid == 0) {
@@ -627,20 +647,6 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
     }
     gw[i] = a.gates[rw[i]];
   }
-  // This wave's packed substrate rows (o = wave * WN ..), copied to LDS by
-  // the global->LDS path in 1 KiB pieces: lane l of piece i fills LDS chunk
-  // c = 64 i + l, which holds row c / CPR's global chunk (c % CPR) ^ swz.
-  // They land while the butterfly runs.
-  {
-    const char* wrows = reinterpret_cast<const char*>(a.wp) + (size_t)wave * C::PW_WAVE;
-#pragma unroll
-    for (int i = 0; i < C::PW_LOADS; ++i) {
-      const int c = 64 * i + lane, R = c / C::CPR, g = (c % C::CPR) ^ C::pw_swz(R);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(wrows + R * C::ROWB + 16 * g),
-          (__attribute__((address_space(3))) void*)(pwl + 1024 * i), 16, 0, 0);
-    }
-  }
   // Input-side tables of the tile's first and last experts (the output
   // side's are computed during the product).
 #pragma unroll
@@ -725,7 +731,7 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      hrows[row * C::HS + col] = a.alpha * acc[j][r];
+      hrow(row)[col ^ C::hswz(row)] = a.alpha * acc[j][r];
     }
   }
   lds_barrier();  // the H rows are complete
@@ -734,7 +740,7 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
 #pragma unroll
   for (int i = 0; i < kRowsW; ++i) {
     const int q = wave * kRowsW + i;
-    const float* hr = hrows + q * C::HS + VPL * lane;
+    const float* hr = hrow(q) + ((VPL * lane) ^ C::hswz(q));
 #pragma unroll
     for (int r = 0; r < VPL; r += 4) {
       const float4 t = *reinterpret_cast<const float4*>(hr + r);
