@@ -460,6 +460,8 @@ BflyParams make_params(int M, int d, int k, const RouteTables& rt, const float2*
 hipError_t launch_bfly_in(bmoe_dtype dt, int M, int d, int k, const void* x,
                           const RouteTables& rt, const float2* cs_in, void* z, hipStream_t s,
                           const KernelTiming& t, bool routed_out) {
+  if (bfly_wave_supported(dt, d))
+    return launch_bfly_wave(true, M, d, k, rt, cs_in, x, z, nullptr, routed_out, s, t);
   BflyParams p = make_params(M, d, k, rt, cs_in, x, z, nullptr);
   p.routed_out = routed_out ? 1 : 0;
   if (dt == BMOE_BF16 && d >= 256 && d <= 4096) return launch_big_d<true>(p, s, t);
@@ -470,6 +472,8 @@ hipError_t launch_bfly_in(bmoe_dtype dt, int M, int d, int k, const void* x,
 hipError_t launch_bfly_out(bmoe_dtype dt, int M, int d, const void* h, const float* gates,
                            const RouteTables& rt, const float2* cs_out, void* u,
                            hipStream_t s, const KernelTiming& t) {
+  if (bfly_wave_supported(dt, d))
+    return launch_bfly_wave(false, M, d, 1, rt, cs_out, h, u, gates, false, s, t);
   const BflyParams p = make_params(M, d, 1, rt, cs_out, h, u, gates);
   if (dt == BMOE_BF16 && d >= 256 && d <= 4096) return launch_big_d<false>(p, s, t);
   if (dt == BMOE_BF16) return launch_rows(bfly_kernel<false, uint16_t, uint16_t>, p, s, t);

@@ -122,4 +122,52 @@ __device__ __forceinline__ bf16x8 unpack_frag(uint32_t w, int h) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// Wave-level exchanges of the register-resident butterflies.
+__device__ __forceinline__ float fneg_if(float v, int neg) {
+  return __int_as_float(__float_as_int(v) ^ (neg << 31));
+}
+
+// Register-resident rows are spread over the lanes in "row lane" order: the
+// row position c of physical lane l is row_lane(l) = l ^ 3 * bit2(l) (an
+// involution). Flipping bit 0, 1 or 3 of c flips the same lane bit, and
+// flipping bit 2 of c flips lane bits 0-2 together, i.e. lane ^ 7, which is
+// DPP row_half_mirror. So every partner within a row of 16 lanes is one
+// full-mask DPP move that folds into the multiply using it.
+__device__ __forceinline__ int row_lane(int l) { return l ^ (((l >> 2) & 1) * 3); }
+
+// Partner value across bit M (0..3) of the row position (lanes in row_lane
+// order).
+template <int M>
+__device__ __forceinline__ float lane_partner(float v) {
+  const int iv = __float_as_int(v);
+  int r;
+  if constexpr (M == 0) {
+    r = __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]: lane ^ 1
+  } else if constexpr (M == 1) {
+    r = __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]: lane ^ 2
+  } else if constexpr (M == 2) {
+    r = __builtin_amdgcn_mov_dpp(iv, 0x141, 0xF, 0xF, true); // row_half_mirror: lane ^ 7
+  } else {
+    r = __builtin_amdgcn_mov_dpp(iv, 0x128, 0xF, 0xF, true);  // row_ror:8: lane ^ 8
+  }
+  return __int_as_float(r);
+}
+
+// Swap half of register a with half of register b across lane bit M (4 or
+// 5, equal in row-lane order): afterwards lanes with that bit clear hold (a, partner of a), lanes with
+// it set hold (partner of b, b). Applying it twice restores both.
+template <int M>
+__device__ __forceinline__ void lane_swap(float& a, float& b) {
+  const unsigned ia = __float_as_uint(a), ib = __float_as_uint(b);
+  if constexpr (M == 4) {
+    const auto r = __builtin_amdgcn_permlane16_swap(ia, ib, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(ia, ib, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  }
+}
+
 }  // namespace bmoe

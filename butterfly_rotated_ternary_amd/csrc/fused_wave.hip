@@ -6,13 +6,14 @@
 //
 // One workgroup (8 waves) per 32 consecutive sorted slots. Each wave owns four
 // of those rows outright: a row of d values lives in one wave, d/64 values per
-// lane (lane l holds elements VPL*l .. VPL*l + VPL-1), so every butterfly
-// stage is a wave-local operation and no barrier separates stages:
+// lane (lane l holds elements VPL*c .. VPL*c + VPL-1 of row position
+// c = row_lane(l)), so every butterfly stage is a wave-local operation and no
+// barrier separates stages:
 //   * stages whose partner is in the same lane (the low log2(VPL) bits) run
 //     in registers;
-//   * partners 1, 2 and 8 lanes away come through DPP (quad_perm, row_ror)
-//     and 4 lanes away through two masked row shifts; each lane computes its
-//     own element of the pair, c * mine +- s * partner;
+//   * partners across row-position bits 0-3 come through one DPP move each
+//     (quad_perm, row_half_mirror, row_ror), folded into a multiply; each
+//     lane computes its own element of the pair, c * mine +- s * partner;
 //   * partners 16 and 32 lanes away: v_permlane16_swap / v_permlane32_swap
 //     exchange half of one register with half of another, so that each lane
 //     holds a whole pair, the pair is rotated in registers, and a second swap
@@ -228,47 +229,6 @@ struct AngSrc {
   }
 };
 
-__device__ __forceinline__ float fneg_if(float v, int neg) {
-  return __int_as_float(__float_as_int(v) ^ (neg << 31));
-}
-
-// Partner value m lanes' bit away (bit m of the lane index flipped), m = 0..3.
-template <int M>
-__device__ __forceinline__ float lane_partner(float v) {
-  const int iv = __float_as_int(v);
-  int r;
-  if constexpr (M == 0) {
-    r = __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
-  } else if constexpr (M == 1) {
-    r = __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
-  } else if constexpr (M == 2) {
-    // lanes 0-3 and 8-11 of each row read 4 lanes up (row_shl:4), lanes
-    // 4-7 and 12-15 read 4 lanes down (row_shr:4)
-    r = __builtin_amdgcn_update_dpp(0, iv, 0x104, 0xF, 0x5, false);
-    r = __builtin_amdgcn_update_dpp(r, iv, 0x114, 0xF, 0xA, false);
-  } else {
-    r = __builtin_amdgcn_mov_dpp(iv, 0x128, 0xF, 0xF, true);  // row_ror:8
-  }
-  return __int_as_float(r);
-}
-
-// Swap half of register a with half of register b across lane bit M (4 or
-// 5): afterwards lanes with that bit clear hold (a, partner of a), lanes with
-// it set hold (partner of b, b). Applying it twice restores both.
-template <int M>
-__device__ __forceinline__ void lane_swap(float& a, float& b) {
-  const unsigned ia = __float_as_uint(a), ib = __float_as_uint(b);
-  if constexpr (M == 4) {
-    const auto r = __builtin_amdgcn_permlane16_swap(ia, ib, false, false);
-    a = __uint_as_float(r[0]);
-    b = __uint_as_float(r[1]);
-  } else {
-    const auto r = __builtin_amdgcn_permlane32_swap(ia, ib, false, false);
-    a = __uint_as_float(r[0]);
-    b = __uint_as_float(r[1]);
-  }
-}
-
 // One butterfly stage s on NR rows held VPL values per lane (element
 // VPL*lane + r in v[.][r]). TR: the transposed side (angle negated).
 template <int D, bool TR, int NR, int S, class Src>
@@ -464,6 +424,7 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
     return reinterpret_cast<float*>(r < kSlots / 2 ? pst : zt) + (r % (kSlots / 2)) * D;
   };
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int rl = row_lane(lane);  // this lane's position in a butterfly row
   char* const pwl = pst + wave * C::PW_WAVE;  // this wave's substrate rows
   const int tile = blockIdx.x;
   const int q0 = tile * kSlots;
@@ -638,7 +599,7 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
     const int qq = q < nr ? q : nr - 1;  // rows past the end repeat the last one
     ew[i] = sh_e[qq];
     rw[i] = sh_r[qq];
-    const uint16_t* xr = a.x + (size_t)(rw[i] / a.k) * D + VPL * lane;
+    const uint16_t* xr = a.x + (size_t)(rw[i] / a.k) * D + VPL * rl;
     if constexpr (VPL == 8) {
       xraw[i] = *reinterpret_cast<const uint4*>(xr);
     } else {
@@ -664,12 +625,12 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
       v[i][r + 1] = bf16_hi(w4[r / 2]);
     }
   }
-  butterfly_rows<D, true>(v, ew, e_first, e_last, tin_first, tin_last, a.theta, lane);
+  butterfly_rows<D, true>(v, ew, e_first, e_last, tin_first, tin_last, a.theta, rl);
   // Row q's 16-byte chunk c sits at chunk c ^ (q & 15) (conflict-free A reads).
 #pragma unroll
   for (int i = 0; i < kRowsW; ++i) {
     const int q = wave * kRowsW + i;
-    const int e0 = VPL * lane;
+    const int e0 = VPL * rl;
     char* dst = zt + q * (2 * D) + 16 * ((e0 / 8) ^ (q & 15)) + 2 * (e0 % 8);
     if constexpr (VPL == 8) {
       *reinterpret_cast<uint4*>(dst) =
@@ -740,7 +701,7 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
 #pragma unroll
   for (int i = 0; i < kRowsW; ++i) {
     const int q = wave * kRowsW + i;
-    const float* hr = hrow(q) + ((VPL * lane) ^ C::hswz(q));
+    const float* hr = hrow(q) + ((VPL * rl) ^ C::hswz(q));
 #pragma unroll
     for (int r = 0; r < VPL; r += 4) {
       const float4 t = *reinterpret_cast<const float4*>(hr + r);
@@ -750,13 +711,13 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
       v[i][r + 3] = t.w;
     }
   }
-  butterfly_rows<D, false>(v, ew, e_first, e_last, tout_first, tout_last, a.phi, lane);
+  butterfly_rows<D, false>(v, ew, e_first, e_last, tout_first, tout_last, a.phi, rl);
 #pragma unroll
   for (int i = 0; i < kRowsW; ++i) {
     const int q = wave * kRowsW + i;
     if (q >= nr) continue;
     const float g = gw[i];
-    uint16_t* dst = a.u + (size_t)rw[i] * D + VPL * lane;
+    uint16_t* dst = a.u + (size_t)rw[i] * D + VPL * rl;
     if constexpr (VPL == 8) {
       *reinterpret_cast<uint4*>(dst) =
           make_uint4(pack_bf16x2(g * v[i][0], g * v[i][1]), pack_bf16x2(g * v[i][2], g * v[i][3]),

@@ -113,6 +113,16 @@ hipError_t launch_bfly_in(bmoe_dtype dt, int M, int d, int k, const void* x,
                           const RouteTables& rt, const float2* cs_in, void* z, hipStream_t s,
                           const KernelTiming& t = {}, bool routed_out = false);
 
+// Register-resident butterflies for bf16 at d = 1024, 2048, 4096 (what
+// launch_bfly_in / launch_bfly_out use there): in_side: dst = B(theta_e)^T of
+// src row perm[q] / k, into row q (or perm[q] with routed_out); otherwise
+// dst[perm[q]] = gates[perm[q]] * B(phi_e) src[q]. cs: that side's [N][L][d/2]
+// (cos, sin).
+bool bfly_wave_supported(bmoe_dtype dt, int d);
+hipError_t launch_bfly_wave(bool in_side, int M, int d, int k, const RouteTables& rt,
+                            const float2* cs, const void* src, void* dst, const float* gates,
+                            bool routed_out, hipStream_t s, const KernelTiming& t = {});
+
 // H = alpha * Z W_base^T over all M sorted rows (H bf16 on the bf16 path,
 // fp32 on the fp32 path; Z likewise).
 hipError_t launch_gemm(bmoe_dtype dt, int M, int d, const void* z, const uint32_t* w_packed,
