@@ -130,7 +130,7 @@ def backward_work(name, act_bytes, T, d, N, k):
         return kernel_work(name, act_bytes, T, d, N, k)
     if name == "gemm_t_kernel":
         return kernel_work("gemm_kernel", act_bytes, T, d, N, k)
-    if name == "substrate_grad_gemm":
+    if name == "dw_kernel":
         return {"bytes": 2 * M * d * act_bytes + d * d * 4, "mfma_flops": 2 * M * d * d,
                 "valu_flops": 0}
     if name in ("bfly_bwd_out_kernel", "bfly_bwd_in_kernel"):

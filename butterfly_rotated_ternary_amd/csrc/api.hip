@@ -4,7 +4,6 @@
 #include <climits>
 #include <mutex>
 
-#include <rocblas/rocblas.h>
 
 #include "common.h"
 #include "kernels.h"
@@ -110,27 +109,14 @@ struct BwdLayout {
   int max_tiles, wt_block;
 };
 
-// bf16 with 128 <= d <= 1024: the library's own MFMA kernel (launch_dw), whose
-// row splits need dw_kernel_splits() partial slices. Otherwise (fp32, small d) the
-// library GEMM, with the reduction over M routed rows split into dw_splits()
-// equal row ranges (plus one for the remainder) when d is small, so it has
-// enough output tiles to fill the chip. Either way the fp32 partial products
-// are summed in a fixed order.
-bool dw_own_kernel(bmoe_dtype dt, int d) { return dt == BMOE_BF16 && d >= 128 && d <= 1024; }
-int dw_splits(int M, int d) {
-  if (d >= 2048) return 1;
-  const int tiles = d >= 128 ? (d / 128) * (d / 128) : 1;
-  int S = (256 + tiles - 1) / tiles;
-  if (S > M / 256) S = M / 256;
-  return S < 1 ? 1 : S;
-}
+// The substrate gradient's kernel: bf16 with 128 <= d <= 4096 on bf16 MFMA
+// (launch_dw), otherwise (fp32, small d) on fp32 MFMA (launch_dw_f32). Both
+// may split the reduction over the M routed rows into row ranges whose fp32
+// partial products the backward's closing kernel sums in a fixed order.
+bool dw_own_kernel(bmoe_dtype dt, int d) { return dt == BMOE_BF16 && d >= 128 && d <= 4096; }
 int dw_slots(bmoe_dtype dt, int M, int d) {
-  if (dw_own_kernel(dt, d)) {
-    const int S = dw_kernel_splits(M, d);
-    return S > 1 ? S : 0;
-  }
-  const int S = dw_splits(M, d);
-  return S == 1 ? 0 : S + (M % S != 0 ? 1 : 0);
+  const int S = dw_own_kernel(dt, d) ? dw_kernel_splits(M, d) : dw_f32_splits(M, d);
+  return S > 1 ? S : 0;
 }
 
 BwdLayout bwd_layout(bmoe_dtype dt, int T, int d, int N, int k) {
@@ -174,61 +160,19 @@ bool bwd_shape_ok(bmoe_dtype dt, int T, int d, int N, int k) {
   return shape_ok(dt, T, d, N, k) && valid_d16(d) && d <= 4096;
 }
 
-// dW = alpha * dH^T Z (row-major [d][d], fp32). bf16 with d = 128 .. 1024:
-// the library's kernel. Otherwise the library GEMM: the column-major product
-// Z_cm * dH_cm^T of the row-major [M][d] matrices viewed column-major; with
-// S > 1 splits, batch b takes rows b*Kb .. (b+1)*Kb - 1 into part[b] and the
-// remainder rows go to part[S]; the backward's closing kernel sums the slices
-// in order.
+// dW = alpha * dH^T Z (row-major [d][d], fp32), see dw_own_kernel.
 // *slices: the number of fp32 partial products left in part for the
 // backward's closing kernel to sum (0: dw written directly).
 bmoe_status substrate_grad(bmoe_dtype dt, int M, int d, const void* dh, const void* z,
-                           float alpha, float* dw, float* part, int* slices, hipStream_t s) {
+                           float alpha, float* dw, float* part, int* slices, hipStream_t s,
+                           const KernelTiming& t) {
   *slices = dw_slots(dt, M, d);
-  if (dw_own_kernel(dt, d))
-    return launch_dw(M, d, static_cast<const uint16_t*>(dh), static_cast<const uint16_t*>(z),
-                     alpha, dw, part, s) == hipSuccess
-               ? BMOE_OK
-               : BMOE_E_HIP;
-  static std::once_flag once;
-  static rocblas_handle handle = nullptr;
-  static rocblas_status created = rocblas_status_internal_error;
-  // One handle for the process: the stream it is bound to and the GEMMs
-  // enqueued on it are set under one lock, so concurrent callers on other
-  // streams cannot interleave (only host-side enqueueing is serialised).
-  static std::mutex mu;
-  std::call_once(once, [] { created = rocblas_create_handle(&handle); });
-  if (created != rocblas_status_success) return BMOE_E_HIP;
-  std::lock_guard<std::mutex> lock(mu);
-  if (rocblas_set_stream(handle, s) != rocblas_status_success) return BMOE_E_HIP;
-  const float beta = 0.f;
-  const rocblas_datatype at = dt == BMOE_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
-  const rocblas_datatype f32 = rocblas_datatype_f32_r;
-  const size_t el = dt == BMOE_BF16 ? 2 : 4;
-  const int S = dw_splits(M, d);
-  if (S == 1) {
-    const rocblas_status st = rocblas_gemm_ex(
-        handle, rocblas_operation_none, rocblas_operation_transpose, d, d, M, &alpha, z, at, d,
-        dh, at, d, &beta, dw, f32, d, dw, f32, d, f32, rocblas_gemm_algo_standard, 0, 0);
-    return st == rocblas_status_success ? BMOE_OK : BMOE_E_HIP;
-  }
-  const int kb = M / S, rest = M - S * kb;
-  const rocblas_stride sab = (rocblas_stride)kb * d, sc = (rocblas_stride)d * d;
-  rocblas_status st = rocblas_gemm_strided_batched_ex(
-      handle, rocblas_operation_none, rocblas_operation_transpose, d, d, kb, &alpha, z, at, d, sab,
-      dh, at, d, sab, &beta, part, f32, d, sc, part, f32, d, sc, S, f32,
-      rocblas_gemm_algo_standard, 0, 0);
-  if (st != rocblas_status_success) return BMOE_E_HIP;
-  if (rest > 0) {
-    const char* z1 = static_cast<const char*>(z) + el * (size_t)S * kb * d;
-    const char* dh1 = static_cast<const char*>(dh) + el * (size_t)S * kb * d;
-    float* p1 = part + (size_t)S * d * d;
-    st = rocblas_gemm_ex(handle, rocblas_operation_none, rocblas_operation_transpose, d, d, rest,
-                         &alpha, z1, at, d, dh1, at, d, &beta, p1, f32, d, p1, f32, d, f32,
-                         rocblas_gemm_algo_standard, 0, 0);
-    if (st != rocblas_status_success) return BMOE_E_HIP;
-  }
-  return BMOE_OK;
+  const hipError_t e =
+      dw_own_kernel(dt, d)
+          ? launch_dw(M, d, static_cast<const uint16_t*>(dh), static_cast<const uint16_t*>(z),
+                      alpha, dw, part, s, t)
+          : launch_dw_f32(dt, M, d, dh, z, alpha, dw, part, s, t);
+  return e == hipSuccess ? BMOE_OK : BMOE_E_HIP;
 }
 
 }  // namespace
@@ -659,10 +603,13 @@ bmoe_status backward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, con
   int dw_slices = 0;
   {
     const KernelTiming t = timing();
-    if (t.start && hipEventRecord(t.start, s) != hipSuccess) return BMOE_E_HIP;
-    if (dw && substrate_grad(dt, M, d, dh, z, alpha, dw, dw_part, &dw_slices, s) != BMOE_OK)
-      return BMOE_E_HIP;
-    if (t.stop && hipEventRecord(t.stop, s) != hipSuccess) return BMOE_E_HIP;
+    if (dw) {
+      if (substrate_grad(dt, M, d, dh, z, alpha, dw, dw_part, &dw_slices, s, t) != BMOE_OK)
+        return BMOE_E_HIP;
+    } else if ((t.start && hipEventRecord(t.start, s) != hipSuccess) ||
+               (t.stop && hipEventRecord(t.stop, s) != hipSuccess)) {
+      return BMOE_E_HIP;  // no dw: the slot's events bracket nothing
+    }
   }
   // dZ = alpha dH W (the product with the transposed substrate).
   if (launch_gemm(dt, M, d, dh, wpt, wtt, alpha, dz, s, timing()) != hipSuccess) return BMOE_E_HIP;
@@ -724,7 +671,7 @@ bmoe_status bmoe_backward(bmoe_dtype dt, int T, int d, int n_experts, int k, con
 namespace {
 const char* const kBackwardNames[] = {
     "prep_kernel",         "bfly_in_kernel",      "gemm_kernel",        "bfly_bwd_out_kernel",
-    "substrate_grad_gemm", "gemm_t_kernel",       "bfly_bwd_in_kernel", "finish_kernel"};
+    "dw_kernel",           "gemm_t_kernel",       "bfly_bwd_in_kernel", "finish_kernel"};
 constexpr int kBackwardLaunches = sizeof(kBackwardNames) / sizeof(kBackwardNames[0]);
 }  // namespace
 

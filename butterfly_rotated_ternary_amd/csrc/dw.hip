@@ -12,8 +12,7 @@
 // one column in one instruction.
 //
 // Tiles of 128 x 128 outputs, 4 waves of 64 x 64, v_mfma_f32_32x32x16_bf16
-// fragments, for d = 128 .. 1024 (at d = 2048 and 4096 the library GEMM
-// measured as fast or faster). The rows are split into S equal ranges
+// fragments, for d = 128 .. 4096. The rows are split into S equal ranges
 // (multiples of 32) so the grid fills the CUs; split s writes its fp32
 // partial product to part[s], and the backward's closing kernel adds the S
 // slices in order, so the result does not depend on scheduling.
@@ -267,10 +266,121 @@ hipError_t launch_dw_cfg(int M, int d, const uint16_t* dh, const uint16_t* z, fl
                        alpha, out);
 }
 
+// ---------------------------------------------------------------------------
+// The same gradient for fp32 activations (any d) and for bf16 below d = 128,
+// on v_mfma_f32_32x32x2_f32. Its A operand (32 x 2) gives lane l element
+// (l % 32, l / 32) and its B operand (2 x 32) element (l / 32, l % 32): with
+// A[o][q] = dH[q][o] and B[q][c] = Z[q][c], lanes 0-31 read 32 consecutive
+// columns of row q and lanes 32-63 the same columns of row q + 1, straight
+// from memory (bf16 widened exactly to fp32). One wave per output tile of
+// WT x WT (WT = 64, or 32 when d < 64; outputs past d are masked) and row
+// range; accumulation in fp32 like the bf16 kernel.
+constexpr int kF32Unroll = 8;  // K-steps (two rows each) loaded ahead
+
+template <typename T>
+__device__ __forceinline__ float ld_f32(const T* p) {
+  if constexpr (sizeof(T) == 2) return bf16_lo(*reinterpret_cast<const uint16_t*>(p));
+  else return *p;
+}
+
+template <typename T, int WT>
+__global__ __launch_bounds__(kWave) void dw_f32_kernel(const T* dH, const T* Z, int M, int d,
+                                                       int rows_per_split, float alpha,
+                                                       float* out) {
+  constexpr int F = WT / 32;  // 32 x 32 blocks per side
+  const int tn = (d + WT - 1) / WT, tiles = tn * tn;
+  const int split = blockIdx.x / tiles, t = blockIdx.x % tiles;
+  const int o0 = (t / tn) * WT, c0 = (t % tn) * WT;
+  const int q_begin = split * rows_per_split;
+  const int q_end = min(M, q_begin + rows_per_split);
+  float* dst = out + (size_t)split * d * d;
+  const int lane = threadIdx.x, col = lane & 31, kq = lane >> 5;
+  bool okA[F], okB[F];
+#pragma unroll
+  for (int i = 0; i < F; ++i) {
+    okA[i] = o0 + 32 * i + col < d;
+    okB[i] = c0 + 32 * i + col < d;
+  }
+  f32x16 acc[F][F];
+#pragma unroll
+  for (int i = 0; i < F; ++i)
+#pragma unroll
+    for (int j = 0; j < F; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  for (int q0 = q_begin; q0 < q_end; q0 += 2 * kF32Unroll) {
+    float a[kF32Unroll][F], b[kF32Unroll][F];
+#pragma unroll
+    for (int u = 0; u < kF32Unroll; ++u) {
+      const int q = q0 + 2 * u + kq;
+      const bool row_ok = q < q_end;
+#pragma unroll
+      for (int i = 0; i < F; ++i) {
+        a[u][i] = row_ok && okA[i] ? ld_f32(dH + (size_t)q * d + o0 + 32 * i + col) : 0.f;
+        b[u][i] = row_ok && okB[i] ? ld_f32(Z + (size_t)q * d + c0 + 32 * i + col) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kF32Unroll; ++u)
+#pragma unroll
+      for (int i = 0; i < F; ++i)
+#pragma unroll
+        for (int j = 0; j < F; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u][i], b[u][j], acc[i][j], 0, 0, 0);
+  }
+  // 32x32 block layout: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4,
+  // column l%32.
+#pragma unroll
+  for (int i = 0; i < F; ++i)
+#pragma unroll
+    for (int j = 0; j < F; ++j) {
+      const int c = c0 + 32 * j + col;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int o = o0 + 32 * i + 8 * (r >> 2) + 4 * kq + (r & 3);
+        if (o < d && c < d) dst[(size_t)o * d + c] = alpha * acc[i][j][r];
+      }
+    }
+}
+
+int f32_tile(int d) { return d >= 64 ? 64 : 32; }
+
 }  // namespace
 
+int dw_f32_splits(int M, int d) {
+  const int wt = f32_tile(d), tn = (d + wt - 1) / wt, tiles = tn * tn;
+  int S = (2048 + tiles - 1) / tiles;
+  const int max_s = M / 256;  // at least 256 rows per split
+  if (S > max_s) S = max_s;
+  return S < 1 ? 1 : S;
+}
+
+hipError_t launch_dw_f32(bmoe_dtype dt, int M, int d, const void* dh, const void* z,
+                         float alpha, float* dw, float* part, hipStream_t s,
+                         const KernelTiming& t) {
+  const int S = dw_f32_splits(M, d);
+  const int wt = f32_tile(d), tn = (d + wt - 1) / wt;
+  const int rows = ((M + S - 1) / S + 2 * kF32Unroll - 1) / (2 * kF32Unroll) * (2 * kF32Unroll);
+  float* out = S == 1 ? dw : part;
+  const dim3 grid(tn * tn * S), block(kWave);
+  if (dt == BMOE_BF16) {
+    const uint16_t* a = static_cast<const uint16_t*>(dh);
+    const uint16_t* b = static_cast<const uint16_t*>(z);
+    return wt == 64 ? launch_kernel(dw_f32_kernel<uint16_t, 64>, grid, block, 0, s, t, a, b, M, d,
+                                    rows, alpha, out)
+                    : launch_kernel(dw_f32_kernel<uint16_t, 32>, grid, block, 0, s, t, a, b, M, d,
+                                    rows, alpha, out);
+  }
+  const float* a = static_cast<const float*>(dh);
+  const float* b = static_cast<const float*>(z);
+  return wt == 64 ? launch_kernel(dw_f32_kernel<float, 64>, grid, block, 0, s, t, a, b, M, d, rows,
+                                  alpha, out)
+                  : launch_kernel(dw_f32_kernel<float, 32>, grid, block, 0, s, t, a, b, M, d, rows,
+                                  alpha, out);
+}
+
 int dw_kernel_splits(int M, int d) {
-  if (d < 128 || d > 1024) return 0;
+  if (d < 128 || d > 4096) return 0;
   const int tiles = (d / 128) * (d / 128);
   int S = (256 + tiles - 1) / tiles;
   const int max_s = M / (16 * kDwRows);  // at least 16 K-steps per split

@@ -162,13 +162,19 @@ hipError_t launch_bfly_bwd(bool in_side, bmoe_dtype dt, int M, int d, int k, con
                            int max_tiles, const int32_t* perm, const float2* cs,
                            const float* gates, const void* src, const void* grad, void* dst,
                            float* dgates, float* partial, hipStream_t s, const KernelTiming& t = {});
-// dW [d][d] fp32 = alpha * dH^T Z for bf16 dH, Z [M][d] (128 <= d <= 1024):
-// MFMA tiles over row ranges. With dw_kernel_splits(M, d) = S > 1 the ranges'
-// partial products go to part [S][d][d] (launch_bwd_finish sums them), else
-// straight to dw. 0 splits: d outside that range.
+// dW [d][d] fp32 = alpha * dH^T Z for bf16 dH, Z [M][d] (128 <= d <= 4096):
+// bf16 MFMA tiles over row ranges. With dw_kernel_splits(M, d) = S > 1 the
+// ranges' partial products go to part [S][d][d] (launch_bwd_finish sums
+// them), else straight to dw. 0 splits: d outside that range.
 int dw_kernel_splits(int M, int d);
 hipError_t launch_dw(int M, int d, const uint16_t* dh, const uint16_t* z, float alpha, float* dw,
                      float* part, hipStream_t s, const KernelTiming& t = {});
+// The same for fp32 dH, Z (any d) or bf16 below d = 128, on fp32 MFMA; its
+// row ranges: dw_f32_splits(M, d) (always >= 1), same slice convention.
+int dw_f32_splits(int M, int d);
+hipError_t launch_dw_f32(bmoe_dtype dt, int M, int d, const void* dh, const void* z,
+                         float alpha, float* dw, float* part, hipStream_t s,
+                         const KernelTiming& t = {});
 // The backward's closing sums in one launch: dx[t] = sum_j dxr[t k + j]
 // (ascending j, fp32; dtype dt); dphi / dtheta [N][L][d/2] = sums over each
 // expert's tiles of the output / input side partials [tiles][L][d/2], in tile

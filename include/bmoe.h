@@ -25,11 +25,7 @@
  * Conventions for every entry point:
  *   - All array pointers are DEVICE pointers owned by the caller, 16-byte
  *     aligned. The library allocates nothing on the call path and keeps no
- *     state between calls besides the loaded code object, with one
- *     exception: bmoe_backward with dw != NULL, when rocBLAS computes dw
- *     (fp32, or d outside 128..1024), creates on its first such call a
- *     rocBLAS handle (which holds device memory of its own) that lives until
- *     the process ends.
+ *     state between calls besides the loaded code object.
  *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *     asynchronously; a call returns before the GPU finishes.
  *   - A non-BMOE_OK return comes from host-side validation, before anything
@@ -267,11 +263,10 @@ size_t bmoe_backward_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts,
  * The other arguments are bmoe_forward's (same routing and rounding points;
  * the forward is recomputed inside). All outputs are overwritten; dtheta and
  * dphi are summed per expert in a fixed order (run-to-run bit-identical). The
- * dw product is a plain GEMM over the routed rows: the library's own MFMA
- * kernel for bf16 with 128 <= d <= 1024, else rocBLAS; for d < 2048 it is
- * split into row ranges whose fp32 products are summed in a fixed order. The
- * first call that runs it on rocBLAS creates a rocBLAS handle kept for the
- * life of the process.
+ * dw product is a plain GEMM over the routed rows, one launch of the
+ * library's own kernel (bf16 MFMA for bf16 with 128 <= d <= 4096, fp32 MFMA
+ * otherwise); when d is small it is split into row ranges whose fp32
+ * products are summed in a fixed order.
  * ws: at least bmoe_backward_workspace_bytes(), 16-byte aligned. Errors as
  * bmoe_forward.
  */
@@ -283,16 +278,15 @@ bmoe_status bmoe_backward(bmoe_dtype dt, int T, int d, int n_experts, int k, con
 
 /* Number and names of the launches of one bmoe_backward (0 / "" when the
  * shape is unsupported or T == 0, or i is out of range). The substrate
- * gradient is a library GEMM that may run as several kernels; its slot
- * covers all of them (and is empty when dw is NULL). */
+ * gradient's slot ("dw_kernel") launches nothing when dw is NULL. */
 int bmoe_backward_kernel_count(bmoe_dtype dt, int T, int d, int n_experts, int k);
 const char* bmoe_backward_kernel_name(bmoe_dtype dt, int T, int d, int n_experts, int k, int i);
 
 /*
  * bmoe_backward, additionally timing each launch: launch i records
  * events[2i] and events[2i+1] around its own execution, as in
- * bmoe_forward_timed (the library-GEMM slot with hipEventRecord on `stream`
- * before and after it). `events` holds 2 * bmoe_backward_kernel_count(...)
+ * bmoe_forward_timed (with dw NULL, the dw_kernel slot's two events are
+ * recorded back to back on `stream`). `events` holds 2 * bmoe_backward_kernel_count(...)
  * hipEvent_t created by the caller on the current device; NULL behaves as
  * bmoe_backward. Results are identical to bmoe_backward.
  */
