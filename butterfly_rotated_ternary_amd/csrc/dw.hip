@@ -11,7 +11,8 @@
 // transposing LDS read (ds_read_b64_tr_b16) gathers a lane's 4 q values of
 // one column in one instruction.
 //
-// Tiles of 128 x 128 outputs, 4 waves of 64 x 64, v_mfma_f32_32x32x16_bf16
+// Tiles of 128 x 128 outputs (4 waves of 64 x 64) up to d = 1024 and of
+// 256 x 256 (8 waves of 128 x 64) above, v_mfma_f32_32x32x16_bf16
 // fragments, for d = 128 .. 4096. The rows are split into S equal ranges
 // (multiples of 32) so the grid fills the CUs; split s writes its fp32
 // partial product to part[s], and the backward's closing kernel adds the S
@@ -24,13 +25,15 @@ namespace {
 
 constexpr int kDwRows = 32;  // rows of dH and Z per K-step
 
-template <int BM_, int BN_>
+// BM x BN outputs per workgroup, WM x WN waves of TM x TN each.
+template <int BM_, int BN_, int WM_, int WN_>
 struct DwCfg {
-  static constexpr int BM = BM_, BN = BN_, THREADS = 256;
-  static constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int WAVES = WM * WN, THREADS = 64 * WAVES;
+  static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   static constexpr int A_BYTES = kDwRows * BM * 2, B_BYTES = kDwRows * BN * 2;
   static constexpr int STAGE = A_BYTES + B_BYTES, NSTAGE = 4;
-  static constexpr int A_LOADS = A_BYTES / 1024 / 4, B_LOADS = B_BYTES / 1024 / 4;
+  static constexpr int A_LOADS = A_BYTES / 1024 / WAVES, B_LOADS = B_BYTES / 1024 / WAVES;
   static constexpr int V = A_LOADS + B_LOADS;  // DMA instructions per wave and K-step
   static_assert(A_LOADS >= 1 && B_LOADS >= 1 && 2 * V <= 63, "DMA counts");
   static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS budget");
@@ -101,8 +104,28 @@ __device__ __forceinline__ void dw_read(bf16x8 (&fa)[C::FM], bf16x8 (&fb)[C::FN]
                                         const uint32_t (&aB)[C::FN]) {
   constexpr int LO_A = KK * 16 * C::BM * 2, HI_A = LO_A + 4 * C::BM * 2;
   constexpr int LO_B = KK * 16 * C::BN * 2, HI_B = LO_B + 4 * C::BN * 2;
-  static_assert(C::FM == 2 && C::FN == 2, "operand counts");
+  static_assert((C::FM == 2 || C::FM == 4) && C::FN == 2, "operand counts");
   uint64_t v[2 * (C::FM + C::FN)];
+  if constexpr (C::FM == 4) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %12 offset:%18\n\t"
+        "ds_read_b64_tr_b16 %1, %12 offset:%19\n\t"
+        "ds_read_b64_tr_b16 %2, %13 offset:%18\n\t"
+        "ds_read_b64_tr_b16 %3, %13 offset:%19\n\t"
+        "ds_read_b64_tr_b16 %4, %14 offset:%18\n\t"
+        "ds_read_b64_tr_b16 %5, %14 offset:%19\n\t"
+        "ds_read_b64_tr_b16 %6, %15 offset:%18\n\t"
+        "ds_read_b64_tr_b16 %7, %15 offset:%19\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %9, %16 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %10, %17 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %11, %17 offset:%21\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+          "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11])
+        : "v"(aA[0]), "v"(aA[1]), "v"(aA[2]), "v"(aA[3]), "v"(aB[0]), "v"(aB[1]), "n"(LO_A),
+          "n"(HI_A), "n"(LO_B), "n"(HI_B));
+  } else {
   asm volatile(
       "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
       "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
@@ -117,6 +140,7 @@ __device__ __forceinline__ void dw_read(bf16x8 (&fa)[C::FM], bf16x8 (&fb)[C::FN]
         "=&v"(v[6]), "=&v"(v[7])
       : "v"(aA[0]), "v"(aA[1]), "v"(aB[0]), "v"(aB[1]), "n"(LO_A), "n"(HI_A), "n"(LO_B),
         "n"(HI_B));
+  }
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
     const u64x2 x = {v[2 * i], v[2 * i + 1]};
@@ -207,7 +231,7 @@ __global__ __launch_bounds__(C::THREADS) void dw_kernel(const uint16_t* dH, cons
   float* dst = out + (size_t)split * d * d;
 
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WN, wn = wave % C::WN;
   uint32_t offA[C::FM], offB[C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) offA[i] = dw_frag_offset<C::BM>(wm * C::TM + 32 * i, lane);
@@ -379,9 +403,17 @@ hipError_t launch_dw_f32(bmoe_dtype dt, int M, int d, const void* dh, const void
                                   alpha, out);
 }
 
+// 128 x 128 tiles of four waves up to d = 1024; from d = 2048, 256 x 256 tiles
+// of eight waves (128 x 64 each), which read half as many operand bytes per
+// MFMA: the smaller tile needs L2 bandwidth at the per-CU limit to keep its
+// MFMAs busy.
+using DwSmall = DwCfg<128, 128, 2, 2>;
+using DwLarge = DwCfg<256, 256, 2, 4>;
+
 int dw_kernel_splits(int M, int d) {
   if (d < 128 || d > 4096) return 0;
-  const int tiles = (d / 128) * (d / 128);
+  const int bm = d >= 2048 ? DwLarge::BM : DwSmall::BM;
+  const int tiles = (d / bm) * (d / bm);
   int S = (256 + tiles - 1) / tiles;
   const int max_s = M / (16 * kDwRows);  // at least 16 K-steps per split
   if (S > max_s) S = max_s;
@@ -392,7 +424,8 @@ hipError_t launch_dw(int M, int d, const uint16_t* dh, const uint16_t* z, float 
                      float* part, hipStream_t s, const KernelTiming& t) {
   const int S = dw_kernel_splits(M, d);
   if (S == 0) return hipErrorInvalidValue;
-  return launch_dw_cfg<DwCfg<128, 128>>(M, d, dh, z, alpha, dw, part, S, s, t);
+  if (d >= 2048) return launch_dw_cfg<DwLarge>(M, d, dh, z, alpha, dw, part, S, s, t);
+  return launch_dw_cfg<DwSmall>(M, d, dh, z, alpha, dw, part, S, s, t);
 }
 
 }  // namespace bmoe

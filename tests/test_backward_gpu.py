@@ -129,6 +129,12 @@ def test_backward_edge_shapes(d, N, k, T, dtype):
     _run("tiny_d64_e8_top2_f32", T, d=d, N=N, k=k, dtype=dtype, seed=900 + d)
 
 
+def test_backward_dw_row_ranges_at_d2048():
+    # 2200 routed rows: the d >= 2048 substrate-gradient kernel splits its
+    # reduction over rows into 4 ranges, which the closing kernel sums
+    _run("d2048_e64_top2_outliers_bf16", 1100, seed=17)
+
+
 def test_backward_is_deterministic():
     inp = W.make_inputs(W.HEADLINE, T=200)
     dev = to_device(inp)
