@@ -93,62 +93,35 @@ __device__ __forceinline__ uint32_t dw_frag_offset(int col, int lane) {
 }
 
 typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+typedef short dw_v4s __attribute__((ext_vector_type(4)));
 
-// The FM + FN MFMA operands of K-slice KK from LDS addresses aA[i] / aB[j]
-// (first reads): lane l gets column l % 32 of each, rows 16 KK + 8 (l / 32)
-// + 0..7. Inline asm, waiting for its own reads, so the compiler does not add
-// a wait for the DMA filling other stages (it cannot tell them apart).
+// The FM + FN MFMA operands of K-slice KK of stage `stg`: lane l gets column
+// l % 32 of each, rows 16 KK + 8 (l / 32) + 0..7, two transposing reads per
+// operand. The stages are separate arrays, so the compiler can tell the stage
+// read here from the stages the DMA still fills, and waits only for these
+// reads, where their results are used (one slice's reads overlap the other
+// slice's MFMAs).
 template <class C, int KK>
 __device__ __forceinline__ void dw_read(bf16x8 (&fa)[C::FM], bf16x8 (&fb)[C::FN],
-                                        const uint32_t (&aA)[C::FM],
-                                        const uint32_t (&aB)[C::FN]) {
+                                        const char* stg, const uint32_t (&offA)[C::FM],
+                                        const uint32_t (&offB)[C::FN]) {
   constexpr int LO_A = KK * 16 * C::BM * 2, HI_A = LO_A + 4 * C::BM * 2;
   constexpr int LO_B = KK * 16 * C::BN * 2, HI_B = LO_B + 4 * C::BN * 2;
-  static_assert((C::FM == 2 || C::FM == 4) && C::FN == 2, "operand counts");
-  uint64_t v[2 * (C::FM + C::FN)];
-  if constexpr (C::FM == 4) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %12 offset:%18\n\t"
-        "ds_read_b64_tr_b16 %1, %12 offset:%19\n\t"
-        "ds_read_b64_tr_b16 %2, %13 offset:%18\n\t"
-        "ds_read_b64_tr_b16 %3, %13 offset:%19\n\t"
-        "ds_read_b64_tr_b16 %4, %14 offset:%18\n\t"
-        "ds_read_b64_tr_b16 %5, %14 offset:%19\n\t"
-        "ds_read_b64_tr_b16 %6, %15 offset:%18\n\t"
-        "ds_read_b64_tr_b16 %7, %15 offset:%19\n\t"
-        "ds_read_b64_tr_b16 %8, %16 offset:%20\n\t"
-        "ds_read_b64_tr_b16 %9, %16 offset:%21\n\t"
-        "ds_read_b64_tr_b16 %10, %17 offset:%20\n\t"
-        "ds_read_b64_tr_b16 %11, %17 offset:%21\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
-          "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11])
-        : "v"(aA[0]), "v"(aA[1]), "v"(aA[2]), "v"(aA[3]), "v"(aB[0]), "v"(aB[1]), "n"(LO_A),
-          "n"(HI_A), "n"(LO_B), "n"(HI_B));
-  } else {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
-      "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
-      "ds_read_b64_tr_b16 %4, %10 offset:%14\n\t"
-      "ds_read_b64_tr_b16 %5, %10 offset:%15\n\t"
-      "ds_read_b64_tr_b16 %6, %11 offset:%14\n\t"
-      "ds_read_b64_tr_b16 %7, %11 offset:%15\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
-        "=&v"(v[6]), "=&v"(v[7])
-      : "v"(aA[0]), "v"(aA[1]), "v"(aB[0]), "v"(aB[1]), "n"(LO_A), "n"(HI_A), "n"(LO_B),
-        "n"(HI_B));
-  }
+  typedef __attribute__((address_space(3))) dw_v4s lds_v4s;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
-    const u64x2 x = {v[2 * i], v[2 * i + 1]};
+    const char* p = stg + offA[i];
+    const dw_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + LO_A));
+    const dw_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + HI_A));
+    const u64x2 x = {__builtin_bit_cast(uint64_t, lo), __builtin_bit_cast(uint64_t, hi)};
     fa[i] = __builtin_bit_cast(bf16x8, x);
   }
 #pragma unroll
   for (int j = 0; j < C::FN; ++j) {
-    const u64x2 x = {v[2 * C::FM + 2 * j], v[2 * C::FM + 2 * j + 1]};
+    const char* p = stg + C::A_BYTES + offB[j];
+    const dw_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + LO_B));
+    const dw_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + HI_B));
+    const u64x2 x = {__builtin_bit_cast(uint64_t, lo), __builtin_bit_cast(uint64_t, hi)};
     fb[j] = __builtin_bit_cast(bf16x8, x);
   }
 }
@@ -164,7 +137,7 @@ __device__ __forceinline__ void dw_wait() {
 // below are exact.
 template <class C, int S>
 __device__ __forceinline__ void dw_step(f32x16 (&acc)[C::FM][C::FN], char* const (&ring)[4],
-                                        const uint32_t (&lds)[4], const uint32_t (&offA)[C::FM],
+                                        const uint32_t (&offA)[C::FM],
                                         const uint32_t (&offB)[C::FN], const uint16_t* dH,
                                         const uint16_t* Z, int d, int kt, int q_begin,
                                         int q_end, int o0, int c0, int lane, int wave) {
@@ -177,19 +150,18 @@ __device__ __forceinline__ void dw_step(f32x16 (&acc)[C::FM][C::FN], char* const
   lds_barrier();
   dw_load<C>(ring[(S + 3) & 3], dH, Z, d, q_begin + (kt + 3) * kDwRows, q_end, o0, c0, lane, wave);
   __asm__ volatile("" ::: "memory");
-  uint32_t aA[C::FM], aB[C::FN];
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i) aA[i] = lds[S] + offA[i];
-#pragma unroll
-  for (int j = 0; j < C::FN; ++j) aB[j] = lds[S] + C::A_BYTES + offB[j];
-  bf16x8 fa[C::FM], fb[C::FN];
-  dw_read<C, 0>(fa, fb, aA, aB);
+  bf16x8 fa[C::FM], fb[C::FN], ga[C::FM], gb[C::FN];
+  dw_read<C, 0>(fa, fb, ring[S], offA, offB);
+  dw_read<C, 1>(ga, gb, ring[S], offA, offB);
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-  dw_read<C, 1>(fa, fb, aA, aB);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) fa[i] = ga[i];
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) fb[j] = gb[j];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -211,11 +183,6 @@ __global__ __launch_bounds__(C::THREADS) void dw_kernel(const uint16_t* dH, cons
   __shared__ __attribute__((aligned(1024))) char st2[C::STAGE];
   __shared__ __attribute__((aligned(1024))) char st3[C::STAGE];
   char* const ring[4] = {st0, st1, st2, st3};
-  // LDS byte addresses of the stages, for the reads written in asm.
-  const uint32_t lds[4] = {(uint32_t)(size_t)(__attribute__((address_space(3))) char*)st0,
-                           (uint32_t)(size_t)(__attribute__((address_space(3))) char*)st1,
-                           (uint32_t)(size_t)(__attribute__((address_space(3))) char*)st2,
-                           (uint32_t)(size_t)(__attribute__((address_space(3))) char*)st3};
 
   const int tn = d / C::BN, tm = d / C::BM, tiles = tm * tn;
   const int n = gridDim.x;
@@ -254,13 +221,13 @@ __global__ __launch_bounds__(C::THREADS) void dw_kernel(const uint16_t* dH, cons
   dw_load<C>(st2, dH, Z, d, q_begin + 2 * kDwRows, q_end, o0, c0, lane, wave);
   __asm__ volatile("" ::: "memory");
   for (int kt = 0; kt < nsteps; kt += 4) {
-    dw_step<C, 0>(acc, ring, lds, offA, offB, dH, Z, d, kt, q_begin, q_end, o0, c0,
+    dw_step<C, 0>(acc, ring, offA, offB, dH, Z, d, kt, q_begin, q_end, o0, c0,
                   lane, wave);
-    dw_step<C, 1>(acc, ring, lds, offA, offB, dH, Z, d, kt + 1, q_begin, q_end, o0, c0,
+    dw_step<C, 1>(acc, ring, offA, offB, dH, Z, d, kt + 1, q_begin, q_end, o0, c0,
                   lane, wave);
-    dw_step<C, 2>(acc, ring, lds, offA, offB, dH, Z, d, kt + 2, q_begin, q_end, o0, c0,
+    dw_step<C, 2>(acc, ring, offA, offB, dH, Z, d, kt + 2, q_begin, q_end, o0, c0,
                   lane, wave);
-    dw_step<C, 3>(acc, ring, lds, offA, offB, dH, Z, d, kt + 3, q_begin, q_end, o0, c0,
+    dw_step<C, 3>(acc, ring, offA, offB, dH, Z, d, kt + 3, q_begin, q_end, o0, c0,
                   lane, wave);
   }
   dw_wait<0>();  // no DMA may land in LDS after the workgroup ends
