@@ -285,8 +285,10 @@ __device__ __forceinline__ void d_load_a(char* abuf, const uint16_t* Z, int M, i
 // (one register per word), or the base-3 stream (five ternary digits per
 // byte, row-major entries), decoded into the same words as they are written
 // to LDS. Both give exactly the same bf16 B tiles.
+// REGS: registers per word in flight; VMEM: vector-memory instructions per
+// word, which the step-end wait counts.
 struct Packed2Src {
-  static constexpr int REGS = 1;  // registers per word in flight
+  static constexpr int REGS = 1, VMEM = 1;
   const uint32_t* wp;
   __device__ __forceinline__ void load(uint32_t* r, int o, int d, int k0, int g) const {
     r[0] = wp[(size_t)o * (d / 16) + k0 / 16 + g];
@@ -297,18 +299,21 @@ struct Packed2Src {
   }
 };
 
+typedef uint64_t u64_dw_aligned __attribute__((aligned(4)));
+
 struct Base3Src {
-  static constexpr int REGS = 2;
+  static constexpr int REGS = 2, VMEM = 1;
   const uint8_t* w3;
   // The word's 16 entries e0 .. e0+15 (e0 = o d + k0 + 16 g) lie in bytes
-  // e0/5 .. e0/5 + 3: the two aligned dwords from (e0/5) & ~3 hold them. For
-  // the stream's last words the second dword reaches up to 7 bytes past its
-  // end (the caller's buffer extends 8 bytes beyond it; those bytes are never
-  // decoded), so every lane issues the same two loads.
+  // e0/5 .. e0/5 + 3: the 8 bytes from the dword boundary (e0/5) & ~3 hold
+  // them, read as one 8-byte load. For the stream's last words it reaches up
+  // to 7 bytes past its end (the caller's buffer extends 8 bytes beyond it;
+  // those bytes are never decoded), so every lane issues the same load.
   __device__ __forceinline__ void load(uint32_t* r, int o, int d, int k0, int g) const {
     const size_t e0 = (size_t)o * d + k0 + 16 * g, a = (e0 / 5) & ~(size_t)3;
-    r[0] = *reinterpret_cast<const uint32_t*>(w3 + a);
-    r[1] = *reinterpret_cast<const uint32_t*>(w3 + a + 4);
+    const uint64_t v = *reinterpret_cast<const u64_dw_aligned*>(w3 + a);
+    r[0] = (uint32_t)v;
+    r[1] = (uint32_t)(v >> 32);
   }
   // lut[b]: the five digits of byte b as 2-bit codes in entry order (digit 0,
   // 1, 2 -> code 3, 0, 1, i.e. -1, 0, +1).
@@ -420,7 +425,7 @@ __device__ __forceinline__ void d_step(f32x16 (&acc)[C::FM][C::FN], const char* 
   if constexpr (WRITE) d_write_b<C>(rn, src, lut, bnxt, d, n0, kw, 2);
   d_mfma<C>(acc, f1);
   if constexpr (WRITE) d_write_b<C>(rn, src, lut, bnxt, d, n0, kw, 3);
-  if constexpr (LOAD) wait_vmcnt<C::B_PER * Src::REGS>();  // Z tile of kt+1 has landed
+  if constexpr (LOAD) wait_vmcnt<C::B_PER * Src::VMEM>();  // Z tile of kt+1 has landed
   else wait_vmcnt<0>();
   lds_barrier();
 }
@@ -574,27 +579,33 @@ struct RbFrag {
 // Issue step kt's DMA into `stg`: first this wave's blocks of packed words
 // (each one contiguous KiB of the tile-major copy wt: 64 columns x 16 B),
 // then its share of the Z tile.
+// Addresses: a wave-uniform base (scalar registers) plus a 32-bit offset
+// per lane, so the DMA uses the scalar-base form and a lane keeps one
+// 32-bit register per load rather than a 64-bit address.
 template <class C>
 __device__ __forceinline__ void rb_load(char* stg, const uint16_t* Z, const uint32_t* wt, int M,
                                         int d, int m0, int n0, int kt, int lane, int wave) {
+  const char* wbase = reinterpret_cast<const char*>(wt) +
+                      ((size_t)(n0 / C::BN) * (d / BK) + kt) * C::BN * 16;
 #pragma unroll
   for (int b = 0; b < C::B_LOADS; ++b) {
     const int blk = wave * C::B_LOADS + b;  // 64 columns
-    const uint32_t* g =
-        wt + (((size_t)(n0 / C::BN) * (d / BK) + kt) * C::BN + blk * 64 + lane) * 4;
+    const char* g = wbase + blk * 1024 + (uint32_t)(lane * 16);
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
                                      (__attribute__((address_space(3))) void*)(stg + C::A_BYTES +
                                                                               blk * 1024),
                                      16, 0, 0);
   }
   __asm__ volatile("" ::: "memory");
+  const char* zbase = reinterpret_cast<const char*>(Z) + ((size_t)m0 * d + kt * BK) * 2;
+  const int last = M - 1 - m0;  // rows past the end repeat the last row
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j) {
     const int blk = wave * C::A_LOADS + j;  // 8 rows
     const int row = blk * 8 + lane / 8;
     const int chunk = (lane % 8) ^ ((row >> 1) & 7);
-    const int grow = min(m0 + row, M - 1);
-    const uint16_t* z = Z + (size_t)grow * d + kt * BK + chunk * 8;
+    const uint32_t off = (uint32_t)(min(row, last) * d * 2 + chunk * 16);
+    const char* z = zbase + off;
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)z,
                                      (__attribute__((address_space(3))) void*)(stg + blk * 1024),
                                      16, 0, 0);
@@ -788,7 +799,8 @@ __global__ __launch_bounds__(C::THREADS) void gemm_rb_kernel(const uint16_t* Z,
   ring[2] = st2;
   ring[3] = st3;
 
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int hshift = 8 * (lane >> 5);  // K half of the slice -> its 4 code pairs
 
