@@ -60,7 +60,7 @@ FwdLayout fwd_layout(bmoe_dtype dt, int T, int d, int N, int k, bool keep = fals
   const bool fused = !keep && fused_supported(dt, d);
   // The routed fused kernel computes its own coefficient tables and streams
   // no bf16 substrate.
-  const bool routed = fused && fused_routes(dt, (int)M, d, N);
+  const bool routed = fused && fused_wave_routes(dt, (int)M, d, N);
   l.cs_in = off;   if (!routed) off = align_up(off + sizeof(float2) * N * L * (d / 2));
   l.cs_out = off;  if (!routed) off = align_up(off + sizeof(float2) * N * L * (d / 2));
   // The fused path keeps Z and H on chip; only U (and the bf16 substrate)
@@ -320,7 +320,7 @@ bmoe_status forward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, cons
     return t;
   };
   const bool fused = !keep && fused_supported(dt, d);
-  const bool routed = fused && fused_routes(dt, M, d, n_experts);
+  const bool routed = fused && fused_wave_routes(dt, M, d, n_experts);
   uint16_t* w16 = fused && !routed ? reinterpret_cast<uint16_t*>(base + l.w16) : nullptr;
   const int wt_block = gemm_tiled_w_block(dt, M, d);
   uint32_t* wt = wt_block ? reinterpret_cast<uint32_t*>(base + l.wt) : nullptr;
@@ -460,7 +460,7 @@ bmoe_status bmoe_forward(bmoe_dtype dt, int T, int d, int n_experts, int k, cons
 int bmoe_forward_kernel_count(bmoe_dtype dt, int T, int d, int n_experts, int k) {
   if (!shape_ok(dt, T, d, n_experts, k) || T == 0) return 0;
   if (small_d(d)) return 2;
-  if (fused_routes(dt, T * k, d, n_experts)) return 2;
+  if (fused_wave_routes(dt, T * k, d, n_experts)) return 2;
   return fused_supported(dt, d) ? 3 : 5;
 }
 
@@ -472,7 +472,7 @@ const char* bmoe_forward_kernel_name(bmoe_dtype dt, int T, int d, int n_experts,
                                       "bfly_out_kernel", "combine_kernel"};
   if (i < 0 || i >= bmoe_forward_kernel_count(dt, T, d, n_experts, k)) return "";
   if (small_d(d)) return small_names[i];
-  if (fused_routes(dt, T * k, d, n_experts)) return routed_names[i];
+  if (fused_wave_routes(dt, T * k, d, n_experts)) return routed_names[i];
   return fused_supported(dt, d) ? fused_names[i] : split_names[i];
 }
 

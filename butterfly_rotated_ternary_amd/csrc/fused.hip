@@ -19,15 +19,9 @@
 // GEMM take the substrate from packed words in registers, which leaves time
 // for the ring to fill after the rows are dead.
 //
-// Routed variant (no preparation launch, M <= 8192 and N <= 512): every
-// workgroup reads all expert ids, builds the per-expert counts and offsets in
-// LDS, and ranks only the rows of its own tile (stable: ascending routed
-// index inside an expert). It computes the cos/sin tables of the tile's first
-// expert (stage 0) and last expert (stage 3) itself, in-side before the first
-// butterfly and out-side after it; rows of any expert in between take their
-// coefficients straight from the angles. All K-steps then come from the
-// packed words (there is no bf16 substrate copy). It writes the same routing
-// tables as the preparation kernel.
+// This kernel runs after the preparation launch (routing and cos/sin tables),
+// for batches the register-resident fused kernel does not route itself
+// (M > 8192 or N > 512).
 #include "common.h"
 #include "kernels.h"
 
@@ -37,10 +31,6 @@ namespace {
 constexpr int kThreads = 512;  // 8 waves: two per SIMD
 constexpr int kWavesF = kThreads / 64;
 constexpr int kBM = 32;
-// Routed variant: ids per thread (M <= kRouteIds * kThreads) and experts.
-constexpr int kRouteIds = 16;
-constexpr int kRouteMaxM = kRouteIds * kThreads;
-constexpr int kRouteMaxN = 512;
 
 __device__ __forceinline__ int padi(int i) { return i + (i >> 3); }
 
@@ -186,51 +176,19 @@ __device__ __forceinline__ void table_load(char* dst, const float2* cs, int e) {
 // expert of its first row (prefetch) and reloaded only when the expert of a
 // later row differs (rows are sorted by expert): from the LDS copy of expert
 // e_tab's table when the row belongs to it, else from global memory.
-template <int D, bool TR, bool RT = false>
+template <int D, bool TR>
 struct BflyCoef {
   using Gr = Groups<D, TR>;
   float2 c[Gr::N][3][4];
   int e[Gr::N];
-  // Routed variant: expert e_a's table in LDS at tab_a (the last expert's is
-  // the e_tab table). The n_mid experts listed at mid (those of the tile
-  // between its first and last) have no table: after each stage group's
-  // main pass the workgroup writes that group's part of one of their tables
-  // to `scratch` and rotates its rows from there.
-  const float* ang = nullptr;
-  const float2* tab_a = nullptr;
-  int e_a = -1;
-  const int* mid = nullptr;
-  int n_mid = 0;
-  float2* scratch = nullptr;
 
   // Coefficients of group g for expert ei: from the LDS table of e_tab, else
-  // (prep path) the global tables cs, else (routed) e_a's table; a routed
-  // expert without a table marks the group as holding none.
+  // the global tables cs.
   template <int G>
   __device__ __forceinline__ void fetch(int g, int ei, const float2* cs, const float2* tab,
                                         int e_tab, int s_lo, int base) {
-    if constexpr (RT) {
-      if (ei == e_tab || ei == e_a) load_coef_lds<D, G>(c[g], ei == e_tab ? tab : tab_a, s_lo, base);
-      else e[g] = -1;
-    } else if (ei == e_tab) {
-      load_coef_lds<D, G>(c[g], tab, s_lo, base);
-    } else {
-      load_coef<D, G>(c[g], cs, ei, s_lo, base);
-    }
-  }
-
-  // Routed variant: as prefetch_from_lanes, from the LDS tables.
-  __device__ __forceinline__ void prefetch_tables(int lane_e, const float2* tab, int e_tab) {
-#pragma unroll
-    for (int g = 0; g < Gr::N; ++g) {
-      const int G = Gr::G(g), s_lo = Gr::s_lo(g);
-      const int nb = D >> G;
-      const int base = block_base(threadIdx.x % nb, s_lo, G);
-      e[g] = __shfl(lane_e, threadIdx.x / nb, 64);
-      if (G == 3) fetch<3>(g, e[g], nullptr, tab, e_tab, s_lo, base);
-      else if (G == 2) fetch<2>(g, e[g], nullptr, tab, e_tab, s_lo, base);
-      else fetch<1>(g, e[g], nullptr, tab, e_tab, s_lo, base);
-    }
+    if (ei == e_tab) load_coef_lds<D, G>(c[g], tab, s_lo, base);
+    else load_coef<D, G>(c[g], cs, ei, s_lo, base);
   }
 
   // Coefficients of every group for the expert of the thread's first row,
@@ -284,48 +242,9 @@ struct BflyCoef {
     for (int j = 0; j < rpt; ++j) {
       const int i = ph + j * tpb;
       const int ei = sh_e[i];
-      if constexpr (RT) {
-        if (ei != e_a && ei != e_tab) continue;  // a middle expert: its own pass
-      }
       if (ei != e[g]) {
         e[g] = ei;
         fetch<G>(g, ei, cs, tab, e_tab, s_lo, base);
-      }
-      float* row = rows.row(i);
-      float v[8];
-#pragma unroll
-      for (int m = 0; m < (1 << G); ++m) v[m] = row[off[m]];
-      rotate<G, TR>(v, c[g]);
-#pragma unroll
-      for (int m = 0; m < (1 << G); ++m) row[off[m]] = v[m];
-    }
-  }
-
-  // Routed variant: middle expert em's table of stages s_lo .. s_lo+G-1 in
-  // `scratch`, computed by the whole workgroup as the tile tables are.
-  __device__ __forceinline__ void mid_table(int em, int s_lo, int G) {
-    constexpr int L = FCfg<D>::L;
-    lds_barrier();  // the previous pass is done with scratch
-    for (int j = threadIdx.x; j < G * (D / 2); j += kThreads) {
-      const int t = j / (D / 2), p = j % (D / 2);
-      scratch[j] = tile_cos_sin(ang[((size_t)em * L + s_lo + t) * (D / 2) + p]);
-    }
-    lds_barrier();
-  }
-
-  // Routed variant: this thread's rows of middle expert em for stage group
-  // g, from its group table in `scratch`.
-  template <int G>
-  __device__ __forceinline__ void rotate_mid(const RowMap<D>& rows, const int* sh_e, int g,
-                                             int em, int s_lo, int base, const int (&off)[8],
-                                             int ph, int tpb) {
-    const int rpt = kBM / tpb;
-    for (int j = 0; j < rpt; ++j) {
-      const int i = ph + j * tpb;
-      if (sh_e[i] != em) continue;
-      if (e[g] != em) {
-        e[g] = em;
-        load_coef_lds<D, G>(c[g], scratch - s_lo * (D / 2), s_lo, base);
       }
       float* row = rows.row(i);
       float v[8];
@@ -352,15 +271,6 @@ struct BflyCoef {
       if (G == 3) rotate_rows<3>(rows, sh_e, cs, tab, e_tab, g, s_lo, base, off, ph, tpb);
       else if (G == 2) rotate_rows<2>(rows, sh_e, cs, tab, e_tab, g, s_lo, base, off, ph, tpb);
       else rotate_rows<1>(rows, sh_e, cs, tab, e_tab, g, s_lo, base, off, ph, tpb);
-      if constexpr (RT) {
-        for (int mi = 0; mi < n_mid; ++mi) {
-          const int em = mid[mi];
-          mid_table(em, s_lo, G);
-          if (G == 3) rotate_mid<3>(rows, sh_e, g, em, s_lo, base, off, ph, tpb);
-          else if (G == 2) rotate_mid<2>(rows, sh_e, g, em, s_lo, base, off, ph, tpb);
-          else rotate_mid<1>(rows, sh_e, g, em, s_lo, base, off, ph, tpb);
-        }
-      }
       lds_barrier();
     }
   }
@@ -388,21 +298,8 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
 }
 
-// Routed variant: one side's cos/sin tables of the tile's first expert (ta)
-// and, when e_tab >= 0, its last expert (tb) from that side's angles, which
-// thread holds in ang[i] (entry tid + i * kThreads).
-template <int TBL, int NTB>
-__device__ __forceinline__ void write_tables(const float (&ang)[NTB], float2* ta, float2* tb,
-                                             int e_tab) {
-#pragma unroll
-  for (int i = 0; i < NTB; ++i) {
-    const int j = threadIdx.x + i * kThreads;
-    if (j < TBL || e_tab >= 0) (j < TBL ? ta : tb)[j < TBL ? j : j - TBL] = tile_cos_sin(ang[i]);
-  }
-}
-
 struct FusedArgs {
-  int M, k, N;
+  int M, k;
   const uint16_t* x;
   const float* gates;
   float alpha;  // the kernel's scale for the +-2 substrate values
@@ -415,31 +312,13 @@ struct FusedArgs {
   const float2* cs_in;
   const float2* cs_out;
   const uint16_t* w16;
-  // Routed variant: ids and angles in; routing tables and status out.
-  const int32_t* ids;
-  const float* theta;
-  const float* phi;
-  RouteTables rt;
-  int32_t* status;
 };
 
-template <int D, bool RT>
+template <int D>
 __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   using C = FCfg<D>;
-  constexpr int NR = RT ? 0 : C::NR;  // ring K-steps
+  constexpr int NR = C::NR;           // ring K-steps
   constexpr int NP = C::NSTEP - NR;   // K-steps from packed words
-  // Packed K-steps requested before the first butterfly (the routed variant
-  // requests the rest after it).
-  constexpr int NPE = RT ? C::NSTEP / 2 : C::NP;
-  // Routed variant: one side's table entries of the tile's two experts,
-  // kThreads-strided over the threads.
-  constexpr int TBL = C::L * (D / 2);
-  constexpr int NTB = 2 * TBL / kThreads;
-  static_assert(!RT || (2 * TBL) % kThreads == 0, "table entries must split over the threads");
-  static_assert(!RT || (C::TAB_BYTES <= C::STAGE_BYTES &&
-                        kWavesF * kRouteMaxN * 4 <= C::STAGE_BYTES &&
-                        (kRouteMaxN + 16) * 4 <= C::STAGE_BYTES),
-                "routing scratch and the first expert's table must fit in a stage");
   __shared__ __attribute__((aligned(1024))) char st0[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st1[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st2[C::STAGE_BYTES];
@@ -452,12 +331,9 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   auto stage = [&](int i) -> char* { return i == 0 ? st0 : i == 1 ? st1 : i == 2 ? st2 : st3; };
   int* const sh_e = reinterpret_cast<int*>(st3 + C::META_OFF);
   int* const sh_r = sh_e + kBM;
-  int* const sh_mid = sh_r + kBM;  // routed: the tile's middle experts, then their count
-  static_assert(C::META_OFF + (3 * kBM + 1) * 4 <= C::TAB_OFF, "row metadata overlaps the table");
-  // The last expert's table when the tile holds more than one (stage 3); in
-  // the routed variant also the first expert's (stage 0).
+  static_assert(C::META_OFF + 2 * kBM * 4 <= C::TAB_OFF, "row metadata overlaps the table");
+  // The last expert's table when the tile holds more than one (stage 3).
   const float2* const tab = reinterpret_cast<const float2*>(st3 + C::TAB_OFF);
-  const float2* const tab_a = reinterpret_cast<const float2*>(st0);
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int q0 = blockIdx.x * kBM;
@@ -466,167 +342,8 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   // that is of slot slot_of_row(l), in registers (an LDS copy serves the
   // butterflies). Rows of slots past the end repeat the last slot (computed,
   // never stored).
-  int my_e, my_r, e_tab, e_first = -1, e_last = -1;
-  float th[RT ? NTB : 1];
-  if constexpr (RT) {
-    // ---- routing of this tile's rows -------------------------------------
-    // Per-wave counts, then each wave's count of the ids before it (stage
-    // 1), and the offsets (stage 2).
-    int* const wcnt = reinterpret_cast<int*>(st1);  // [kWavesF][N]
-    int* const cnt = reinterpret_cast<int*>(st2);   // [N + 1]
-    int* const misc = cnt + kRouteMaxN + 4;         // bad id; first, last expert
-    const int N = a.N;
-    // Thread t owns ids [kRouteIds * t, +kRouteIds), nv of them valid.
-    const int i0 = kRouteIds * tid;
-    const int nv = max(0, min(kRouteIds, a.M - i0));
-    int id[kRouteIds];
-    if (nv == kRouteIds) {
-#pragma unroll
-      for (int j = 0; j < kRouteIds / 4; ++j) {
-        const int4 v = reinterpret_cast<const int4*>(a.ids + i0)[j];
-        id[4 * j] = v.x; id[4 * j + 1] = v.y; id[4 * j + 2] = v.z; id[4 * j + 3] = v.w;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kRouteIds; ++j) id[j] = j < nv ? a.ids[i0 + j] : 0;
-    }
-    for (int e = tid; e < kWavesF * N; e += kThreads) wcnt[e] = 0;
-    if (tid == 0) {
-      misc[0] = 0;
-      misc[1] = 0;
-      misc[2] = 0;
-      sh_mid[kBM] = 0;
-    }
-    if (tid < kBM) {  // every slot is ranked below; valid indices regardless
-      sh_e[tid] = 0;
-      sh_r[tid] = 0;
-    }
-    lds_barrier();
-    // Per-wave counts (ids outside [0, N) are clamped for addressing and
-    // reported).
-    bool bad = false;
-    int* const mine = wcnt + wave * N;
-#pragma unroll
-    for (int j = 0; j < kRouteIds; ++j) {
-      if (j < nv) {
-        int e = id[j];
-        if ((unsigned)e >= (unsigned)N) {
-          bad = true;
-          e = e < 0 ? 0 : N - 1;
-        }
-        id[j] = e;
-        atomicAdd(&mine[e], 1);
-      }
-    }
-    if (bad) misc[0] = 1;
-    lds_barrier();
-    // Wave 0: totals, each wave's exclusive prefix in place, the exclusive
-    // offsets over experts (expert u * 64 + lane in pass u), and the experts
-    // of the tile's first and last rows (exactly one non-empty expert holds
-    // each sorted slot).
-    if (wave == 0) {
-      const int q_last = q0 + nr - 1;
-      int carry = 0;
-      for (int e0 = 0; e0 < N; e0 += kWave) {
-        const int e = e0 + lane;
-        int tot = 0;
-        if (e < N) {
-#pragma unroll
-          for (int w = 0; w < kWavesF; ++w) {
-            const int c = wcnt[w * N + e];
-            wcnt[w * N + e] = tot;
-            tot += c;
-          }
-        }
-        int incl = tot;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-          const int t = __shfl_up(incl, off, kWave);
-          if (lane >= off) incl += t;
-        }
-        const int run = carry + incl - tot;
-        if (e < N) {
-          cnt[e] = run;
-          if (blockIdx.x == 0) a.rt.offsets[e] = run;
-          if (run <= q0 && q0 < run + tot) misc[1] = e;
-          if (run <= q_last && q_last < run + tot) misc[2] = e;
-        }
-        carry += __shfl(incl, kWave - 1, kWave);
-      }
-      if (lane == 0) {
-        cnt[N] = a.M;
-        if (blockIdx.x == 0) {
-          a.rt.offsets[N] = a.M;
-          *a.status = misc[0] ? BMOE_E_EXPERT : BMOE_OK;
-        }
-      }
-    }
-    lds_barrier();
-    e_first = misc[1];
-    e_last = misc[2];
-    e_tab = e_last != e_first ? e_last : -1;
-    // The in-side angles of the two tables, in flight during the ranking.
-#pragma unroll
-    for (int i = 0; i < NTB; ++i) {
-      const int j = tid + i * kThreads;
-      th[i] = a.theta[j < TBL ? (size_t)e_first * TBL + j : (size_t)e_last * TBL + (j - TBL)];
-    }
-    // The non-empty experts strictly between the first and the last (all
-    // their rows lie inside the tile), in any order.
-    for (int e = e_first + 1 + tid; e < e_last; e += kThreads)
-      if (cnt[e + 1] > cnt[e]) {
-        const int at = atomicAdd(&sh_mid[kBM], 1);  // < nr - 2: each has a row here
-        if (at < kBM) sh_mid[at] = e;
-      }
-    // Stable ranks of the tile's experts: the sorted slot of an id is its
-    // expert's offset, plus that expert's ids in earlier waves, plus those in
-    // earlier lanes of this wave and earlier positions of this thread.
-    for (int e = e_first; e <= e_last; ++e) {
-      if (cnt[e + 1] == cnt[e]) continue;  // uniform: no ids of e
-      // This wave's ids of e rank in [w_lo, w_hi) within e; the tile needs
-      // ranks [q0 - cnt[e], q0 + nr - cnt[e]). Waves outside skip (uniform
-      // per wave).
-      const int w_lo = wcnt[wave * N + e];
-      const int w_hi = wave + 1 < kWavesF ? wcnt[(wave + 1) * N + e] : cnt[e + 1] - cnt[e];
-      if (w_hi <= q0 - cnt[e] || w_lo >= q0 + nr - cnt[e]) continue;
-      // ids of e held by lower lanes of this wave (every position)
-      int below = 0;
-#pragma unroll
-      for (int j = 0; j < kRouteIds; ++j) {
-        const uint64_t m = __ballot(j < nv && id[j] == e);
-        below += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-      }
-      int q = cnt[e] + w_lo + below - q0;
-#pragma unroll
-      for (int j = 0; j < kRouteIds; ++j) {
-        if (j < nv && id[j] == e) {
-          if ((unsigned)q < (unsigned)nr) {
-            sh_e[row_of_slot(q)] = e;
-            sh_r[row_of_slot(q)] = i0 + j;
-          }
-          ++q;
-        }
-      }
-    }
-    lds_barrier();
-    // Lane l < 32 holds LDS row l (slot sl); rows of slots past nr repeat
-    // the last slot.
-    const int sl = slot_of_row(lane & 31);
-    const int li = sl < nr ? (lane & 31) : row_of_slot(nr - 1);
-    my_e = sh_e[li];
-    my_r = sh_r[li];
-    if (tid < kBM) {
-      if (sl < nr) {
-        a.rt.perm[q0 + sl] = my_r;
-        a.rt.inv[my_r] = q0 + sl;
-        a.rt.slot_e[q0 + sl] = my_e;
-      } else {
-        sh_e[tid] = my_e;
-        sh_r[tid] = my_r;
-      }
-    }
-  } else {
+  int my_e, my_r, e_tab;
+  {
     const int q_meta = q0 + min(slot_of_row(lane & 31), nr - 1);
     my_e = a.slot_e[q_meta];
     my_r = a.perm[q_meta];
@@ -643,10 +360,6 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
     __asm__ volatile("" ::: "memory");
   }
   const int my_t = my_r / a.k;
-  // Routed: lane i holds row i's gate, requested now (it is long in by the
-  // stores).
-  float my_g = 0.f;
-  if constexpr (RT) my_g = a.gates[my_r];
 
   // Gather x rows (8 bf16 per 16-byte chunk) into registers and fetch the
   // butterfly-in coefficients. Token indices come from the lanes holding them
@@ -662,23 +375,8 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
     const int t = __shfl(my_t, i, 64);
     xv[it] = *reinterpret_cast<const uint4*>(a.x + (size_t)t * D + ch * 8);
   }
-  BflyCoef<D, true, RT> cin;
-  if constexpr (RT) {
-    // In-side tables: the first expert's in stage 0, the last expert's (if
-    // different) in stage 3, in the prep kernel's layout and arithmetic.
-    write_tables<TBL, NTB>(th, reinterpret_cast<float2*>(st0),
-                           reinterpret_cast<float2*>(st3 + C::TAB_OFF), e_tab);
-    lds_barrier();
-    cin.ang = a.theta;
-    cin.tab_a = tab_a;
-    cin.e_a = e_first;
-    cin.mid = sh_mid;
-    cin.n_mid = sh_mid[kBM];
-    cin.scratch = reinterpret_cast<float2*>(zt);  // free until the A tile is written
-    cin.prefetch_tables(my_e, tab, e_tab);
-  } else {
-    cin.prefetch_from_lanes(a.cs_in, my_e);
-  }
+  BflyCoef<D, true> cin;
+  cin.prefetch_from_lanes(a.cs_in, my_e);
 #pragma unroll
   for (int it = 0; it < XPT; ++it) {
     const int c = tid + it * kThreads;
@@ -688,14 +386,13 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
     dst[0] = bf16_lo(v.x); dst[1] = bf16_hi(v.x); dst[2] = bf16_lo(v.y); dst[3] = bf16_hi(v.y);
     dst[4] = bf16_lo(v.z); dst[5] = bf16_hi(v.z); dst[6] = bf16_lo(v.w); dst[7] = bf16_hi(v.w);
   }
-  if (!RT && e_tab >= 0) wait_vm<0>();  // this wave's part of the table has landed
+  if (e_tab >= 0) wait_vm<0>();  // this wave's part of the table has landed
   __syncthreads();
-  // The packed substrate words of the first NPE K-steps, for the GEMM (the
-  // routed variant requests the rest after the first butterfly). Lane l needs W rows o = wave*WN + 32j + (l & 31), two words
-  // per K-step.
+  // The packed substrate words of the packed K-steps, for the GEMM. Lane l
+  // needs W rows o = wave*WN + 32j + (l & 31), two words per K-step.
   uint2 pw[NP][C::FN];
 #pragma unroll
-  for (int ks = 0; ks < NPE; ++ks)
+  for (int ks = 0; ks < NP; ++ks)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
       const int o = wave * C::WN + j * 32 + (lane & 31);
@@ -715,37 +412,19 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
                    pack_bf16x2(s[6], s[7]));
   }
   lds_barrier();  // rows are dead from here until the GEMM ends
-  BflyCoef<D, false, RT> cout;
-  float ph[RT ? NTB : 1];
-  if constexpr (RT) {
-    // The out-side angles of the two tables (their tables are computed
-    // halfway through the GEMM) and the last packed K-steps.
-#pragma unroll
-    for (int i = 0; i < NTB; ++i) {
-      const int j = tid + i * kThreads;
-      ph[i] = a.phi[j < TBL ? (size_t)e_first * TBL + j : (size_t)e_last * TBL + (j - TBL)];
-    }
-#pragma unroll
-    for (int ks = NPE; ks < NP; ++ks)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        const int o = wave * C::WN + j * 32 + (lane & 31);
-        pw[ks][j] = *reinterpret_cast<const uint2*>(a.wp + (size_t)o * (D / 16) + 2 * ks);
-      }
-  } else {
-    // Butterfly-out coefficients (for the expert of each thread's first row)
-    // and then every ring stage are requested now; the packed K-steps run
-    // while they land. Loads complete in issue order, so the coefficients go
-    // first.
-    cout.prefetch_from_lanes(a.cs_out, my_e);
-    // The output side's table replaces the input side's (that butterfly is
-    // done); it goes out before the ring, so it has landed once the ring has.
-    if (e_tab >= 0) table_load<D>(st3 + C::TAB_OFF, a.cs_out, e_tab);
-    __asm__ volatile("" ::: "memory");
-    ring_load<D>(st0, a.w16, NP);
-    if (NR > 1) ring_load<D>(st1, a.w16, NP + 1);
-    if (NR > 2) ring_load<D>(st2, a.w16, NP + 2);
-  }
+  BflyCoef<D, false> cout;
+  // Butterfly-out coefficients (for the expert of each thread's first row)
+  // and then every ring stage are requested now; the packed K-steps run
+  // while they land. Loads complete in issue order, so the coefficients go
+  // first.
+  cout.prefetch_from_lanes(a.cs_out, my_e);
+  // The output side's table replaces the input side's (that butterfly is
+  // done); it goes out before the ring, so it has landed once the ring has.
+  if (e_tab >= 0) table_load<D>(st3 + C::TAB_OFF, a.cs_out, e_tab);
+  __asm__ volatile("" ::: "memory");
+  ring_load<D>(st0, a.w16, NP);
+  if (NR > 1) ring_load<D>(st1, a.w16, NP + 1);
+  if (NR > 2) ring_load<D>(st2, a.w16, NP + 2);
 
   // ---- substrate GEMM: wave w computes rows 0..31 x columns [w*WN, (w+1)*WN)
   f32x16 acc[C::FN];
@@ -766,23 +445,6 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
       for (int j = 0; j < C::FN; ++j) {
         const bf16x8 b = unpack_frag(kk == 0 ? pw[ks][j].x : pw[ks][j].y, lane >> 5);
         acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b, acc[j], 0, 0, 0);
-      }
-    }
-    if constexpr (RT) {
-      if (ks == NP / 2) {
-        // Out-side tables in place of the in-side ones (that butterfly is
-        // done), VALU work beside the other waves' MFMAs, then each thread's
-        // butterfly-out coefficients for the rest of the GEMM to hide.
-        write_tables<TBL, NTB>(ph, reinterpret_cast<float2*>(st0),
-                               reinterpret_cast<float2*>(st3 + C::TAB_OFF), e_tab);
-        lds_barrier();
-        cout.ang = a.phi;
-        cout.tab_a = tab_a;
-        cout.e_a = e_first;
-        cout.mid = sh_mid;
-        cout.n_mid = sh_mid[kBM];
-        cout.scratch = reinterpret_cast<float2*>(zt);  // free after the GEMM
-        cout.prefetch_tables(my_e, tab, e_tab);
       }
     }
   }
@@ -810,10 +472,8 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
       }
     }
   }
-  // Every wave is done with the ring: rows may be rewritten. (Without a ring
-  // the GEMM reads only the A tile and the tables, which the rows do not
-  // overlap.)
-  if constexpr (!RT) __syncthreads();
+  // Every wave is done with the ring: rows may be rewritten.
+  __syncthreads();
 
   // alpha * H -> fp32 rows. 32x32 block layout: lane l, register r ->
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
@@ -826,10 +486,8 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
       rows.row(row)[padi(col)] = a.alpha * acc[j][r];
     }
   }
-  // The rows are complete (the routed variant has no global loads left to
-  // order here).
-  if constexpr (RT) lds_barrier();
-  else __syncthreads();
+  // The rows are complete.
+  __syncthreads();
 
   cout.apply(rows, a.cs_out, sh_e, tab, e_tab);
 
@@ -838,11 +496,9 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   for (int it = 0; it < XPT; ++it) {
     const int c = tid + it * kThreads;
     const int i = c / CPR, ch = c % CPR;
-    float g = 0.f;
-    if constexpr (RT) g = __shfl(my_g, i, 64);
     if (slot_of_row(i) < nr) {
       const int r = sh_r[i];
-      if constexpr (!RT) g = a.gates[r];
+      const float g = a.gates[r];
       const float* s = rows.row(i) + padi(ch * 8);
       *reinterpret_cast<uint4*>(a.u + (size_t)r * D + ch * 8) =
           make_uint4(pack_bf16x2(g * s[0], g * s[1]), pack_bf16x2(g * s[2], g * s[3]),
@@ -851,20 +507,15 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   }
 }
 
-template <int D, bool RT>
+template <int D>
 hipError_t launch_d(const FusedArgs& a, hipStream_t s, const KernelTiming& t) {
-  return launch_kernel(fused_kernel<D, RT>, dim3((a.M + kBM - 1) / kBM), dim3(kThreads), 0, s, t,
-                       a);
+  return launch_kernel(fused_kernel<D>, dim3((a.M + kBM - 1) / kBM), dim3(kThreads), 0, s, t, a);
 }
 
 }  // namespace
 
 bool fused_supported(bmoe_dtype dt, int d) {
   return dt == BMOE_BF16 && (d == 256 || d == 512);
-}
-
-bool fused_routes(bmoe_dtype dt, int M, int d, int N) {
-  return fused_supported(dt, d) && M <= kRouteMaxM && N <= kRouteMaxN;
 }
 
 hipError_t launch_fused(int M, int d, int k, const void* x, const float* gates,
@@ -885,34 +536,8 @@ hipError_t launch_fused(int M, int d, int k, const void* x, const float* gates,
   a.cs_out = cs_out;
   a.w16 = w16;
   switch (d) {
-    case 256: return launch_d<256, false>(a, s, t);
-    case 512: return launch_d<512, false>(a, s, t);
-  }
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_fused_routed(int M, int d, int k, int N, const void* x, const int32_t* ids,
-                               const float* gates, const float* theta, const float* phi,
-                               const uint32_t* wp, float alpha, void* u, const RouteTables& rt,
-                               int32_t* status, hipStream_t s, const KernelTiming& t) {
-  if (!fused_routes(BMOE_BF16, M, d, N)) return hipErrorInvalidValue;
-  FusedArgs a{};
-  a.M = M;
-  a.k = k;
-  a.N = N;
-  a.x = static_cast<const uint16_t*>(x);
-  a.gates = gates;
-  a.alpha = substrate_scale(alpha);
-  a.wp = wp;
-  a.u = static_cast<uint16_t*>(u);
-  a.ids = ids;
-  a.theta = theta;
-  a.phi = phi;
-  a.rt = rt;
-  a.status = status;
-  switch (d) {
-    case 256: return launch_d<256, true>(a, s, t);
-    case 512: return launch_d<512, true>(a, s, t);
+    case 256: return launch_d<256>(a, s, t);
+    case 512: return launch_d<512>(a, s, t);
   }
   return hipErrorInvalidValue;
 }

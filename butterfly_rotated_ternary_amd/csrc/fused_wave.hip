@@ -24,7 +24,7 @@
 // the tile's first and last expert. Rows of any expert strictly between those
 // two take their coefficients straight from the angles.
 //
-// Routing (as in the first fused kernel): every workgroup reads all ids,
+// Routing: every workgroup reads all ids,
 // counts them per wave in LDS, derives the per-expert offsets and ranks only
 // its own slots (stable: ascending routed index within an expert), and writes
 // the same routing tables as the preparation kernel.
