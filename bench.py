@@ -71,31 +71,36 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
-def kernel_work(name, act_bytes, T, d, N, k, routed=False):
+def kernel_work(name, act_bytes, T, d, N, k, routed=False, trig=None):
     """Algorithmic work of one launch of a forward kernel: the bytes it must
     move to or from HBM (each input read once, each output written once), the
     flops of its dense contraction (MFMA) and the flops of its rotations
     (fp32 VALU: 2 multiplies and 2 fused multiply-adds, 6 flops, per pair and
     stage). act_bytes is the size of one activation element (x, Z, H, U, y).
     routed: the fused kernel routes itself (no prep launch): it reads the ids,
-    both angle sets and the packed substrate, and writes the routing tables."""
+    both angle sets and the packed substrate, and writes the routing tables.
+    trig: prep writes the cos/sin tables (default: unless the fused kernel
+    runs after it, which evaluates its own tiles' tables from the angles)."""
     M = T * k
     L = d.bit_length() - 1
     A = N * L * (d // 2)                     # angles (pairs) per side
     rot = M * L * (d // 2) * 6               # flops of one rotation side
     routing = M * 4                          # one int32 per routed row
     if name.startswith("prep"):
-        b = M * 4 + 2 * A * 4 + 2 * A * 8 + 3 * routing + (N + 1) * 4
-        if act_bytes == 2 and d in (256, 512):
-            b += d * d // 4 + d * d * 2      # bf16 expansion of the packed substrate
+        fused = act_bytes == 2 and d in (256, 512)
+        b = M * 4 + 3 * routing + (N + 1) * 4          # ids in; perm, inv, slot_e out
+        if trig if trig is not None else not fused:
+            b += 2 * A * 4 + 2 * A * 8               # angles in, cos/sin tables out
+        if act_bytes == 2 and d % 512 == 0 and -(-M // 128) * (d // 512) >= 512:
+            b += 2 * (d * d // 4)                    # tile-major copy of the packed substrate
         return {"bytes": b, "mfma_flops": 0, "valu_flops": 0}
     if name.startswith("fused") and routed:
         b = (T * d * act_bytes + M * d * act_bytes + d * d // 4 + 2 * A * 4
              + 5 * routing + (N + 1) * 4)     # ids and gates in; perm, inv, slot_e out
         return {"bytes": b, "mfma_flops": 2 * M * d * d, "valu_flops": 2 * rot}
-    if name.startswith("fused"):
-        b = (T * d * act_bytes + M * d * act_bytes + d * d * 2 + 2 * A * 8
-             + 2 * routing + M * 4)
+    if name.startswith("fused"):             # after prep: perm and slot_e in
+        b = (T * d * act_bytes + M * d * act_bytes + d * d // 4 + 2 * A * 4
+             + 3 * routing)                  # perm, slot_e, gates
         return {"bytes": b, "mfma_flops": 2 * M * d * d, "valu_flops": 2 * rot}
     if name.startswith("bfly_in"):
         b = T * d * act_bytes + M * d * act_bytes + A * 8 + 2 * routing
@@ -123,7 +128,7 @@ def backward_work(name, act_bytes, T, d, N, k):
     partial = tiles * L * (d // 2) * 4
     routing = M * 4
     if name == "prep_kernel":               # the forward's prep + tile list and packed W_base^T
-        w = kernel_work(name, act_bytes, T, d, N, k)
+        w = kernel_work(name, act_bytes, T, d, N, k, trig=True)
         w["bytes"] += d * d // 4 * (3 if d % 512 == 0 else 2) + (N + 1) * 4 * 2 + tiles * 16
         return w
     if name in ("bfly_in_kernel", "gemm_kernel", "combine_kernel"):

@@ -31,7 +31,7 @@ int log2i(int d) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct FwdLayout {
-  size_t status, offsets, perm, inv, slot_e, cs_in, cs_out, z, h, u, w16, wt, tiles, tile_base,
+  size_t status, offsets, perm, inv, slot_e, cs_in, cs_out, z, h, u, wt, tiles, tile_base,
       wpt, wtt, total;
   int max_tiles;
 };
@@ -58,19 +58,16 @@ FwdLayout fwd_layout(bmoe_dtype dt, int T, int d, int N, int k, bool keep = fals
   l.inv = off;     off = align_up(off + sizeof(int32_t) * M);
   l.slot_e = off;  off = align_up(off + sizeof(int32_t) * M);
   const bool fused = !keep && fused_supported(dt, d);
-  // The routed fused kernel computes its own coefficient tables and streams
-  // no bf16 substrate.
-  const bool routed = fused && fused_wave_routes(dt, (int)M, d, N);
-  l.cs_in = off;   if (!routed) off = align_up(off + sizeof(float2) * N * L * (d / 2));
-  l.cs_out = off;  if (!routed) off = align_up(off + sizeof(float2) * N * L * (d / 2));
+  // The fused kernels evaluate their own tiles' coefficient tables from the
+  // angles and read the packed substrate words.
+  l.cs_in = off;   if (!fused) off = align_up(off + sizeof(float2) * N * L * (d / 2));
+  l.cs_out = off;  if (!fused) off = align_up(off + sizeof(float2) * N * L * (d / 2));
   // The fused path keeps Z and H on chip; only U (and the bf16 substrate)
   // live in the workspace.
   const bool small = small_d(d);
   l.z = off;       if (!fused && !small) off = align_up(off + zel * M * d);
   l.h = off;       if (!fused && !small) off = align_up(off + zel * M * d);
   l.u = off;       if (!small) off = align_up(off + zel * M * d);
-  l.w16 = off;
-  if (fused && !routed) off = align_up(off + sizeof(uint16_t) * (size_t)d * d);
   // Tile-major copy of the packed substrate for the large-tile product.
   l.wt = off;
   const bool wt_copy = gemm_tiled_w_block(dt, (int)M, d) != 0;
@@ -321,7 +318,6 @@ bmoe_status forward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, cons
   };
   const bool fused = !keep && fused_supported(dt, d);
   const bool routed = fused && fused_wave_routes(dt, M, d, n_experts);
-  uint16_t* w16 = fused && !routed ? reinterpret_cast<uint16_t*>(base + l.w16) : nullptr;
   const int wt_block = gemm_tiled_w_block(dt, M, d);
   uint32_t* wt = wt_block ? reinterpret_cast<uint32_t*>(base + l.wt) : nullptr;
   BwdSetup bs;  // keep: the backward's tiles and W_base^T, for bmoe_backward_kept
@@ -342,8 +338,11 @@ bmoe_status forward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, cons
     if (launch_combine(dt, T, d, k, u, y, s, timing()) != hipSuccess) return BMOE_E_HIP;
     return BMOE_OK;
   }
-  if (launch_prep(ids, M, n_experts, theta, phi, d, rt, cs_in, cs_out, status, w_packed, w16, wt,
-                  wt_block, s, timing(), bs) != hipSuccess)
+  // The fused kernel after prep evaluates its own tiles' tables from the
+  // angles: prep only routes.
+  if (launch_prep(ids, M, n_experts, fused ? nullptr : theta, fused ? nullptr : phi, d, rt,
+                  cs_in, cs_out, status, w_packed, wt, wt_block, s, timing(), bs) !=
+      hipSuccess)
     return BMOE_E_HIP;
   if (small_d(d)) {
     // Rotations, product, gates and the sum over j in one launch.
@@ -353,8 +352,8 @@ bmoe_status forward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, cons
                : BMOE_E_HIP;
   }
   if (fused) {
-    if (launch_fused(M, d, k, x, gates, rt, cs_in, cs_out, w16, w_packed, alpha, u, s,
-                     timing()) != hipSuccess)
+    if (launch_fused_wave_prepped(M, d, k, x, gates, theta, phi, w_packed, alpha, u, rt, s,
+                                  timing()) != hipSuccess)
       return BMOE_E_HIP;
   } else {
     if (launch_bfly_in(dt, M, d, k, x, rt, cs_in, z, s, timing()) != hipSuccess)
@@ -467,7 +466,7 @@ int bmoe_forward_kernel_count(bmoe_dtype dt, int T, int d, int n_experts, int k)
 const char* bmoe_forward_kernel_name(bmoe_dtype dt, int T, int d, int n_experts, int k, int i) {
   static const char* routed_names[] = {"fused_wave_kernel", "combine_kernel"};
   static const char* small_names[] = {"prep_kernel", "small_kernel"};
-  static const char* fused_names[] = {"prep_kernel", "fused_kernel", "combine_kernel"};
+  static const char* fused_names[] = {"prep_kernel", "fused_wave_kernel", "combine_kernel"};
   static const char* split_names[] = {"prep_kernel", "bfly_in_kernel", "gemm_kernel",
                                       "bfly_out_kernel", "combine_kernel"};
   if (i < 0 || i >= bmoe_forward_kernel_count(dt, T, d, n_experts, k)) return "";
@@ -584,8 +583,8 @@ bmoe_status backward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, con
     bs.wpt = wpt;
     bs.wtt = wtt;
     bs.wtt_block = l.wt_block;
-    if (launch_prep(ids, M, n_experts, theta, phi, d, rt, cs_in, cs_out, status, w_packed, nullptr,
-                    wt, l.wt_block, s, timing(), bs) != hipSuccess)
+    if (launch_prep(ids, M, n_experts, theta, phi, d, rt, cs_in, cs_out, status, w_packed, wt,
+                    l.wt_block, s, timing(), bs) != hipSuccess)
       return BMOE_E_HIP;
   }
   if (kept) {
@@ -702,8 +701,8 @@ bmoe_status bmoe_rotate_in(bmoe_dtype dt, int T, int d, int n_experts, int k, co
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int M = T * k;
   if (launch_prep(ids, M, n_experts, theta, nullptr, d, rt, cs_in, nullptr,
-                  reinterpret_cast<int32_t*>(base + l.status), nullptr, nullptr, nullptr, 0,
-                  s) != hipSuccess)
+                  reinterpret_cast<int32_t*>(base + l.status), nullptr, nullptr, 0, s) !=
+      hipSuccess)
     return BMOE_E_HIP;
   if (launch_bfly_in(dt, M, d, k, x, rt, cs_in, z, s, KernelTiming{}, true) != hipSuccess)
     return BMOE_E_HIP;

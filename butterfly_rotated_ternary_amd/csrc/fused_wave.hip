@@ -400,7 +400,10 @@ __device__ __forceinline__ void write_table_entry(int i, float ang, float2* tab,
   if (ex == 0 || two) tab[ex * WCfg<D>::TBL + s * WCfg<D>::P + k] = tile_cos_sin(ang);
 }
 
-template <int D>
+// ROUTE: the kernel routes its own rows (reads the ids, writes the routing
+// tables and the status word); otherwise the rows' experts and routed
+// indices come from the preparation kernel's tables (any M and N).
+template <int D, bool ROUTE>
 __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
   using C = WCfg<D>;
   constexpr int VPL = C::VPL;
@@ -433,9 +436,12 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
 
   // ---- routing of this tile's slots ---------------------------------------
   const int i0 = kIdsW * tid;
-  const int nv = max(0, min(kIdsW, a.M - i0));
+  const int nv = ROUTE ? max(0, min(kIdsW, a.M - i0)) : 0;
   int id[kIdsW];
-  if (nv == kIdsW) {
+  if constexpr (!ROUTE) {
+#pragma unroll
+    for (int j = 0; j < kIdsW; ++j) id[j] = 0;
+  } else if (nv == kIdsW) {
 #pragma unroll
     for (int j = 0; j < kIdsW / 4; ++j) {
       const int4 v = reinterpret_cast<const int4*>(a.ids + i0)[j];
@@ -472,6 +478,20 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
           (__attribute__((address_space(3))) void*)(pwl + 1024 * i), 16, 0, 0);
     }
   }
+  if constexpr (!ROUTE) {
+    // The preparation kernel's routing: slot -> (expert, routed index);
+    // rows past the end repeat the last one.
+    if (tid < kSlots) {
+      const int q = q0 + min(tid, nr - 1);
+      sh_e[tid] = a.rt.slot_e[q];
+      sh_r[tid] = a.rt.perm[q];
+    }
+    if (tid == 0) {
+      misc[1] = a.rt.slot_e[q0];
+      misc[2] = a.rt.slot_e[q0 + nr - 1];
+    }
+    lds_barrier();
+  } else {
   for (int e = tid; e < kWavesW * N; e += kThreadsW) wcnt[e] = 0;
   if (tid == 0) {
     misc[0] = 0;
@@ -539,6 +559,7 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
     }
   }
   lds_barrier();
+  }
   const int e_first = misc[1], e_last = misc[2];
   // Both sides' angles of the two tables, in flight during the ranking.
   const bool two = e_last != e_first;                    // a second table is needed
@@ -557,6 +578,7 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
   // Stable ranks of the tile's experts: an id's slot is its expert's offset,
   // plus that expert's ids in earlier waves, earlier lanes of this wave and
   // earlier positions of this thread.
+  if constexpr (ROUTE) {
   for (int e = e_first; e <= e_last; ++e) {
     if (cnt[e + 1] == cnt[e]) continue;  // uniform: no ids of e
     const int w_lo = wcnt[wave * N + e];
@@ -587,6 +609,7 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
     a.rt.perm[q0 + tid] = r;
     a.rt.inv[r] = q0 + tid;
     a.rt.slot_e[q0 + tid] = sh_e[tid];
+  }
   }
 
   // ---- this wave's rows: x, gates -----------------------------------------
@@ -729,13 +752,17 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
   }
 }
 
-template <int D>
+template <int D, bool ROUTE>
 hipError_t launch_w(const WaveArgs& a, hipStream_t s, const KernelTiming& t) {
-  return launch_kernel(fused_wave_kernel<D>, dim3((a.M + kSlots - 1) / kSlots), dim3(kThreadsW),
-                       0, s, t, a);
+  return launch_kernel(fused_wave_kernel<D, ROUTE>, dim3((a.M + kSlots - 1) / kSlots),
+                       dim3(kThreadsW), 0, s, t, a);
 }
 
 }  // namespace
+
+bool fused_supported(bmoe_dtype dt, int d) {
+  return dt == BMOE_BF16 && (d == 256 || d == 512);
+}
 
 bool fused_wave_routes(bmoe_dtype dt, int M, int d, int N) {
   return dt == BMOE_BF16 && (d == 256 || d == 512) && M <= kMaxMW && N <= kMaxNW;
@@ -761,8 +788,31 @@ hipError_t launch_fused_wave(int M, int d, int k, int N, const void* x, const in
   a.rt = rt;
   a.status = status;
   switch (d) {
-    case 256: return launch_w<256>(a, s, t);
-    case 512: return launch_w<512>(a, s, t);
+    case 256: return launch_w<256, true>(a, s, t);
+    case 512: return launch_w<512, true>(a, s, t);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fused_wave_prepped(int M, int d, int k, const void* x, const float* gates,
+                                     const float* theta, const float* phi, const uint32_t* wp,
+                                     float alpha, void* u, const RouteTables& rt, hipStream_t s,
+                                     const KernelTiming& t) {
+  if (M <= 0) return hipSuccess;
+  WaveArgs a{};
+  a.M = M;
+  a.k = k;
+  a.x = static_cast<const uint16_t*>(x);
+  a.gates = gates;
+  a.theta = theta;
+  a.phi = phi;
+  a.wp = wp;
+  a.alpha = substrate_scale(alpha);
+  a.u = static_cast<uint16_t*>(u);
+  a.rt = rt;
+  switch (d) {
+    case 256: return launch_w<256, false>(a, s, t);
+    case 512: return launch_w<512, false>(a, s, t);
   }
   return hipErrorInvalidValue;
 }

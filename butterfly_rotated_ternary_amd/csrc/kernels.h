@@ -46,13 +46,13 @@ struct BwdSetup {
 };
 
 // Routing (histogram, scan, stable scatter), the per-call cos/sin tables of
-// both rotation sides, optionally a per-call copy of the packed substrate for
-// the product (w16: bf16 expansion, d <= 512 fused path; wt: tile-major
-// packed words for the large-tile GEMM) and optionally the backward's setup,
-// in one launch.
+// both rotation sides (none with theta NULL; the input side only with phi
+// NULL), optionally a per-call tile-major copy of the packed substrate for
+// the large-tile GEMM (wt) and optionally the backward's setup, in one
+// launch.
 hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, const float* phi,
                        int d, RouteTables rt, float2* cs_in, float2* cs_out, int32_t* status,
-                       const uint32_t* w_packed, uint16_t* w16, uint32_t* wt, int wt_block,
+                       const uint32_t* w_packed, uint32_t* wt, int wt_block,
                        hipStream_t s, const KernelTiming& t = {}, const BwdSetup& bs = {});
 
 // Column block CB of the tile-major substrate copy `wt` the large-tile GEMM
@@ -69,6 +69,12 @@ int gemm_tiled_w_block(bmoe_dtype dt, int M, int d);
 // both butterflies, the product and the gate for those rows, U in routed
 // order.
 bool fused_wave_routes(bmoe_dtype dt, int M, int d, int N);
+// The same kernel after the preparation launch (any M and N): the rows'
+// experts and routed indices from rt (perm, slot_e), nothing of rt written.
+hipError_t launch_fused_wave_prepped(int M, int d, int k, const void* x, const float* gates,
+                                     const float* theta, const float* phi, const uint32_t* wp,
+                                     float alpha, void* u, const RouteTables& rt, hipStream_t s,
+                                     const KernelTiming& t = {});
 hipError_t launch_fused_wave(int M, int d, int k, int N, const void* x, const int32_t* ids,
                              const float* gates, const float* theta, const float* phi,
                              const uint32_t* wp, float alpha, void* u, const RouteTables& rt,
@@ -88,17 +94,9 @@ hipError_t launch_small(bmoe_dtype dt, int T, int d, int k, int N, const void* x
                         const float2* cs_out, const uint32_t* w_packed, float alpha, void* y,
                         hipStream_t s, const KernelTiming& t = {});
 
-// Whether the fused d <= 512 path handles this shape (the routed variant,
-// launch_fused_wave, when fused_wave_routes also holds; launch_fused after
-// the prep launch otherwise).
+// Whether the fused d <= 512 path handles this shape (launch_fused_wave when
+// fused_wave_routes also holds, else launch_fused_wave_prepped after prep).
 bool fused_supported(bmoe_dtype dt, int d);
-
-// Fused per-tile forward for d <= 512 (bf16): U[r] = g_r * B(phi_e) *
-// alpha * W_base * B(theta_e)^T x[t] for every routed row, in routed order.
-hipError_t launch_fused(int M, int d, int k, const void* x, const float* gates,
-                        const RouteTables& rt, const float2* cs_in, const float2* cs_out,
-                        const uint16_t* w16, const uint32_t* w_packed, float alpha, void* u,
-                        hipStream_t s, const KernelTiming& t = {});
 
 // Z[q] = B(theta_e)^T x[t]   (t = perm[q] / k, e = slot_e[q]).
 // routed_out: row perm[q] of z instead of row q (routed order).

@@ -32,7 +32,6 @@ struct PrepParams {
   // Optional per-call copy of the packed substrate (both NULL: none): bf16
   // expansion [d][d], or tile-major packed words.
   const uint32_t* w_packed;
-  uint16_t* w16;
   uint32_t* wt;
   int wt_block;
   int d, n_trig_blocks, n_w_blocks, n_wt_blocks;
@@ -143,19 +142,6 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
       const size_t o = ob * cb + oo;
       reinterpret_cast<uint4*>(p.wt)[u] =
           *reinterpret_cast<const uint4*>(p.w_packed + o * (p.d / 16) + kt * 4);
-    }
-    return;
-  }
-  if ((int)blockIdx.x >= b_w) {
-    // ---- packed substrate -> bf16 rows ----------------------------------
-    const int G = p.d / 16;
-    const size_t nwords = (size_t)p.d * G;
-    const int b = blockIdx.x - b_w, nb = p.n_w_blocks;
-    for (size_t i = (size_t)b * kThreads + threadIdx.x; i < nwords; i += (size_t)nb * kThreads) {
-      const uint32_t w = p.w_packed[i];
-      uint4* dst = reinterpret_cast<uint4*>(p.w16 + i * 16);
-      dst[0] = make_uint4(unpack_pair(w, 0), unpack_pair(w, 1), unpack_pair(w, 2), unpack_pair(w, 3));
-      dst[1] = make_uint4(unpack_pair(w, 4), unpack_pair(w, 5), unpack_pair(w, 6), unpack_pair(w, 7));
     }
     return;
   }
@@ -308,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
 
 hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, const float* phi,
                        int d, RouteTables rt, float2* cs_in, float2* cs_out, int32_t* status,
-                       const uint32_t* w_packed, uint16_t* w16, uint32_t* wt, int wt_block,
+                       const uint32_t* w_packed, uint32_t* wt, int wt_block,
                        hipStream_t s, const KernelTiming& t, const BwdSetup& bs) {
   int L = 0;
   while ((1 << L) < d) ++L;
@@ -330,17 +316,14 @@ hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, con
   p.n_ang = (long long)N * L * (d / 2);
   long long trig_blocks = ((phi ? 2 : 1) * p.n_ang + kThreads * 8 - 1) / (kThreads * 8);
   if (trig_blocks > 65536) trig_blocks = 65536;
+  if (!theta) trig_blocks = 0;  // no tables wanted
   p.n_trig_blocks = (int)trig_blocks;
   p.w_packed = w_packed;
-  p.w16 = w16;
-  p.wt = (w16 || wt_block <= 0 || d % wt_block != 0) ? nullptr : wt;
+  p.wt = (wt_block <= 0 || d % wt_block != 0) ? nullptr : wt;
   p.wt_block = wt_block;
   p.d = d;
   int w_blocks = 0;
-  if (w16) {
-    const long long words = (long long)d * (d / 16);
-    w_blocks = (int)((words + kThreads * 4 - 1) / (kThreads * 4));
-  } else if (p.wt) {
+  if (p.wt) {
     const long long quads = (long long)d * (d / 64);
     w_blocks = (int)((quads + kThreads * 4 - 1) / (kThreads * 4));
   }

@@ -134,8 +134,8 @@ def test_forward_launch_table():
     assert names(bf, 4096, 512, 64, 2) == ["fused_wave_kernel", "combine_kernel"]
     assert names(bf, 4096, 512, 512, 2) == ["fused_wave_kernel", "combine_kernel"]
     # beyond either limit the prep kernel routes
-    assert names(bf, 4097, 512, 64, 2) == ["prep_kernel", "fused_kernel", "combine_kernel"]
-    assert names(bf, 64, 256, 513, 2) == ["prep_kernel", "fused_kernel", "combine_kernel"]
+    assert names(bf, 4097, 512, 64, 2) == ["prep_kernel", "fused_wave_kernel", "combine_kernel"]
+    assert names(bf, 64, 256, 513, 2) == ["prep_kernel", "fused_wave_kernel", "combine_kernel"]
     # split path
     assert names(f32, 64, 512, 8, 2) == ["prep_kernel", "bfly_in_kernel", "gemm_kernel",
                                          "bfly_out_kernel", "combine_kernel"]

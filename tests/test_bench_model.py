@@ -21,18 +21,32 @@ def test_routed_fused_bytes_follow_the_stated_per_unit_figures():
     # tables written; per call d^2/4 B of packed W, 4 B per angle on both
     # sides, (N+1) * 4 B of offsets
     want = T * 2 * D + M * (2 * D + 4 + 4 + 12) + D * D // 4 + 2 * A * 4 + (N + 1) * 4
-    w = bench.kernel_work("fused_kernel", 2, T, D, N, K, routed=True)
+    w = bench.kernel_work("fused_wave_kernel", 2, T, D, N, K, routed=True)
     assert w["bytes"] == want == 13_992_196
     assert w["mfma_flops"] == 2 * M * D * D
     assert w["valu_flops"] == 2 * M * L * (D // 2) * 6
 
 
 def test_prep_path_fused_bytes_differ_from_the_routed_ones():
-    routed = bench.kernel_work("fused_kernel", 2, T, D, N, K, routed=True)["bytes"]
-    after_prep = bench.kernel_work("fused_kernel", 2, T, D, N, K)["bytes"]
-    # after prep: bf16 W and both cos/sin tables in, metadata per row
-    assert after_prep == (T * 2 * D + M * 2 * D + D * D * 2 + 2 * A * 8 + 2 * M * 4 + M * 4)
+    routed = bench.kernel_work("fused_wave_kernel", 2, T, D, N, K, routed=True)["bytes"]
+    after_prep = bench.kernel_work("fused_wave_kernel", 2, T, D, N, K)["bytes"]
+    # after prep: packed W and both angle sets in, perm, slot_e and gates per
+    # routed row; nothing written back but U
+    assert after_prep == (T * 2 * D + M * 2 * D + D * D // 4 + 2 * A * 4 + 3 * M * 4)
     assert after_prep != routed
+
+
+def test_prep_writes_tables_only_where_no_fused_kernel_follows():
+    routing = M * 4 + 3 * M * 4 + (N + 1) * 4
+    assert bench.kernel_work("prep_kernel", 2, T, D, N, K)["bytes"] == routing
+    assert bench.kernel_work("prep_kernel", 2, T, D, N, K, trig=True)["bytes"] == (
+        routing + 2 * A * 4 + 2 * A * 8)
+    # d = 4096, T = 32768, top-4: 1024 row tiles x 8 column tiles of the large
+    # product, which reads a tile-major copy of the packed substrate
+    d, n, k, t = 4096, 256, 4, 32768
+    a = n * 12 * (d // 2)
+    want = t * k * 16 + (n + 1) * 4 + 2 * a * 12 + 2 * (d * d // 4)
+    assert bench.kernel_work("prep_kernel", 2, t, d, n, k)["bytes"] == want
 
 
 def test_roofline_takes_the_resource_with_the_largest_ideal_time():
@@ -52,7 +66,7 @@ def test_alu_peak_and_per_resource_fractions():
     # the routed d = 512 fused kernel: its bytes at 8 TB/s (1.75 us) take
     # longer than its product at 2.5 PFLOP/s (1.72 us) or its rotations at
     # 157 TFLOP/s (1.44 us)
-    w = bench.kernel_work("fused_kernel", 2, T, D, N, K, routed=True)
+    w = bench.kernel_work("fused_wave_kernel", 2, T, D, N, K, routed=True)
     r = bench.roofline(w, 26e-6, bench.PEAK_BF16_TFLOPS)
     assert r["bound"] == "hbm"
     assert r["frac_by_resource"]["mfma"] == pytest.approx(2 * M * D * D / 2.5e15 / 26e-6)
