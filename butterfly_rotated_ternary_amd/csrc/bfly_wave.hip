@@ -12,13 +12,16 @@
 // bits of element i split three ways:
 //   layout X: bits 0-2 in the lane, bits 3-8 the row position of the lane,
 //             bits 9.. the wave;
-//   layout Y: bits 0-2 in the lane, bits 9.. the low row-position bits,
-//             bits 3.. the remaining ones, the wave the rest.
-// Stages 0-8 are wave-local in X, stages 9.. in Y (in the lane, through DPP
-// for lane distances 1, 2, 4, 8, through v_permlane16/32_swap for 16 and 32),
-// so a row changes layout once, through LDS. The output side runs stages
-// 0-8 in X, then 9.. in Y; the input side (B^T: stages descending) the
-// reverse. Rows are loaded four ahead.
+//   layout Y: bits 0-2 in the lane, bits 7.. the low row-position bits,
+//             bits 3-6 the remaining row-position bits and the wave.
+// Stages 0-6 run in X (in the lane, then through DPP for lane distances 1,
+// 2, 4, 8), stages 7.. in Y (DPP for the first four; at d = 4096 stage 11
+// sits 16 lanes away and goes through v_permlane16_swap), so a row changes
+// layout once, through LDS. A DPP-fed multiply costs about two plain VALU
+// operations and a permlane swap about five, so the layouts keep every stage
+// but one off the swaps. The output side runs stages 0-6 in X, then 7.. in
+// Y; the input side (B^T: stages descending) the reverse. Rows are loaded
+// four ahead.
 #include "common.h"
 #include "kernels.h"
 
@@ -29,8 +32,11 @@ template <int D>
 struct WB {
   static_assert(D == 1024 || D == 2048 || D == 4096, "register butterfly sizes");
   static constexpr int W = D / 512;                          // waves per row
-  static constexpr int LW = W == 2 ? 1 : W == 4 ? 2 : 3;     // stages in layout Y
+  static constexpr int LW = W == 2 ? 1 : W == 4 ? 2 : 3;     // wave bits
   static constexpr int L = 9 + LW;
+  static constexpr int B = L - 7;                            // stages in layout Y
+  static constexpr int NYD = B < 4 ? B : 4;                  // of them on DPP
+  static constexpr int NYS = B - NYD;                        // on a swap (d = 4096)
   static constexpr int P = D / 2;
   static constexpr int THREADS = 64 * W;
   static constexpr int PF = 4;                               // rows loaded ahead
@@ -43,13 +49,13 @@ struct WB {
   static __device__ __forceinline__ int chunk_x(int w, int l) { return (w << 6) | row_lane(l); }
   static __device__ __forceinline__ int chunk_y(int w, int l) {
     const int c = row_lane(l);
-    return (c >> LW) | (w << (6 - LW)) | ((c & (W - 1)) << 6);
+    return ((c & ((1 << B) - 1)) << 4) | (c >> B) | (w << (6 - B));
   }
-  // LDS slot of chunk c in each of the two 16-byte planes: consecutive chunks
-  // (layout X) and chunks 64 apart (layout Y) both fall on distinct 16-byte
-  // bank groups within any 16 lanes.
+  // LDS slot of chunk c in each of the two 16-byte planes: any 16 lanes fall
+  // on distinct 16-byte bank groups, in layout X (chunk bits 0-3 vary) and in
+  // layout Y (chunk bits 4-7 vary; at d = 1024 bits 4-6 and bit 0).
   static __device__ __forceinline__ int lds_pos(int c) {
-    return c ^ (((c >> 6) & (W - 1)) << (4 - LW));
+    return c ^ ((c >> 4) & 15) ^ ((c & 1) << 3);
   }
 };
 
@@ -58,10 +64,11 @@ struct WB {
 // out = cos * mine + (+-sin) * partner.
 template <int D>
 struct Coef {
-  float2 y[WB<D>::LW][8];  // stages 9.. (layout Y, lane bit s - 9)
-  float2 in[3][4];         // stages 0-2, in the lane: (cos, sin) per pair
-  float2 dp[4][8];         // stages 3-6 (layout X, lane bit s - 3)
-  float2 sw[2][4];         // stages 7, 8 (lane bits 4, 5): whole pairs after a swap
+  float2 in[3][4];          // stages 0-2, in the lane: (cos, sin) per pair
+  float2 dp[4][8];          // stages 3-6 (layout X, lane bit s - 3)
+  float2 y[WB<D>::NYD][8];  // stages 7.. (layout Y, lane bit s - 7)
+  float2 sw[1][4];          // stage 11 at d = 4096 (lane bit 4): whole pairs
+                            // after a swap
 };
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left alone), visible to the
@@ -83,13 +90,22 @@ __device__ __forceinline__ void load_coef(Coef<D>& k, const float2* tab, int w, 
   __asm__ volatile("" : "+v"(lane));
   const int cx = C::chunk_x(w, lane), cy = C::chunk_y(w, lane);
 #pragma unroll
-  for (int t = 0; t < C::LW; ++t) {
-    const int s = 9 + t;
+  for (int t = 0; t < C::NYD; ++t) {
+    const int s = 7 + t;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int i = (cy << 3) | j;
       k.y[t][j] = signed_coef<TR>(tab[s * C::P + pair_index(i, s)], i, s);
     }
+  }
+  if constexpr (C::NYS > 0) {
+    // after the swap on lane bit 4, register pair (r, r + 1) holds the pair
+    // of this lane's element r (bit clear) or of the partner lane's element
+    // r + 1 (bit set)
+    const int s = 7 + C::NYD, bit = 16;
+    const int lower = (lane & bit) ? ((C::chunk_y(w, lane ^ bit) << 3) | 1) : (cy << 3);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) k.sw[0][r] = tab[s * C::P + pair_index(lower + 2 * r, s)];
   }
 #pragma unroll
   for (int s = 0; s < 3; ++s)
@@ -106,16 +122,6 @@ __device__ __forceinline__ void load_coef(Coef<D>& k, const float2* tab, int w, 
       const int i = (cx << 3) | j;
       k.dp[t][j] = signed_coef<TR>(tab[s * C::P + pair_index(i, s)], i, s);
     }
-  }
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    // after the swap on lane bit 4 + t, register pair (r, r + 1) holds the
-    // pair of this lane's element r (bit clear) or of the partner lane's
-    // element r + 1 (bit set)
-    const int s = 7 + t, bit = 1 << (4 + t);
-    const int lower = (lane & bit) ? ((C::chunk_x(w, lane ^ bit) << 3) | 1) : (cx << 3);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) k.sw[t][r] = tab[s * C::P + pair_index(lower + 2 * r, s)];
   }
   // Let every load complete here: the row loop's wait counts then stay exact
   // where this (rare) branch rejoins it, so the rows loaded ahead stay in
@@ -164,12 +170,10 @@ __device__ __forceinline__ void swap_stage(float (&v)[8], const float2 (&c)[4]) 
   }
 }
 
-// Stages 0-8 in layout X, ascending (output side) or descending (input side).
+// Stages 0-6 in layout X, ascending (output side) or descending (input side).
 template <bool TR, class K>
 __device__ __forceinline__ void stages_x(float (&v)[8], const K& k) {
   if constexpr (TR) {
-    swap_stage<5, true>(v, k.sw[1]);
-    swap_stage<4, true>(v, k.sw[0]);
     dpp_stage<3>(v, k.dp[3]);
     dpp_stage<2>(v, k.dp[2]);
     dpp_stage<1>(v, k.dp[1]);
@@ -185,23 +189,25 @@ __device__ __forceinline__ void stages_x(float (&v)[8], const K& k) {
     dpp_stage<1>(v, k.dp[1]);
     dpp_stage<2>(v, k.dp[2]);
     dpp_stage<3>(v, k.dp[3]);
-    swap_stage<4, false>(v, k.sw[0]);
-    swap_stage<5, false>(v, k.sw[1]);
   }
 }
 
-// Stages 9.. in layout Y (lane bits 0 .. LW-1).
+// Stages 7.. in layout Y (lane bits 0 .. B-1).
 template <int D, bool TR>
 __device__ __forceinline__ void stages_y(float (&v)[8], const Coef<D>& k) {
-  constexpr int LW = WB<D>::LW;
+  constexpr int N = WB<D>::NYD;
   if constexpr (TR) {
-    if constexpr (LW > 2) dpp_stage<2>(v, k.y[LW > 2 ? 2 : 0]);
-    if constexpr (LW > 1) dpp_stage<1>(v, k.y[LW > 1 ? 1 : 0]);
+    if constexpr (WB<D>::NYS > 0) swap_stage<4, true>(v, k.sw[0]);
+    if constexpr (N > 3) dpp_stage<3>(v, k.y[N > 3 ? 3 : 0]);
+    if constexpr (N > 2) dpp_stage<2>(v, k.y[N > 2 ? 2 : 0]);
+    dpp_stage<1>(v, k.y[1]);
     dpp_stage<0>(v, k.y[0]);
   } else {
     dpp_stage<0>(v, k.y[0]);
-    if constexpr (LW > 1) dpp_stage<1>(v, k.y[LW > 1 ? 1 : 0]);
-    if constexpr (LW > 2) dpp_stage<2>(v, k.y[LW > 2 ? 2 : 0]);
+    dpp_stage<1>(v, k.y[1]);
+    if constexpr (N > 2) dpp_stage<2>(v, k.y[N > 2 ? 2 : 0]);
+    if constexpr (N > 3) dpp_stage<3>(v, k.y[N > 3 ? 3 : 0]);
+    if constexpr (WB<D>::NYS > 0) swap_stage<4, false>(v, k.sw[0]);
   }
 }
 
