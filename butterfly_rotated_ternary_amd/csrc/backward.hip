@@ -518,6 +518,9 @@ hipError_t launch_bfly_bwd(bool in_side, bmoe_dtype dt, int M, int d, int k, con
                            const float* gates, const void* src, const void* grad, void* dst,
                            float* dgates, float* partial, hipStream_t s,
                            const KernelTiming& t) {
+  if (bwd_wave_supported(dt, d))
+    return launch_bfly_bwd_wave(in_side, d, k, tiles, max_tiles, perm, cs, gates, src, grad, dst,
+                                dgates, partial, s, t);
   BwdParams p;
   p.M = M;
   p.k = k;
