@@ -35,10 +35,12 @@ __device__ __forceinline__ int pad(int i) { return i + (i >> 3); }
 // pairs sum in registers over those rows, and each element crosses LDS once
 // per group and pass.
 constexpr int bwd_rows(int d) { return d >= 4096 ? 2 : (8192 / d > 32 ? 32 : 8192 / d); }
-// Rows per tile (a workgroup walks them bwd_rows at a time). Two passes per
-// tile at d = 512 keep the grid within one round of two workgroups per CU at
-// the usual row counts; more passes per tile measured slower.
-constexpr int bwd_tile_rows(int d) { return d >= 1024 ? 64 : d == 512 ? 32 : bwd_rows(d); }
+// Rows per tile (a workgroup walks them bwd_rows at a time). At d = 256 and
+// 512 (bf16: the register-resident kernel, four rows per wave) 16-row tiles
+// spread the rows more evenly over the SIMDs than 32-row ones.
+constexpr int bwd_tile_rows(int d) {
+  return d >= 1024 ? 64 : (d == 256 || d == 512) ? 16 : bwd_rows(d);
+}
 
 template <int D>
 struct BwdCfg {

@@ -5,8 +5,8 @@
 //                                   dphi partials;
 //   input side (z = B(theta)^T x):  dX = B(theta) dZ, dtheta partials.
 //
-// A workgroup of four waves takes one expert-aligned tile of at most 32
-// sorted rows; each wave rotates up to eight of them, one at a time, a row of
+// A workgroup of four waves takes one expert-aligned tile of at most 16
+// sorted rows; each wave rotates up to four of them, one at a time, a row of
 // d values spread over its 64 lanes (d/64 consecutive elements per lane, row
 // position row_lane(l) as in the forward's fused kernel): stages inside a lane
 // run in registers, partners across row-position bits 0-3 are one DPP move,
@@ -32,7 +32,7 @@ namespace {
 
 constexpr int kWavesB = 4;
 constexpr int kThreadsB = kWavesB * kWave;
-constexpr int kTileRowsB = 32;              // rows per tile (the tile list's)
+constexpr int kTileRowsB = 16;              // rows per tile (the tile list's)
 constexpr int kRowsB = kTileRowsB / kWavesB;
 
 template <int D>

@@ -146,7 +146,7 @@ hipError_t launch_pack(const int8_t* w, int d, uint32_t* packed, int32_t* status
 int bwd_max_tiles(int M, int N, int d);
 int bwd_tile_rows_for(int d);
 // Register-resident variant of launch_bfly_bwd for bf16 d = 256 and 512 (same
-// arguments and results; the tiles must have 32 rows).
+// arguments and results; the tiles must have 16 rows).
 bool bwd_wave_supported(bmoe_dtype dt, int d);
 hipError_t launch_bfly_bwd_wave(bool in_side, int d, int k, const int4* tiles, int max_tiles,
                                 const int32_t* perm, const float2* cs, const float* gates,
