@@ -124,7 +124,8 @@ def backward_work(name, act_bytes, T, d, N, k):
     M = T * k
     L = d.bit_length() - 1
     A = N * L * (d // 2)
-    tiles = -(-M // 64) + N                  # upper bound on expert-aligned row tiles
+    tile_rows = 64 if d >= 1024 else 16 if d in (256, 512) else 32
+    tiles = -(-M // tile_rows) + N           # upper bound on expert-aligned row tiles
     partial = tiles * L * (d // 2) * 4
     routing = M * 4
     if name == "prep_kernel":               # the forward's prep + tile list and packed W_base^T

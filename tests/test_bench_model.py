@@ -92,3 +92,14 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "--gpus 1" in (r.stdout + r.stderr)
+
+
+def test_backward_partials_follow_the_tile_rows():
+    # 16-row tiles at d = 512: M / 16 + N tiles, each one [L][d/2] fp32 partial
+    tiles = M // 16 + N
+    w = bench.backward_work("finish_kernel", 2, T, D, N, K)
+    slices = bench.dw_slices(M, D)
+    want = (M + T) * D * 2 + 2 * (tiles * L * (D // 2) * 4 + A * 4)
+    if slices > 1:
+        want += (slices + 1) * D * D * 4
+    assert w["bytes"] == want
