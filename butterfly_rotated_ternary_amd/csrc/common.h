@@ -51,6 +51,11 @@ __host__ __device__ __forceinline__ float substrate_scale(float alpha) { return 
 // them explicitly (vmcnt) first. The memory clobber keeps the compiler from
 // moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() {
+  // The wait goes through the builtin too, so the compiler's own wait-count
+  // tracking sees that every LDS operation issued before the barrier has
+  // completed (an opaque asm wait makes it wait again after the barrier,
+  // together with whatever LDS reads were issued there).
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
   __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 

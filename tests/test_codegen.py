@@ -63,7 +63,8 @@ def _counted_waits(ins):
     those N ops lie in the same basic block."""
     out = []
     for i, s in enumerate(ins):
-        m = re.match(r"s_waitcnt vmcnt\((\d+)\)$", s)
+        # vmcnt alone, or merged with the lgkmcnt / expcnt wait of the barrier
+        m = re.match(r"s_waitcnt vmcnt\((\d+)\)(?: (?:lgkmcnt|expcnt)\(\d+\))*$", s)
         if not m or int(m.group(1)) == 0:
             continue
         if not any(x.startswith("s_barrier") for x in ins[i + 1:i + 4]):
