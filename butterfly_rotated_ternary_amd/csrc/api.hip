@@ -58,12 +58,11 @@ FwdLayout fwd_layout(bmoe_dtype dt, int T, int d, int N, int k, bool keep = fals
   l.inv = off;     off = align_up(off + sizeof(int32_t) * M);
   l.slot_e = off;  off = align_up(off + sizeof(int32_t) * M);
   const bool fused = !keep && fused_supported(dt, d);
-  // The fused kernels evaluate their own tiles' coefficient tables from the
-  // angles and read the packed substrate words.
+  // The fused kernel evaluates its own tiles' coefficient tables from the
+  // angles and reads the packed substrate words.
   l.cs_in = off;   if (!fused) off = align_up(off + sizeof(float2) * N * L * (d / 2));
   l.cs_out = off;  if (!fused) off = align_up(off + sizeof(float2) * N * L * (d / 2));
-  // The fused path keeps Z and H on chip; only U (and the bf16 substrate)
-  // live in the workspace.
+  // The fused path keeps Z and H on chip; only U lives in the workspace.
   const bool small = small_d(d);
   l.z = off;       if (!fused && !small) off = align_up(off + zel * M * d);
   l.h = off;       if (!fused && !small) off = align_up(off + zel * M * d);

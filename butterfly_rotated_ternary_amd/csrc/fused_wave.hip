@@ -492,73 +492,73 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
     }
     lds_barrier();
   } else {
-  for (int e = tid; e < kWavesW * N; e += kThreadsW) wcnt[e] = 0;
-  if (tid == 0) {
-    misc[0] = 0;
-    misc[1] = 0;
-    misc[2] = 0;
-  }
-  if (tid < kSlots) {  // every valid slot is ranked below
-    sh_e[tid] = 0;
-    sh_r[tid] = 0;
-  }
-  lds_barrier();
-  bool bad = false;
-  int* const mine = wcnt + wave * N;
-#pragma unroll
-  for (int j = 0; j < kIdsW; ++j) {
-    if (j < nv) {
-      int e = id[j];
-      if ((unsigned)e >= (unsigned)N) {
-        bad = true;
-        e = e < 0 ? 0 : N - 1;
-      }
-      id[j] = e;
-      atomicAdd(&mine[e], 1);
+    for (int e = tid; e < kWavesW * N; e += kThreadsW) wcnt[e] = 0;
+    if (tid == 0) {
+      misc[0] = 0;
+      misc[1] = 0;
+      misc[2] = 0;
     }
-  }
-  if (bad) misc[0] = 1;
-  lds_barrier();
-  // Wave 0: totals, each wave's exclusive prefix in place, the exclusive
-  // offsets over experts, and the experts of the tile's first and last slot.
-  if (wave == 0) {
-    const int q_last = q0 + nr - 1;
-    int carry = 0;
-    for (int e0 = 0; e0 < N; e0 += kWave) {
-      const int e = e0 + lane;
-      int tot = 0;
-      if (e < N) {
+    if (tid < kSlots) {  // every valid slot is ranked below
+      sh_e[tid] = 0;
+      sh_r[tid] = 0;
+    }
+    lds_barrier();
+    bool bad = false;
+    int* const mine = wcnt + wave * N;
 #pragma unroll
-        for (int w = 0; w < kWavesW; ++w) {
-          const int c = wcnt[w * N + e];
-          wcnt[w * N + e] = tot;
-          tot += c;
+    for (int j = 0; j < kIdsW; ++j) {
+      if (j < nv) {
+        int e = id[j];
+        if ((unsigned)e >= (unsigned)N) {
+          bad = true;
+          e = e < 0 ? 0 : N - 1;
+        }
+        id[j] = e;
+        atomicAdd(&mine[e], 1);
+      }
+    }
+    if (bad) misc[0] = 1;
+    lds_barrier();
+    // Wave 0: totals, each wave's exclusive prefix in place, the exclusive
+    // offsets over experts, and the experts of the tile's first and last slot.
+    if (wave == 0) {
+      const int q_last = q0 + nr - 1;
+      int carry = 0;
+      for (int e0 = 0; e0 < N; e0 += kWave) {
+        const int e = e0 + lane;
+        int tot = 0;
+        if (e < N) {
+#pragma unroll
+          for (int w = 0; w < kWavesW; ++w) {
+            const int c = wcnt[w * N + e];
+            wcnt[w * N + e] = tot;
+            tot += c;
+          }
+        }
+        int incl = tot;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+          const int t = __shfl_up(incl, off, kWave);
+          if (lane >= off) incl += t;
+        }
+        const int run = carry + incl - tot;
+        if (e < N) {
+          cnt[e] = run;
+          if (tile == 0) a.rt.offsets[e] = run;
+          if (run <= q0 && q0 < run + tot) misc[1] = e;
+          if (run <= q_last && q_last < run + tot) misc[2] = e;
+        }
+        carry += __shfl(incl, kWave - 1, kWave);
+      }
+      if (lane == 0) {
+        cnt[N] = a.M;
+        if (tile == 0) {
+          a.rt.offsets[N] = a.M;
+          *a.status = misc[0] ? BMOE_E_EXPERT : BMOE_OK;
         }
       }
-      int incl = tot;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int t = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += t;
-      }
-      const int run = carry + incl - tot;
-      if (e < N) {
-        cnt[e] = run;
-        if (tile == 0) a.rt.offsets[e] = run;
-        if (run <= q0 && q0 < run + tot) misc[1] = e;
-        if (run <= q_last && q_last < run + tot) misc[2] = e;
-      }
-      carry += __shfl(incl, kWave - 1, kWave);
     }
-    if (lane == 0) {
-      cnt[N] = a.M;
-      if (tile == 0) {
-        a.rt.offsets[N] = a.M;
-        *a.status = misc[0] ? BMOE_E_EXPERT : BMOE_OK;
-      }
-    }
-  }
-  lds_barrier();
+    lds_barrier();
   }
   const int e_first = misc[1], e_last = misc[2];
   // Both sides' angles of the two tables, in flight during the ranking.
@@ -579,37 +579,37 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
   // plus that expert's ids in earlier waves, earlier lanes of this wave and
   // earlier positions of this thread.
   if constexpr (ROUTE) {
-  for (int e = e_first; e <= e_last; ++e) {
-    if (cnt[e + 1] == cnt[e]) continue;  // uniform: no ids of e
-    const int w_lo = wcnt[wave * N + e];
-    const int w_hi = wave + 1 < kWavesW ? wcnt[(wave + 1) * N + e] : cnt[e + 1] - cnt[e];
-    if (w_hi <= q0 - cnt[e] || w_lo >= q0 + nr - cnt[e]) continue;  // uniform per wave
-    int below = 0;
+    for (int e = e_first; e <= e_last; ++e) {
+      if (cnt[e + 1] == cnt[e]) continue;  // uniform: no ids of e
+      const int w_lo = wcnt[wave * N + e];
+      const int w_hi = wave + 1 < kWavesW ? wcnt[(wave + 1) * N + e] : cnt[e + 1] - cnt[e];
+      if (w_hi <= q0 - cnt[e] || w_lo >= q0 + nr - cnt[e]) continue;  // uniform per wave
+      int below = 0;
 #pragma unroll
-    for (int j = 0; j < kIdsW; ++j) {
-      const uint64_t m = __ballot(j < nv && id[j] == e);
-      below += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-    }
-    int q = cnt[e] + w_lo + below - q0;
+      for (int j = 0; j < kIdsW; ++j) {
+        const uint64_t m = __ballot(j < nv && id[j] == e);
+        below += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      }
+      int q = cnt[e] + w_lo + below - q0;
 #pragma unroll
-    for (int j = 0; j < kIdsW; ++j) {
-      if (j < nv && id[j] == e) {
-        if ((unsigned)q < (unsigned)nr) {
-          sh_e[q] = e;
-          sh_r[q] = i0 + j;
+      for (int j = 0; j < kIdsW; ++j) {
+        if (j < nv && id[j] == e) {
+          if ((unsigned)q < (unsigned)nr) {
+            sh_e[q] = e;
+            sh_r[q] = i0 + j;
+          }
+          ++q;
         }
-        ++q;
       }
     }
-  }
-  lds_barrier();  // ranks are in; the routing scratch is dead from here on
-  if (tid < nr) {
-    const int r = sh_r[tid];
-    a.rt.perm[q0 + tid] = r;
-    a.rt.inv[r] = q0 + tid;
-    a.rt.slot_e[q0 + tid] = sh_e[tid];
-  }
+    lds_barrier();  // ranks are in; the routing scratch is dead from here on
+    if (tid < nr) {
+      const int r = sh_r[tid];
+      a.rt.perm[q0 + tid] = r;
+      a.rt.inv[r] = q0 + tid;
+      a.rt.slot_e[q0 + tid] = sh_e[tid];
+    }
   }
 
   // ---- this wave's rows: x, gates -----------------------------------------

@@ -157,12 +157,13 @@ bmoe_status bmoe_unpack_ternary_b3_timed(const uint8_t* packed3, int d, uint32_t
  * runs its k rows after the preparation launch: Z is rounded to the
  * activation type before the product, H stays fp32, and each gate-weighted
  * row is rounded to the activation type before the fp32 sum over j.
- * For bf16 with d = 256 or 512, T*k <= 8192 and N <= 512, one kernel does
- * the whole per-row computation, routing included (then the combine); it
- * evaluates the rotation coefficients on the hardware sine/cosine unit
- * (at most 4e-7 absolute error for angles up to 1000 in magnitude). Other
- * shapes compute them with sincosf in a preparation launch. Both are far
- * inside the bf16 tolerance, but the two are not bit-identical.
+ * For bf16 with d = 256 or 512 one kernel does the whole per-row
+ * computation (then the combine): with T*k <= 8192 and N <= 512 it routes
+ * its rows itself, otherwise it follows a preparation launch that only
+ * routes. It evaluates the rotation coefficients on the hardware sine/cosine
+ * unit (at most 4e-7 absolute error for angles up to 1000 in magnitude).
+ * Other shapes compute them with sincosf in a preparation launch. Both are
+ * far inside the bf16 tolerance, but the two are not bit-identical.
  */
 bmoe_status bmoe_forward(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,
                          const int32_t* ids, const float* gates, const float* theta,
