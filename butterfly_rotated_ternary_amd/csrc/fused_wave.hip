@@ -429,7 +429,10 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int rl = row_lane(lane);  // this lane's position in a butterfly row
   char* const pwl = pst + wave * C::PW_WAVE;  // this wave's substrate rows
-  const int tile = blockIdx.x;
+  // After prep, the last tiles (the many small experts of a skewed routing,
+  // which take the slower per-row coefficient paths) go first, so they do
+  // not form the last round of the grid.
+  const int tile = ROUTE ? (int)blockIdx.x : (int)(gridDim.x - 1 - blockIdx.x);
   const int q0 = tile * kSlots;
   const int nr = min(kSlots, a.M - q0);
   const int N = a.N;
