@@ -285,7 +285,10 @@ def test_identity_substrate_equal_angles(dtype):
                                      # 8192 routed rows, 512 experts
                                      (256, 64, 2, 4096), (512, 512, 1, 8192),
                                      # routed: top-3 and top-4, one expert
-                                     (256, 8, 3, 111), (512, 16, 4, 300), (512, 1, 1, 100)])
+                                     (256, 8, 3, 111), (512, 16, 4, 300), (512, 1, 1, 100),
+                                     # fused after prep, ragged, more tiles than
+                                     # workgroups (three or two per workgroup)
+                                     (256, 64, 3, 5555), (512, 600, 2, 9000)])
 def test_edge_shapes(d, N, k, T):
     inp = W.make_inputs("custom", d=d, N=N, k=k, T=T, seed=d + N, dtype="bf16")
     _announce(f"[edge] d={d} N={N} k={k} T={T}")
