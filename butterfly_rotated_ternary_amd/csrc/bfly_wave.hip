@@ -15,13 +15,14 @@
 //   layout Y: bits 0-2 in the lane, bits 7.. the low row-position bits,
 //             bits 3-6 the remaining row-position bits and the wave.
 // Stages 0-6 run in X (in the lane, then through DPP for lane distances 1,
-// 2, 4, 8), stages 7.. in Y (DPP for the first four; at d = 4096 stage 11
-// sits 16 lanes away and goes through v_permlane16_swap), so a row changes
-// layout once, through LDS. A DPP-fed multiply costs about two plain VALU
-// operations and a permlane swap about five, so the layouts keep every stage
-// but one off the swaps. The output side runs stages 0-6 in X, then 7.. in
-// Y; the input side (B^T: stages descending) the reverse. Rows are loaded
-// four ahead.
+// 2, 4, 8), stages 7.. in Y (DPP for the first four), so a row changes
+// layout once, through LDS. At d = 4096 layout Y keeps element bit 11 in the
+// lane instead of bit 2 (a lane holds elements 4g .. 4g+3 and 2048 + 4g ..
+// 2048 + 4g+3 of its row), so stage 11 is a rotation in registers too: no
+// stage needs a permlane swap, which costs about five plain VALU operations
+// against two for a DPP-fed multiply. The output side runs stages 0-6 in X,
+// then 7.. in Y; the input side (B^T: stages descending) the reverse. Rows
+// are loaded four ahead.
 #include "common.h"
 #include "kernels.h"
 
@@ -36,7 +37,8 @@ struct WB {
   static constexpr int L = 9 + LW;
   static constexpr int B = L - 7;                            // stages in layout Y
   static constexpr int NYD = B < 4 ? B : 4;                  // of them on DPP
-  static constexpr int NYS = B - NYD;                        // on a swap (d = 4096)
+  static constexpr int NYS = B - NYD;                        // in the lane (d = 4096)
+  static constexpr bool YG = NYS > 0;                        // Y holds 4-element groups
   static constexpr int P = D / 2;
   static constexpr int THREADS = 64 * W;
   static constexpr int PF = 4;                               // rows loaded ahead
@@ -51,9 +53,23 @@ struct WB {
     const int c = row_lane(l);
     return ((c & ((1 << B) - 1)) << 4) | (c >> B) | (w << (6 - B));
   }
+  // d = 4096, layout Y: 4-element group g (elements 4g .. 4g+3, registers
+  // 0-3; registers 4-7 hold group g + 512). Group bits: 0-1 from row-position
+  // bits 4-5, 2-4 the wave, 5-8 row-position bits 0-3 (element bits 7-10).
+  static __device__ __forceinline__ int group_y(int w, int l) {
+    const int c = row_lane(l);
+    return ((c >> 4) & 3) | (w << 2) | ((c & 15) << 5);
+  }
+  // Element held in register r of lane l in layout Y.
+  static __device__ __forceinline__ int elem_y(int w, int l, int r) {
+    if constexpr (YG) return ((r >> 2) << 11) | (group_y(w, l) << 2) | (r & 3);
+    else return (chunk_y(w, l) << 3) | r;
+  }
   // LDS slot of chunk c in each of the two 16-byte planes: any 16 lanes fall
   // on distinct 16-byte bank groups, in layout X (chunk bits 0-3 vary) and in
-  // layout Y (chunk bits 4-7 vary; at d = 1024 bits 4-6 and bit 0).
+  // layout Y (chunk bits 4-7 vary; at d = 1024 bits 4-6 and bit 0; at d =
+  // 4096 group g sits in plane g & 1 at chunk g >> 1, and 16 lanes vary
+  // chunk bits 4-7 too).
   static __device__ __forceinline__ int lds_pos(int c) {
     return c ^ ((c >> 4) & 15) ^ ((c & 1) << 3);
   }
@@ -67,8 +83,8 @@ struct Coef {
   float2 in[3][4];          // stages 0-2, in the lane: (cos, sin) per pair
   float2 dp[4][8];          // stages 3-6 (layout X, lane bit s - 3)
   float2 y[WB<D>::NYD][8];  // stages 7.. (layout Y, lane bit s - 7)
-  float2 sw[1][4];          // stage 11 at d = 4096 (lane bit 4): whole pairs
-                            // after a swap
+  float2 hi[1][4];          // stage 11 at d = 4096, in the lane (layout Y):
+                            // registers r and r + 4
 };
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left alone), visible to the
@@ -88,24 +104,21 @@ __device__ __forceinline__ void load_coef(Coef<D>& k, const float2* tab, int w, 
   // Recompute the (many) table offsets here rather than let the compiler
   // keep them live across the row loop: a reload is rare, registers are not.
   __asm__ volatile("" : "+v"(lane));
-  const int cx = C::chunk_x(w, lane), cy = C::chunk_y(w, lane);
+  const int cx = C::chunk_x(w, lane);
 #pragma unroll
   for (int t = 0; t < C::NYD; ++t) {
     const int s = 7 + t;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int i = (cy << 3) | j;
+      const int i = C::elem_y(w, lane, j);
       k.y[t][j] = signed_coef<TR>(tab[s * C::P + pair_index(i, s)], i, s);
     }
   }
   if constexpr (C::NYS > 0) {
-    // after the swap on lane bit 4, register pair (r, r + 1) holds the pair
-    // of this lane's element r (bit clear) or of the partner lane's element
-    // r + 1 (bit set)
-    const int s = 7 + C::NYD, bit = 16;
-    const int lower = (lane & bit) ? ((C::chunk_y(w, lane ^ bit) << 3) | 1) : (cy << 3);
+    // stage 11: register r (element bit 11 clear) pairs with register r + 4
+    const int s = 7 + C::NYD;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) k.sw[0][r] = tab[s * C::P + pair_index(lower + 2 * r, s)];
+    for (int r = 0; r < 4; ++r) k.hi[0][r] = tab[s * C::P + pair_index(C::elem_y(w, lane, r), s)];
   }
 #pragma unroll
   for (int s = 0; s < 3; ++s)
@@ -157,19 +170,6 @@ __device__ __forceinline__ void dpp_stage(float (&v)[8], const float2 (&c)[8]) {
   for (int j = 0; j < 8; ++j) v[j] = fmaf(c[j].x, v[j], c[j].y * lane_partner<M>(v[j]));
 }
 
-template <int M, bool TR>
-__device__ __forceinline__ void swap_stage(float (&v)[8], const float2 (&c)[4]) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float a = v[2 * r], b = v[2 * r + 1];
-    lane_swap<M>(a, b);
-    rot_pair<TR>(a, b, c[r]);
-    lane_swap<M>(a, b);
-    v[2 * r] = a;
-    v[2 * r + 1] = b;
-  }
-}
-
 // Stages 0-6 in layout X, ascending (output side) or descending (input side).
 template <bool TR, class K>
 __device__ __forceinline__ void stages_x(float (&v)[8], const K& k) {
@@ -197,7 +197,7 @@ template <int D, bool TR>
 __device__ __forceinline__ void stages_y(float (&v)[8], const Coef<D>& k) {
   constexpr int N = WB<D>::NYD;
   if constexpr (TR) {
-    if constexpr (WB<D>::NYS > 0) swap_stage<4, true>(v, k.sw[0]);
+    if constexpr (WB<D>::NYS > 0) inlane_stage<2, true>(v, k.hi[0]);
     if constexpr (N > 3) dpp_stage<3>(v, k.y[N > 3 ? 3 : 0]);
     if constexpr (N > 2) dpp_stage<2>(v, k.y[N > 2 ? 2 : 0]);
     dpp_stage<1>(v, k.y[1]);
@@ -207,7 +207,7 @@ __device__ __forceinline__ void stages_y(float (&v)[8], const Coef<D>& k) {
     dpp_stage<1>(v, k.y[1]);
     if constexpr (N > 2) dpp_stage<2>(v, k.y[N > 2 ? 2 : 0]);
     if constexpr (N > 3) dpp_stage<3>(v, k.y[N > 3 ? 3 : 0]);
-    if constexpr (WB<D>::NYS > 0) swap_stage<4, false>(v, k.sw[0]);
+    if constexpr (WB<D>::NYS > 0) inlane_stage<2, false>(v, k.hi[0]);
   }
 }
 
@@ -256,8 +256,31 @@ void bfly_wave_kernel(WaveBflyArgs p) {
   const int cin = IN_SIDE ? C::chunk_y(w, lane) : C::chunk_x(w, lane);
   const int cout = IN_SIDE ? C::chunk_x(w, lane) : C::chunk_y(w, lane);
   const int wpos = C::lds_pos(cin), rpos = C::lds_pos(cout);
+  // d = 4096, layout Y: groups gy and gy + 512, in plane gy & 1 at slots
+  // ya and yb.
+  const int gy = C::group_y(w, lane), py = gy & 1;
+  const int ya = C::lds_pos(gy >> 1), yb = C::lds_pos((gy >> 1) + 256);
   auto load_row = [&](int i) -> u32x4 {
-    return *reinterpret_cast<const u32x4*>(p.src + (size_t)row_meta(ms, i) * D + cin * 8);
+    const uint16_t* row = p.src + (size_t)row_meta(ms, i) * D;
+    if constexpr (IN_SIDE && C::YG) {
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(row + 4 * gy);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 2048 + 4 * gy);
+      u32x4 x;
+      x[0] = lo[0]; x[1] = lo[1]; x[2] = hi[0]; x[3] = hi[1];
+      return x;
+    } else {
+      return *reinterpret_cast<const u32x4*>(row + cin * 8);
+    }
+  };
+  // The first layout's values of a row into LDS buffer b, row q.
+  auto put = [&](int b, int q, const float (&v)[8]) {
+    if constexpr (IN_SIDE && C::YG) {
+      tb[b][q][py][ya] = make_float4(v[0], v[1], v[2], v[3]);
+      tb[b][q][py][yb] = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+      tb[b][q][0][wpos] = make_float4(v[0], v[1], v[2], v[3]);
+      tb[b][q][1][wpos] = make_float4(v[4], v[5], v[6], v[7]);
+    }
   };
 
   // Runs of rows with one expert: load the run's first rows and the expert's
@@ -307,8 +330,7 @@ void bfly_wave_kernel(WaveBflyArgs p) {
     for (int q = 0; q < 2; ++q) {
       take(ring[q], va[q]);
       first_layout(va[q], cf);
-      tb[0][q][0][wpos] = make_float4(va[q][0], va[q][1], va[q][2], va[q][3]);
-      tb[0][q][1][wpos] = make_float4(va[q][4], va[q][5], va[q][6], va[q][7]);
+      put(0, q, va[q]);
       ring[q] = load_row(row(C::PF + q));
     }
     for (int r0 = 0; r0 < end - i; r0 += C::PF) {
@@ -319,7 +341,14 @@ void bfly_wave_kernel(WaveBflyArgs p) {
         lds_barrier();
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const float4 a = tb[h & 1][q][0][rpos], b = tb[h & 1][q][1][rpos];
+          float4 a, b;
+          if constexpr (!IN_SIDE && C::YG) {
+            a = tb[h & 1][q][py][ya];
+            b = tb[h & 1][q][py][yb];
+          } else {
+            a = tb[h & 1][q][0][rpos];
+            b = tb[h & 1][q][1][rpos];
+          }
           vb[q][0] = a.x; vb[q][1] = a.y; vb[q][2] = a.z; vb[q][3] = a.w;
           vb[q][4] = b.x; vb[q][5] = b.y; vb[q][6] = b.z; vb[q][7] = b.w;
         }
@@ -327,8 +356,7 @@ void bfly_wave_kernel(WaveBflyArgs p) {
         for (int q = 0; q < 2; ++q) {
           take(ring[sn + q], va[q]);
           first_layout(va[q], cf);
-          tb[(h + 1) & 1][q][0][wpos] = make_float4(va[q][0], va[q][1], va[q][2], va[q][3]);
-          tb[(h + 1) & 1][q][1][wpos] = make_float4(va[q][4], va[q][5], va[q][6], va[q][7]);
+          put((h + 1) & 1, q, va[q]);
           ring[sn + q] = load_row(row(pr + 2 + C::PF + q));
         }
 #pragma unroll
@@ -339,7 +367,15 @@ void bfly_wave_kernel(WaveBflyArgs p) {
           u32x4 o;
 #pragma unroll
           for (int c = 0; c < 4; ++c) o[c] = pack_bf16x2(vb[q][2 * c] * g, vb[q][2 * c + 1] * g);
-          *reinterpret_cast<u32x4*>(p.dst + (size_t)row_meta(md, r) * D + cout * 8) = o;
+          uint16_t* drow = p.dst + (size_t)row_meta(md, r) * D;
+          if constexpr (!IN_SIDE && C::YG) {
+            u32x2 lo, hi;
+            lo[0] = o[0]; lo[1] = o[1]; hi[0] = o[2]; hi[1] = o[3];
+            *reinterpret_cast<u32x2*>(drow + 4 * gy) = lo;
+            *reinterpret_cast<u32x2*>(drow + 2048 + 4 * gy) = hi;
+          } else {
+            *reinterpret_cast<u32x4*>(drow + cout * 8) = o;
+          }
         }
       }
     }
