@@ -17,6 +17,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
+constexpr int kTrig = 8;  // angles per thread in the cos/sin role
 
 struct PrepParams {
   const int32_t* ids;
@@ -147,16 +148,29 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
   }
   if ((int)blockIdx.x >= p.n_route_blocks) {
     // ---- cos/sin tables -------------------------------------------------
+    // A thread's angles are kTrig grid strides apart; all of their loads are
+    // issued before the first sincosf, so a wave waits on memory once per
+    // kTrig angles rather than once per angle.
     const long long total = p.phi ? 2 * p.n_ang : p.n_ang;  // no phi: input side only
     const long long stride = (long long)p.n_trig_blocks * kThreads;
-    for (long long i = (long long)(blockIdx.x - p.n_route_blocks) * kThreads + threadIdx.x;
-         i < total; i += stride) {
-      const bool out_side = i >= p.n_ang;
-      const long long j = out_side ? i - p.n_ang : i;
-      const float a = out_side ? p.phi[j] : p.theta[j];
-      float s, c;
-      sincosf(a, &s, &c);
-      (out_side ? p.cs_out : p.cs_in)[j] = make_float2(c, s);
+    for (long long i0 = (long long)(blockIdx.x - p.n_route_blocks) * kThreads + threadIdx.x;
+         i0 < total; i0 += kTrig * stride) {
+      float a[kTrig];
+#pragma unroll
+      for (int u = 0; u < kTrig; ++u) {
+        const long long i = i0 + u * stride;
+        a[u] = i < total ? (i >= p.n_ang ? p.phi[i - p.n_ang] : p.theta[i]) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kTrig; ++u) {
+        const long long i = i0 + u * stride;
+        if (i < total) {
+          float s, c;
+          sincosf(a[u], &s, &c);
+          if (i >= p.n_ang) p.cs_out[i - p.n_ang] = make_float2(c, s);
+          else p.cs_in[i] = make_float2(c, s);
+        }
+      }
     }
     return;
   }
@@ -314,7 +328,7 @@ hipError_t launch_prep(const int32_t* ids, int M, int N, const float* theta, con
   p.cs_in = cs_in;
   p.cs_out = cs_out;
   p.n_ang = (long long)N * L * (d / 2);
-  long long trig_blocks = ((phi ? 2 : 1) * p.n_ang + kThreads * 8 - 1) / (kThreads * 8);
+  long long trig_blocks = ((phi ? 2 : 1) * p.n_ang + kThreads * kTrig - 1) / (kThreads * kTrig);
   if (trig_blocks > 65536) trig_blocks = 65536;
   if (!theta) trig_blocks = 0;  // no tables wanted
   p.n_trig_blocks = (int)trig_blocks;
