@@ -159,6 +159,20 @@ __device__ __forceinline__ float lane_partner(float v) {
   return __int_as_float(r);
 }
 
+// Inclusive prefix sum of v over the 64 lanes, in lane order, through DPP
+// (no LDS round trip): shifts by 1, 2, 4 and 8 within each row of 16 lanes,
+// then the last lane of row 0 (and 2) into row 1 (and 3), and lane 31 into
+// rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false); // row_bcast:15, rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false); // row_bcast:31, rows 2, 3
+  return v;
+}
+
 // Swap half of register a with half of register b across lane bit M (4 or
 // 5, equal in row-lane order): afterwards lanes with that bit clear hold (a, partner of a), lanes with
 // it set hold (partner of b, b). Applying it twice restores both.

@@ -531,19 +531,18 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
         const int e = e0 + lane;
         int tot = 0;
         if (e < N) {
+          // all eight counts read before any is overwritten, so the reads go
+          // out together
+          int cw[kWavesW];
+#pragma unroll
+          for (int w = 0; w < kWavesW; ++w) cw[w] = wcnt[w * N + e];
 #pragma unroll
           for (int w = 0; w < kWavesW; ++w) {
-            const int c = wcnt[w * N + e];
             wcnt[w * N + e] = tot;
-            tot += c;
+            tot += cw[w];
           }
         }
-        int incl = tot;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-          const int t = __shfl_up(incl, off, kWave);
-          if (lane >= off) incl += t;
-        }
+        const int incl = wave_incl_scan(tot);
         const int run = carry + incl - tot;
         if (e < N) {
           cnt[e] = run;
@@ -551,7 +550,7 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
           if (run <= q0 && q0 < run + tot) misc[1] = e;
           if (run <= q_last && q_last < run + tot) misc[2] = e;
         }
-        carry += __shfl(incl, kWave - 1, kWave);
+        carry += __builtin_amdgcn_readlane(incl, kWave - 1);
       }
       if (lane == 0) {
         cnt[N] = a.M;

@@ -17,7 +17,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kTrig = 8;  // angles per thread in the cos/sin role
+constexpr int kTrig = 4;  // angles per thread in the cos/sin role
 
 struct PrepParams {
   const int32_t* ids;
@@ -90,12 +90,7 @@ __device__ __forceinline__ int clamp_expert(int e, int N, bool& bad) {
 // Exclusive prefix sum of one int per thread over the 256-thread block.
 __device__ int block_exclusive_scan(int v, int* scratch) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    int u = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += u;
-  }
+  const int incl = wave_incl_scan(v);
   if (lane == kWave - 1) scratch[wave] = incl;
   __syncthreads();
   int before = 0;
