@@ -87,9 +87,6 @@ struct Coef {
                             // registers r and r + 4
 };
 
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left alone), visible to the
-// compiler's own wait-count tracking.
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <bool TR>
 __device__ __forceinline__ float2 signed_coef(float2 c, int i, int s) {

@@ -51,6 +51,11 @@ __host__ __device__ __forceinline__ float substrate_scale(float alpha) { return 
 // global->LDS loads still in flight; code that needs their data waits for
 // them explicitly (vmcnt) first. The memory clobber keeps the compiler from
 // moving memory accesses across it.
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left alone), visible to the
+// compiler's own wait-count tracking: registers loaded before it need no
+// further wait afterwards, on any path.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ void lds_barrier() {
   // The wait goes through the builtin too, so the compiler's own wait-count
   // tracking sees that every LDS operation issued before the barrier has

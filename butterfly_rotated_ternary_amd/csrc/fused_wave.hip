@@ -506,6 +506,12 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
       sh_r[tid] = 0;
     }
     lds_barrier();
+    // The histogram needs the ids, and everything issued before them lands
+    // first anyway. Waiting here visibly to the compiler keeps it from
+    // waiting again at the ranking (each histogram add sits in its own
+    // branch), where the angle loads issued in between would be waited for
+    // too instead of landing during it.
+    wait_vm_all();
     bool bad = false;
     int* const mine = wcnt + wave * N;
 #pragma unroll
