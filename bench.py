@@ -134,6 +134,9 @@ def backward_work(name, act_bytes, T, d, N, k):
         return w
     if name in ("bfly_in_kernel", "gemm_kernel", "combine_kernel"):
         return kernel_work(name, act_bytes, T, d, N, k)
+    if name == "fused_wave_kernel":         # d = 256, 512: Z and H recomputed in one launch
+        b = T * d * act_bytes + 2 * M * d * act_bytes + d * d // 4 + A * 4 + 2 * routing
+        return {"bytes": b, "mfma_flops": 2 * M * d * d, "valu_flops": M * L * (d // 2) * 6}
     if name == "gemm_t_kernel":
         return kernel_work("gemm_kernel", act_bytes, T, d, N, k)
     if name == "dw_kernel":

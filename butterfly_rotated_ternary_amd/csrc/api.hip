@@ -315,8 +315,10 @@ bmoe_status forward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, cons
     }
     return t;
   };
-  const bool fused = !keep && fused_supported(dt, d);
-  const bool routed = fused && fused_wave_routes(dt, M, d, n_experts);
+  // keep: the fused kernel also writes Z and H (d = 256, 512), or the
+  // unfused path leaves them in the workspace.
+  const bool fused = fused_supported(dt, d);
+  const bool routed = !keep && fused && fused_wave_routes(dt, M, d, n_experts);
   const int wt_block = gemm_tiled_w_block(dt, M, d);
   uint32_t* wt = wt_block ? reinterpret_cast<uint32_t*>(base + l.wt) : nullptr;
   BwdSetup bs;  // keep: the backward's tiles and W_base^T, for bmoe_backward_kept
@@ -338,8 +340,10 @@ bmoe_status forward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, cons
     return BMOE_OK;
   }
   // The fused kernel after prep evaluates its own tiles' tables from the
-  // angles: prep only routes.
-  if (launch_prep(ids, M, n_experts, fused ? nullptr : theta, fused ? nullptr : phi, d, rt,
+  // angles: prep only routes, or with keep also writes the tables the
+  // backward reads.
+  const bool tables = !fused || keep;
+  if (launch_prep(ids, M, n_experts, tables ? theta : nullptr, tables ? phi : nullptr, d, rt,
                   cs_in, cs_out, status, w_packed, wt, wt_block, s, timing(), bs) !=
       hipSuccess)
     return BMOE_E_HIP;
@@ -351,7 +355,8 @@ bmoe_status forward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, cons
                : BMOE_E_HIP;
   }
   if (fused) {
-    if (launch_fused_wave_prepped(M, d, k, x, gates, theta, phi, w_packed, alpha, u, rt, s,
+    if (launch_fused_wave_prepped(M, d, k, x, gates, theta, phi, w_packed, alpha, u,
+                                  keep ? z : nullptr, keep ? h : nullptr, rt, s,
                                   timing()) != hipSuccess)
       return BMOE_E_HIP;
   } else {
@@ -586,8 +591,15 @@ bmoe_status backward_impl(bmoe_dtype dt, int T, int d, int n_experts, int k, con
                     l.wt_block, s, timing(), bs) != hipSuccess)
       return BMOE_E_HIP;
   }
+  // d = 256, 512 (bf16): Z and H from the fused kernel, as bmoe_forward_keep
+  // writes them; otherwise the input-side butterfly and the product.
+  const bool fused_zh = fused_supported(dt, d);
   if (kept) {
-    if (!skip() || !skip()) return BMOE_E_HIP;
+    if (!skip() || (!fused_zh && !skip())) return BMOE_E_HIP;
+  } else if (fused_zh) {
+    if (launch_fused_wave_prepped(M, d, k, x, gates, theta, phi, w_packed, alpha, nullptr, z, h,
+                                  rt, s, timing()) != hipSuccess)
+      return BMOE_E_HIP;
   } else {
     if (launch_bfly_in(dt, M, d, k, x, rt, cs_in, z, s, timing()) != hipSuccess) return BMOE_E_HIP;
     if (launch_gemm(dt, M, d, z, w_packed, wt, alpha, h, s, timing()) != hipSuccess)
@@ -670,7 +682,10 @@ namespace {
 const char* const kBackwardNames[] = {
     "prep_kernel",         "bfly_in_kernel",      "gemm_kernel",        "bfly_bwd_out_kernel",
     "dw_kernel",           "gemm_t_kernel",       "bfly_bwd_in_kernel", "finish_kernel"};
-constexpr int kBackwardLaunches = sizeof(kBackwardNames) / sizeof(kBackwardNames[0]);
+// d = 256, 512 (bf16): Z and H recomputed by the fused kernel in one launch.
+const char* const kBackwardNamesFused[] = {
+    "prep_kernel",         "fused_wave_kernel",   "bfly_bwd_out_kernel", "dw_kernel",
+    "gemm_t_kernel",       "bfly_bwd_in_kernel",  "finish_kernel"};
 }  // namespace
 
 size_t bmoe_rotate_in_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts, int k) {
@@ -765,12 +780,12 @@ bmoe_status bmoe_router(bmoe_dtype dt, int T, int d, int n_experts, int k, const
 
 int bmoe_backward_kernel_count(bmoe_dtype dt, int T, int d, int n_experts, int k) {
   if (!bwd_shape_ok(dt, T, d, n_experts, k) || T == 0) return 0;
-  return kBackwardLaunches;
+  return fused_supported(dt, d) ? 7 : 8;
 }
 
 const char* bmoe_backward_kernel_name(bmoe_dtype dt, int T, int d, int n_experts, int k, int i) {
   if (i < 0 || i >= bmoe_backward_kernel_count(dt, T, d, n_experts, k)) return "";
-  return kBackwardNames[i];
+  return fused_supported(dt, d) ? kBackwardNamesFused[i] : kBackwardNames[i];
 }
 
 const char* bmoe_status_str(bmoe_status s) {

@@ -106,9 +106,15 @@ struct WaveArgs {
   const uint32_t* wp;
   float alpha;  // scale for the +-2 substrate values
   uint16_t* u;
+  uint16_t* z;  // kZH: Z and H rows, bf16 [M][D] in sorted order
+  uint16_t* h;
   RouteTables rt;
   int32_t* status;
 };
+
+// What a launch writes: g * U rows (the forward), Z and H rows (kept for,
+// or recomputed by, the backward), or both.
+constexpr int kU = 1, kZH = 2;
 
 // Which pairs a lane needs in stage s, and where a table keeps them.
 //   in-lane stage (s < RB): the VPL/2 pairs (VPL/2) lane + u;
@@ -402,9 +408,12 @@ __device__ __forceinline__ void write_table_entry(int i, float ang, float2* tab,
 
 // ROUTE: the kernel routes its own rows (reads the ids, writes the routing
 // tables and the status word); otherwise the rows' experts and routed
-// indices come from the preparation kernel's tables (any M and N).
-template <int D, bool ROUTE>
+// indices come from the preparation kernel's tables (any M and N). OUT: kU,
+// kZH or both (kZH only after prep; without kU the output side is skipped).
+template <int D, bool ROUTE, int OUT = kU>
 __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
+  static_assert(!ROUTE || OUT == kU, "a routing launch writes U only");
+  constexpr bool kOut = (OUT & kU) != 0;
   using C = WCfg<D>;
   constexpr int VPL = C::VPL;
   __shared__ __attribute__((aligned(1024))) char lds[C::A_BYTES];
@@ -580,7 +589,7 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
     if (ex == 0 || two) {
       const size_t src = (size_t)(ex ? e_last : e_first) * C::TBL + tix[i];
       th[i] = a.theta[src];
-      ph[i] = a.phi[src];
+      if constexpr (kOut) ph[i] = a.phi[src];
     }
   }
   // Stable ranks of the tile's experts: an id's slot is its expert's offset,
@@ -637,7 +646,7 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
       const uint2 t = *reinterpret_cast<const uint2*>(xr);
       xraw[i] = make_uint4(t.x, t.y, 0u, 0u);
     }
-    gw[i] = a.gates[rw[i]];
+    gw[i] = kOut ? a.gates[rw[i]] : 0.f;
   }
   // Input-side tables of the tile's first and last experts (the output
   // side's are computed during the product).
@@ -658,24 +667,36 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
   }
   butterfly_rows<D, true>(v, ew, e_first, e_last, tin_first, tin_last, a.theta, rl);
   // Row q's 16-byte chunk c sits at chunk c ^ (q & 15) (conflict-free A reads).
+  uint4 zpk[kRowsW];  // this lane's bf16 Z values of each row
 #pragma unroll
   for (int i = 0; i < kRowsW; ++i) {
     const int q = wave * kRowsW + i;
     const int e0 = VPL * rl;
     char* dst = zt + q * (2 * D) + 16 * ((e0 / 8) ^ (q & 15)) + 2 * (e0 % 8);
     if constexpr (VPL == 8) {
-      *reinterpret_cast<uint4*>(dst) =
-          make_uint4(pack_bf16x2(v[i][0], v[i][1]), pack_bf16x2(v[i][2], v[i][3]),
-                     pack_bf16x2(v[i][4], v[i][5]), pack_bf16x2(v[i][6], v[i][7]));
+      zpk[i] = make_uint4(pack_bf16x2(v[i][0], v[i][1]), pack_bf16x2(v[i][2], v[i][3]),
+                          pack_bf16x2(v[i][4], v[i][5]), pack_bf16x2(v[i][6], v[i][7]));
+      *reinterpret_cast<uint4*>(dst) = zpk[i];
     } else {
-      *reinterpret_cast<uint2*>(dst) =
-          make_uint2(pack_bf16x2(v[i][0], v[i][1]), pack_bf16x2(v[i][2], v[i][3]));
+      zpk[i] = make_uint4(pack_bf16x2(v[i][0], v[i][1]), pack_bf16x2(v[i][2], v[i][3]), 0u, 0u);
+      *reinterpret_cast<uint2*>(dst) = make_uint2(zpk[i].x, zpk[i].y);
     }
   }
   // This wave's substrate rows have landed (its own copies only: no other
   // wave reads them), and every wave's A rows are in.
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();
+  if constexpr ((OUT & kZH) != 0) {
+    // Z rows for the backward, stored while the product runs.
+#pragma unroll
+    for (int i = 0; i < kRowsW; ++i) {
+      const int q = wave * kRowsW + i;
+      if (q >= nr) continue;
+      uint16_t* zg = a.z + (size_t)(q0 + q) * D + VPL * rl;
+      if constexpr (VPL == 8) *reinterpret_cast<uint4*>(zg) = zpk[i];
+      else *reinterpret_cast<uint2*>(zg) = make_uint2(zpk[i].x, zpk[i].y);
+    }
+  }
 
   // ---- substrate product: wave w computes all 32 rows x columns
   // [w * WN, (w + 1) * WN) on v_mfma_f32_32x32x16_bf16.
@@ -712,7 +733,9 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
     }
     // One entry per K-step: VALU work beside the matrix cores (no one reads
     // this region before the barrier that follows the H rows).
-    if (ks < NTB) write_table_entry<D>(ks, ph[ks], tout, two, wv, lane);
+    if constexpr (kOut) {
+      if (ks < NTB) write_table_entry<D>(ks, ph[ks], tout, two, wv, lane);
+    }
   }
   lds_barrier();  // every wave is done with Z and P, which the H rows reuse
   // alpha * H -> fp32 rows (32x32 block layout: lane l, register r -> row
@@ -742,6 +765,24 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
       v[i][r + 3] = t.w;
     }
   }
+  if constexpr ((OUT & kZH) != 0) {
+    // H rows (alpha * the product, rounded to bf16) for the backward.
+#pragma unroll
+    for (int i = 0; i < kRowsW; ++i) {
+      const int q = wave * kRowsW + i;
+      if (q >= nr) continue;
+      uint16_t* hg = a.h + (size_t)(q0 + q) * D + VPL * rl;
+      if constexpr (VPL == 8) {
+        *reinterpret_cast<uint4*>(hg) =
+            make_uint4(pack_bf16x2(v[i][0], v[i][1]), pack_bf16x2(v[i][2], v[i][3]),
+                       pack_bf16x2(v[i][4], v[i][5]), pack_bf16x2(v[i][6], v[i][7]));
+      } else {
+        *reinterpret_cast<uint2*>(hg) =
+            make_uint2(pack_bf16x2(v[i][0], v[i][1]), pack_bf16x2(v[i][2], v[i][3]));
+      }
+    }
+  }
+  if constexpr (!kOut) return;
   butterfly_rows<D, false>(v, ew, e_first, e_last, tout_first, tout_last, a.phi, rl);
 #pragma unroll
   for (int i = 0; i < kRowsW; ++i) {
@@ -760,9 +801,9 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
   }
 }
 
-template <int D, bool ROUTE>
+template <int D, bool ROUTE, int OUT = kU>
 hipError_t launch_w(const WaveArgs& a, hipStream_t s, const KernelTiming& t) {
-  return launch_kernel(fused_wave_kernel<D, ROUTE>, dim3((a.M + kSlots - 1) / kSlots),
+  return launch_kernel(fused_wave_kernel<D, ROUTE, OUT>, dim3((a.M + kSlots - 1) / kSlots),
                        dim3(kThreadsW), 0, s, t, a);
 }
 
@@ -804,9 +845,12 @@ hipError_t launch_fused_wave(int M, int d, int k, int N, const void* x, const in
 
 hipError_t launch_fused_wave_prepped(int M, int d, int k, const void* x, const float* gates,
                                      const float* theta, const float* phi, const uint32_t* wp,
-                                     float alpha, void* u, const RouteTables& rt, hipStream_t s,
+                                     float alpha, void* u, void* z, void* h,
+                                     const RouteTables& rt, hipStream_t s,
                                      const KernelTiming& t) {
   if (M <= 0) return hipSuccess;
+  if (!u && !(z && h)) return hipErrorInvalidValue;
+  if (!z != !h) return hipErrorInvalidValue;
   WaveArgs a{};
   a.M = M;
   a.k = k;
@@ -817,10 +861,17 @@ hipError_t launch_fused_wave_prepped(int M, int d, int k, const void* x, const f
   a.wp = wp;
   a.alpha = substrate_scale(alpha);
   a.u = static_cast<uint16_t*>(u);
+  a.z = static_cast<uint16_t*>(z);
+  a.h = static_cast<uint16_t*>(h);
   a.rt = rt;
-  switch (d) {
-    case 256: return launch_w<256, false>(a, s, t);
-    case 512: return launch_w<512, false>(a, s, t);
+  const int out = (u ? kU : 0) | (z ? kZH : 0);
+  switch (d * 4 + out) {
+    case 256 * 4 + kU: return launch_w<256, false, kU>(a, s, t);
+    case 256 * 4 + kZH: return launch_w<256, false, kZH>(a, s, t);
+    case 256 * 4 + (kU | kZH): return launch_w<256, false, kU | kZH>(a, s, t);
+    case 512 * 4 + kU: return launch_w<512, false, kU>(a, s, t);
+    case 512 * 4 + kZH: return launch_w<512, false, kZH>(a, s, t);
+    case 512 * 4 + (kU | kZH): return launch_w<512, false, kU | kZH>(a, s, t);
   }
   return hipErrorInvalidValue;
 }

@@ -71,9 +71,13 @@ int gemm_tiled_w_block(bmoe_dtype dt, int M, int d);
 bool fused_wave_routes(bmoe_dtype dt, int M, int d, int N);
 // The same kernel after the preparation launch (any M and N): the rows'
 // experts and routed indices from rt (perm, slot_e), nothing of rt written.
+// Writes the g * U rows to u, and/or (z and h both non-NULL) the bf16 Z rows
+// and H = alpha * Z W_base^T rows in sorted order, as the backward reads
+// them; with u NULL the output side is skipped.
 hipError_t launch_fused_wave_prepped(int M, int d, int k, const void* x, const float* gates,
                                      const float* theta, const float* phi, const uint32_t* wp,
-                                     float alpha, void* u, const RouteTables& rt, hipStream_t s,
+                                     float alpha, void* u, void* z, void* h,
+                                     const RouteTables& rt, hipStream_t s,
                                      const KernelTiming& t = {});
 hipError_t launch_fused_wave(int M, int d, int k, int N, const void* x, const int32_t* ids,
                              const float* gates, const float* theta, const float* phi,

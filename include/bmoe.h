@@ -300,12 +300,15 @@ bmoe_status bmoe_backward_timed(bmoe_dtype dt, int T, int d, int n_experts, int 
 
 /*
  * Forward that keeps its intermediates for the backward (a training step):
- * as bmoe_forward, but always on the unfused path, so that after the call
- * the workspace holds the routing tables, both cos/sin tables, Z and H.
- * bmoe_backward_kept then reads them instead of recomputing the forward.
- * No route_out (the tables stay in the workspace). ws: at least
- * bmoe_forward_keep_workspace_bytes(). y is identical to the unfused
- * forward's.
+ * as bmoe_forward, but after the call the workspace holds the routing
+ * tables, both cos/sin tables, Z and H (bf16 d = 256, 512: the fused kernel
+ * after the preparation launch writes Z and H beside its U rows; other
+ * shapes: the unfused path). bmoe_backward_kept then reads them instead of
+ * recomputing the forward; bmoe_backward recomputes them with the same
+ * kernels, so the gradients of the two are bit-identical. No route_out (the
+ * tables stay in the workspace). ws: at least
+ * bmoe_forward_keep_workspace_bytes(). y is that of bmoe_forward up to the
+ * rounding of the path taken (the same fused or unfused kernels).
  */
 size_t bmoe_forward_keep_workspace_bytes(bmoe_dtype dt, int T, int d, int n_experts, int k);
 bmoe_status bmoe_forward_keep(bmoe_dtype dt, int T, int d, int n_experts, int k, const void* x,

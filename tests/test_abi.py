@@ -145,14 +145,23 @@ def test_forward_launch_table():
 
 def test_backward_launch_table_and_validation():
     bf = bmoe.BMOE_BF16
-    names = [bmoe.bmoe_backward_kernel_name(bf, 64, 512, 8, 2, i)
-             for i in range(bmoe.bmoe_backward_kernel_count(bf, 64, 512, 8, 2))]
-    assert len(names) == 8 and len(set(names)) == 8
-    assert "bfly_bwd_out_kernel" in names and "gemm_t_kernel" in names
-    assert names[0] == "prep_kernel" and names[-1] == "finish_kernel"
+    def names(dt, d):
+        return [bmoe.bmoe_backward_kernel_name(dt, 64, d, 8, 2, i)
+                for i in range(bmoe.bmoe_backward_kernel_count(dt, 64, d, 8, 2))]
+    # bf16 d = 256, 512: Z and H recomputed by the fused kernel in one launch
+    fused = names(bf, 512)
+    assert fused == names(bf, 256)
+    assert fused == ["prep_kernel", "fused_wave_kernel", "bfly_bwd_out_kernel", "dw_kernel",
+                     "gemm_t_kernel", "bfly_bwd_in_kernel", "finish_kernel"]
+    for other in (names(bf, 1024), names(bmoe.BMOE_F32, 512), names(bf, 128)):
+        assert len(other) == 8 and len(set(other)) == 8
+        assert other[1:3] == ["bfly_in_kernel", "gemm_kernel"]
+        assert "bfly_bwd_out_kernel" in other and "gemm_t_kernel" in other
+        assert other[0] == "prep_kernel" and other[-1] == "finish_kernel"
     assert bmoe.bmoe_backward_kernel_count(bf, 64, 8192, 8, 2) == 0   # d > 4096
     assert bmoe.bmoe_backward_kernel_count(bf, 0, 512, 8, 2) == 0
-    assert bmoe.bmoe_backward_kernel_name(bf, 64, 512, 8, 2, 8) == ""
+    assert bmoe.bmoe_backward_kernel_name(bf, 64, 512, 8, 2, 7) == ""
+    assert bmoe.bmoe_backward_kernel_name(bf, 64, 1024, 8, 2, 8) == ""
     assert bmoe.bmoe_backward_workspace_bytes(bf, 64, 8192, 8, 2) == 0
     assert bmoe.bmoe_backward_workspace_bytes(bf, 64, 4096, 8, 2) > 0
     lib = bmoe.lib()

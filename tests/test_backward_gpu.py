@@ -222,12 +222,16 @@ def test_backward_empty_batch_is_a_noop():
 
 @pytest.mark.parametrize("name,T", [("tiny_d64_e8_top2_f32", 200), ("d512_e64_top2_bf16", 301),
                                     ("d2048_e64_top2_outliers_bf16", 90),
-                                    ("d4096_e256_top4_bf16", 30)])
+                                    ("d4096_e256_top4_bf16", 30), ("custom_d256", 157)])
 def test_backward_after_kept_forward_is_bit_identical(name, T):
     """bmoe_forward_keep + bmoe_backward_kept gives exactly bmoe_backward's
     gradients (same kernels on the same inputs), and the kept forward's y
-    matches the oracle."""
-    inp = W.make_inputs(name, T=T)
+    matches the oracle. At d = 256 and 512 (bf16) both take Z and H from the
+    fused kernel; the other shapes from the unfused path."""
+    if name == "custom_d256":
+        inp = W.make_inputs("custom", d=256, N=12, k=3, T=T, seed=256, dtype="bf16")
+    else:
+        inp = W.make_inputs(name, T=T)
     print(f"[kept] {name} T={T}", flush=True)
     dev = to_device(inp)
     dy = torch.randn(inp.T, inp.d, device="cuda").to(dev["x"].dtype)
