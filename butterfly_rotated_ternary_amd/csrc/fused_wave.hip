@@ -106,10 +106,10 @@ struct WaveArgs {
   const uint32_t* wp;
   float alpha;  // scale for the +-2 substrate values
   uint16_t* u;
-  uint16_t* z;  // kZH: Z and H rows, bf16 [M][D] in sorted order
-  uint16_t* h;
   RouteTables rt;
   int32_t* status;
+  uint16_t* z;  // kZH: Z and H rows, bf16 [M][D] in sorted order
+  uint16_t* h;
 };
 
 // What a launch writes: g * U rows (the forward), Z and H rows (kept for,
