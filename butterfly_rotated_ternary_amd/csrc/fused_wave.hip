@@ -160,26 +160,42 @@ __host__ __device__ constexpr int table_pair(int s, int k) {
   return pair_of<D>(s, f % 64, 2 * (f / 64) + h);
 }
 
-// Angle index (stage * D/2 + pair) of every table position, fixed at
-// compile time; each thread reads its few entries at the start of the kernel.
+// Table position of every pair (the inverse of table_pair), fixed at compile
+// time: pos[stage * D/2 + pair]. A thread that builds table entries reads the
+// angles of four consecutive pairs with one 16-byte load and the positions
+// of those four pairs with one 8-byte load, both coalesced across the wave.
 template <int D>
-struct TabIdx {
-  uint16_t v[WCfg<D>::TBL];
+struct TabPos {
+  alignas(16) uint16_t v[WCfg<D>::TBL];
 };
 template <int D>
-constexpr TabIdx<D> make_tab_idx() {
-  TabIdx<D> t{};
+constexpr TabPos<D> make_tab_pos() {
+  TabPos<D> t{};
   for (int s = 0; s < WCfg<D>::L; ++s)
     for (int k = 0; k < WCfg<D>::P; ++k)
-      t.v[s * WCfg<D>::P + k] = (uint16_t)(s * WCfg<D>::P + table_pair<D>(s, k));
+      t.v[s * WCfg<D>::P + table_pair<D>(s, k)] = (uint16_t)k;
   return t;
 }
-__device__ constexpr TabIdx<256> kTabIdx256 = make_tab_idx<256>();
-__device__ constexpr TabIdx<512> kTabIdx512 = make_tab_idx<512>();
+// every stage's table order is a permutation of its pairs
 template <int D>
-__device__ __forceinline__ const uint16_t* tab_idx() {
-  if constexpr (D == 256) return kTabIdx256.v;
-  else return kTabIdx512.v;
+constexpr bool table_order_is_permutation() {
+  bool seen[WCfg<D>::TBL] = {};
+  for (int s = 0; s < WCfg<D>::L; ++s)
+    for (int k = 0; k < WCfg<D>::P; ++k) {
+      const int p = table_pair<D>(s, k);
+      if (p < 0 || p >= WCfg<D>::P || seen[s * WCfg<D>::P + p]) return false;
+      seen[s * WCfg<D>::P + p] = true;
+    }
+  return true;
+}
+static_assert(table_order_is_permutation<256>() && table_order_is_permutation<512>(),
+              "table positions invert the table order");
+__device__ constexpr TabPos<256> kTabPos256 = make_tab_pos<256>();
+__device__ constexpr TabPos<512> kTabPos512 = make_tab_pos<512>();
+template <int D>
+__device__ __forceinline__ const uint16_t* tab_pos() {
+  if constexpr (D == 256) return kTabPos256.v;
+  else return kTabPos512.v;
 }
 
 // Coefficients of one side of one expert from its LDS table.
@@ -374,36 +390,41 @@ __device__ __forceinline__ void butterfly_rows(float (&v)[kRowsW][D / 64], const
   }
 }
 
-// The tables of the tile's first and last experts hold 2 * L stage blocks of
-// D/2 float2 positions, cut into pieces of 64; wave w fills pieces w, w + 8,
-// .. (NTB of them), lane l position 64 * (piece within the block) + l, so the
-// stage of a piece is uniform over the wave and the LDS writes are
-// consecutive; the angles are gathered in the table's order.
+// The tables of the tile's first and last experts hold L stage blocks of
+// D/2 pairs each; cut into chunks of four consecutive pairs of one stage,
+// CPE chunks per expert, the two experts' 2 * CPE chunks are dealt to the
+// threads in turn: chunk c = tid + kThreadsW * i is thread tid's i-th, so a
+// wave reads 64 consecutive chunks (1 KiB of angles) at once.
 template <int D>
 struct TableJob {
-  static constexpr int PPB = WCfg<D>::P / kWave;          // pieces per block
-  static constexpr int NQ = 2 * WCfg<D>::L * PPB;         // pieces
-  static constexpr int NTB = NQ / kWavesW;                // entries per thread
-  static_assert(NQ % kWavesW == 0, "pieces must split over the waves");
-  static_assert(NTB <= WCfg<D>::NSTEP, "one output-side entry per K-step");
-  // entry i of this thread: expert (0 first, 1 last), stage, position k
-  __device__ static __forceinline__ void at(int i, int wave, int lane, int& ex, int& s, int& k) {
-    const int q = wave + kWavesW * i;
-    const int blk = q / PPB;
-    ex = blk / WCfg<D>::L;
-    s = blk % WCfg<D>::L;
-    k = kWave * (q % PPB) + lane;
+  static constexpr int QPS = WCfg<D>::P / 4;                          // chunks per stage
+  static constexpr int CPE = WCfg<D>::TBL / 4;                        // chunks per expert
+  static constexpr int NTB = (2 * CPE + kThreadsW - 1) / kThreadsW;  // chunks per thread
+  static_assert(NTB <= WCfg<D>::NSTEP, "one output-side chunk per K-step");
+  // chunk i of thread tid: expert (0 first, 1 last), stage, first pair;
+  // false past the last chunk
+  __device__ static __forceinline__ bool at(int i, int tid, int& ex, int& s, int& p0) {
+    const int c = tid + kThreadsW * i;
+    ex = c / CPE;
+    s = (c % CPE) / QPS;
+    p0 = 4 * (c % QPS);
+    return c < 2 * CPE;
   }
 };
 
-// Entry i of this thread's share of one side's tables (see TableJob), from
-// its angle; the last expert's entries only when it differs from the first.
+// Chunk i of this thread's share of one side's tables (see TableJob), from
+// its four angles and the four pairs' table positions; the last expert's
+// chunks only when it differs from the first.
 template <int D>
-__device__ __forceinline__ void write_table_entry(int i, float ang, float2* tab, bool two,
-                                                  int wave, int lane) {
-  int ex, s, k;
-  TableJob<D>::at(i, wave, lane, ex, s, k);
-  if (ex == 0 || two) tab[ex * WCfg<D>::TBL + s * WCfg<D>::P + k] = tile_cos_sin(ang);
+__device__ __forceinline__ void write_table_chunk(int i, float4 ang, uint2 pos, float2* tab,
+                                                  bool two, int tid) {
+  int ex, s, p0;
+  if (!TableJob<D>::at(i, tid, ex, s, p0) || (ex == 1 && !two)) return;
+  float2* t = tab + ex * WCfg<D>::TBL + s * WCfg<D>::P;
+  t[pos.x & 0xFFFFu] = tile_cos_sin(ang.x);
+  t[pos.x >> 16] = tile_cos_sin(ang.y);
+  t[pos.y & 0xFFFFu] = tile_cos_sin(ang.z);
+  t[pos.y >> 16] = tile_cos_sin(ang.w);
 }
 
 // ROUTE: the kernel routes its own rows (reads the ids, writes the routing
@@ -464,16 +485,16 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
     for (int j = 0; j < kIdsW; ++j) id[j] = j < nv ? a.ids[i0 + j] : 0;
   }
 
-  // Angle indices of this thread's table entries (they do not depend on
+  // Table positions of this thread's table chunks (they do not depend on
   // the routing).
   constexpr int NTB = TableJob<D>::NTB;
-  const int wv = __builtin_amdgcn_readfirstlane(wave);  // uniform: scalar table indexing
-  int tix[NTB];
+  uint2 tpos[NTB];
 #pragma unroll
   for (int i = 0; i < NTB; ++i) {
-    int ex, s, k;
-    TableJob<D>::at(i, wv, lane, ex, s, k);
-    tix[i] = tab_idx<D>()[s * C::P + k];
+    int ex, s, p0;
+    tpos[i] = make_uint2(0u, 0u);
+    if (TableJob<D>::at(i, tid, ex, s, p0))
+      tpos[i] = *reinterpret_cast<const uint2*>(tab_pos<D>() + s * C::P + p0);
   }
   // This wave's packed substrate rows (o = wave * WN ..), copied to LDS by
   // the global->LDS path in 1 KiB pieces: lane l of piece i fills LDS chunk
@@ -580,16 +601,15 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
   const int e_first = misc[1], e_last = misc[2];
   // Both sides' angles of the two tables, in flight during the ranking.
   const bool two = e_last != e_first;                    // a second table is needed
-  float th[NTB], ph[NTB];
+  float4 th[NTB], ph[NTB];
 #pragma unroll
   for (int i = 0; i < NTB; ++i) {
-    int ex, s, k;
-    TableJob<D>::at(i, wv, lane, ex, s, k);
-    th[i] = ph[i] = 0.f;
-    if (ex == 0 || two) {
-      const size_t src = (size_t)(ex ? e_last : e_first) * C::TBL + tix[i];
-      th[i] = a.theta[src];
-      if constexpr (kOut) ph[i] = a.phi[src];
+    int ex, s, p0;
+    th[i] = ph[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (TableJob<D>::at(i, tid, ex, s, p0) && (ex == 0 || two)) {
+      const size_t src = (size_t)(ex ? e_last : e_first) * C::TBL + s * C::P + p0;
+      th[i] = *reinterpret_cast<const float4*>(a.theta + src);
+      if constexpr (kOut) ph[i] = *reinterpret_cast<const float4*>(a.phi + src);
     }
   }
   // Stable ranks of the tile's experts: an id's slot is its expert's offset,
@@ -651,7 +671,7 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
   // Input-side tables of the tile's first and last experts (the output
   // side's are computed during the product).
 #pragma unroll
-  for (int i = 0; i < NTB; ++i) write_table_entry<D>(i, th[i], tin, two, wv, lane);
+  for (int i = 0; i < NTB; ++i) write_table_chunk<D>(i, th[i], tpos[i], tin, two, tid);
   lds_barrier();
 
   // ---- butterfly-in, Z rows into the A tile --------------------------------
@@ -731,10 +751,10 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
         acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b, acc[j], 0, 0, 0);
       }
     }
-    // One entry per K-step: VALU work beside the matrix cores (no one reads
+    // One chunk per K-step: VALU work beside the matrix cores (no one reads
     // this region before the barrier that follows the H rows).
     if constexpr (kOut) {
-      if (ks < NTB) write_table_entry<D>(ks, ph[ks], tout, two, wv, lane);
+      if (ks < NTB) write_table_chunk<D>(ks, ph[ks], tpos[ks], tout, two, tid);
     }
   }
   lds_barrier();  // every wave is done with Z and P, which the H rows reuse
