@@ -1,11 +1,13 @@
 // Fused ButterflyMoE expert forward with register-resident butterflies, for
-// bf16 d = 256 and 512 when the kernel routes its own rows (M <= 8192 routed
-// rows, N <= 512 experts). ButterflyMoE gist.science summary, §2.3: rotate
+// bf16 d = 256 and 512, routing its own rows (M <= 8192 routed rows, N <= 512
+// experts at d = 256, N <= 256 at d = 512) or reading the preparation
+// kernel's routing. ButterflyMoE gist.science summary, §2.3: rotate
 // each routed token by B(theta_e)^T, multiply by the one ternary W_base,
 // rotate by B(phi_e); §2.1 for the butterfly structure.
 //
-// One workgroup (8 waves) per 32 consecutive sorted slots. Each wave owns four
-// of those rows outright: a row of d values lives in one wave, d/64 values per
+// One workgroup per 32 consecutive sorted slots: 16 waves of two rows each at
+// d = 512, 8 waves of four rows at d = 256. Each wave owns its rows
+// outright: a row of d values lives in one wave, d/64 values per
 // lane (lane l holds elements VPL*c .. VPL*c + VPL-1 of row position
 // c = row_lane(l)), so every butterfly stage is a wave-local operation and no
 // barrier separates stages:
@@ -36,13 +38,21 @@
 namespace bmoe {
 namespace {
 
-constexpr int kThreadsW = 512;
-constexpr int kWavesW = kThreadsW / kWave;
 constexpr int kSlots = 32;                 // sorted slots per workgroup
-constexpr int kRowsW = kSlots / kWavesW;   // rows per wave
-constexpr int kIdsW = 16;                  // ids per thread: M <= 8192
-constexpr int kMaxMW = kIdsW * kThreadsW;
-constexpr int kMaxNW = 512;
+constexpr int kMaxMW = 8192;               // routed rows the routing launch takes
+
+// Workgroup shape: 16 waves of two rows at d = 512 (four waves per SIMD, so
+// one wave's DPP and LDS waits are covered by the others' work), 8 waves of
+// four rows at d = 256 (each wave's product columns must fill 32-wide MFMA
+// tiles).
+template <int D>
+struct WG {
+  static constexpr int THREADS = D == 512 ? 1024 : 512;
+  static constexpr int WAVES = THREADS / kWave;
+  static constexpr int ROWS = kSlots / WAVES;       // rows per wave
+  static constexpr int IDS = kMaxMW / THREADS;      // ids per thread
+  static constexpr int MAX_N = D == 512 ? 256 : 512;  // experts the routing launch takes
+};
 
 template <int D>
 struct WCfg {
@@ -59,11 +69,11 @@ struct WCfg {
   // c ^ hswz(r).
   static constexpr int H_HALF_BYTES = (kSlots / 2) * D * 4;
   static __device__ __forceinline__ int hswz(int r) { return 32 * ((r >> 2) & 1); }
-  static constexpr int WN = D / kWavesW;                       // product columns per wave
+  static constexpr int WN = D / WG<D>::WAVES;                  // product columns per wave
   static constexpr int FN = WN / 32;
   static constexpr int KS = 32;
   static constexpr int NSTEP = D / KS;
-  static constexpr int ROUTE_BYTES = (kWavesW * kMaxNW + kMaxNW + 16) * 4;
+  static constexpr int ROUTE_BYTES = (WG<D>::WAVES * WG<D>::MAX_N + WG<D>::MAX_N + 16) * 4;
   // The packed substrate rows of one wave's output columns, copied to LDS
   // as they lie in memory (WN rows of D/4 bytes), 16-byte chunks permuted
   // within each row (see pw_chunk).
@@ -84,7 +94,7 @@ struct WCfg {
   static constexpr int OFF_TOUT = 0;
   static constexpr int A_BYTES = OFF_TIN + 2 * TAB_BYTES;
   static constexpr int META_BYTES = (3 * kSlots + 8) * 4;
-  static constexpr int P_BYTES = kWavesW * PW_WAVE;
+  static constexpr int P_BYTES = WG<D>::WAVES * PW_WAVE;
   static constexpr int Z_BYTES = kSlots * D * 2;
   static constexpr int LDS_BYTES = A_BYTES + META_BYTES + P_BYTES + Z_BYTES;
   static_assert(P_BYTES >= H_HALF_BYTES && Z_BYTES >= H_HALF_BYTES, "H rows reuse P and Z");
@@ -231,7 +241,7 @@ struct TabSrc {
 template <int D>
 struct TabRowSrc {
   static constexpr bool kPerRow = true;
-  const float4* tab[kRowsW];
+  const float4* tab[WG<D>::ROWS];
   template <int S, int N>
   __device__ __forceinline__ void get(float2 (&c)[N], int lane, int row) const {
     TabSrc<D>::template load<S, N>(tab[row], c, lane);
@@ -353,38 +363,51 @@ __device__ __forceinline__ void butterfly(float (&v)[NR][D / 64], const Src& src
 // wave), else one row at a time. Each pass takes its coefficients from one
 // kind of source, so its stages hold no branches.
 template <int D, bool TR>
-__device__ __forceinline__ void butterfly_rows(float (&v)[kRowsW][D / 64], const int (&e)[kRowsW],
-                                               int e_first, int e_last, const float4* tab_first,
+__device__ __forceinline__ void butterfly_rows(float (&v)[WG<D>::ROWS][D / 64],
+                                               const int (&e)[WG<D>::ROWS], int e_first,
+                                               int e_last, const float4* tab_first,
                                                const float4* tab_last, const float* ang,
                                                int lane) {
   using C = WCfg<D>;
-  constexpr int VPL = C::VPL;
+  constexpr int VPL = C::VPL, NR = WG<D>::ROWS;
   auto table = [&](int ex) -> const float4* {
     return ex == e_first ? tab_first : ex == e_last ? tab_last : nullptr;
   };
-  if (e[0] == e[1] && e[0] == e[2] && e[0] == e[3] && table(e[0])) {
-    butterfly<D, TR, kRowsW>(v, TabSrc<D>{table(e[0])}, lane);
+  bool same = true, tables = true;
+  TabRowSrc<D> rows;
+#pragma unroll
+  for (int q = 0; q < NR; ++q) {
+    same = same && e[q] == e[0];
+    rows.tab[q] = table(e[q]);
+    tables = tables && rows.tab[q] != nullptr;
+  }
+  if (same && tables) {
+    butterfly<D, TR, NR>(v, TabSrc<D>{rows.tab[0]}, lane);
     return;
   }
-  const TabRowSrc<D> rows{{table(e[0]), table(e[1]), table(e[2]), table(e[3])}};
-  if (rows.tab[0] && rows.tab[1] && rows.tab[2] && rows.tab[3]) {
+  if (tables) {
     // rows of the tile's first and last experts: one pass, per-row tables
-    butterfly<D, TR, kRowsW>(v, rows, lane);
+    butterfly<D, TR, NR>(v, rows, lane);
     return;
   }
 #pragma unroll 1
-  for (int q = 0; q < kRowsW; ++q) {
+  for (int q = 0; q < NR; ++q) {
     // row q through selects (q is uniform; no dynamic register indexing)
     float one[1][VPL];
-    const int ex = q == 0 ? e[0] : q == 1 ? e[1] : q == 2 ? e[2] : e[3];
+    int ex = e[0];
 #pragma unroll
-    for (int r = 0; r < VPL; ++r)
-      one[0][r] = q == 0 ? v[0][r] : q == 1 ? v[1][r] : q == 2 ? v[2][r] : v[3][r];
+    for (int i = 1; i < NR; ++i) ex = q == i ? e[i] : ex;
+#pragma unroll
+    for (int r = 0; r < VPL; ++r) {
+      one[0][r] = v[0][r];
+#pragma unroll
+      for (int i = 1; i < NR; ++i) one[0][r] = q == i ? v[i][r] : one[0][r];
+    }
     const float4* tab = table(ex);
     if (tab) butterfly<D, TR, 1>(one, TabSrc<D>{tab}, lane);
     else butterfly<D, TR, 1>(one, AngSrc<D>{ang + (size_t)ex * C::TBL}, lane);
 #pragma unroll
-    for (int i = 0; i < kRowsW; ++i)
+    for (int i = 0; i < NR; ++i)
 #pragma unroll
       for (int r = 0; r < VPL; ++r) v[i][r] = q == i ? one[0][r] : v[i][r];
   }
@@ -393,18 +416,18 @@ __device__ __forceinline__ void butterfly_rows(float (&v)[kRowsW][D / 64], const
 // The tables of the tile's first and last experts hold L stage blocks of
 // D/2 pairs each; cut into chunks of four consecutive pairs of one stage,
 // CPE chunks per expert, the two experts' 2 * CPE chunks are dealt to the
-// threads in turn: chunk c = tid + kThreadsW * i is thread tid's i-th, so a
+// threads in turn: chunk c = tid + THREADS * i is thread tid's i-th, so a
 // wave reads 64 consecutive chunks (1 KiB of angles) at once.
 template <int D>
 struct TableJob {
   static constexpr int QPS = WCfg<D>::P / 4;                          // chunks per stage
   static constexpr int CPE = WCfg<D>::TBL / 4;                        // chunks per expert
-  static constexpr int NTB = (2 * CPE + kThreadsW - 1) / kThreadsW;  // chunks per thread
+  static constexpr int NTB = (2 * CPE + WG<D>::THREADS - 1) / WG<D>::THREADS;  // per thread
   static_assert(NTB <= WCfg<D>::NSTEP, "one output-side chunk per K-step");
   // chunk i of thread tid: expert (0 first, 1 last), stage, first pair;
   // false past the last chunk
   __device__ static __forceinline__ bool at(int i, int tid, int& ex, int& s, int& p0) {
-    const int c = tid + kThreadsW * i;
+    const int c = tid + WG<D>::THREADS * i;
     ex = c / CPE;
     s = (c % CPE) / QPS;
     p0 = 4 * (c % QPS);
@@ -432,11 +455,14 @@ __device__ __forceinline__ void write_table_chunk(int i, float4 ang, uint2 pos, 
 // indices come from the preparation kernel's tables (any M and N). OUT: kU,
 // kZH or both (kZH only after prep; without kU the output side is skipped).
 template <int D, bool ROUTE, int OUT = kU>
-__global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
+__global__ __launch_bounds__(WG<D>::THREADS) void fused_wave_kernel(WaveArgs a) {
   static_assert(!ROUTE || OUT == kU, "a routing launch writes U only");
   constexpr bool kOut = (OUT & kU) != 0;
   using C = WCfg<D>;
+  using G = WG<D>;
   constexpr int VPL = C::VPL;
+  constexpr int kThreadsW = G::THREADS, kWavesW = G::WAVES, kRowsW = G::ROWS, kIdsW = G::IDS;
+  constexpr int kMaxNW = G::MAX_N;
   __shared__ __attribute__((aligned(1024))) char lds[C::A_BYTES];
   __shared__ __attribute__((aligned(16))) int meta[C::META_BYTES / 4];
   __shared__ __attribute__((aligned(1024))) char pst[C::P_BYTES];
@@ -824,7 +850,7 @@ __global__ __launch_bounds__(kThreadsW) void fused_wave_kernel(WaveArgs a) {
 template <int D, bool ROUTE, int OUT = kU>
 hipError_t launch_w(const WaveArgs& a, hipStream_t s, const KernelTiming& t) {
   return launch_kernel(fused_wave_kernel<D, ROUTE, OUT>, dim3((a.M + kSlots - 1) / kSlots),
-                       dim3(kThreadsW), 0, s, t, a);
+                       dim3(WG<D>::THREADS), 0, s, t, a);
 }
 
 }  // namespace
@@ -834,7 +860,8 @@ bool fused_supported(bmoe_dtype dt, int d) {
 }
 
 bool fused_wave_routes(bmoe_dtype dt, int M, int d, int N) {
-  return dt == BMOE_BF16 && (d == 256 || d == 512) && M <= kMaxMW && N <= kMaxNW;
+  return dt == BMOE_BF16 && (d == 256 || d == 512) && M <= kMaxMW &&
+         N <= (d == 512 ? WG<512>::MAX_N : WG<256>::MAX_N);
 }
 
 hipError_t launch_fused_wave(int M, int d, int k, int N, const void* x, const int32_t* ids,

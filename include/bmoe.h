@@ -158,8 +158,9 @@ bmoe_status bmoe_unpack_ternary_b3_timed(const uint8_t* packed3, int d, uint32_t
  * activation type before the product, H stays fp32, and each gate-weighted
  * row is rounded to the activation type before the fp32 sum over j.
  * For bf16 with d = 256 or 512 one kernel does the whole per-row
- * computation (then the combine): with T*k <= 8192 and N <= 512 it routes
- * its rows itself, otherwise it follows a preparation launch that only
+ * computation (then the combine): with T*k <= 8192 and N <= 256 (N <= 512
+ * at d = 256) it routes its rows itself, otherwise it follows a preparation
+ * launch that only
  * routes. It evaluates the rotation coefficients on the hardware sine/cosine
  * unit (at most 4e-7 absolute error for angles up to 1000 in magnitude).
  * Other shapes compute them with sincosf in a preparation launch. Both are

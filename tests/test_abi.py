@@ -130,11 +130,14 @@ def test_forward_launch_table():
     def names(dt, T, d, N, k):
         return [bmoe.bmoe_forward_kernel_name(dt, T, d, N, k, i)
                 for i in range(bmoe.bmoe_forward_kernel_count(dt, T, d, N, k))]
-    # fused d = 512 with routing inside: up to 8192 routed rows and 512 experts
+    # fused with routing inside: up to 8192 routed rows, and 256 experts at
+    # d = 512 or 512 at d = 256
     assert names(bf, 4096, 512, 64, 2) == ["fused_wave_kernel", "combine_kernel"]
-    assert names(bf, 4096, 512, 512, 2) == ["fused_wave_kernel", "combine_kernel"]
+    assert names(bf, 4096, 512, 256, 2) == ["fused_wave_kernel", "combine_kernel"]
+    assert names(bf, 4096, 256, 512, 2) == ["fused_wave_kernel", "combine_kernel"]
     # beyond either limit the prep kernel routes
     assert names(bf, 4097, 512, 64, 2) == ["prep_kernel", "fused_wave_kernel", "combine_kernel"]
+    assert names(bf, 64, 512, 257, 2) == ["prep_kernel", "fused_wave_kernel", "combine_kernel"]
     assert names(bf, 64, 256, 513, 2) == ["prep_kernel", "fused_wave_kernel", "combine_kernel"]
     # split path
     assert names(f32, 64, 512, 8, 2) == ["prep_kernel", "bfly_in_kernel", "gemm_kernel",

@@ -282,8 +282,9 @@ def test_identity_substrate_equal_angles(dtype):
 @pytest.mark.parametrize("d,N,k,T", [(16, 1, 1, 1), (32, 3, 3, 5), (64, 300, 1, 1000),
                                      (1024, 2, 2, 33), (8192, 4, 2, 3),
                                      # the routed fused kernel at its limits:
-                                     # 8192 routed rows, 512 experts
-                                     (256, 64, 2, 4096), (512, 512, 1, 8192),
+                                     # 8192 routed rows; 512 experts at
+                                     # d = 256, 256 at d = 512
+                                     (256, 512, 2, 4096), (512, 256, 1, 8192),
                                      # routed: top-3 and top-4, one expert
                                      (256, 8, 3, 111), (512, 16, 4, 300), (512, 1, 1, 100),
                                      # fused after prep, ragged, more tiles than
@@ -324,11 +325,11 @@ def test_fused_tiles_holding_several_experts(d, tail):
     assert O.max_rel_err(y, ref) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("N", [512, 513])
+@pytest.mark.parametrize("N", [256, 257, 512])
 def test_fused_tiles_of_many_small_experts(N):
-    """600 routed rows over N experts: most tiles hold about 20 experts,
-    nearly all of them middle experts. N = 512 routes inside the fused
-    kernel, N = 513 in the prep kernel."""
+    """600 routed rows over N experts: most tiles hold 13 to 27 experts,
+    nearly all of them middle experts. N = 256 routes inside the fused
+    kernel, N = 257 and 512 in the prep kernel."""
     inp = W.make_inputs("custom", d=512, N=N, k=2, T=300, seed=N, dtype="bf16")
     _announce(f"[many experts] d=512 N={N} T=300")
     dev = to_device(inp)
