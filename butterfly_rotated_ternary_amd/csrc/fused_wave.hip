@@ -71,6 +71,12 @@ struct WCfg {
   static __device__ __forceinline__ int hswz(int r) { return 32 * ((r >> 2) & 1); }
   static constexpr int WN = D / WG<D>::WAVES;                  // product columns per wave
   static constexpr int FN = WN / 32;
+  // The product runs on the first eight waves, 32 rows x PWN columns each
+  // (PFN 32x32 fragments): with sixteen waves, one 32-column fragment per
+  // wave would read every A fragment sixteen times from LDS.
+  static constexpr int PWAVES = WG<D>::WAVES < 8 ? WG<D>::WAVES : 8;
+  static constexpr int PWN = D / PWAVES;
+  static constexpr int PFN = PWN / 32;
   static constexpr int KS = 32;
   static constexpr int NSTEP = D / KS;
   static constexpr int ROUTE_BYTES = (WG<D>::WAVES * WG<D>::MAX_N + WG<D>::MAX_N + 16) * 4;
@@ -744,55 +750,66 @@ __global__ __launch_bounds__(WG<D>::THREADS) void fused_wave_kernel(WaveArgs a) 
     }
   }
 
-  // ---- substrate product: wave w computes all 32 rows x columns
-  // [w * WN, (w + 1) * WN) on v_mfma_f32_32x32x16_bf16.
-  f32x16 acc[C::FN];
-#pragma unroll
-  for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+  // ---- substrate product: product wave w (w < PWAVES) computes all 32 rows
+  // x columns [w * PWN, (w + 1) * PWN) on v_mfma_f32_32x32x16_bf16; the
+  // other waves write their share of the output-side tables meanwhile.
+  f32x16 acc[C::PFN];
   const int ra = lane & 31;
-  // B operand: lane l takes, in K-step ks, word 2 ks + (l >> 5) of W row
-  // o = wave * WN + 32 j + (l & 31) (K values 32 ks + 16 (l >> 5) .. + 15);
-  // the step's two MFMAs take its low and high eight values, and their A
-  // fragments the same K values.
+  if (wave < C::PWAVES) {
 #pragma unroll
-  for (int ks = 0; ks < C::NSTEP; ++ks) {
-    uint32_t pw[C::FN];
+    for (int j = 0; j < C::PFN; ++j)
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const int R = 32 * j + ra, w = 2 * ks + (lane >> 5);
-      pw[j] = *reinterpret_cast<const uint32_t*>(pwl + R * C::ROWB +
-                                                 16 * ((w / 4) ^ C::pw_swz(R)) + 4 * (w % 4));
-    }
+      for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+    // this wave's columns: the substrate rows copied by waves
+    // PFN w .. PFN w + PFN - 1, consecutive in P
+    const char* const pwp = pst + wave * C::PFN * C::PW_WAVE;
+    // B operand: lane l takes, in K-step ks, word 2 ks + (l >> 5) of W row
+    // o = wave * PWN + 32 j + (l & 31) (K values 32 ks + 16 (l >> 5) .. + 15);
+    // the step's two MFMAs take its low and high eight values, and their A
+    // fragments the same K values.
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // K values 32 ks + 16 (lane >> 5) + 8 h .. + 7: 16-byte chunk ca of row ra
-      const int ca = 4 * ks + 2 * (lane >> 5) + h;
-      const bf16x8 av =
-          *reinterpret_cast<const bf16x8*>(zt + ra * (2 * D) + 16 * (ca ^ (ra & 15)));
+    for (int ks = 0; ks < C::NSTEP; ++ks) {
+      uint32_t pw[C::PFN];
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        const bf16x8 b = unpack_frag(pw[j], h);
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b, acc[j], 0, 0, 0);
+      for (int j = 0; j < C::PFN; ++j) {
+        const int R = 32 * j + ra, w = 2 * ks + (lane >> 5);
+        pw[j] = *reinterpret_cast<const uint32_t*>(pwp + R * C::ROWB +
+                                                   16 * ((w / 4) ^ C::pw_swz(R)) + 4 * (w % 4));
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // K values 32 ks + 16 (lane >> 5) + 8 h .. + 7: 16-byte chunk ca of row ra
+        const int ca = 4 * ks + 2 * (lane >> 5) + h;
+        const bf16x8 av =
+            *reinterpret_cast<const bf16x8*>(zt + ra * (2 * D) + 16 * (ca ^ (ra & 15)));
+#pragma unroll
+        for (int j = 0; j < C::PFN; ++j) {
+          const bf16x8 b = unpack_frag(pw[j], h);
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b, acc[j], 0, 0, 0);
+        }
+      }
+      // One chunk per K-step: VALU work beside the matrix cores (no one reads
+      // this region before the barrier that follows the H rows).
+      if constexpr (kOut) {
+        if (ks < NTB) write_table_chunk<D>(ks, ph[ks], tpos[ks], tout, two, tid);
       }
     }
-    // One chunk per K-step: VALU work beside the matrix cores (no one reads
-    // this region before the barrier that follows the H rows).
-    if constexpr (kOut) {
-      if (ks < NTB) write_table_chunk<D>(ks, ph[ks], tpos[ks], tout, two, tid);
-    }
+  } else if constexpr (kOut) {
+#pragma unroll
+    for (int i = 0; i < NTB; ++i) write_table_chunk<D>(i, ph[i], tpos[i], tout, two, tid);
   }
   lds_barrier();  // every wave is done with Z and P, which the H rows reuse
   // alpha * H -> fp32 rows (32x32 block layout: lane l, register r -> row
   // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32).
+  if (wave < C::PWAVES) {
 #pragma unroll
-  for (int j = 0; j < C::FN; ++j) {
-    const int col = wave * C::WN + j * 32 + (lane & 31);
+    for (int j = 0; j < C::PFN; ++j) {
+      const int col = wave * C::PWN + j * 32 + (lane & 31);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      hrow(row)[col ^ C::hswz(row)] = a.alpha * acc[j][r];
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        hrow(row)[col ^ C::hswz(row)] = a.alpha * acc[j][r];
+      }
     }
   }
   lds_barrier();  // the H rows are complete
