@@ -41,10 +41,11 @@ namespace {
 constexpr int kSlots = 32;                 // sorted slots per workgroup
 constexpr int kMaxMW = 8192;               // routed rows the routing launch takes
 
-// Workgroup shape: 16 waves of two rows at d = 512 (four waves per SIMD, so
-// one wave's DPP and LDS waits are covered by the others' work), 8 waves of
-// four rows at d = 256 (each wave's product columns must fill 32-wide MFMA
-// tiles).
+// Workgroup shape: at d = 512, 16 waves of two rows (four waves per SIMD, so
+// one wave's DPP and LDS waits are covered by the others' work); at d = 256,
+// 8 waves of four rows, whose 68 KiB of LDS let two workgroups share a CU
+// when there are more tiles than CUs (16 waves need 85 KiB: measured 4%
+// faster when routing, 20% slower after prep at 1024 tiles).
 template <int D>
 struct WG {
   static constexpr int THREADS = D == 512 ? 1024 : 512;
@@ -69,8 +70,7 @@ struct WCfg {
   // c ^ hswz(r).
   static constexpr int H_HALF_BYTES = (kSlots / 2) * D * 4;
   static __device__ __forceinline__ int hswz(int r) { return 32 * ((r >> 2) & 1); }
-  static constexpr int WN = D / WG<D>::WAVES;                  // product columns per wave
-  static constexpr int FN = WN / 32;
+  static constexpr int WN = D / WG<D>::WAVES;  // substrate rows each wave copies to LDS
   // The product runs on the first eight waves, 32 rows x PWN columns each
   // (PFN 32x32 fragments): with sixteen waves, one 32-column fragment per
   // wave would read every A fragment sixteen times from LDS.
@@ -761,8 +761,9 @@ __global__ __launch_bounds__(WG<D>::THREADS) void fused_wave_kernel(WaveArgs a) 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
     // this wave's columns: the substrate rows copied by waves
-    // PFN w .. PFN w + PFN - 1, consecutive in P
-    const char* const pwp = pst + wave * C::PFN * C::PW_WAVE;
+    // (PWN / WN) w .., consecutive in P; each copy's chunk swizzle is by its
+    // own row (R mod WN)
+    const char* const pwp = pst + wave * C::PWN * C::ROWB;
     // B operand: lane l takes, in K-step ks, word 2 ks + (l >> 5) of W row
     // o = wave * PWN + 32 j + (l & 31) (K values 32 ks + 16 (l >> 5) .. + 15);
     // the step's two MFMAs take its low and high eight values, and their A
@@ -773,8 +774,8 @@ __global__ __launch_bounds__(WG<D>::THREADS) void fused_wave_kernel(WaveArgs a) 
 #pragma unroll
       for (int j = 0; j < C::PFN; ++j) {
         const int R = 32 * j + ra, w = 2 * ks + (lane >> 5);
-        pw[j] = *reinterpret_cast<const uint32_t*>(pwp + R * C::ROWB +
-                                                   16 * ((w / 4) ^ C::pw_swz(R)) + 4 * (w % 4));
+        pw[j] = *reinterpret_cast<const uint32_t*>(
+            pwp + R * C::ROWB + 16 * ((w / 4) ^ C::pw_swz(R % C::WN)) + 4 * (w % 4));
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
