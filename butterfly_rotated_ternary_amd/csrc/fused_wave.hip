@@ -21,7 +21,7 @@
 //     holds a whole pair, the pair is rotated in registers, and a second swap
 //     restores the layout.
 // LDS carries only what must cross waves: the bf16 A tile of the product, the
-// fp32 H rows coming back from the product (each wave's MFMA output is a
+// fp32 H rows coming back from the product (each product wave's MFMA output is a
 // column slice of all 32 rows), the routing scratch and the cos/sin tables of
 // the tile's first and last expert. Rows of any expert strictly between those
 // two take their coefficients straight from the angles.
