@@ -23,6 +23,9 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
     "-Wno-unused-command-line-argument",
+    # the first 16 dwords of kernel arguments arrive in SGPRs at wave launch
+    # instead of through a scalar load (headline step 23.2 -> 22.8 us)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 
